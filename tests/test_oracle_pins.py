@@ -1,0 +1,406 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Which pin covers which oracle function:
+
+* momentum          exact hand values (beta = 0.5), M0 = 0 and beta = 0 special
+                    cases, correctly rounded binary32 from float64 (exact for
+                    one product or sum of binary32 values), a case where a fused
+                    multiply-add would differ.
+* to_bf16 / split   torch's round-to-nearest-even conversion, hand-made ties.
+* newton_schulz /   SVD polar limit (cubic and textbook quintic); the
+  orthogonalise     singular-value closed form U p^k(S) V^T on non-normal
+                    inputs; exact rational brute force (fractions) on 2x2 and
+                    3x3; rank-1 closed form; scaling, transpose and orthogonal
+                    equivariance; zero input; singular-value band per
+                    coefficient set after every step.
+* orient            transpose identity on tall inputs; shapes.
+* scale_factor      closed values.
+* write_back        exact hand values, a bf16 tie.
+* bf16 storage      with the identity in place of rounding it reduces to
+  emulation         `orthogonalise`; ns_steps = 0 and c = 0 branches.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from muon_newton_schulz_02_amd import workloads as wlm
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+CUBIC = (1.5, -0.5, 0.0)
+TEXTBOOK = (15 / 8, -5 / 4, 3 / 8)
+MUON = (3.4445, -4.7750, 2.0315)
+
+
+def scalar_map(coeffs, k, sigma):
+    """p^k applied to singular values, p(s) = a s + b s^3 + c s^5."""
+    a, b, c = coeffs
+    s = np.asarray(sigma, dtype=np.float64)
+    for _ in range(k):
+        s = a * s + b * s ** 3 + c * s ** 5
+    return s
+
+
+def random_orthonormal(rng, n, r):
+    q, _ = np.linalg.qr(rng.standard_normal((n, r)))
+    return q
+
+
+# ---------------------------------------------------------------------------
+# momentum
+# ---------------------------------------------------------------------------
+
+def test_momentum_hand_values():
+    m = np.array([1.0, -2.0, 0.0], np.float32)
+    g = np.array([0.25, 0.5, -3.0], np.float32)
+    m1, u = orc.momentum(m, g, 0.5, True)
+    assert m1.tolist() == [0.75, -0.5, -3.0]
+    assert u.tolist() == [0.25 + 0.375, 0.5 - 0.25, -3.0 - 1.5]
+    m2, u2 = orc.momentum(m, g, 0.5, False)
+    assert m2.tolist() == m1.tolist() and u2.tolist() == m1.tolist()
+    assert m1.dtype == np.float32 and u.dtype == np.float32
+
+
+def test_momentum_special_cases():
+    rng = np.random.default_rng(1)
+    g = rng.standard_normal(1000).astype(np.float32)
+    m1, u = orc.momentum(np.zeros_like(g), g, 0.95, True)
+    assert np.array_equal(m1.view(np.uint32), g.view(np.uint32))
+    m0, u0 = orc.momentum(rng.standard_normal(1000).astype(np.float32), g, 0.0, True)
+    assert np.array_equal(m0, g) and np.array_equal(u0, g)
+
+
+def test_momentum_is_correctly_rounded_binary32():
+    # One product or one sum of binary32 values rounded once to float64 and
+    # then to binary32 is the correctly rounded binary32 result (53 >= 2*24+2).
+    rng = np.random.default_rng(2)
+    m = rng.standard_normal(20000).astype(np.float32) * np.float32(3.0)
+    g = (rng.standard_normal(20000) * 1e-3).astype(np.float32)
+    beta = 0.95
+    b32 = np.float32(beta)
+    bm = (np.float64(b32) * m.astype(np.float64)).astype(np.float32)
+    m_ref = (bm.astype(np.float64) + g.astype(np.float64)).astype(np.float32)
+    bm2 = (np.float64(b32) * m_ref.astype(np.float64)).astype(np.float32)
+    u_ref = (g.astype(np.float64) + bm2.astype(np.float64)).astype(np.float32)
+    m1, u = orc.momentum(m, g, beta, True)
+    assert np.array_equal(m1.view(np.uint32), m_ref.view(np.uint32))
+    assert np.array_equal(u.view(np.uint32), u_ref.view(np.uint32))
+    # a fused multiply-add (single rounding of b*m + g) differs somewhere
+    fused = (np.float64(b32) * m.astype(np.float64) + g.astype(np.float64)).astype(np.float32)
+    assert not np.array_equal(fused, m1)
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding
+# ---------------------------------------------------------------------------
+
+def test_bf16_matches_torch_rne():
+    rng = np.random.default_rng(3)
+    x = np.concatenate([
+        rng.standard_normal(5000).astype(np.float32),
+        (rng.standard_normal(1000) * 1e-39).astype(np.float32),   # subnormals
+        np.array([np.inf, -np.inf, 3.4e38, -3.4e38, 0.0, -0.0, 1.0, 65504.0], np.float32),
+    ])
+    # exact ties: bit 15 set, bits 0..14 clear
+    ties = (rng.integers(0x3F000000, 0x40000000, 2000, dtype=np.uint32) & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    x = np.concatenate([x, ties.view(np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    got = orc.to_bf16(x)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert np.isnan(orc.to_bf16(np.array([np.nan], np.float32)))[0]
+    # hand ties: 1 + 2^-8 is halfway between 1 and 1 + 2^-7 -> even (1.0);
+    # 1 + 3*2^-8 is halfway between 1 + 2^-7 and 1 + 2^-6 -> even (1 + 2^-6)
+    assert orc.to_bf16(np.float32(1 + 2 ** -8)) == 1.0
+    assert orc.to_bf16(np.float32(1 + 3 * 2 ** -8)) == np.float32(1 + 2 ** -6)
+
+
+def test_split_bf16x2_represents_value():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(10000).astype(np.float32)
+    hi, lo = orc.split_bf16x2(x)
+    assert np.array_equal(orc.to_bf16(hi), hi) and np.array_equal(orc.to_bf16(lo), lo)
+    err = np.abs(hi.astype(np.float64) + lo - x) / np.abs(x)
+    assert err.max() < 2.0 ** -16
+
+
+# ---------------------------------------------------------------------------
+# Newton-Schulz: limits, closed forms, exact cases, invariants, bands
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(64, 64), (48, 80), (80, 48), (1, 17), (33, 1)])
+@pytest.mark.parametrize("coeffs,k", [(CUBIC, 60), (TEXTBOOK, 40)])
+def test_polar_limit(shape, coeffs, k):
+    rng = np.random.default_rng(10 + shape[0])
+    g = rng.standard_normal(shape)
+    o = orc.orthogonalise(g, coeffs, k)
+    ref = orc.polar_factor(g)
+    assert o.shape == g.shape
+    assert np.max(np.abs(o - ref)) < 1e-6
+
+
+@pytest.mark.parametrize("shape", [(40, 40), (24, 56), (56, 24)])
+@pytest.mark.parametrize("coeffs", [CUBIC, TEXTBOOK, MUON, (2.0, -1.5, 0.5)])
+def test_spectral_closed_form(shape, coeffs):
+    rng = np.random.default_rng(20 + shape[1])
+    rows, cols = shape
+    r = min(shape)
+    uu = random_orthonormal(rng, rows, r)
+    vv = random_orthonormal(rng, cols, r)
+    s = rng.uniform(0.05, 1.0, r) * np.arange(1, r + 1) ** -0.5
+    g = (uu * s) @ vv.T
+    k = 5
+    sig0 = s / (np.linalg.norm(s) + orc.EPS)
+    ref = (uu * scalar_map(coeffs, k, sig0)) @ vv.T
+    o = orc.orthogonalise(g, coeffs, k)
+    assert orc.rel_frobenius(o, ref) < 1e-10
+
+
+def _exact_scalar_map(coeffs, k, sigma):
+    a, b, c = (Fraction(str(v)) if not isinstance(v, Fraction) else v for v in coeffs)
+    s = Fraction(sigma)
+    for _ in range(k):
+        s = a * s + b * s ** 3 + c * s ** 5
+    return s
+
+
+def _fmat(rows):
+    return [[Fraction(v) for v in r] for r in rows]
+
+
+def _fmul(x, y):
+    return [[sum(x[i][t] * y[t][j] for t in range(len(y))) for j in range(len(y[0]))]
+            for i in range(len(x))]
+
+
+def _ftr(x):
+    return [list(r) for r in zip(*x)]
+
+
+def _exact_ns(x, coeffs, k):
+    """Brute-force matrix Newton-Schulz in exact rationals."""
+    a, b, c = (Fraction(str(v)) for v in coeffs)
+    n = len(x)
+    for _ in range(k):
+        gram = _fmul(x, _ftr(x))
+        gg = _fmul(gram, gram)
+        poly = [[b * gram[i][j] + c * gg[i][j] for j in range(n)] for i in range(n)]
+        px = _fmul(poly, x)
+        x = [[a * x[i][j] + px[i][j] for j in range(len(x[0]))] for i in range(n)]
+    return x
+
+
+def _as_np(x):
+    return np.array([[float(v) for v in r] for r in x])
+
+
+@pytest.mark.parametrize("coeffs", [CUBIC, MUON])
+def test_exact_rational_2x2(coeffs):
+    # G = R diag(3, 4) with the rational rotation R = [[3/5, -4/5], [4/5, 3/5]]:
+    # singular values 3 and 4, Frobenius norm exactly 5.
+    r = _fmat([[Fraction(3, 5), Fraction(-4, 5)], [Fraction(4, 5), Fraction(3, 5)]])
+    g = _fmul(r, _fmat([[3, 0], [0, 4]]))
+    k = 5
+    d = _fmat([[_exact_scalar_map(coeffs, k, Fraction(3, 5)), 0],
+               [0, _exact_scalar_map(coeffs, k, Fraction(4, 5))]])
+    expect = _as_np(_fmul(r, d))
+    o = orc.orthogonalise(_as_np(g), coeffs, k, eps=0.0)
+    assert np.max(np.abs(o - expect)) < 1e-13
+    # a non-normal rational matrix with Frobenius norm 5, by exact brute force
+    m = _fmat([[2, 1], [-2, 4]])
+    x0 = [[v / 5 for v in row] for row in m]
+    expect2 = _as_np(_exact_ns(x0, coeffs, k))
+    o2 = orc.orthogonalise(_as_np(m), coeffs, k, eps=0.0)
+    assert np.max(np.abs(o2 - expect2)) < 1e-13
+
+
+@pytest.mark.parametrize("coeffs", [CUBIC, MUON, TEXTBOOK])
+def test_exact_rational_3x3(coeffs):
+    q = _fmat([[Fraction(1, 3), Fraction(2, 3), Fraction(2, 3)],
+               [Fraction(2, 3), Fraction(1, 3), Fraction(-2, 3)],
+               [Fraction(2, 3), Fraction(-2, 3), Fraction(1, 3)]])
+    p = _fmat([[Fraction(2, 7), Fraction(3, 7), Fraction(6, 7)],
+               [Fraction(3, 7), Fraction(-6, 7), Fraction(2, 7)],
+               [Fraction(6, 7), Fraction(2, 7), Fraction(-3, 7)]])
+    g = _fmul(_fmul(q, _fmat([[2, 0, 0], [0, 3, 0], [0, 0, 6]])), _ftr(p))
+    k = 5
+    d = [[Fraction(0)] * 3 for _ in range(3)]
+    for i, s in enumerate((2, 3, 6)):
+        d[i][i] = _exact_scalar_map(coeffs, k, Fraction(s, 7))
+    expect = _as_np(_fmul(_fmul(q, d), _ftr(p)))
+    o = orc.orthogonalise(_as_np(g), coeffs, k, eps=0.0)
+    assert np.max(np.abs(o - expect)) < 1e-13
+    # brute force on a non-normal 3x3 (norm^2 = 49)
+    m = _fmat([[2, 3, 0], [0, 6, 0], [0, 0, 0]])
+    m[2][2] = Fraction(0)
+    x0 = [[v / 7 for v in row] for row in m]
+    expect2 = _as_np(_exact_ns(x0, coeffs, k))
+    o2 = orc.orthogonalise(_as_np(m), coeffs, k, eps=0.0)
+    assert np.max(np.abs(o2 - expect2)) < 1e-13
+
+
+@pytest.mark.parametrize("coeffs", [CUBIC, MUON])
+def test_rank_one(coeffs):
+    rng = np.random.default_rng(5)
+    u = rng.standard_normal(30)
+    v = rng.standard_normal(50)
+    g = np.outer(u, v)
+    k = 5
+    nrm = np.linalg.norm(u) * np.linalg.norm(v)
+    sig = nrm / (nrm + orc.EPS)
+    ref = scalar_map(coeffs, k, sig) * np.outer(u / np.linalg.norm(u), v / np.linalg.norm(v))
+    assert orc.rel_frobenius(orc.orthogonalise(g, coeffs, k), ref) < 1e-12
+
+
+def test_invariants():
+    rng = np.random.default_rng(6)
+    g = rng.standard_normal((37, 53))
+    k = 5
+    o = orc.orthogonalise(g, MUON, k)
+    # scale invariance (up to eps)
+    assert orc.rel_frobenius(orc.orthogonalise(3.0 * g, MUON, k), o) < 1e-6
+    # transpose
+    assert np.max(np.abs(orc.orthogonalise(g.T, MUON, k) - o.T)) < 1e-13
+    sq = rng.standard_normal((41, 41))
+    assert orc.rel_frobenius(orc.orthogonalise(sq.T, MUON, k), orc.orthogonalise(sq, MUON, k).T) < 1e-10
+    # orthogonal equivariance
+    p = random_orthonormal(rng, 37, 37)
+    q = random_orthonormal(rng, 53, 53)
+    assert orc.rel_frobenius(orc.orthogonalise(p @ g @ q, MUON, k), p @ o @ q) < 1e-10
+    # zero input
+    z = orc.orthogonalise(np.zeros((8, 12)), MUON, k)
+    assert np.all(z == 0.0)
+
+
+def _band(coeffs, k, lo_in):
+    grid = np.concatenate([np.geomspace(lo_in, 1.0, 20001), np.linspace(lo_in, 1.0, 20001)])
+    vals = scalar_map(coeffs, k, grid)
+    return float(vals.min()), float(vals.max())
+
+
+@pytest.mark.parametrize("coeffs", [CUBIC, TEXTBOOK, MUON])
+def test_singular_value_band_each_step(coeffs):
+    rng = np.random.default_rng(7)
+    n, r = 48, 32
+    uu = random_orthonormal(rng, n, r)
+    vv = random_orthonormal(rng, 64, r)
+    s = rng.uniform(0.1, 1.0, r)
+    g = (uu * s) @ vv.T
+    sig_in_min = float((s / np.linalg.norm(s)).min())
+    x0 = orc.normalise(g)
+    for k in range(1, 6):
+        xk = orc.newton_schulz(x0, coeffs, k)
+        sv = np.linalg.svd(xk, compute_uv=False)[:r]
+        lo, hi = _band(coeffs, k, sig_in_min * 0.999)
+        assert sv.min() >= lo - 1e-9 and sv.max() <= hi + 1e-9
+    if coeffs == MUON:
+        lo5, hi5 = _band(MUON, 5, 1e-2)
+        assert abs(lo5 - 0.6818) < 1e-3 and abs(hi5 - 1.1344) < 1e-3
+        # the largest value the quintic reaches on [0, 1]
+        assert abs(_band(MUON, 1, 1e-6)[1] - 1.2024) < 1e-4
+    else:
+        # monotone maps with fixed point 1: the band is [p^5(min), 1]
+        lo5, hi5 = _band(coeffs, 5, sig_in_min)
+        assert hi5 <= 1.0 + 1e-12
+
+
+def test_orientation_shapes():
+    x = np.zeros((7, 3))
+    w, tr = orc.orient(x)
+    assert w.shape == (3, 7) and tr
+    w, tr = orc.orient(np.zeros((3, 7)))
+    assert w.shape == (3, 7) and not tr
+    w, tr = orc.orient(np.zeros((5, 5)))
+    assert not tr
+
+
+def test_ns_zero_steps_is_normalised_input():
+    rng = np.random.default_rng(8)
+    g = rng.standard_normal((9, 4))
+    o = orc.orthogonalise(g, MUON, 0)
+    assert orc.rel_frobenius(o, g / (np.linalg.norm(g) + orc.EPS)) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# scale rule and write-back
+# ---------------------------------------------------------------------------
+
+def test_scale_rules():
+    assert orc.scale_factor(orc.SCALE_NONE, 6144, 1536) == 1.0
+    assert orc.scale_factor(orc.SCALE_SQRT_ASPECT, 6144, 1536) == 2.0
+    assert orc.scale_factor(orc.SCALE_SQRT_ASPECT, 1536, 6144) == 1.0
+    assert orc.scale_factor(orc.SCALE_RMS_MATCH, 1536, 6144) == pytest.approx(0.2 * math.sqrt(6144))
+    with pytest.raises(ValueError):
+        orc.scale_factor(9, 1, 1)
+
+
+def test_write_back_hand_values():
+    w = np.array([1.0, 0.5], np.float32)
+    o = np.array([0.5, -1.0])
+    assert orc.write_back(w, o, 0.5, 1.0, False).tolist() == [0.75, 1.0]
+    # 1 - 2^-9 lies halfway between the bf16 neighbours 1 - 2^-8 and 1: ties to even -> 1
+    assert orc.write_back(np.float32([1.0]), np.array([2.0 ** -9]), 1.0, 1.0, True)[0] == 1.0
+    # without bf16 rounding the binary32 value is kept
+    assert orc.write_back(np.float32([1.0]), np.array([2.0 ** -9]), 1.0, 1.0, False)[0] == np.float32(1 - 2 ** -9)
+    # t = fl32(lr * s): lr * s rounded once
+    w2 = orc.write_back(np.float32([0.0]), np.array([1.0]), 0.1, 3.0, False)
+    assert w2[0] == -np.float32(0.1 * 3.0)
+
+
+def test_muon_step_zero_gradient_leaves_weight():
+    w = np.float32(np.arange(12).reshape(3, 4))
+    r = orc.muon_step(w, np.zeros((3, 4), np.float32), np.zeros((3, 4), np.float32), lr=0.02,
+                      beta=0.95, nesterov=True, coeffs=MUON, steps=5)
+    assert np.array_equal(r.w, w) and np.all(r.m == 0) and np.all(r.o == 0)
+
+
+# ---------------------------------------------------------------------------
+# bf16 storage emulation
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("coeffs", [MUON, CUBIC])
+@pytest.mark.parametrize("shape", [(20, 33), (33, 20), (16, 16)])
+def test_bf16_emulation_reduces_to_definition(coeffs, shape):
+    rng = np.random.default_rng(9)
+    u = rng.standard_normal(shape).astype(np.float32)
+    ident = lambda v: np.asarray(v, dtype=np.float64)  # noqa: E731
+    for k in (0, 1, 5):
+        a = orc.orthogonalise_bf16_storage(u, coeffs, k, rnd=ident)
+        b = orc.orthogonalise(u, coeffs, k)
+        assert orc.rel_frobenius(a, b) < 1e-12
+    # with rounding the error is the bf16 storage error, not more
+    e = orc.rel_frobenius(orc.orthogonalise_bf16_storage(u, coeffs, 5), orc.orthogonalise(u, coeffs, 5))
+    assert 1e-5 < e < 5e-2
+
+
+# ---------------------------------------------------------------------------
+# the pages' shapes
+# ---------------------------------------------------------------------------
+
+def test_d24_stack_matches_page_counts():
+    gold = json.load(open(os.path.join(GOLDEN, "d24_shapes.json")))
+    wl = wlm.workload("d24_bf16")
+    assert len(wl.specs) == 6 * gold["layers"] == 144
+    assert {(s.rows, s.cols) for s in wl.specs} == {(1536, 1536), (1536, 6144), (6144, 1536)}
+    assert gold["width"] // gold["heads"] == 128
+    assert gold["lm_head"] == gold["vocab"] * gold["width"]
+    n = wl.elements
+    assert n == 679_477_248
+    # the page's transformer_matrices figure holds 192 more parameters per
+    # layer than the six projections; those are not 2-D projection weights
+    assert gold["transformer_matrices"] - n == 24 * 192
+
+
+def test_lm38_stack_matches_page_heads():
+    gold = json.load(open(os.path.join(GOLDEN, "lm3p8b_heads.json")))
+    wl = wlm.workload("lm3p8b_bf16")
+    head_dim = 128
+    q = gold["query_heads"] * head_dim
+    kv = gold["kv_heads"] * head_dim
+    assert {(s.rows, s.cols) for s in wl.specs} == {(q, q), (q, kv), (q, 4 * q), (4 * q, q)}
+    assert wl.elements < gold["total_params_billion"] * 1e9
