@@ -1,0 +1,228 @@
+"""Benchmark of the Muon step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload d24_bf16]
+                    [--no-cpu-baseline] [--quiet-kernels]
+
+A step is one muon_step_batched call over every matrix of the workload
+(momentum, norm, Newton-Schulz, write-back), with weights, gradients and
+momenta resident in HBM before the timed region.  Prints one JSON line.
+
+The roofline object is for the kernel class with the largest share of the
+timed region; per-launch durations come from HIP events the library
+records around each launch on the launch stream (muon_timing_*).
+The cpu_baseline is the CPU oracle timed on a bounded sample of the same
+workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3      # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+METRIC = "Muon steps/sec on d24-like stack; NS TFLOP/s and % bf16 MFMA peak"
+
+WORKLOAD_TEXT = {
+    "d24_bf16": "d24-like stack: 24 layers x {Q,K,V,O 1536x1536, up 1536x6144, down 6144x1536} = 144 bf16 "
+                "matrices, rank-16 + N(0,1) gradients, 5 quintic NS steps, bf16 MFMA",
+    "lm3p8b_bf16": "3.8B-like stack: 32 layers x {Q,O 3072x3072, K,V 3072x1024, up 3072x12288, "
+                   "down 12288x3072} = 192 bf16 matrices, N(0,1) gradients, 5 quintic NS steps",
+    "gpt2s_attn768_bf16": "12 x 768x768 bf16, 5 quintic NS steps",
+    "single256_f32": "1 x 256x256 f32, 5 cubic NS steps, f32 MFMA",
+    "stress_mixed_bf16": "64 mixed-aspect bf16 matrices from {512..8192}^2, 10 quintic NS steps, split-bf16",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="d24_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=2, help="layers in the oracle's sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU layout is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from muon_newton_schulz_02_amd import binding as mb
+    from muon_newton_schulz_02_amd import workloads as wlm
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    wl = wlm.workload(args.workload)
+    n = len(wl.specs)
+    print(f"[bench] generating {args.workload}: {n} matrices, {wl.elements} elements", file=sys.stderr,
+          flush=True)
+    ws, ms, gs = [], [], []
+    for i in range(n):
+        w, m = wlm.initial_state(wl, i, device=dev)
+        ws.append(w)
+        ms.append(m)
+        gs.append(wlm.gradient(wl, i, 0, device=dev))
+    torch.cuda.synchronize()
+    # keep host copies of the oracle's sample before the weights move
+    sample_idx = []
+    if not args.no_cpu_baseline:
+        per_layer = 6 if args.workload in ("d24_bf16", "lm3p8b_bf16") else 1
+        sample_idx = list(range(min(n, per_layer * args.cpu_layers)))
+    sample = [(ws[i].float().cpu().numpy(), gs[i].float().cpu().numpy(), ms[i].cpu().numpy())
+              for i in sample_idx]
+
+    sargs = mb.StepArgs(ws, gs, ms, precision=wl.precision)
+    kw = dict(lr=float(np.float32(wl.lr)), beta=wl.beta, nesterov=int(wl.nesterov), ns_coeffs=wl.coeffs,
+              ns_steps=wl.ns_steps, scale_rule=wl.scale_rule)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        mb.muon_step_batched(sargs, **kw, stream=stream)
+    torch.cuda.synchronize()
+
+    mb.muon_timing_enable(True)
+    mb.muon_timing_read()  # clear
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        mb.muon_step_batched(sargs, **kw, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = mb.muon_timing_read()
+    mb.muon_timing_enable(False)
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (event), wall {wall / args.steps * 1e3:.3f} ms",
+          file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------ accounting
+    k = wl.ns_steps
+    c_nz = wl.coeffs[2] != 0.0
+    nominal = 0.0
+    alg = {"gram": 0.0, "poly": 0.0, "combine": 0.0}
+    for s in wl.specs:
+        m_, n_ = min(s.rows, s.cols), max(s.rows, s.cols)
+        nominal += (4.0 * m_ * m_ * n_ + (2.0 * m_ ** 3 if c_nz else 0.0)) * k
+        alg["gram"] += float(m_) * (m_ + 1) * n_ * k          # unique entries of X X^T
+        alg["poly"] += (float(m_) * (m_ + 1) * m_ * k) if c_nz else 0.0
+        alg["combine"] += 2.0 * m_ * m_ * n_ * k
+    elems = wl.elements
+    gbytes = 2 if wl.grad_dtype == torch.bfloat16 else 4
+    pbytes = 2 if wl.param_dtype == torch.bfloat16 else 4
+    # momentum kernel: read g and M, write M, write U once (algorithmic)
+    alg_bytes_mom = elems * (gbytes + 4 + 4 + 2)
+    peak_mfma = PEAK_F32_TFLOPS if wl.precision == mb.NS_F32 else PEAK_BF16_TFLOPS
+
+    kernels = {}
+    steps = args.steps
+    for name, (tot_ms, launches) in kern.items():
+        if launches == 0:
+            continue
+        avg_ms = tot_ms / launches
+        entry = {"launches_per_step": launches / steps, "avg_ms": round(avg_ms, 5),
+                 "share": round(tot_ms / ms_total, 4)}
+        if name in alg:
+            flops_launch = alg[name] / k
+            tf = flops_launch / (avg_ms * 1e-3) / 1e12
+            entry.update({"bound": "mfma", "tflops": round(tf, 2), "frac": round(tf / peak_mfma, 4)})
+        elif name == "momentum":
+            gbs = alg_bytes_mom / (avg_ms * 1e-3) / 1e9
+            entry.update({"bound": "hbm", "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)})
+        kernels[name] = entry
+    dom = max(kernels, key=lambda x: kernels[x]["share"])
+    d = kernels[dom]
+    if d.get("bound") == "mfma":
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": d["tflops"], "peak": peak_mfma,
+                    "unit": "TFLOP/s", "frac": d["frac"], "traffic": None}
+    else:
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": d.get("gbs"), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": d.get("frac"), "traffic": None}
+    ns_ms = sum(kern[x][0] for x in ("gram", "poly", "combine")) / steps
+    ns_exec = sum(alg.values())
+    ns_chain = {"nominal_tflop_per_step": round(nominal / 1e12, 4),
+                "ms_per_step": round(ns_ms, 4),
+                "nominal_tflops": round(nominal / (ns_ms * 1e-3) / 1e12, 2),
+                "nominal_frac": round(nominal / (ns_ms * 1e-3) / 1e12 / peak_mfma, 4),
+                "algorithmic_tflops": round(ns_exec / (ns_ms * 1e-3) / 1e12, 2),
+                "algorithmic_frac": round(ns_exec / (ns_ms * 1e-3) / 1e12 / peak_mfma, 4)}
+
+    # ------------------------------------------------------------ CPU oracle
+    cpu = None
+    if sample:
+        cpu = cpu_baseline(wl, sample, sample_idx, kw, n)
+
+    out = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_step, 4),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.precision == mb.NS_BF16 else ("f32" if wl.precision == mb.NS_F32 else "bf16x3"),
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT.get(args.workload, args.workload), "name": args.workload,
+                   "matrices": n, "elements": elems, "ns_steps": k, "coeffs": list(wl.coeffs),
+                   "matrices_per_s": round(n * 1e3 / ms_step, 1), "parallelism": "1 GPU"},
+        "roofline": roofline,
+        "ns_chain": ns_chain,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(wl, sample, sample_idx, kw, n_total):
+    """Time the float64 oracle on the sample; scale by nominal FLOPs to a full step."""
+    import numpy as np
+
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    for w, g, m in sample:
+        orc.muon_step(w, g, m, lr=kw["lr"], beta=kw["beta"], nesterov=bool(kw["nesterov"]),
+                      coeffs=kw["ns_coeffs"], steps=kw["ns_steps"], scale_rule=kw["scale_rule"],
+                      param_bf16=str(wl.param_dtype) == "torch.bfloat16")
+    dt = time.perf_counter() - t0
+
+    def cost(s):
+        m_, n_ = min(s.rows, s.cols), max(s.rows, s.cols)
+        return 4.0 * m_ * m_ * n_ + 2.0 * m_ ** 3
+
+    frac = sum(cost(wl.specs[i]) for i in sample_idx) / sum(cost(s) for s in wl.specs)
+    step_s = dt / frac
+    return {"value": round(1.0 / step_s, 6), "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(sample)} of {n_total} matrices (first layers), float64 NumPy oracle, "
+                      f"{dt:.2f} s, scaled by nominal NS FLOPs to the full step",
+            "seconds_per_step": round(step_s, 3)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+/*
+ * muon.h -- C ABI of libmuon_mi355x.so: the Muon optimizer step for
+ * MI355X (gfx950), run as hand-written HIP kernels.
+ *
+ * What the step computes, per 2-D weight matrix W (rows x cols) with
+ * gradient G and momentum buffer M:
+ *
+ *   M <- beta*M + G                      heavy-ball momentum, binary32, unfused
+ *   U <- nesterov ? G + beta*M : M       (M is the updated buffer)
+ *   X <- U / (||U||_F + 1e-7)            Frobenius normalisation
+ *   repeat ns_steps times:               polynomial Newton-Schulz
+ *       A <- X X^T ; B <- b A + c A A ; X <- a X + B X
+ *   W <- W - fl32(lr*s) * X              scaled write-back (s: scale rule)
+ *
+ * Matrices with rows > cols are iterated on their transpose so that the
+ * Gram matrix X X^T is min(rows, cols) square; the update is transposed
+ * back before the write-back.
+ *
+ * Sources.  The pages that motivate this library describe Muon only in
+ * words: "把 GPT-2 的训练租金估算从 4.3 万美元压到 40 美元…" (magicnetworld.com),
+ * table 符号与约定, row "Muon", defines it as an optimizer for matrix
+ * parameters that orthogonalises the momentum; "开发者千美元训3.8B模型
+ * 击败GPT-2" (aiproducthub.cn), paragraph 影响, says the orthogonalisation
+ * is Newton-Schulz and that every non-matrix parameter goes to AdamW (so
+ * this ABI accepts 2-D matrices only).  The polynomial form of the
+ * iteration is the textbook one (N. J. Higham, Functions of Matrices,
+ * ch. 8); the momentum form, eps, orientation and scale rules are readings
+ * the pages leave open, stated at each declaration below.
+ *
+ * Conventions for every entry point:
+ *   - All tensors are device memory on the current HIP device, owned by the
+ *     caller.  The library never frees or keeps caller pointers after the
+ *     call returns (it may cache their values as a lookup key).
+ *   - Matrices are row-major with a row stride `ld_*` in elements
+ *     (ld >= cols).  Pointers must be aligned to their element size.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     on it and the call returns without synchronising; a kernel fault
+ *     surfaces at the caller's next synchronisation.
+ *   - Every argument is validated on the host before anything is enqueued,
+ *     so a call that returns an error has changed nothing.
+ *   - The library keeps a per-device workspace (grown on demand, freed by
+ *     muon_release_workspace) and a cache of launch plans keyed by the
+ *     pointers and shapes.  Calls that overlap in time on one device (two
+ *     host threads, or two streams) share that workspace and race; issue
+ *     them on one stream or serialise them.
+ *   - Nothing crosses the ABI as an exception; errors are status codes with
+ *     a thread-local message from muon_last_error().
+ */
+#ifndef MUON_MI355X_H
+#define MUON_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUON_ABI_VERSION 1
+
+typedef enum muon_status {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad scalar     */
+  MUON_ERR_UNSUPPORTED = 2,      /* dtype combination, alignment, size cap */
+  MUON_ERR_ALIAS = 3,            /* written buffers overlap another buffer */
+  MUON_ERR_OUT_OF_MEMORY = 4,    /* workspace or plan allocation failed    */
+  MUON_ERR_HIP = 5               /* a HIP call or launch failed            */
+} muon_status;
+
+typedef enum muon_dtype { MUON_DTYPE_F32 = 0, MUON_DTYPE_BF16 = 1 } muon_dtype;
+
+/* Arithmetic of the Newton-Schulz matrix products.
+ *   BF16    operands stored in bfloat16, binary32 accumulation (MFMA).
+ *   BF16X3  operands stored as hi + lo bfloat16 pairs; each product is
+ *           hi*hi + hi*lo + lo*hi in binary32 (about 16 significant bits).
+ *   F32     binary32 operands and binary32 MFMA.                          */
+typedef enum muon_ns_precision {
+  MUON_NS_BF16 = 0,
+  MUON_NS_BF16X3 = 1,
+  MUON_NS_F32 = 2
+} muon_ns_precision;
+
+/* Per-matrix scale s of the update (the pages give none; NONE is the
+ * default reading).  SQRT_ASPECT: s = sqrt(max(1, rows/cols)).
+ * RMS_MATCH: s = 0.2*sqrt(max(rows, cols)).                               */
+typedef enum muon_scale_rule {
+  MUON_SCALE_NONE = 0,
+  MUON_SCALE_SQRT_ASPECT = 1,
+  MUON_SCALE_RMS_MATCH = 2
+} muon_scale_rule;
+
+/* Newton-Schulz step X <- a X + (b A + c A^2) X, A = X X^T.               */
+typedef struct muon_ns_coeffs {
+  float a, b, c;
+} muon_ns_coeffs;
+
+/* One 2-D matrix.  rows, cols in [1, 65536]; ld_* >= cols.
+ * param_dtype and grad_dtype: MUON_DTYPE_F32 or MUON_DTYPE_BF16;
+ * mom_dtype: MUON_DTYPE_F32 only; precision: a muon_ns_precision.        */
+typedef struct muon_matrix_desc {
+  int64_t rows, cols;
+  int64_t ld_param, ld_grad, ld_mom;
+  int32_t param_dtype, grad_dtype, mom_dtype;
+  int32_t precision;
+} muon_matrix_desc;
+
+/* One Muon step on `count` matrices in one grouped launch sequence.
+ *
+ * params[i]  rows x cols weight (param_dtype), updated in place.
+ * grads[i]   rows x cols gradient (grad_dtype), read only.
+ * momenta[i] rows x cols binary32 momentum buffer, updated in place.
+ * shapes[i]  the descriptor of matrix i.
+ * lr         learning rate, finite, as a binary32 value; t = fl32(lr*s).
+ * beta       momentum coefficient in [0, 1), used as its binary32 value.
+ * nesterov   0 or 1.
+ * ns_coeffs  finite a, b, c (c = 0 skips the A*A product).
+ * ns_steps   >= 0; 0 writes back the normalised momentum direction.
+ * scale_rule a muon_scale_rule.
+ *
+ * The momentum update is bit-exact binary32 (one rounding per operation,
+ * no fused multiply-add).  The result does not depend on the order of the
+ * matrices in the arrays.  count == 0 is a no-op returning MUON_OK.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, ALIAS (a written buffer overlaps
+ * any other buffer), OUT_OF_MEMORY, HIP.                                  */
+muon_status muon_step_batched(void* const* params, const void* const* grads,
+                              void* const* momenta, const muon_matrix_desc* shapes,
+                              int32_t count, float lr, float beta, int32_t nesterov,
+                              muon_ns_coeffs ns_coeffs, int32_t ns_steps,
+                              int32_t scale_rule, void* stream);
+
+/* muon_step_batched, and additionally exports the update O (the
+ * orthogonalised, oriented-back Newton-Schulz output before the lr*s
+ * scaling) as binary32 rows x cols, row stride cols, into updates_out[i].
+ * updates_out may be NULL, and so may any entry.  The exported O is the
+ * binary32 value the write-back used, so W_new = rnd(W - fl32(t*O))
+ * holds bit for bit.                                                      */
+muon_status muon_step_batched_ex(void* const* params, const void* const* grads,
+                                 void* const* momenta, const muon_matrix_desc* shapes,
+                                 int32_t count, float lr, float beta, int32_t nesterov,
+                                 muon_ns_coeffs ns_coeffs, int32_t ns_steps,
+                                 int32_t scale_rule, float* const* updates_out,
+                                 void* stream);
+
+/* Newton-Schulz orthogonalisation only: x_out[i] = NS^ns_steps(x / (||x||_F
+ * + 1e-7)) for x = x_in[i] (rows x cols, grad_dtype, row stride ld_grad),
+ * oriented as above.  x_out[i] is binary32 rows x cols with row stride
+ * cols.  param, momentum fields of the descriptors are ignored.            */
+muon_status muon_ns_batched(const void* const* x_in, float* const* x_out,
+                            const muon_matrix_desc* shapes, int32_t count,
+                            muon_ns_coeffs ns_coeffs, int32_t ns_steps, void* stream);
+
+/* Frobenius norms: norms_out[i] = ||x_in[i]||_F (binary32, device array of
+ * `count` floats), summed as binary32 partials per 64x64 tile and reduced in
+ * a fixed order (deterministic).  x_in[i] is grad_dtype with row stride
+ * ld_grad.                                                                */
+muon_status muon_frobenius_norms(const void* const* x_in, const muon_matrix_desc* shapes,
+                                 int32_t count, float* norms_out, void* stream);
+
+/* Kernel classes of the launch sequence, for muon_timing_read.            */
+typedef enum muon_kernel_class {
+  MUON_KC_MOMENTUM = 0,  /* momentum / Nesterov + U copies + norm partials  */
+  MUON_KC_NORM = 1,      /* norm finalize                                  */
+  MUON_KC_GRAM = 2,      /* A = X X^T                                      */
+  MUON_KC_POLY = 3,      /* B = b A + c A A                                */
+  MUON_KC_COMBINE = 4,   /* X = a X + B X (last step: write-back)          */
+  MUON_KC_WRITEBACK = 5, /* write-back when ns_steps == 0                  */
+  MUON_KC_COUNT = 6
+} muon_kernel_class;
+
+/* Measurement hook.  While enabled (enable = 1), every launch the library
+ * enqueues is bracketed by two HIP events recorded on the launch stream.
+ * muon_timing_read waits for the recorded events, writes the summed
+ * milliseconds and the launch count of each kernel class into
+ * ms_out[MUON_KC_COUNT] and launches_out[MUON_KC_COUNT] (host arrays), and
+ * clears the record.  enable = 0 stops recording and drops what was held.
+ * Not thread-safe against concurrent steps.                                */
+muon_status muon_timing_enable(int32_t enable);
+muon_status muon_timing_read(double* ms_out, int64_t* launches_out);
+
+/* Bytes of device workspace a step on these shapes needs (0 on error).    */
+uint64_t muon_workspace_bytes(const muon_matrix_desc* shapes, int32_t count);
+
+/* Free the workspace and cached plans of every device (synchronises each). */
+muon_status muon_release_workspace(void);
+
+/* Static string for a status code.                                         */
+const char* muon_status_string(muon_status status);
+
+/* Detail of the last error on the calling thread ("" if none).             */
+const char* muon_last_error(void);
+
+/* MUON_ABI_VERSION of the built library.                                   */
+int32_t muon_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_MI355X_H */

@@ -1,0 +1,309 @@
+"""ctypes binding of libmuon_mi355x.so (declared in include/muon.h).
+
+Argument marshalling only: tensors become device pointers, row strides and
+dtype codes; the torch stream becomes a hipStream_t.  Every step of the
+computation runs in the library's HIP kernels.  If the library is not
+built, the first call raises `MuonLibraryMissing`; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmuon_mi355x.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "muon.h")
+
+MUON_OK = 0
+MUON_ERR_INVALID_ARGUMENT = 1
+MUON_ERR_UNSUPPORTED = 2
+MUON_ERR_ALIAS = 3
+MUON_ERR_OUT_OF_MEMORY = 4
+MUON_ERR_HIP = 5
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+NS_BF16 = 0
+NS_BF16X3 = 1
+NS_F32 = 2
+
+SCALE_NONE = 0
+SCALE_SQRT_ASPECT = 1
+SCALE_RMS_MATCH = 2
+
+
+class MuonLibraryMissing(RuntimeError):
+    pass
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_name(status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class MatrixDesc(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+        ("ld_param", ctypes.c_int64), ("ld_grad", ctypes.c_int64), ("ld_mom", ctypes.c_int64),
+        ("param_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
+        ("mom_dtype", ctypes.c_int32), ("precision", ctypes.c_int32),
+    ]
+
+
+class NsCoeffs(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_float), ("b", ctypes.c_float), ("c", ctypes.c_float)]
+
+
+_VP = ctypes.c_void_p
+_PP = ctypes.POINTER(ctypes.c_void_p)
+_lib = None
+
+
+def exported_names() -> list[str]:
+    """Function names declared in include/muon.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(muon_[a-z0-9_]+)\s*\(", text)))
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise MuonLibraryMissing(
+            f"{LIB_PATH} is not built; run `python -m muon_newton_schulz_02_amd.build` "
+            "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, f32, u64 = ctypes.c_int32, ctypes.c_float, ctypes.c_uint64
+    D = ctypes.POINTER(MatrixDesc)
+    L.muon_step_batched.argtypes = [_PP, _PP, _PP, D, i32, f32, f32, i32, NsCoeffs, i32, i32, _VP]
+    L.muon_step_batched.restype = i32
+    L.muon_step_batched_ex.argtypes = [_PP, _PP, _PP, D, i32, f32, f32, i32, NsCoeffs, i32, i32, _PP, _VP]
+    L.muon_step_batched_ex.restype = i32
+    L.muon_ns_batched.argtypes = [_PP, _PP, D, i32, NsCoeffs, i32, _VP]
+    L.muon_ns_batched.restype = i32
+    L.muon_frobenius_norms.argtypes = [_PP, D, i32, _VP, _VP]
+    L.muon_frobenius_norms.restype = i32
+    L.muon_workspace_bytes.argtypes = [D, i32]
+    L.muon_workspace_bytes.restype = u64
+    L.muon_release_workspace.argtypes = []
+    L.muon_release_workspace.restype = i32
+    L.muon_status_string.argtypes = [i32]
+    L.muon_status_string.restype = ctypes.c_char_p
+    L.muon_last_error.argtypes = []
+    L.muon_last_error.restype = ctypes.c_char_p
+    L.muon_timing_enable.argtypes = [i32]
+    L.muon_timing_enable.restype = i32
+    L.muon_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    L.muon_timing_read.restype = i32
+    L.muon_abi_version.argtypes = []
+    L.muon_abi_version.restype = i32
+    _lib = L
+    return L
+
+
+def status_name(status: int) -> str:
+    try:
+        return lib().muon_status_string(int(status)).decode()
+    except MuonLibraryMissing:
+        return f"status {status}"
+
+
+def muon_status_string(status: int) -> str:
+    return lib().muon_status_string(int(status)).decode()
+
+
+def muon_last_error() -> str:
+    return lib().muon_last_error().decode()
+
+
+def muon_abi_version() -> int:
+    return int(lib().muon_abi_version())
+
+
+def muon_release_workspace() -> None:
+    _check(lib().muon_release_workspace())
+
+
+KERNEL_CLASSES = ("momentum", "norm", "gram", "poly", "combine", "writeback")
+
+
+def muon_timing_enable(enable: bool) -> None:
+    _check(lib().muon_timing_enable(1 if enable else 0))
+
+
+def muon_timing_read() -> dict:
+    """{class: (total_ms, launches)} of the launches recorded since the last read."""
+    n = len(KERNEL_CLASSES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(lib().muon_timing_read(ms, cnt))
+    return {k: (float(ms[i]), int(cnt[i])) for i, k in enumerate(KERNEL_CLASSES)}
+
+
+def _check(status: int) -> None:
+    if status != MUON_OK:
+        raise MuonError(status, muon_last_error())
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return DTYPE_F32
+    if dt == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {dt}; use float32 or bfloat16")
+
+
+def _row_stride(t: torch.Tensor, name: str) -> int:
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D (got shape {tuple(t.shape)})")
+    if t.stride(1) != 1 and t.shape[1] > 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return max(int(t.stride(0)), int(t.shape[1])) if t.shape[0] == 1 else int(t.stride(0))
+
+
+def _ptr_array(ptrs) -> ctypes.Array:
+    arr = (ctypes.c_void_p * max(len(ptrs), 1))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p
+    return arr
+
+
+def _stream_handle(stream) -> int | None:
+    if stream is None:
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _precisions(precision, n):
+    if isinstance(precision, (list, tuple)):
+        if len(precision) != n:
+            raise ValueError("one precision per matrix")
+        return [int(p) for p in precision]
+    return [int(precision)] * n
+
+
+class StepArgs:
+    """Pointer and descriptor arrays for a fixed list of tensors, built once
+    and reused by every call on the same tensors."""
+
+    def __init__(self, params, grads, momenta, precision=NS_BF16, updates_out=None):
+        n = len(grads)
+        if len(params) != n or len(momenta) != n:
+            raise ValueError("params, grads and momenta must have the same length")
+        precs = _precisions(precision, n)
+        self.count = n
+        self.descs = (MatrixDesc * max(n, 1))()
+        for i, (w, g, m) in enumerate(zip(params, grads, momenta)):
+            d = self.descs[i]
+            d.ld_param = _row_stride(w, "param")
+            d.ld_grad = _row_stride(g, "grad")
+            d.ld_mom = _row_stride(m, "momentum")
+            if tuple(w.shape) != tuple(g.shape) or tuple(m.shape) != tuple(g.shape):
+                raise ValueError(f"matrix {i}: param, grad and momentum shapes differ")
+            d.rows, d.cols = int(g.shape[0]), int(g.shape[1])
+            d.param_dtype = dtype_code(w.dtype)
+            d.grad_dtype = dtype_code(g.dtype)
+            d.mom_dtype = dtype_code(m.dtype)
+            d.precision = precs[i]
+        self.params = _ptr_array([t.data_ptr() for t in params])
+        self.grads = _ptr_array([t.data_ptr() for t in grads])
+        self.momenta = _ptr_array([t.data_ptr() for t in momenta])
+        self.updates = None
+        if updates_out is not None:
+            if len(updates_out) != n:
+                raise ValueError("one updates_out entry per matrix (None allowed)")
+            for i, u in enumerate(updates_out):
+                if u is not None and (u.dtype != torch.float32 or not u.is_contiguous()
+                                      or tuple(u.shape) != (self.descs[i].rows, self.descs[i].cols)):
+                    raise ValueError(f"updates_out[{i}] must be a contiguous float32 rows x cols tensor")
+            self.updates = _ptr_array([0 if u is None else u.data_ptr() for u in updates_out])
+        self._keep = (params, grads, momenta, updates_out)
+
+
+def muon_step_batched(params, grads=None, momenta=None, *, lr, beta, nesterov, ns_coeffs, ns_steps,
+                      scale_rule=SCALE_NONE, precision=NS_BF16, stream=None, updates_out=None):
+    """One Muon step on lists of 2-D tensors (or on a prebuilt StepArgs)."""
+    args = params if isinstance(params, StepArgs) else StepArgs(params, grads, momenta, precision, updates_out)
+    a, b, c = ns_coeffs
+    co = NsCoeffs(float(a), float(b), float(c))
+    st = _stream_handle(stream)
+    if args.updates is None:
+        status = lib().muon_step_batched(args.params, args.grads, args.momenta, args.descs, args.count,
+                                         float(lr), float(beta), int(nesterov), co, int(ns_steps),
+                                         int(scale_rule), st)
+    else:
+        status = lib().muon_step_batched_ex(args.params, args.grads, args.momenta, args.descs, args.count,
+                                            float(lr), float(beta), int(nesterov), co, int(ns_steps),
+                                            int(scale_rule), args.updates, st)
+    _check(status)
+
+
+def muon_step_batched_ex(params, grads, momenta, updates_out, **kw):
+    """muon_step_batched that also exports the binary32 update O of each matrix."""
+    return muon_step_batched(params, grads, momenta, updates_out=updates_out, **kw)
+
+
+def muon_ns_batched(x_in, x_out, *, ns_coeffs, ns_steps, precision=NS_BF16, stream=None):
+    """x_out[i] (float32) = Newton-Schulz orthogonalisation of x_in[i]."""
+    n = len(x_in)
+    if len(x_out) != n:
+        raise ValueError("x_in and x_out must have the same length")
+    precs = _precisions(precision, n)
+    descs = (MatrixDesc * max(n, 1))()
+    for i, (x, y) in enumerate(zip(x_in, x_out)):
+        if y.dtype != torch.float32 or not y.is_contiguous() or tuple(y.shape) != tuple(x.shape):
+            raise ValueError(f"x_out[{i}] must be a contiguous float32 tensor shaped like x_in[{i}]")
+        d = descs[i]
+        d.rows, d.cols = int(x.shape[0]), int(x.shape[1])
+        d.ld_grad = _row_stride(x, "x_in")
+        d.ld_param = d.ld_mom = d.cols
+        d.grad_dtype = dtype_code(x.dtype)
+        d.param_dtype = DTYPE_F32
+        d.mom_dtype = DTYPE_F32
+        d.precision = precs[i]
+    a, b, c = ns_coeffs
+    _check(lib().muon_ns_batched(_ptr_array([t.data_ptr() for t in x_in]),
+                                 _ptr_array([t.data_ptr() for t in x_out]), descs, n,
+                                 NsCoeffs(float(a), float(b), float(c)), int(ns_steps),
+                                 _stream_handle(stream)))
+
+
+def muon_frobenius_norms(x_in, norms_out, *, stream=None):
+    """norms_out (float32 device tensor of len(x_in)) = Frobenius norms."""
+    n = len(x_in)
+    if norms_out.dtype != torch.float32 or norms_out.numel() < n:
+        raise ValueError("norms_out must be float32 with one entry per matrix")
+    descs = (MatrixDesc * max(n, 1))()
+    for i, x in enumerate(x_in):
+        d = descs[i]
+        d.rows, d.cols = int(x.shape[0]), int(x.shape[1])
+        d.ld_grad = _row_stride(x, "x_in")
+        d.ld_param = d.ld_mom = d.cols
+        d.grad_dtype = dtype_code(x.dtype)
+    _check(lib().muon_frobenius_norms(_ptr_array([t.data_ptr() for t in x_in]), descs, n,
+                                      norms_out.data_ptr(), _stream_handle(stream)))
+
+
+def muon_workspace_bytes(shapes, precision=NS_BF16) -> int:
+    """Workspace bytes for [(rows, cols), ...]."""
+    n = len(shapes)
+    precs = _precisions(precision, n)
+    descs = (MatrixDesc * max(n, 1))()
+    for i, (r, c) in enumerate(shapes):
+        d = descs[i]
+        d.rows, d.cols = int(r), int(c)
+        d.ld_param = d.ld_grad = d.ld_mom = int(c)
+        d.precision = precs[i]
+        d.grad_dtype = DTYPE_BF16
+    return int(lib().muon_workspace_bytes(descs, n))

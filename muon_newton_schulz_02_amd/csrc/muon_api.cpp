@@ -1,0 +1,740 @@
+// Host runtime and C ABI of libmuon_mi355x.so: argument validation, the
+// per-device workspace, cached launch plans and the launch sequence of one
+// Muon step (declared in include/muon.h).
+#include "../../include/muon.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <list>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "muon_internal.h"
+
+namespace muon {
+namespace {
+
+thread_local std::string t_last_error;
+
+muon_status fail(muon_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  t_last_error = buf;
+  return s;
+}
+
+constexpr int64_t MAX_DIM = 65536;
+constexpr int32_t MAX_COUNT = 1 << 20;
+constexpr int32_t MAX_NS_STEPS = 1000;
+constexpr size_t MAX_PLANS = 8;
+
+enum Mode { MODE_STEP = 0, MODE_NS = 1, MODE_NORMS = 2 };
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int dtype_size(int32_t dt) { return dt == MUON_DTYPE_BF16 ? 2 : 4; }
+
+struct Interval {
+  uintptr_t lo, hi;  // [lo, hi)
+  bool written;
+  int idx;
+  const char* what;
+};
+
+// Bytes spanned by a rows x cols matrix with row stride ld.
+uint64_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int esz) {
+  return uint64_t((rows - 1) * ld + cols) * uint64_t(esz);
+}
+
+struct MatGeom {
+  int64_t m, n, Mp, Np;
+  bool transposed;
+  int prec;
+  int esz, npl;
+  size_t x_bytes, a_bytes;  // one X buffer, one A buffer (all planes)
+};
+
+MatGeom geom_of(const muon_matrix_desc& d) {
+  MatGeom g;
+  g.transposed = d.rows > d.cols;
+  g.m = std::min(d.rows, d.cols);
+  g.n = std::max(d.rows, d.cols);
+  g.Mp = round_up(g.m, PAD);
+  g.Np = round_up(g.n, PAD);
+  g.prec = d.precision;
+  g.esz = g.prec == PREC_F32 ? 4 : 2;
+  g.npl = g.prec == PREC_BF16X3 ? 2 : 1;
+  g.x_bytes = align256(size_t(g.Mp) * size_t(g.Np) * g.esz * g.npl);
+  g.a_bytes = align256(size_t(g.Mp) * size_t(g.Mp) * g.esz * g.npl);
+  return g;
+}
+
+size_t workspace_bytes(const muon_matrix_desc* shapes, int32_t count) {
+  size_t tot = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    MatGeom g = geom_of(shapes[i]);
+    tot += 4 * g.x_bytes + 2 * g.a_bytes;
+  }
+  return tot;
+}
+
+muon_status validate_desc(const muon_matrix_desc* shapes, int32_t count, Mode mode) {
+  for (int32_t i = 0; i < count; ++i) {
+    const muon_matrix_desc& d = shapes[i];
+    if (d.rows < 1 || d.cols < 1)
+      return fail(MUON_ERR_INVALID_ARGUMENT, "matrix %d: rows and cols must be >= 1 (got %lld x %lld)", i,
+                  (long long)d.rows, (long long)d.cols);
+    if (d.rows > MAX_DIM || d.cols > MAX_DIM)
+      return fail(MUON_ERR_UNSUPPORTED, "matrix %d: rows and cols must be <= %lld", i, (long long)MAX_DIM);
+    if (d.grad_dtype != MUON_DTYPE_F32 && d.grad_dtype != MUON_DTYPE_BF16)
+      return fail(MUON_ERR_UNSUPPORTED, "matrix %d: grad_dtype %d is not F32 or BF16", i, d.grad_dtype);
+    if (d.ld_grad < d.cols)
+      return fail(MUON_ERR_INVALID_ARGUMENT, "matrix %d: ld_grad %lld < cols %lld", i, (long long)d.ld_grad,
+                  (long long)d.cols);
+    if (mode != MODE_NORMS && d.precision != MUON_NS_BF16 && d.precision != MUON_NS_BF16X3 &&
+        d.precision != MUON_NS_F32)
+      return fail(MUON_ERR_INVALID_ARGUMENT, "matrix %d: unknown precision %d", i, d.precision);
+    if (mode == MODE_STEP) {
+      if (d.param_dtype != MUON_DTYPE_F32 && d.param_dtype != MUON_DTYPE_BF16)
+        return fail(MUON_ERR_UNSUPPORTED, "matrix %d: param_dtype %d is not F32 or BF16", i, d.param_dtype);
+      if (d.mom_dtype != MUON_DTYPE_F32)
+        return fail(MUON_ERR_UNSUPPORTED, "matrix %d: momentum must be F32 (mom_dtype %d)", i, d.mom_dtype);
+      if (d.ld_param < d.cols || d.ld_mom < d.cols)
+        return fail(MUON_ERR_INVALID_ARGUMENT, "matrix %d: ld_param/ld_mom < cols", i);
+    }
+  }
+  return MUON_OK;
+}
+
+muon_status check_ptr(const void* p, int esz, int i, const char* what) {
+  if (!p) return fail(MUON_ERR_INVALID_ARGUMENT, "matrix %d: %s pointer is NULL", i, what);
+  if (reinterpret_cast<uintptr_t>(p) % uintptr_t(esz) != 0)
+    return fail(MUON_ERR_UNSUPPORTED, "matrix %d: %s pointer is not aligned to %d bytes", i, what, esz);
+  return MUON_OK;
+}
+
+// Overlap check in O(k log k): sort by start; track the maximum end seen so
+// far over all intervals and over written ones.
+muon_status check_alias_fast(std::vector<Interval>& iv) {
+  std::sort(iv.begin(), iv.end(), [](const Interval& a, const Interval& b) { return a.lo < b.lo; });
+  uintptr_t max_any = 0, max_w = 0;
+  int any_i = -1, w_i = -1;
+  for (size_t i = 0; i < iv.size(); ++i) {
+    const Interval& c = iv[i];
+    if (any_i >= 0) {
+      if (c.written && max_any > c.lo)
+        return fail(MUON_ERR_ALIAS, "%s of matrix %d overlaps %s of matrix %d", c.what, c.idx, iv[any_i].what,
+                    iv[any_i].idx);
+      if (w_i >= 0 && max_w > c.lo)
+        return fail(MUON_ERR_ALIAS, "%s of matrix %d overlaps %s of matrix %d", c.what, c.idx, iv[w_i].what,
+                    iv[w_i].idx);
+    }
+    if (any_i < 0 || c.hi > max_any) { max_any = c.hi; any_i = int(i); }
+    if (c.written && (w_i < 0 || c.hi > max_w)) { max_w = c.hi; w_i = int(i); }
+  }
+  return MUON_OK;
+}
+
+struct Plan {
+  std::vector<uint64_t> key;
+  int32_t count = 0;
+  int64_t total_etiles = 0;
+  void* dmem = nullptr;
+  MatDev* d_mats = nullptr;
+  int32_t* d_etile_off = nullptr;
+  MatScal* d_scal = nullptr;
+  float* d_partials = nullptr;
+  struct Group {
+    int prec;
+    int2* tiles[3];
+    int32_t per_xcd[3];
+  };
+  std::vector<Group> groups;
+  hipEvent_t last_use = nullptr;
+};
+
+struct DeviceState {
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  std::list<Plan*> plans;  // most recently used first
+};
+
+std::mutex g_mu;
+std::map<int, DeviceState> g_dev;
+
+// ------------------------------------------------------------ timing hook
+struct TimedLaunch {
+  hipEvent_t beg, end;
+  int kc;
+};
+bool g_timing = false;
+std::vector<TimedLaunch> g_timed;       // recorded, not yet read
+std::vector<hipEvent_t> g_event_pool;   // reusable events
+
+hipEvent_t pool_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return e;
+}
+
+// Runs `launch` bracketed by events when timing is on.
+template <class F>
+hipError_t timed(int kc, hipStream_t stream, F&& launch) {
+  if (!g_timing) return launch();
+  hipEvent_t b = pool_event(), e = pool_event();
+  if (!b || !e) return launch();
+  hipEventRecord(b, stream);
+  hipError_t r = launch();
+  hipEventRecord(e, stream);
+  g_timed.push_back({b, e, kc});
+  return r;
+}
+
+void free_plan(Plan* p) {
+  if (p->last_use) {
+    hipEventSynchronize(p->last_use);
+    hipEventDestroy(p->last_use);
+  }
+  if (p->dmem) hipFree(p->dmem);
+  delete p;
+}
+
+void drop_plans(DeviceState& ds) {
+  for (Plan* p : ds.plans) free_plan(p);
+  ds.plans.clear();
+}
+
+// Split each matrix's tiles over the XCDs: matrices in order, tiles of one
+// matrix contiguous, each XCD taking a contiguous run of about 1/8 of the
+// total cost.  Returns per-XCD lists padded to a common length with -1.
+struct TileSrc {
+  int mat;
+  int ti, tj;
+  double cost;
+};
+
+std::vector<int2> xcd_lists(const std::vector<TileSrc>& src, int32_t* per_xcd) {
+  double total = 0;
+  for (const auto& t : src) total += t.cost;
+  std::vector<std::vector<int2>> bins(NUM_XCD);
+  const double target = total / NUM_XCD;
+  double acc = 0;
+  int bin = 0;
+  for (const auto& t : src) {
+    // move on once this XCD holds its share (the last XCD takes the rest)
+    if (bin < NUM_XCD - 1 && acc + 0.5 * t.cost > target * (bin + 1)) ++bin;
+    bins[bin].push_back(make_int2(t.mat, (t.ti << 16) | t.tj));
+    acc += t.cost;
+  }
+  size_t mx = 0;
+  for (auto& b : bins) mx = std::max(mx, b.size());
+  *per_xcd = int32_t(mx);
+  std::vector<int2> out(mx * NUM_XCD, make_int2(-1, 0));
+  for (int x = 0; x < NUM_XCD; ++x)
+    for (size_t i = 0; i < bins[x].size(); ++i) out[x * mx + i] = bins[x][i];
+  return out;
+}
+
+muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vector<int32_t>& etile_off,
+                       hipStream_t stream) {
+  const int32_t count = int32_t(hm.size());
+  // order the matrices by decreasing Newton-Schulz cost so large ones start first
+  std::vector<int> order(count);
+  for (int i = 0; i < count; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    const double ca = double(hm[a].Mp) * hm[a].Mp * hm[a].Np;
+    const double cb = double(hm[b].Mp) * hm[b].Mp * hm[b].Np;
+    return ca > cb;
+  });
+  std::vector<int> precs;
+  for (const auto& m : hm)
+    if (std::find(precs.begin(), precs.end(), m.prec) == precs.end()) precs.push_back(m.prec);
+  std::sort(precs.begin(), precs.end());
+
+  std::vector<std::vector<int2>> lists;
+  std::vector<Plan::Group> groups;
+  for (int prec : precs) {
+    Plan::Group g;
+    g.prec = prec;
+    for (int ph = 0; ph < 3; ++ph) {
+      std::vector<TileSrc> src;
+      for (int i : order) {
+        const MatDev& m = hm[i];
+        if (m.prec != prec) continue;
+        const int tm = m.Mp / NS_TILE, tn = m.Np / NS_TILE;
+        if (ph == PH_COMB) {
+          for (int a = 0; a < tm; ++a)
+            for (int b = 0; b < tn; ++b) src.push_back({i, a, b, double(m.Mp)});
+        } else {
+          const double k = ph == PH_GRAM ? double(m.Np) : double(m.Mp);
+          for (int a = 0; a < tm; ++a)
+            for (int b = a; b < tm; ++b) src.push_back({i, a, b, k});
+        }
+      }
+      lists.push_back(xcd_lists(src, &g.per_xcd[ph]));
+      g.tiles[ph] = nullptr;
+    }
+    groups.push_back(g);
+  }
+
+  size_t off = 0;
+  const size_t off_mats = off;
+  off = align256(off + sizeof(MatDev) * count);
+  const size_t off_etile = off;
+  off = align256(off + sizeof(int32_t) * (count + 1));
+  const size_t off_scal = off;
+  off = align256(off + sizeof(MatScal) * count);
+  const size_t off_part = off;
+  off = align256(off + sizeof(float) * size_t(std::max<int64_t>(etile_off[count], 1)));
+  std::vector<size_t> off_lists;
+  for (auto& l : lists) {
+    off_lists.push_back(off);
+    off = align256(off + sizeof(int2) * std::max<size_t>(l.size(), 1));
+  }
+  void* dmem = nullptr;
+  if (hipMalloc(&dmem, off) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MUON_ERR_OUT_OF_MEMORY, "plan allocation of %zu bytes failed", off);
+  }
+  std::vector<char> host(off, 0);
+  memcpy(host.data() + off_mats, hm.data(), sizeof(MatDev) * count);
+  memcpy(host.data() + off_etile, etile_off.data(), sizeof(int32_t) * (count + 1));
+  for (size_t i = 0; i < lists.size(); ++i)
+    memcpy(host.data() + off_lists[i], lists[i].data(), sizeof(int2) * lists[i].size());
+  if (hipMemcpyAsync(dmem, host.data(), off, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    hipFree(dmem);
+    return fail(MUON_ERR_HIP, "plan upload failed: %s", hipGetErrorString(hipGetLastError()));
+  }
+  char* base = reinterpret_cast<char*>(dmem);
+  plan->dmem = dmem;
+  plan->count = count;
+  plan->total_etiles = etile_off[count];
+  plan->d_mats = reinterpret_cast<MatDev*>(base + off_mats);
+  plan->d_etile_off = reinterpret_cast<int32_t*>(base + off_etile);
+  plan->d_scal = reinterpret_cast<MatScal*>(base + off_scal);
+  plan->d_partials = reinterpret_cast<float*>(base + off_part);
+  size_t li = 0;
+  for (auto& g : groups)
+    for (int ph = 0; ph < 3; ++ph) g.tiles[ph] = reinterpret_cast<int2*>(base + off_lists[li++]);
+  plan->groups = groups;
+  if (hipEventCreateWithFlags(&plan->last_use, hipEventDisableTiming) != hipSuccess) {
+    plan->last_use = nullptr;
+    return fail(MUON_ERR_HIP, "hipEventCreate failed");
+  }
+  return MUON_OK;
+}
+
+struct Call {
+  Mode mode;
+  void* const* params;
+  const void* const* grads;
+  void* const* momenta;
+  float* const* updates;
+  const muon_matrix_desc* shapes;
+  int32_t count;
+  float lr, beta;
+  int32_t nesterov;
+  muon_ns_coeffs co;
+  int32_t ns_steps;
+  int32_t scale_rule;
+  float* norms_out;
+  hipStream_t stream;
+};
+
+muon_status validate_call(const Call& c) {
+  if (c.count < 0 || c.count > MAX_COUNT)
+    return fail(MUON_ERR_INVALID_ARGUMENT, "count %d out of range [0, %d]", c.count, MAX_COUNT);
+  if (c.count == 0) return MUON_OK;
+  if (!c.shapes) return fail(MUON_ERR_INVALID_ARGUMENT, "shapes is NULL");
+  if (!c.grads) return fail(MUON_ERR_INVALID_ARGUMENT, "grads (x_in) is NULL");
+  if (c.mode == MODE_STEP) {
+    if (!c.params || !c.momenta) return fail(MUON_ERR_INVALID_ARGUMENT, "params or momenta is NULL");
+    if (!std::isfinite(c.lr)) return fail(MUON_ERR_INVALID_ARGUMENT, "lr is not finite");
+    if (!(c.beta >= 0.f && c.beta < 1.f)) return fail(MUON_ERR_INVALID_ARGUMENT, "beta must be in [0, 1)");
+    if (c.nesterov != 0 && c.nesterov != 1) return fail(MUON_ERR_INVALID_ARGUMENT, "nesterov must be 0 or 1");
+    if (c.scale_rule < MUON_SCALE_NONE || c.scale_rule > MUON_SCALE_RMS_MATCH)
+      return fail(MUON_ERR_INVALID_ARGUMENT, "unknown scale_rule %d", c.scale_rule);
+  }
+  if (c.mode == MODE_NS && !c.updates) return fail(MUON_ERR_INVALID_ARGUMENT, "x_out is NULL");
+  if (c.mode == MODE_NORMS && !c.norms_out) return fail(MUON_ERR_INVALID_ARGUMENT, "norms_out is NULL");
+  if (c.mode != MODE_NORMS) {
+    if (c.ns_steps < 0 || c.ns_steps > MAX_NS_STEPS)
+      return fail(MUON_ERR_INVALID_ARGUMENT, "ns_steps %d out of range [0, %d]", c.ns_steps, MAX_NS_STEPS);
+    if (!std::isfinite(c.co.a) || !std::isfinite(c.co.b) || !std::isfinite(c.co.c))
+      return fail(MUON_ERR_INVALID_ARGUMENT, "ns_coeffs must be finite");
+  }
+  muon_status st = validate_desc(c.shapes, c.count, c.mode);
+  if (st != MUON_OK) return st;
+
+  std::vector<Interval> iv;
+  iv.reserve(size_t(c.count) * 4);
+  for (int32_t i = 0; i < c.count; ++i) {
+    const muon_matrix_desc& d = c.shapes[i];
+    const int gsz = dtype_size(d.grad_dtype);
+    if ((st = check_ptr(c.grads[i], gsz, i, c.mode == MODE_STEP ? "grad" : "x_in")) != MUON_OK) return st;
+    uintptr_t g = reinterpret_cast<uintptr_t>(c.grads[i]);
+    iv.push_back({g, g + span_bytes(d.rows, d.cols, d.ld_grad, gsz), false, i, "grad"});
+    if (c.mode == MODE_STEP) {
+      const int psz = dtype_size(d.param_dtype);
+      if ((st = check_ptr(c.params[i], psz, i, "param")) != MUON_OK) return st;
+      if ((st = check_ptr(c.momenta[i], 4, i, "momentum")) != MUON_OK) return st;
+      uintptr_t p = reinterpret_cast<uintptr_t>(c.params[i]);
+      uintptr_t m = reinterpret_cast<uintptr_t>(c.momenta[i]);
+      iv.push_back({p, p + span_bytes(d.rows, d.cols, d.ld_param, psz), true, i, "param"});
+      iv.push_back({m, m + span_bytes(d.rows, d.cols, d.ld_mom, 4), true, i, "momentum"});
+    }
+    if (c.updates && c.updates[i]) {
+      if ((st = check_ptr(c.updates[i], 4, i, "update")) != MUON_OK) return st;
+      uintptr_t u = reinterpret_cast<uintptr_t>(c.updates[i]);
+      iv.push_back({u, u + span_bytes(d.rows, d.cols, d.cols, 4), true, i, "update"});
+    } else if (c.mode == MODE_NS) {
+      return fail(MUON_ERR_INVALID_ARGUMENT, "matrix %d: x_out pointer is NULL", i);
+    }
+  }
+  if (c.mode == MODE_NORMS) {
+    uintptr_t n = reinterpret_cast<uintptr_t>(c.norms_out);
+    if (n % 4 != 0) return fail(MUON_ERR_UNSUPPORTED, "norms_out is not 4-byte aligned");
+    iv.push_back({n, n + sizeof(float) * size_t(c.count), true, -1, "norms_out"});
+  }
+  return check_alias_fast(iv);
+}
+
+bool vec_aligned(const void* p, int64_t ld, int esz) {
+  return (reinterpret_cast<uintptr_t>(p) % uintptr_t(4 * esz) == 0) && (ld % 4 == 0);
+}
+
+muon_status run(const Call& c) {
+  t_last_error.clear();
+  muon_status st = validate_call(c);
+  if (st != MUON_OK || c.count == 0) return st;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MUON_ERR_HIP, "hipGetDevice failed (no HIP device?)");
+  }
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState& ds = g_dev[dev];
+
+  // workspace
+  const size_t need = c.mode == MODE_NORMS ? 0 : workspace_bytes(c.shapes, c.count);
+  if (need > ds.ws_bytes) {
+    if (hipDeviceSynchronize() != hipSuccess) {
+      return fail(MUON_ERR_HIP, "hipDeviceSynchronize failed: %s", hipGetErrorString(hipGetLastError()));
+    }
+    drop_plans(ds);
+    if (ds.ws) hipFree(ds.ws);
+    ds.ws = nullptr;
+    ds.ws_bytes = 0;
+    void* p = nullptr;
+    if (hipMalloc(&p, need) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MUON_ERR_OUT_OF_MEMORY, "workspace allocation of %zu bytes failed", need);
+    }
+    ds.ws = p;
+    ds.ws_bytes = need;
+  }
+
+  // plan key
+  std::vector<uint64_t> key;
+  key.reserve(size_t(c.count) * 14 + 3);
+  key.push_back(uint64_t(c.mode));
+  key.push_back(uint64_t(c.count));
+  key.push_back(reinterpret_cast<uint64_t>(ds.ws));
+  for (int32_t i = 0; i < c.count; ++i) {
+    const muon_matrix_desc& d = c.shapes[i];
+    key.push_back(reinterpret_cast<uint64_t>(c.grads[i]));
+    key.push_back(c.mode == MODE_STEP ? reinterpret_cast<uint64_t>(c.params[i]) : 0);
+    key.push_back(c.mode == MODE_STEP ? reinterpret_cast<uint64_t>(c.momenta[i]) : 0);
+    key.push_back(c.updates ? reinterpret_cast<uint64_t>(c.updates[i]) : 0);
+    key.push_back(uint64_t(d.rows));
+    key.push_back(uint64_t(d.cols));
+    key.push_back(uint64_t(d.ld_param));
+    key.push_back(uint64_t(d.ld_grad));
+    key.push_back(uint64_t(d.ld_mom));
+    key.push_back((uint64_t(uint32_t(d.param_dtype)) << 32) | uint32_t(d.grad_dtype));
+    key.push_back((uint64_t(uint32_t(d.mom_dtype)) << 32) | uint32_t(d.precision));
+  }
+  Plan* plan = nullptr;
+  for (auto it = ds.plans.begin(); it != ds.plans.end(); ++it) {
+    if ((*it)->key == key) {
+      plan = *it;
+      ds.plans.erase(it);
+      ds.plans.push_front(plan);
+      break;
+    }
+  }
+  if (!plan) {
+    std::vector<MatDev> hm(c.count);
+    std::vector<int32_t> etile_off(c.count + 1, 0);
+    char* ws = reinterpret_cast<char*>(ds.ws);
+    size_t wo = 0;
+    for (int32_t i = 0; i < c.count; ++i) {
+      const muon_matrix_desc& d = c.shapes[i];
+      MatGeom g = geom_of(d);
+      MatDev& m = hm[i];
+      memset(&m, 0, sizeof(m));
+      m.param = c.mode == MODE_STEP ? c.params[i] : nullptr;
+      m.grad = c.grads[i];
+      m.mom = c.mode == MODE_STEP ? reinterpret_cast<float*>(c.momenta[i]) : nullptr;
+      m.upd = c.updates ? c.updates[i] : nullptr;
+      m.ld_param = d.ld_param;
+      m.ld_grad = d.ld_grad;
+      m.ld_mom = d.ld_mom;
+      m.ld_upd = d.cols;
+      m.rows = int32_t(d.rows);
+      m.cols = int32_t(d.cols);
+      m.m = int32_t(g.m);
+      m.n = int32_t(g.n);
+      m.Mp = int32_t(g.Mp);
+      m.Np = int32_t(g.Np);
+      m.transposed = g.transposed ? 1 : 0;
+      m.param_bf16 = (c.mode == MODE_STEP && d.param_dtype == MUON_DTYPE_BF16) ? 1 : 0;
+      m.grad_bf16 = d.grad_dtype == MUON_DTYPE_BF16 ? 1 : 0;
+      bool vec = vec_aligned(c.grads[i], d.ld_grad, dtype_size(d.grad_dtype));
+      if (c.mode == MODE_STEP) vec = vec && vec_aligned(c.momenta[i], d.ld_mom, 4);
+      m.vec_ok = vec ? 1 : 0;
+      m.prec = c.mode == MODE_NORMS ? PREC_BF16 : d.precision;
+      const int64_t rp = g.transposed ? g.Np : g.Mp;  // natural padded rows
+      const int64_t cp = g.transposed ? g.Mp : g.Np;  // natural padded cols
+      m.etile_cols = int32_t(cp / ETILE);
+      etile_off[i + 1] = etile_off[i] + int32_t((rp / ETILE) * (cp / ETILE));
+      if (c.mode != MODE_NORMS) {
+        m.plane_X = g.Mp * g.Np;
+        m.plane_A = g.Mp * g.Mp;
+        m.X[0] = ws + wo; wo += g.x_bytes;
+        m.X[1] = ws + wo; wo += g.x_bytes;
+        m.Xt[0] = ws + wo; wo += g.x_bytes;
+        m.Xt[1] = ws + wo; wo += g.x_bytes;
+        m.A = ws + wo; wo += g.a_bytes;
+        m.B = ws + wo; wo += g.a_bytes;
+      }
+    }
+    if (int64_t(etile_off[c.count]) >= (int64_t(1) << 31) - 1)
+      return fail(MUON_ERR_UNSUPPORTED, "too many elements in one call");
+    plan = new Plan();
+    plan->key = key;
+    st = build_plan(plan, hm, etile_off, c.stream);
+    if (st != MUON_OK) {
+      if (plan->dmem) hipFree(plan->dmem);
+      delete plan;
+      return st;
+    }
+    ds.plans.push_front(plan);
+    while (ds.plans.size() > MAX_PLANS) {
+      free_plan(ds.plans.back());
+      ds.plans.pop_back();
+    }
+  }
+
+  // ------------------------------------------------------------ launches
+  hipError_t e = hipSuccess;
+  const int kmode = c.mode == MODE_STEP ? 0 : (c.mode == MODE_NS ? 1 : 2);
+  e = timed(MUON_KC_MOMENTUM, c.stream, [&] {
+    return launch_momentum(plan->d_mats, plan->d_etile_off, plan->count, plan->total_etiles, c.beta,
+                           c.nesterov, kmode, plan->d_partials, c.stream);
+  });
+  if (e == hipSuccess)
+    e = timed(MUON_KC_NORM, c.stream, [&] {
+      return launch_norm_finalize(plan->d_etile_off, plan->count, plan->d_partials, plan->d_scal,
+                                  c.mode == MODE_NORMS ? c.norms_out : nullptr, c.stream);
+    });
+  if (e == hipSuccess && c.mode != MODE_NORMS) {
+    if (c.ns_steps == 0) {
+      e = timed(MUON_KC_WRITEBACK, c.stream, [&] {
+        return launch_writeback_direct(plan->d_mats, plan->d_etile_off, plan->count, plan->total_etiles,
+                                       plan->d_scal, c.lr, c.scale_rule, c.stream);
+      });
+    } else {
+      for (int it = 0; it < c.ns_steps && e == hipSuccess; ++it) {
+        PhaseArgs pa;
+        pa.a = c.co.a;
+        pa.b = c.co.b;
+        pa.c = c.co.c;
+        pa.lr = c.lr;
+        pa.cur = it & 1;
+        pa.first = it == 0;
+        pa.last = it == c.ns_steps - 1;
+        pa.scale_rule = c.scale_rule;
+        for (const auto& g : plan->groups) {
+          for (int ph = 0; ph < 3 && e == hipSuccess; ++ph) {
+            if (ph == PH_POLY && c.co.c == 0.f) continue;
+            pa.per_xcd = g.per_xcd[ph];
+            e = timed(MUON_KC_GRAM + ph, c.stream, [&] {
+              return launch_ns_phase(g.prec, ph, plan->d_mats, plan->d_scal, g.tiles[ph], pa, c.stream);
+            });
+          }
+        }
+      }
+    }
+  }
+  if (e != hipSuccess) return fail(MUON_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  hipEventRecord(plan->last_use, c.stream);
+  return MUON_OK;
+}
+
+}  // namespace
+}  // namespace muon
+
+using namespace muon;
+
+extern "C" {
+
+muon_status muon_step_batched(void* const* params, const void* const* grads, void* const* momenta,
+                              const muon_matrix_desc* shapes, int32_t count, float lr, float beta,
+                              int32_t nesterov, muon_ns_coeffs ns_coeffs, int32_t ns_steps, int32_t scale_rule,
+                              void* stream) {
+  return muon_step_batched_ex(params, grads, momenta, shapes, count, lr, beta, nesterov, ns_coeffs, ns_steps,
+                              scale_rule, nullptr, stream);
+}
+
+muon_status muon_step_batched_ex(void* const* params, const void* const* grads, void* const* momenta,
+                                 const muon_matrix_desc* shapes, int32_t count, float lr, float beta,
+                                 int32_t nesterov, muon_ns_coeffs ns_coeffs, int32_t ns_steps,
+                                 int32_t scale_rule, float* const* updates_out, void* stream) {
+  Call c{};
+  c.mode = MODE_STEP;
+  c.params = params;
+  c.grads = grads;
+  c.momenta = momenta;
+  c.updates = updates_out;
+  c.shapes = shapes;
+  c.count = count;
+  c.lr = lr;
+  c.beta = beta;
+  c.nesterov = nesterov;
+  c.co = ns_coeffs;
+  c.ns_steps = ns_steps;
+  c.scale_rule = scale_rule;
+  c.stream = reinterpret_cast<hipStream_t>(stream);
+  return run(c);
+}
+
+muon_status muon_ns_batched(const void* const* x_in, float* const* x_out, const muon_matrix_desc* shapes,
+                            int32_t count, muon_ns_coeffs ns_coeffs, int32_t ns_steps, void* stream) {
+  Call c{};
+  c.mode = MODE_NS;
+  c.grads = x_in;
+  c.updates = x_out;
+  c.shapes = shapes;
+  c.count = count;
+  c.co = ns_coeffs;
+  c.ns_steps = ns_steps;
+  c.lr = 0.f;
+  c.stream = reinterpret_cast<hipStream_t>(stream);
+  return run(c);
+}
+
+muon_status muon_frobenius_norms(const void* const* x_in, const muon_matrix_desc* shapes, int32_t count,
+                                 float* norms_out, void* stream) {
+  Call c{};
+  c.mode = MODE_NORMS;
+  c.grads = x_in;
+  c.shapes = shapes;
+  c.count = count;
+  c.norms_out = norms_out;
+  c.stream = reinterpret_cast<hipStream_t>(stream);
+  return run(c);
+}
+
+muon_status muon_timing_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  t_last_error.clear();
+  if (!enable) {
+    for (auto& t : g_timed) {
+      hipEventSynchronize(t.end);
+      g_event_pool.push_back(t.beg);
+      g_event_pool.push_back(t.end);
+    }
+    g_timed.clear();
+  }
+  g_timing = enable != 0;
+  return MUON_OK;
+}
+
+muon_status muon_timing_read(double* ms_out, int64_t* launches_out) {
+  if (!ms_out || !launches_out) return fail(MUON_ERR_INVALID_ARGUMENT, "ms_out or launches_out is NULL");
+  std::lock_guard<std::mutex> lock(g_mu);
+  t_last_error.clear();
+  for (int k = 0; k < MUON_KC_COUNT; ++k) {
+    ms_out[k] = 0.0;
+    launches_out[k] = 0;
+  }
+  muon_status st = MUON_OK;
+  for (auto& t : g_timed) {
+    float ms = 0.f;
+    if (hipEventSynchronize(t.end) != hipSuccess || hipEventElapsedTime(&ms, t.beg, t.end) != hipSuccess) {
+      (void)hipGetLastError();
+      st = fail(MUON_ERR_HIP, "reading a timing event failed");
+    } else {
+      ms_out[t.kc] += double(ms);
+      launches_out[t.kc] += 1;
+    }
+    g_event_pool.push_back(t.beg);
+    g_event_pool.push_back(t.end);
+  }
+  g_timed.clear();
+  return st;
+}
+
+uint64_t muon_workspace_bytes(const muon_matrix_desc* shapes, int32_t count) {
+  if (!shapes || count < 0 || count > MAX_COUNT) return 0;
+  if (validate_desc(shapes, count, MODE_NS) != MUON_OK) return 0;
+  return uint64_t(workspace_bytes(shapes, count));
+}
+
+muon_status muon_release_workspace(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int cur = 0;
+  const bool have_dev = hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : g_dev) {
+    if (hipSetDevice(kv.first) != hipSuccess) continue;
+    hipDeviceSynchronize();
+    drop_plans(kv.second);
+    if (kv.second.ws) hipFree(kv.second.ws);
+    kv.second.ws = nullptr;
+    kv.second.ws_bytes = 0;
+  }
+  if (have_dev) hipSetDevice(cur);
+  g_dev.clear();
+  (void)hipGetLastError();
+  return MUON_OK;
+}
+
+const char* muon_status_string(muon_status status) {
+  switch (status) {
+    case MUON_OK: return "MUON_OK";
+    case MUON_ERR_INVALID_ARGUMENT: return "MUON_ERR_INVALID_ARGUMENT";
+    case MUON_ERR_UNSUPPORTED: return "MUON_ERR_UNSUPPORTED";
+    case MUON_ERR_ALIAS: return "MUON_ERR_ALIAS";
+    case MUON_ERR_OUT_OF_MEMORY: return "MUON_ERR_OUT_OF_MEMORY";
+    case MUON_ERR_HIP: return "MUON_ERR_HIP";
+  }
+  return "MUON_ERR_UNKNOWN";
+}
+
+const char* muon_last_error(void) { return t_last_error.c_str(); }
+
+int32_t muon_abi_version(void) { return MUON_ABI_VERSION; }
+
+}  // extern "C"

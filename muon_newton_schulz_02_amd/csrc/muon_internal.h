@@ -1,0 +1,82 @@
+// Internal types shared by the host runtime and the HIP kernels of
+// libmuon_mi355x.so.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+// Workspace matrices are padded to a multiple of PAD in both dimensions and
+// the padding holds zeros, so the Newton-Schulz products run without bounds
+// checks: zero rows and columns contribute nothing and stay zero.
+constexpr int PAD = 256;
+// Elementwise tiles (momentum, transposed copy, norm partials).
+constexpr int ETILE = 64;
+// Dispatch order puts consecutive workgroups on different XCDs.
+constexpr int NUM_XCD = 8;
+
+enum Prec : int { PREC_BF16 = 0, PREC_BF16X3 = 1, PREC_F32 = 2 };
+
+// Per-matrix device descriptor.  "natural" means the caller's orientation
+// (rows x cols); the iteration runs on the wide orientation m x n (m <= n).
+struct MatDev {
+  // caller memory
+  void* param;            // rows x cols, param dtype; null for NS-only calls
+  const void* grad;       // rows x cols, grad dtype
+  float* mom;             // rows x cols float; null for NS-only calls
+  float* upd;             // rows x cols float export (nullable), row stride ld_upd
+  int64_t ld_param, ld_grad, ld_mom, ld_upd;
+  int32_t rows, cols;     // natural shape
+  int32_t m, n;           // wide shape
+  int32_t Mp, Np;         // padded wide shape
+  int32_t transposed;     // rows > cols
+  int32_t param_bf16, grad_bf16;
+  int32_t vec_ok;         // grad/mom/param rows allow 4-element vector access
+  int32_t prec;           // Prec
+  int32_t etile_cols;     // elementwise tiles along the natural columns
+  // workspace: element buffers; BF16X3 keeps the lo plane `plane_*`
+  // elements after the hi plane
+  void* X[2];             // Mp x Np (ping-pong)
+  void* Xt[2];            // Np x Mp (transposed copies)
+  void* A;                // Mp x Mp Gram
+  void* B;                // Mp x Mp polynomial
+  int64_t plane_X, plane_A;
+};
+
+// Arguments of one Newton-Schulz phase launch.
+struct PhaseArgs {
+  float a, b, c;
+  float lr;
+  int32_t cur;            // which X buffer holds the current iterate
+  int32_t first;          // apply 1/(||U||+eps) folded into this step
+  int32_t last;           // combine: write back instead of storing X
+  int32_t scale_rule;
+  int32_t per_xcd;        // tile-list entries per XCD
+};
+
+// Per-matrix scalars written by the norm finalize kernel.
+struct MatScal {
+  float inv;              // 1 / (||U||_F + eps)
+  float inv2;             // inv * inv
+  float norm;             // ||U||_F
+  float pad;
+};
+
+// Launchers (defined in the .hip files).  All enqueue on `stream`.
+hipError_t launch_momentum(const MatDev* mats, const int32_t* etile_off, int32_t count,
+                           int64_t total_tiles, float beta, int32_t nesterov, int32_t mode,
+                           float* partials, hipStream_t stream);
+hipError_t launch_norm_finalize(const int32_t* etile_off, int32_t count, const float* partials,
+                                MatScal* scal, float* norms_out, hipStream_t stream);
+hipError_t launch_writeback_direct(const MatDev* mats, const int32_t* etile_off, int32_t count,
+                                   int64_t total_tiles, const MatScal* scal, float lr,
+                                   int32_t scale_rule, hipStream_t stream);
+enum Phase : int { PH_GRAM = 0, PH_POLY = 1, PH_COMB = 2 };
+hipError_t launch_ns_phase(int prec, int phase, const MatDev* mats, const MatScal* scal,
+                           const int2* tiles, const PhaseArgs& args, hipStream_t stream);
+
+// Tile edge of the Newton-Schulz products (square tiles).
+constexpr int NS_TILE = 128;
+
+}  // namespace muon

@@ -1,0 +1,161 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+import torch
+
+from muon_newton_schulz_02_amd import binding as mb
+from muon_newton_schulz_02_amd import build as mbuild
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mb.LIB_PATH):
+        mbuild.build(verbose=False)
+    return mb.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = mb.exported_names()
+    assert len(names) == 11
+    out = subprocess.run(["nm", "-D", "--defined-only", mb.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def test_version_and_strings(L):
+    assert mb.muon_abi_version() == 1
+    assert mb.muon_status_string(mb.MUON_OK) == "MUON_OK"
+    assert mb.muon_status_string(mb.MUON_ERR_ALIAS) == "MUON_ERR_ALIAS"
+    assert mb.muon_status_string(99) == "MUON_ERR_UNKNOWN"
+
+
+def _desc(rows, cols, ld=None, pdt=mb.DTYPE_BF16, gdt=mb.DTYPE_BF16, mdt=mb.DTYPE_F32, prec=mb.NS_BF16):
+    d = mb.MatrixDesc()
+    d.rows, d.cols = rows, cols
+    d.ld_param = d.ld_grad = d.ld_mom = cols if ld is None else ld
+    d.param_dtype, d.grad_dtype, d.mom_dtype, d.precision = pdt, gdt, mdt, prec
+    return d
+
+
+def _call(L, descs, params, grads, moms, lr=0.02, beta=0.95, nesterov=1, coeffs=(3.4445, -4.775, 2.0315),
+          steps=5, rule=0, updates=None):
+    n = len(descs)
+    D = (mb.MatrixDesc * max(n, 1))(*descs)
+    P = mb._ptr_array(params)
+    G = mb._ptr_array(grads)
+    M = mb._ptr_array(moms)
+    co = mb.NsCoeffs(*coeffs)
+    if updates is None:
+        return L.muon_step_batched(P, G, M, D, n, lr, beta, nesterov, co, steps, rule, None)
+    return L.muon_step_batched_ex(P, G, M, D, n, lr, beta, nesterov, co, steps, rule,
+                                  mb._ptr_array(updates), None)
+
+
+# Fake device addresses: validation only compares them, nothing dereferences them.
+BASE = 0x7F0000000000
+
+
+def _ptrs(i, rows, cols):
+    p = BASE + i * 0x10000000
+    return p, p + 0x1000000, p + 0x2000000
+
+
+def test_count_zero_is_noop(L):
+    assert _call(L, [], [], [], []) == mb.MUON_OK
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("rows", 0, mb.MUON_ERR_INVALID_ARGUMENT),
+    ("cols", -3, mb.MUON_ERR_INVALID_ARGUMENT),
+    ("rows", 70000, mb.MUON_ERR_UNSUPPORTED),
+    ("ld_grad", 10, mb.MUON_ERR_INVALID_ARGUMENT),
+    ("ld_mom", 10, mb.MUON_ERR_INVALID_ARGUMENT),
+    ("mom_dtype", mb.DTYPE_BF16, mb.MUON_ERR_UNSUPPORTED),
+    ("param_dtype", 7, mb.MUON_ERR_UNSUPPORTED),
+    ("grad_dtype", 7, mb.MUON_ERR_UNSUPPORTED),
+    ("precision", 9, mb.MUON_ERR_INVALID_ARGUMENT),
+])
+def test_descriptor_errors(L, field, value, status):
+    d = _desc(16, 32)
+    setattr(d, field, value)
+    p, g, m = _ptrs(0, 16, 32)
+    assert _call(L, [d], [p], [g], [m]) == status
+    assert mb.muon_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lr=float("nan")), mb.MUON_ERR_INVALID_ARGUMENT),
+    (dict(lr=float("inf")), mb.MUON_ERR_INVALID_ARGUMENT),
+    (dict(beta=1.0), mb.MUON_ERR_INVALID_ARGUMENT),
+    (dict(beta=-0.1), mb.MUON_ERR_INVALID_ARGUMENT),
+    (dict(beta=float("nan")), mb.MUON_ERR_INVALID_ARGUMENT),
+    (dict(nesterov=2), mb.MUON_ERR_INVALID_ARGUMENT),
+    (dict(steps=-1), mb.MUON_ERR_INVALID_ARGUMENT),
+    (dict(rule=5), mb.MUON_ERR_INVALID_ARGUMENT),
+    (dict(coeffs=(float("nan"), 0.0, 0.0)), mb.MUON_ERR_INVALID_ARGUMENT),
+])
+def test_scalar_errors(L, kw, status):
+    p, g, m = _ptrs(0, 16, 32)
+    assert _call(L, [_desc(16, 32)], [p], [g], [m], **kw) == status
+
+
+def test_null_and_alignment(L):
+    p, g, m = _ptrs(0, 16, 32)
+    assert _call(L, [_desc(16, 32)], [0], [g], [m]) == mb.MUON_ERR_INVALID_ARGUMENT
+    assert _call(L, [_desc(16, 32)], [p], [0], [m]) == mb.MUON_ERR_INVALID_ARGUMENT
+    assert _call(L, [_desc(16, 32)], [p + 1], [g], [m]) == mb.MUON_ERR_UNSUPPORTED
+    assert _call(L, [_desc(16, 32)], [p], [g], [m + 2]) == mb.MUON_ERR_UNSUPPORTED
+    D = (mb.MatrixDesc * 1)(_desc(16, 32))
+    assert L.muon_step_batched(None, mb._ptr_array([g]), mb._ptr_array([m]), D, 1, 0.02, 0.9, 0,
+                               mb.NsCoeffs(1.5, -0.5, 0.0), 5, 0, None) == mb.MUON_ERR_INVALID_ARGUMENT
+
+
+def test_alias_detection(L):
+    p, g, m = _ptrs(0, 16, 32)
+    # param overlapping its own gradient
+    assert _call(L, [_desc(16, 32)], [p], [p + 64], [m]) == mb.MUON_ERR_ALIAS
+    # momentum of matrix 1 overlapping the param of matrix 0
+    p1, g1, _ = _ptrs(1, 16, 32)
+    assert _call(L, [_desc(16, 32), _desc(16, 32)], [p, p1], [g, g1], [m, p + 16 * 32 * 2 - 4]) \
+        == mb.MUON_ERR_ALIAS
+    # two matrices reading one gradient is allowed by validation (then fails later
+    # only for want of a GPU, or succeeds on one)
+    st = _call(L, [_desc(16, 32), _desc(16, 32)], [p, p1], [g, g], [m, m + 0x100000])
+    assert st != mb.MUON_ERR_ALIAS
+    # update export overlapping a weight
+    assert _call(L, [_desc(16, 32)], [p], [g], [m], updates=[p + 32]) == mb.MUON_ERR_ALIAS
+    # strided rows are taken into account: ld = 64 makes param 0 reach further
+    d = _desc(16, 32, ld=64)
+    assert _call(L, [d], [p], [p + (15 * 64 + 32) * 2 - 2], [m]) == mb.MUON_ERR_ALIAS
+    assert _call(L, [d], [p], [p + (15 * 64 + 32) * 2], [m]) != mb.MUON_ERR_ALIAS
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU error path")
+def test_valid_call_without_gpu_reports_hip_error(L):
+    p, g, m = _ptrs(0, 16, 32)
+    assert _call(L, [_desc(16, 32)], [p], [g], [m]) == mb.MUON_ERR_HIP
+
+
+def test_workspace_bytes(L):
+    one = mb.muon_workspace_bytes([(1536, 1536)])
+    # X, X' and their transposes (4 x 1536^2) plus A and B (2 x 1536^2), bf16
+    assert one == 6 * 1536 * 1536 * 2
+    tall = mb.muon_workspace_bytes([(6144, 1536)])
+    wide = mb.muon_workspace_bytes([(1536, 6144)])
+    assert tall == wide == (4 * 1536 * 6144 + 2 * 1536 * 1536) * 2
+    assert mb.muon_workspace_bytes([(1536, 1536)], precision=mb.NS_BF16X3) == 2 * one
+    assert mb.muon_workspace_bytes([(0, 4)]) == 0
+
+
+def test_python_binding_rejects_bad_tensors():
+    w = torch.zeros(4, 4, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        mb.StepArgs([w], [w], [w])
+    with pytest.raises(ValueError):
+        mb.StepArgs([torch.zeros(4)], [torch.zeros(4)], [torch.zeros(4)])
