@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--workload", default="d24_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=2, help="layers in the oracle's sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, copy 1 GiB device-to-device once (a plain copy kernel "
+                         "of known size, to scale HBM byte counters)")
     return ap.parse_args()
 
 
@@ -114,6 +117,14 @@ def main():
     ms_step = ms_total / args.steps
     print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (event), wall {wall / args.steps * 1e3:.3f} ms",
           file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ------------------------------------------------------------ accounting
     k = wl.ns_steps
