@@ -37,6 +37,7 @@ constexpr int64_t MAX_DIM = 65536;
 constexpr int32_t MAX_COUNT = 1 << 20;
 constexpr int32_t MAX_NS_STEPS = 1000;
 constexpr size_t MAX_PLANS = 8;
+constexpr int GROUP_M = 8;  // tile rows per raster band
 
 enum Mode { MODE_STEP = 0, MODE_NS = 1, MODE_NORMS = 2 };
 
@@ -281,13 +282,17 @@ muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vec
         const MatDev& m = hm[i];
         if (m.prec != prec) continue;
         const int tm = m.Mp / NS_TILE, tn = m.Np / NS_TILE;
+        // grouped raster: bands of GROUP_M tile rows, walked column by column,
+        // so tiles in flight together share row and column operand panels
         if (ph == PH_COMB) {
-          for (int a = 0; a < tm; ++a)
-            for (int b = 0; b < tn; ++b) src.push_back({i, a, b, double(m.Mp)});
+          for (int g0 = 0; g0 < tm; g0 += GROUP_M)
+            for (int b = 0; b < tn; ++b)
+              for (int a = g0; a < std::min(tm, g0 + GROUP_M); ++a) src.push_back({i, a, b, double(m.Mp)});
         } else {
           const double k = ph == PH_GRAM ? double(m.Np) : double(m.Mp);
-          for (int a = 0; a < tm; ++a)
-            for (int b = a; b < tm; ++b) src.push_back({i, a, b, k});
+          for (int g0 = 0; g0 < tm; g0 += GROUP_M)
+            for (int b = g0; b < tm; ++b)
+              for (int a = g0; a < std::min(tm, g0 + GROUP_M) && a <= b; ++a) src.push_back({i, a, b, k});
         }
       }
       lists.push_back(xcd_lists(src, &g.per_xcd[ph]));
@@ -514,6 +519,12 @@ muon_status run(const Call& c) {
       bool vec = vec_aligned(c.grads[i], d.ld_grad, dtype_size(d.grad_dtype));
       if (c.mode == MODE_STEP) vec = vec && vec_aligned(c.momenta[i], d.ld_mom, 4);
       m.vec_ok = vec ? 1 : 0;
+      if (c.mode == MODE_STEP) {
+        const int psz = dtype_size(d.param_dtype);
+        // rows start 16-byte aligned; columns go in groups of 8 from a multiple of 8
+        m.wvec_ok = (reinterpret_cast<uintptr_t>(c.params[i]) % 16 == 0 && (d.ld_param * psz) % 16 == 0) ? 1 : 0;
+      }
+      if (m.upd) m.uvec_ok = (reinterpret_cast<uintptr_t>(m.upd) % 16 == 0 && d.cols % 4 == 0) ? 1 : 0;
       m.prec = c.mode == MODE_NORMS ? PREC_BF16 : d.precision;
       const int64_t rp = g.transposed ? g.Np : g.Mp;  // natural padded rows
       const int64_t cp = g.transposed ? g.Mp : g.Np;  // natural padded cols

@@ -32,7 +32,9 @@ struct MatDev {
   int32_t Mp, Np;         // padded wide shape
   int32_t transposed;     // rows > cols
   int32_t param_bf16, grad_bf16;
-  int32_t vec_ok;         // grad/mom/param rows allow 4-element vector access
+  int32_t vec_ok;         // grad/mom rows allow 4-element vector access
+  int32_t wvec_ok;        // param rows allow 8-element (16/32-byte) vector access
+  int32_t uvec_ok;        // update-export rows allow 4-float vector access
   int32_t prec;           // Prec
   int32_t etile_cols;     // elementwise tiles along the natural columns
   // workspace: element buffers; BF16X3 keeps the lo plane `plane_*`

@@ -101,6 +101,113 @@ __device__ __forceinline__ void st4(void* base, int64_t plane, int64_t idx, cons
   }
 }
 
+// eight consecutive elements, idx a multiple of 8
+template <int PREC>
+__device__ __forceinline__ void ld8(const void* base, int64_t plane, int64_t idx, float* v) {
+  if constexpr (PREC == PREC_F32) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + idx);
+    const f32x4 a = p[0], b = p[1];
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+    v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(base);
+    const u32x4 h = *reinterpret_cast<const u32x4*>(p + idx);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = bf16_bits_to_float(h[e] & 0xFFFFu);
+      v[2 * e + 1] = bf16_bits_to_float(h[e] >> 16);
+    }
+    if constexpr (PREC == PREC_BF16X3) {
+      const u32x4 l = *reinterpret_cast<const u32x4*>(p + plane + idx);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = v[2 * e] + bf16_bits_to_float(l[e] & 0xFFFFu);
+        v[2 * e + 1] = v[2 * e + 1] + bf16_bits_to_float(l[e] >> 16);
+      }
+    }
+  }
+}
+
+template <int PREC>
+__device__ __forceinline__ void st8(void* base, int64_t plane, int64_t idx, const float* v) {
+  if constexpr (PREC == PREC_F32) {
+    f32x4* p = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + idx);
+    p[0] = f32x4{v[0], v[1], v[2], v[3]};
+    p[1] = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    uint16_t* p = reinterpret_cast<uint16_t*>(base);
+    uint16_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = float_to_bf16_bits(v[e]);
+    u32x4 hv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hv[e] = uint32_t(h[2 * e]) | (uint32_t(h[2 * e + 1]) << 16);
+    *reinterpret_cast<u32x4*>(p + idx) = hv;
+    if constexpr (PREC == PREC_BF16X3) {
+      u32x4 lv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t l0 = float_to_bf16_bits(v[2 * e] - bf16_bits_to_float(h[2 * e]));
+        const uint32_t l1 = float_to_bf16_bits(v[2 * e + 1] - bf16_bits_to_float(h[2 * e + 1]));
+        lv[e] = l0 | (l1 << 16);
+      }
+      *reinterpret_cast<u32x4*>(p + plane + idx) = lv;
+    }
+  }
+}
+
+// W[row][c0 .. c0+7] <- rnd(W - t*o) for the columns below `ncols`, and the
+// optional binary32 export of o.
+__device__ __forceinline__ void write_back8(const MatDev& md, int row, int c0, int ncols, const float* o,
+                                            float t) {
+  const int cnt = ncols - c0;
+  if (cnt <= 0) return;
+  if (md.param) {
+    const int64_t pi = int64_t(row) * md.ld_param + c0;
+    if (md.param_bf16) {
+      uint16_t* pw = reinterpret_cast<uint16_t*>(md.param) + pi;
+      if (cnt >= 8 && md.wvec_ok) {
+        u32x4 raw = *reinterpret_cast<const u32x4*>(pw);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float w0 = bf16_bits_to_float(raw[e] & 0xFFFFu);
+          const float w1 = bf16_bits_to_float(raw[e] >> 16);
+          raw[e] = uint32_t(float_to_bf16_bits(w0 - t * o[2 * e])) |
+                   (uint32_t(float_to_bf16_bits(w1 - t * o[2 * e + 1])) << 16);
+        }
+        *reinterpret_cast<u32x4*>(pw) = raw;
+      } else {
+        for (int e = 0; e < 8 && e < cnt; ++e) pw[e] = float_to_bf16_bits(bf16_bits_to_float(pw[e]) - t * o[e]);
+      }
+    } else {
+      float* pw = reinterpret_cast<float*>(md.param) + pi;
+      if (cnt >= 8 && md.wvec_ok) {
+        f32x4* q = reinterpret_cast<f32x4*>(pw);
+        f32x4 a = q[0], b = q[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = a[e] - t * o[e];
+          b[e] = b[e] - t * o[4 + e];
+        }
+        q[0] = a;
+        q[1] = b;
+      } else {
+        for (int e = 0; e < 8 && e < cnt; ++e) pw[e] = pw[e] - t * o[e];
+      }
+    }
+  }
+  if (md.upd) {
+    float* pu = md.upd + int64_t(row) * md.ld_upd + c0;
+    if (cnt >= 8 && md.uvec_ok) {
+      f32x4* q = reinterpret_cast<f32x4*>(pu);
+      q[0] = f32x4{o[0], o[1], o[2], o[3]};
+      q[1] = f32x4{o[4], o[5], o[6], o[7]};
+    } else {
+      for (int e = 0; e < 8 && e < cnt; ++e) pu[e] = o[e];
+    }
+  }
+}
+
 template <int PREC>
 __device__ __forceinline__ void mfma_step(f32x16& acc, const u32x4* a, const u32x4* b) {
   if constexpr (PREC == PREC_BF16) {
@@ -248,94 +355,112 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(const MatDev* __restrict__
   }
 
   // ---------------------------------------------------------------- epilogue
-  const int half = lane >> 5;
-  const int lc = lane & 31;
-  if constexpr (PHASE == PH_GRAM || PHASE == PH_POLY) {
-    const float gs = (PHASE == PH_GRAM && pa.first) ? scal[te.x].inv2 : 1.f;
-    void* out = (PHASE == PH_GRAM) ? md.A : md.B;
-    const int64_t ld = md.Mp;
-    const bool mirror = ti != tj;
+  // The accumulators go through LDS (the loop above ended with a barrier, so
+  // the operand tiles are dead) and leave in two passes of 16-byte accesses:
+  // a row pass (tile rows, contiguous in the row-major output) and, where a
+  // transposed copy is needed, a column pass (tile columns, contiguous in
+  // the transposed output).
+  constexpr int SP = BT + 4;              // staging pitch in floats
+  static_assert(BT * SP * 4 <= 2 * STAGE, "staging tile does not fit");
+  constexpr int TPR = BT / 8;             // threads per row, 8 elements each
+  constexpr int RPP = 256 / TPR;          // rows per pass
+  float* stg = reinterpret_cast<float*>(smem);
+  {
+    const int half = lane >> 5;
+    const int lc = lane & 31;
 #pragma unroll
     for (int i = 0; i < F; ++i)
 #pragma unroll
       for (int j = 0; j < F; ++j)
 #pragma unroll
-        for (int vg = 0; vg < 4; ++vg) {
-          const int gi0 = ti * BT + wm * WT + i * 32 + 8 * vg + 4 * half;
-          const int gj = tj * BT + wn * WT + j * 32 + lc;
-          float val[4];
+        for (int v = 0; v < 16; ++v)
+          stg[(wm * WT + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3)) * SP + wn * WT + j * 32 + lc] =
+              acc[i][j][v];
+  }
+  __syncthreads();
+  const int pr = tid / TPR;
+  const int pc = (tid % TPR) * 8;
+  const int gi_base = ti * BT, gj_base = tj * BT;
+
+  if constexpr (PHASE == PH_GRAM || PHASE == PH_POLY) {
+    const float gs = (PHASE == PH_GRAM && pa.first) ? scal[te.x].inv2 : 1.f;
+    void* out = (PHASE == PH_GRAM) ? md.A : md.B;
+    const int64_t ld = md.Mp;
+    const bool mirror = ti != tj;
+#pragma unroll 2
+    for (int r = pr; r < BT; r += RPP) {
+      float* sp = stg + r * SP + pc;
+      float v[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float a = acc[i][j][4 * vg + e];
-            if constexpr (PHASE == PH_GRAM) {
-              val[e] = gs * a;
-            } else {
-              const float av = ld1<PREC>(md.A, md.plane_A, int64_t(gi0 + e) * ld + gj);
-              val[e] = pa.b * av + pa.c * a;
-            }
-            st1<PREC>(out, md.plane_A, int64_t(gi0 + e) * ld + gj, val[e]);
-          }
-          if (mirror) st4<PREC>(out, md.plane_A, int64_t(gj) * ld + gi0, val);
-        }
+      for (int e = 0; e < 8; ++e) v[e] = sp[e];
+      const int64_t idx = int64_t(gi_base + r) * ld + gj_base + pc;
+      if constexpr (PHASE == PH_GRAM) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = gs * v[e];
+      } else {
+        float av[8];
+        ld8<PREC>(md.A, md.plane_A, idx, av);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = pa.b * av[e] + pa.c * v[e];
+      }
+      st8<PREC>(out, md.plane_A, idx, v);
+      if (mirror) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sp[e] = v[e];
+      }
+    }
+    if (mirror) {
+      __syncthreads();
+#pragma unroll 2
+      for (int jl = pr; jl < BT; jl += RPP) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = stg[(pc + e) * SP + jl];
+        st8<PREC>(out, md.plane_A, int64_t(gj_base + jl) * ld + gi_base + pc, v);
+      }
+    }
   } else {
     const float s = pa.first ? scal[te.x].inv : 1.f;
     const float cb = (pa.c != 0.f) ? 1.f : pa.b;
     const void* xc = md.X[pa.cur];
     const int64_t ldx = md.Np, ldt = md.Mp;
-    if (!pa.last) {
-      void* xn = md.X[pa.cur ^ 1];
-      void* xtn = md.Xt[pa.cur ^ 1];
+    const bool tr = md.transposed != 0;
+    const float t = update_scale(pa.lr, pa.scale_rule, md.rows, md.cols);
+#pragma unroll 2
+    for (int r = pr; r < BT; r += RPP) {
+      float* sp = stg + r * SP + pc;
+      const int gi = gi_base + r, gj = gj_base + pc;
+      const int64_t idx = int64_t(gi) * ldx + gj;
+      float xv[8], v[8];
+      ld8<PREC>(xc, md.plane_X, idx, xv);
 #pragma unroll
-      for (int i = 0; i < F; ++i)
+      for (int e = 0; e < 8; ++e) v[e] = s * (pa.a * xv[e] + cb * sp[e]);
+      if (!pa.last) {
+        st8<PREC>(md.X[pa.cur ^ 1], md.plane_X, idx, v);
 #pragma unroll
-        for (int j = 0; j < F; ++j)
+        for (int e = 0; e < 8; ++e) sp[e] = v[e];
+      } else if (!tr) {
+        if (gi < md.m) write_back8(md, gi, gj, md.n, v, t);
+      } else {
 #pragma unroll
-          for (int vg = 0; vg < 4; ++vg) {
-            const int gi0 = ti * BT + wm * WT + i * 32 + 8 * vg + 4 * half;
-            const int gj = tj * BT + wn * WT + j * 32 + lc;
-            float val[4];
+        for (int e = 0; e < 8; ++e) sp[e] = v[e];
+      }
+    }
+    if (!pa.last || tr) {
+      __syncthreads();
+#pragma unroll 2
+      for (int jl = pr; jl < BT; jl += RPP) {
+        float v[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float xv = ld1<PREC>(xc, md.plane_X, int64_t(gi0 + e) * ldx + gj);
-              val[e] = s * (pa.a * xv + cb * acc[i][j][4 * vg + e]);
-              st1<PREC>(xn, md.plane_X, int64_t(gi0 + e) * ldx + gj, val[e]);
-            }
-            st4<PREC>(xtn, md.plane_X, int64_t(gj) * ldt + gi0, val);
-          }
-    } else {
-      const float t = update_scale(pa.lr, pa.scale_rule, md.rows, md.cols);
-      const bool tr = md.transposed != 0;
-#pragma unroll
-      for (int i = 0; i < F; ++i)
-#pragma unroll
-        for (int j = 0; j < F; ++j)
-#pragma unroll
-          for (int vg = 0; vg < 4; ++vg) {
-            const int gi0 = ti * BT + wm * WT + i * 32 + 8 * vg + 4 * half;
-            const int gj = tj * BT + wn * WT + j * 32 + lc;
-            if (gj >= md.n) continue;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int gi = gi0 + e;
-              if (gi >= md.m) continue;
-              const float xv = ld1<PREC>(xc, md.plane_X, int64_t(gi) * ldx + gj);
-              const float o = s * (pa.a * xv + cb * acc[i][j][4 * vg + e]);
-              const int r = tr ? gj : gi;
-              const int cidx = tr ? gi : gj;
-              if (md.param) {
-                const int64_t pi = int64_t(r) * md.ld_param + cidx;
-                if (md.param_bf16) {
-                  uint16_t* pw = reinterpret_cast<uint16_t*>(md.param);
-                  const float wv = bf16_bits_to_float(pw[pi]);
-                  pw[pi] = float_to_bf16_bits(wv - t * o);
-                } else {
-                  float* pw = reinterpret_cast<float*>(md.param);
-                  pw[pi] = pw[pi] - t * o;
-                }
-              }
-              if (md.upd) md.upd[int64_t(r) * md.ld_upd + cidx] = o;
-            }
-          }
+        for (int e = 0; e < 8; ++e) v[e] = stg[(pc + e) * SP + jl];
+        const int gj = gj_base + jl, gi = gi_base + pc;
+        if (!pa.last) {
+          st8<PREC>(md.Xt[pa.cur ^ 1], md.plane_X, int64_t(gj) * ldt + gi, v);
+        } else if (gj < md.n) {
+          // tall matrix: natural row gj, natural columns gi .. gi+7
+          write_back8(md, gj, gi, md.m, v, t);
+        }
+      }
     }
   }
 }
