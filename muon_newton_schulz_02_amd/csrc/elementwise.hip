@@ -2,8 +2,8 @@
 //
 //  * momentum_kernel: per element, in binary32 with one rounding per
 //    operation, M <- beta*M + G and U <- G + beta*M (Nesterov) or U <- M;
-//    stores U into the workspace twice (the natural layout and, through an
-//    LDS transpose, the transposed layout) in the Newton-Schulz storage
+//    stores U into the workspace in the wide orientation X (m x n, m <= n;
+//    through an LDS transpose for tall matrices) in the Newton-Schulz storage
 //    format, zero-filling the padding; writes one binary32 sum of u^2 per
 //    64x64 tile (wavefront shuffles, then LDS across the four waves).
 //  * norm_finalize_kernel: sums a matrix's tile partials in a fixed order
@@ -99,11 +99,9 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
   const int rows = md.rows, cols = md.cols;
   const int prec = md.prec;
   const bool tr = md.transposed != 0;
-  // natural-layout and transposed-layout copies of U in the workspace
-  void* nat = tr ? md.Xt[0] : md.X[0];
-  void* trn = tr ? md.X[0] : md.Xt[0];
-  const int64_t nat_ld = tr ? md.Mp : md.Np;
-  const int64_t trn_ld = tr ? md.Np : md.Mp;
+  // X = U (wide) or X = U^T (tall), row stride Np
+  void* xw = md.X[0];
+  const int64_t ldx = md.Np;
   float ss = 0.f;
 
 #pragma unroll
@@ -168,13 +166,16 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
 #pragma unroll
     for (int e = 0; e < 4; ++e) ss += u[e] * u[e];
     if (mode != 2) {
-      store4_ws(nat, md.plane_X, prec, int64_t(row) * nat_ld + col, u);
+      if (!tr) {
+        store4_ws(xw, md.plane_X, prec, int64_t(row) * ldx + col, u);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tile[rl][4 * cg + e] = u[e];
+        for (int e = 0; e < 4; ++e) tile[rl][4 * cg + e] = u[e];
+      }
     }
   }
 
-  if (mode != 2) {
+  if (mode != 2 && tr) {
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = tile[4 * cg + e][j];
-      store4_ws(trn, md.plane_X, prec, int64_t(tc0 + j) * trn_ld + tr0 + 4 * cg, v);
+      store4_ws(xw, md.plane_X, prec, int64_t(tc0 + j) * ldx + tr0 + 4 * cg, v);
     }
   }
 
@@ -230,14 +231,14 @@ __global__ __launch_bounds__(256) void writeback_direct_kernel(const MatDev* __r
   const int tr0 = (local / md.etile_cols) * ETILE;
   const int tc0 = (local % md.etile_cols) * ETILE;
   const bool tr = md.transposed != 0;
-  const void* nat = tr ? md.Xt[0] : md.X[0];
-  const int64_t nat_ld = tr ? md.Mp : md.Np;
+  const void* xw = md.X[0];
   const float inv = scal[mi].inv;
   const float t = update_scale(lr, scale_rule, md.rows, md.cols);
   for (int e = threadIdx.x; e < ETILE * ETILE; e += 256) {
     const int row = tr0 + e / ETILE, col = tc0 + e % ETILE;
     if (row >= md.rows || col >= md.cols) continue;
-    const float o = inv * load_ws(nat, md.plane_X, md.prec, int64_t(row) * nat_ld + col);
+    const int64_t xi = tr ? int64_t(col) * md.Np + row : int64_t(row) * md.Np + col;
+    const float o = inv * load_ws(xw, md.plane_X, md.prec, xi);
     if (md.param) {
       const int64_t pi = int64_t(row) * md.ld_param + col;
       if (md.param_bf16) {

@@ -1,7 +1,7 @@
 // Host runtime and C ABI of libmuon_mi355x.so: argument validation, the
 // per-device workspace, cached launch plans and the launch sequence of one
 // Muon step (declared in include/muon.h).
-#include "../../include/muon.h"
+#include "muon.h"
 
 #include <hip/hip_runtime.h>
 
@@ -37,7 +37,6 @@ constexpr int64_t MAX_DIM = 65536;
 constexpr int32_t MAX_COUNT = 1 << 20;
 constexpr int32_t MAX_NS_STEPS = 1000;
 constexpr size_t MAX_PLANS = 8;
-constexpr int GROUP_M = 8;  // tile rows per raster band
 
 enum Mode { MODE_STEP = 0, MODE_NS = 1, MODE_NORMS = 2 };
 
@@ -85,7 +84,7 @@ size_t workspace_bytes(const muon_matrix_desc* shapes, int32_t count) {
   size_t tot = 0;
   for (int32_t i = 0; i < count; ++i) {
     MatGeom g = geom_of(shapes[i]);
-    tot += 4 * g.x_bytes + 2 * g.a_bytes;
+    tot += 2 * g.x_bytes + 2 * g.a_bytes;
   }
   return tot;
 }
@@ -168,6 +167,7 @@ struct Plan {
 struct DeviceState {
   void* ws = nullptr;
   size_t ws_bytes = 0;
+  int cus_per_xcd = 0;
   std::list<Plan*> plans;  // most recently used first
 };
 
@@ -281,7 +281,9 @@ muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vec
       for (int i : order) {
         const MatDev& m = hm[i];
         if (m.prec != prec) continue;
-        const int tm = m.Mp / NS_TILE, tn = m.Np / NS_TILE;
+        const int T = ns_tile(prec);
+        const int GROUP_M = T == 256 ? 4 : 8;  // tile rows per raster band
+        const int tm = m.Mp / T, tn = m.Np / T;
         // grouped raster: bands of GROUP_M tile rows, walked column by column,
         // so tiles in flight together share row and column operand panels
         if (ph == PH_COMB) {
@@ -440,6 +442,14 @@ muon_status run(const Call& c) {
   }
   std::lock_guard<std::mutex> lock(g_mu);
   DeviceState& ds = g_dev[dev];
+  if (ds.cus_per_xcd == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+      (void)hipGetLastError();
+      return fail(MUON_ERR_HIP, "cannot query the compute-unit count of device %d", dev);
+    }
+    ds.cus_per_xcd = std::max(1, cus / NUM_XCD);
+  }
 
   // workspace
   const size_t need = c.mode == MODE_NORMS ? 0 : workspace_bytes(c.shapes, c.count);
@@ -535,8 +545,6 @@ muon_status run(const Call& c) {
         m.plane_A = g.Mp * g.Mp;
         m.X[0] = ws + wo; wo += g.x_bytes;
         m.X[1] = ws + wo; wo += g.x_bytes;
-        m.Xt[0] = ws + wo; wo += g.x_bytes;
-        m.Xt[1] = ws + wo; wo += g.x_bytes;
         m.A = ws + wo; wo += g.a_bytes;
         m.B = ws + wo; wo += g.a_bytes;
       }
@@ -587,9 +595,10 @@ muon_status run(const Call& c) {
         pa.first = it == 0;
         pa.last = it == c.ns_steps - 1;
         pa.scale_rule = c.scale_rule;
+        pa.cus_per_xcd = ds.cus_per_xcd;
         for (const auto& g : plan->groups) {
           for (int ph = 0; ph < 3 && e == hipSuccess; ++ph) {
-            if (ph == PH_POLY && c.co.c == 0.f) continue;
+            if (ph == PH_POLY && c.co.c == 0.f) continue;  // GRAM already formed B = b A
             pa.per_xcd = g.per_xcd[ph];
             e = timed(MUON_KC_GRAM + ph, c.stream, [&] {
               return launch_ns_phase(g.prec, ph, plan->d_mats, plan->d_scal, g.tiles[ph], pa, c.stream);

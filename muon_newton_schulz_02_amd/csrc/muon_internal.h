@@ -33,16 +33,15 @@ struct MatDev {
   int32_t transposed;     // rows > cols
   int32_t param_bf16, grad_bf16;
   int32_t vec_ok;         // grad/mom rows allow 4-element vector access
-  int32_t wvec_ok;        // param rows allow 8-element (16/32-byte) vector access
+  int32_t wvec_ok;        // param rows allow 8-element vector access (16-byte aligned)
   int32_t uvec_ok;        // update-export rows allow 4-float vector access
   int32_t prec;           // Prec
   int32_t etile_cols;     // elementwise tiles along the natural columns
   // workspace: element buffers; BF16X3 keeps the lo plane `plane_*`
   // elements after the hi plane
   void* X[2];             // Mp x Np (ping-pong)
-  void* Xt[2];            // Np x Mp (transposed copies)
-  void* A;                // Mp x Mp Gram
-  void* B;                // Mp x Mp polynomial
+  void* A;                // Mp x Mp Gram matrix (tiles on or above the diagonal)
+  void* B;                // Mp x Mp b A + c A^2 (tiles on or above the diagonal)
   int64_t plane_X, plane_A;
 };
 
@@ -55,6 +54,7 @@ struct PhaseArgs {
   int32_t last;           // combine: write back instead of storing X
   int32_t scale_rule;
   int32_t per_xcd;        // tile-list entries per XCD
+  int32_t cus_per_xcd;    // compute units per XCD (persistent grid size)
 };
 
 // Per-matrix scalars written by the norm finalize kernel.
@@ -78,7 +78,9 @@ enum Phase : int { PH_GRAM = 0, PH_POLY = 1, PH_COMB = 2 };
 hipError_t launch_ns_phase(int prec, int phase, const MatDev* mats, const MatScal* scal,
                            const int2* tiles, const PhaseArgs& args, hipStream_t stream);
 
-// Tile edge of the Newton-Schulz products (square tiles).
-constexpr int NS_TILE = 128;
+// Tile edge of the Newton-Schulz products (square tiles) per format: 256 for
+// bf16 (LDS holds two stages of 256x64 bf16 per operand); 128 where an
+// operand takes twice the bytes (split-bf16 planes, float32).
+constexpr int ns_tile(int prec) { return prec == PREC_BF16 ? 256 : 128; }
 
 }  // namespace muon

@@ -1,37 +1,57 @@
-// Newton-Schulz matrix products on gfx950 MFMA, one grouped launch per
-// phase over every matrix of the call.
+// Newton-Schulz matrix products on gfx950 MFMA: one persistent, grouped
+// launch per phase over every matrix of the call.
 //
 // A polynomial Newton-Schulz step (N. J. Higham, Functions of Matrices,
 // ch. 8; the Muon optimizer's orthogonalisation in "开发者千美元训3.8B模型
-// 击败GPT-2", paragraph 影响) on a wide matrix X (m x n, m <= n) is three
-// products, each written here as C = P Q^T with both operands read along
-// their contiguous (K) dimension:
+// 击败GPT-2", paragraph 影响) on a wide matrix X (m x n, m <= n),
 //
-//   GRAM  A = s^2 * X X^T          P = Q = X (m x n), K = n; symmetric, so only
-//                                  tiles on or above the diagonal run and each
-//                                  stores itself and its mirror.
-//   POLY  B = b A + c A A^T        P = Q = A (A is symmetric, A A = A A^T);
-//                                  symmetric like GRAM; b A added in the
-//                                  epilogue.  Skipped when c == 0.
-//   COMB  X' = s (a X + B X)       P = B (or A when c == 0, with B X -> b A X),
-//                                  Q = X^T (n x m), K = m.  The epilogue adds
-//                                  a X and stores X' in both layouts (X' for
-//                                  the next GRAM, X'^T for the next COMB); on
-//                                  the last step it writes the update back
-//                                  into the weight instead.
+//     X' = a X + (b A + c A^2) X,   A = X X^T,
+//
+// is three products, each C[i][j] = sum_k P[i][k] Q[j][k] + alpha D[i][j]:
+//
+//   GRAM  A  = s^2 X X^T            P = Q = X (rows of X, K = n).  With c == 0
+//                                   it stores B = b A instead and POLY is skipped.
+//   POLY  B  = c (A A + (b/c) A)    P = Q = A (A symmetric), K = m.
+//   COMB  X' = s (B X + a X)        P = B (symmetric), Q[j][k] = X[k][j], K = m.
+//                                   The last step writes the update back into
+//                                   the weight instead of storing X'.
 //
 // s = 1/(||U||_F + eps) on the first step (the momentum kernel stores U
 // unscaled) and 1 afterwards.
 //
-// Tiles: NS_TILE x NS_TILE outputs per 256-thread workgroup (four waves,
-// 2 x 2, each NS_TILE/2 square), K staged 128 bytes per row at a time through
-// double-buffered LDS with a 16-byte row pad.  Operands are zero-padded to a
-// multiple of 256 in the workspace, so no load is predicated.  Tile lists
-// are split into one contiguous, cost-balanced segment per XCD; workgroup b
-// runs on XCD b % 8 and takes entry b / 8 of that XCD's segment, so tiles
-// that share operand panels share an L2.
+// Design points:
+//  * The MFMA A operand is the Q side and the B operand the P side, so each
+//    lane's accumulators hold four consecutive output columns of one output
+//    row: row-major outputs leave as 8-byte stores, and no transposed copy of
+//    any matrix is kept.
+//  * A and B are symmetric, so GRAM and POLY compute and store only the tiles
+//    on or above the diagonal.  A consumer that needs a block below the
+//    diagonal stages the mirror block transposed.
+//  * Q in COMB reads X along its rows (the contraction index k is X's row
+//    index): each thread loads an 8 x 8 block (4 x 4 for float32), transposes
+//    it in registers and writes one 16-byte LDS chunk per row.  The same path
+//    serves the lower triangle of A and B.
+//  * The additive terms a X and (b/c) A run on the matrix cores: where the
+//    k-slab meets the tile's own rows, extra MFMAs pair the Q fragment with
+//    a scaled identity fragment (for bf16 the scale is split into hi + lo, so
+//    the term carries about 17 significant bits, far inside the bf16 storage
+//    error), and no epilogue reads memory.
+//  * LDS rows hold 128 bytes of K at a pitch of 144 bytes; the 16-byte chunk
+//    ch of row r sits at chunk position ch ^ ((r >> 4) & 7).  Fragment reads
+//    (16 consecutive rows) and transposed writes (rows 8 apart) are then both
+//    free of bank conflicts.
+//  * Tiles: T x T per 256-thread workgroup (T = 256 for bf16, 128 for the
+//    split-bf16 and float32 formats), four waves in a 2 x 2 layout, each
+//    T/2 square; K staged 128 bytes per row, double-buffered through LDS
+//    with register staging.  Operands are zero-padded to a multiple of 256.
+//  * Tile lists are split into one contiguous, cost-balanced segment per XCD;
+//    a persistent grid walks them, workgroup b on XCD b % 8 taking entries
+//    b/8, b/8 + grid/8, ... of that XCD's segment, so tiles that share
+//    operand panels share an L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "muon_internal.h"
 #include "numeric.h"
@@ -46,6 +66,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// Loads through address space 1 compile to global_load (counted by vmcnt
+// only); generic pointers give flat loads, which also count in lgkmcnt and
+// so make every LDS wait also wait for the in-flight global loads.
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+typedef __attribute__((address_space(1))) const u32x2 gu32x2;
 
 constexpr int KB = 128;     // bytes of K per operand row per stage
 constexpr int PITCH = 144;  // LDS row pitch in bytes
@@ -55,422 +81,527 @@ template <> struct Fmt<PREC_BF16> { static constexpr int esz = 2, npl = 1; };
 template <> struct Fmt<PREC_BF16X3> { static constexpr int esz = 2, npl = 2; };
 template <> struct Fmt<PREC_F32> { static constexpr int esz = 4, npl = 1; };
 
-template <int PREC>
-__device__ __forceinline__ float ld1(const void* base, int64_t plane, int64_t idx) {
-  if constexpr (PREC == PREC_F32) {
-    return reinterpret_cast<const float*>(base)[idx];
-  } else {
-    const uint16_t* p = reinterpret_cast<const uint16_t*>(base);
-    float v = bf16_bits_to_float(p[idx]);
-    if constexpr (PREC == PREC_BF16X3) v = v + bf16_bits_to_float(p[plane + idx]);
-    return v;
-  }
-}
+__device__ __forceinline__ int lds_off(int r, int ch) { return r * PITCH + ((ch ^ ((r >> 4) & 7)) << 4); }
 
-template <int PREC>
-__device__ __forceinline__ void st1(void* base, int64_t plane, int64_t idx, float v) {
-  if constexpr (PREC == PREC_F32) {
-    reinterpret_cast<float*>(base)[idx] = v;
-  } else {
-    uint16_t* p = reinterpret_cast<uint16_t*>(base);
-    const uint16_t h = float_to_bf16_bits(v);
-    p[idx] = h;
-    if constexpr (PREC == PREC_BF16X3) p[plane + idx] = float_to_bf16_bits(v - bf16_bits_to_float(h));
-  }
-}
+// ------------------------------------------------------------------ storage
 
-// four consecutive elements, idx a multiple of 4
+// Four consecutive values of the working format at element idx (a multiple
+// of 4); the split-bf16 format keeps its lo plane `plane` elements further.
 template <int PREC>
 __device__ __forceinline__ void st4(void* base, int64_t plane, int64_t idx, const float* v) {
   if constexpr (PREC == PREC_F32) {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + idx) = f32x4{v[0], v[1], v[2], v[3]};
   } else {
     uint16_t* p = reinterpret_cast<uint16_t*>(base);
-    uint16_t h[4];
+    uint32_t h[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) h[e] = float_to_bf16_bits(v[e]);
-    *reinterpret_cast<uint2*>(p + idx) =
-        make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+    *reinterpret_cast<u32x2*>(p + idx) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
     if constexpr (PREC == PREC_BF16X3) {
-      uint16_t l[4];
+      uint32_t l[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) l[e] = float_to_bf16_bits(v[e] - bf16_bits_to_float(h[e]));
-      *reinterpret_cast<uint2*>(p + plane + idx) =
-          make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
+      *reinterpret_cast<u32x2*>(p + plane + idx) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
     }
   }
 }
 
-// eight consecutive elements, idx a multiple of 8
-template <int PREC>
-__device__ __forceinline__ void ld8(const void* base, int64_t plane, int64_t idx, float* v) {
-  if constexpr (PREC == PREC_F32) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + idx);
-    const f32x4 a = p[0], b = p[1];
-    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
-    v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
-  } else {
-    const uint16_t* p = reinterpret_cast<const uint16_t*>(base);
-    const u32x4 h = *reinterpret_cast<const u32x4*>(p + idx);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[2 * e] = bf16_bits_to_float(h[e] & 0xFFFFu);
-      v[2 * e + 1] = bf16_bits_to_float(h[e] >> 16);
-    }
-    if constexpr (PREC == PREC_BF16X3) {
-      const u32x4 l = *reinterpret_cast<const u32x4*>(p + plane + idx);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[2 * e] = v[2 * e] + bf16_bits_to_float(l[e] & 0xFFFFu);
-        v[2 * e + 1] = v[2 * e + 1] + bf16_bits_to_float(l[e] >> 16);
-      }
-    }
-  }
-}
-
-template <int PREC>
-__device__ __forceinline__ void st8(void* base, int64_t plane, int64_t idx, const float* v) {
-  if constexpr (PREC == PREC_F32) {
-    f32x4* p = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + idx);
-    p[0] = f32x4{v[0], v[1], v[2], v[3]};
-    p[1] = f32x4{v[4], v[5], v[6], v[7]};
-  } else {
-    uint16_t* p = reinterpret_cast<uint16_t*>(base);
-    uint16_t h[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = float_to_bf16_bits(v[e]);
-    u32x4 hv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) hv[e] = uint32_t(h[2 * e]) | (uint32_t(h[2 * e + 1]) << 16);
-    *reinterpret_cast<u32x4*>(p + idx) = hv;
-    if constexpr (PREC == PREC_BF16X3) {
-      u32x4 lv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t l0 = float_to_bf16_bits(v[2 * e] - bf16_bits_to_float(h[2 * e]));
-        const uint32_t l1 = float_to_bf16_bits(v[2 * e + 1] - bf16_bits_to_float(h[2 * e + 1]));
-        lv[e] = l0 | (l1 << 16);
-      }
-      *reinterpret_cast<u32x4*>(p + plane + idx) = lv;
-    }
-  }
-}
-
-// W[row][c0 .. c0+7] <- rnd(W - t*o) for the columns below `ncols`, and the
-// optional binary32 export of o.
-__device__ __forceinline__ void write_back8(const MatDev& md, int row, int c0, int ncols, const float* o,
-                                            float t) {
-  const int cnt = ncols - c0;
-  if (cnt <= 0) return;
+// W[row][col] <- rnd(W - t*o), and the optional binary32 export of o.
+__device__ __forceinline__ void write_back1(const MatDev& md, int row, int col, float o, float t) {
   if (md.param) {
-    const int64_t pi = int64_t(row) * md.ld_param + c0;
+    const int64_t pi = int64_t(row) * md.ld_param + col;
     if (md.param_bf16) {
       uint16_t* pw = reinterpret_cast<uint16_t*>(md.param) + pi;
-      if (cnt >= 8 && md.wvec_ok) {
-        u32x4 raw = *reinterpret_cast<const u32x4*>(pw);
+      *pw = float_to_bf16_bits(bf16_bits_to_float(*pw) - t * o);
+    } else {
+      float* pw = reinterpret_cast<float*>(md.param) + pi;
+      *pw = *pw - t * o;
+    }
+  }
+  if (md.upd) md.upd[int64_t(row) * md.ld_upd + col] = o;
+}
+
+// The same for W[row][c0 .. c0+NE-1] (NE = 4 or 8, c0 a multiple of NE),
+// columns below ncols only.  wvec_ok promises 16-byte aligned rows.
+template <int NE>
+__device__ __forceinline__ void write_back_n(const MatDev& md, int row, int c0, int ncols, const float* o,
+                                             float t) {
+  const int cnt = ncols - c0;
+  if (cnt <= 0) return;
+  if (cnt >= NE && md.wvec_ok) {
+    const int64_t pi = int64_t(row) * md.ld_param + c0;
+    if (md.param) {
+      if (md.param_bf16) {
+        uint16_t* pw = reinterpret_cast<uint16_t*>(md.param) + pi;
+        uint32_t raw[NE / 2];
+        if constexpr (NE == 8) {
+          const u32x4 r4 = *reinterpret_cast<const u32x4*>(pw);
+          raw[0] = r4[0]; raw[1] = r4[1]; raw[2] = r4[2]; raw[3] = r4[3];
+        } else {
+          const u32x2 r2 = *reinterpret_cast<const u32x2*>(pw);
+          raw[0] = r2[0]; raw[1] = r2[1];
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float w0 = bf16_bits_to_float(raw[e] & 0xFFFFu);
-          const float w1 = bf16_bits_to_float(raw[e] >> 16);
+        for (int e = 0; e < NE / 2; ++e) {
+          const float w0 = bf16_bits_to_float(raw[e] & 0xFFFFu), w1 = bf16_bits_to_float(raw[e] >> 16);
           raw[e] = uint32_t(float_to_bf16_bits(w0 - t * o[2 * e])) |
                    (uint32_t(float_to_bf16_bits(w1 - t * o[2 * e + 1])) << 16);
         }
-        *reinterpret_cast<u32x4*>(pw) = raw;
-      } else {
-        for (int e = 0; e < 8 && e < cnt; ++e) pw[e] = float_to_bf16_bits(bf16_bits_to_float(pw[e]) - t * o[e]);
-      }
-    } else {
-      float* pw = reinterpret_cast<float*>(md.param) + pi;
-      if (cnt >= 8 && md.wvec_ok) {
-        f32x4* q = reinterpret_cast<f32x4*>(pw);
-        f32x4 a = q[0], b = q[1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = a[e] - t * o[e];
-          b[e] = b[e] - t * o[4 + e];
+        if constexpr (NE == 8) {
+          *reinterpret_cast<u32x4*>(pw) = u32x4{raw[0], raw[1], raw[2], raw[3]};
+        } else {
+          *reinterpret_cast<u32x2*>(pw) = u32x2{raw[0], raw[1]};
         }
-        q[0] = a;
-        q[1] = b;
       } else {
-        for (int e = 0; e < 8 && e < cnt; ++e) pw[e] = pw[e] - t * o[e];
+        f32x4* pw = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(md.param) + pi);
+#pragma unroll
+        for (int h = 0; h < NE / 4; ++h) {
+          f32x4 w = pw[h];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = w[e] - t * o[4 * h + e];
+          pw[h] = w;
+        }
       }
     }
+    if (md.upd) {
+      float* pu = md.upd + int64_t(row) * md.ld_upd + c0;
+      if (md.uvec_ok) {
+#pragma unroll
+        for (int h = 0; h < NE / 4; ++h)
+          reinterpret_cast<f32x4*>(pu)[h] = f32x4{o[4 * h], o[4 * h + 1], o[4 * h + 2], o[4 * h + 3]};
+      } else {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) pu[e] = o[e];
+      }
+    }
+    return;
   }
-  if (md.upd) {
-    float* pu = md.upd + int64_t(row) * md.ld_upd + c0;
-    if (cnt >= 8 && md.uvec_ok) {
-      f32x4* q = reinterpret_cast<f32x4*>(pu);
-      q[0] = f32x4{o[0], o[1], o[2], o[3]};
-      q[1] = f32x4{o[4], o[5], o[6], o[7]};
-    } else {
-      for (int e = 0; e < 8 && e < cnt; ++e) pu[e] = o[e];
+  for (int e = 0; e < NE && e < cnt; ++e) write_back1(md, row, c0 + e, o[e], t);
+}
+
+// ------------------------------------------------------------------ MFMA
+
+// acc += A operand (Q side) x B operand (P side) over one k-slab.
+template <int PREC>
+__device__ __forceinline__ void mfma_step(f32x16& acc, const u32x4* q, const u32x4* p) {
+  if constexpr (PREC == PREC_BF16) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q[0]),
+                                                   __builtin_bit_cast(bf16x8, p[0]), acc, 0, 0, 0);
+  } else if constexpr (PREC == PREC_BF16X3) {
+    // small cross terms first, then hi*hi
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q[1]),
+                                                   __builtin_bit_cast(bf16x8, p[0]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q[0]),
+                                                   __builtin_bit_cast(bf16x8, p[1]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q[0]),
+                                                   __builtin_bit_cast(bf16x8, p[0]), acc, 0, 0, 0);
+  } else {
+    const f32x4 fq = __builtin_bit_cast(f32x4, q[0]);
+    const f32x4 fp = __builtin_bit_cast(f32x4, p[0]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fq.x, fp.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fq.y, fp.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fq.z, fp.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fq.w, fp.w, acc, 0, 0, 0);
+  }
+}
+
+// A P-side fragment of alpha * I for one k-slab: this lane's values are the
+// k-values of one row; `pos` is the index of the diagonal entry among them
+// (outside the range: none).  For the bf16 formats alpha is split into
+// hi + lo bf16 values: out[0] carries hi, out[1] lo.
+template <int PREC>
+__device__ __forceinline__ void identity_frag(u32x4* out, int pos, float alpha) {
+  if constexpr (PREC == PREC_F32) {
+    const uint32_t bits = __float_as_uint(alpha);
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (pos == e) ? bits : 0u;
+    out[0] = v;
+  } else {
+    const uint32_t hi = float_to_bf16_bits(alpha);
+    const uint32_t lo = float_to_bf16_bits(alpha - bf16_bits_to_float(hi));
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl) {
+      const uint32_t bits = pl == 0 ? hi : lo;
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (pos == 2 * e ? bits : 0u) | (pos == 2 * e + 1 ? (bits << 16) : 0u);
+      out[pl] = v;
     }
   }
 }
 
 template <int PREC>
-__device__ __forceinline__ void mfma_step(f32x16& acc, const u32x4* a, const u32x4* b) {
+__device__ __forceinline__ void mfma_identity(f32x16& acc, const u32x4* q, const u32x4* id) {
   if constexpr (PREC == PREC_BF16) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
-                                                   __builtin_bit_cast(bf16x8, b[0]), acc, 0, 0, 0);
-  } else if constexpr (PREC == PREC_BF16X3) {
-    // small cross terms first, then hi*hi
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[1]),
-                                                   __builtin_bit_cast(bf16x8, b[0]), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
-                                                   __builtin_bit_cast(bf16x8, b[1]), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
-                                                   __builtin_bit_cast(bf16x8, b[0]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q[0]),
+                                                   __builtin_bit_cast(bf16x8, id[1]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q[0]),
+                                                   __builtin_bit_cast(bf16x8, id[0]), acc, 0, 0, 0);
   } else {
-    const f32x4 fa = __builtin_bit_cast(f32x4, a[0]);
-    const f32x4 fb = __builtin_bit_cast(f32x4, b[0]);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.x, fb.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.y, fb.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.z, fb.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.w, fb.w, acc, 0, 0, 0);
+    mfma_step<PREC>(acc, q, id);
   }
 }
 
-// Global -> registers: one stage (KB bytes of K) of BT rows, 16 bytes per
-// chunk, eight chunks per row, chunk c = tid + 256*q.
-template <int NPL, int CH, int ESZ>
-__device__ __forceinline__ void load_tile(u32x4 (&r)[NPL][CH], const char* g, int64_t plane, int64_t ld,
-                                          int kt, int tid) {
+// ------------------------------------------------------------------ staging
+
+// Staging geometry of one operand of a T x T tile for one stage (KB bytes of K).
+//   direct: the operand's rows are K-contiguous; chunk c = tid + 256 q is
+//           row c / 8, 16-byte chunk c % 8.  CH chunks per thread.
+//   trans:  the operand's element (row r, k) sits at memory (k, r), row
+//           stride ld; a block is KPB k-values x KPB rows (KPB = 16 / esz), one
+//           16-byte load per k-value, transposed in registers into one 16-byte
+//           chunk per row.  NB blocks per stage, PER per thread.
+template <int ESZ, int BT>
+struct Geo {
+  static constexpr int CH = BT * (KB / 16) / 256;
+  static constexpr int KPB = 16 / ESZ;
+  static constexpr int RB = BT / KPB;
+  static constexpr int NB = RB * (KB / 16);
+  static constexpr int PER = (NB + 255) / 256;
+  static constexpr int NREG = (CH > PER * KPB) ? CH : PER * KPB;
+};
+
+// Where one operand of one tile comes from.
+struct OpSrc {
+  const char* direct;      // its row 0, k = 0 (direct layout); null if never direct
+  const char* trans;       // memory element (k = 0, its row 0) of the transposed layout
+  int64_t ld_b;            // row stride in bytes (both layouts)
+  int64_t plane_b;         // bytes between the hi and lo planes
+  int sym_tile;            // symmetric operand: its tile-row index; -1: fixed layout
+  int always_trans;        // COMB's X operand
+};
+
+template <int ESZ, int BT>
+__device__ __forceinline__ bool stage_is_trans(const OpSrc& s, int kt) {
+  if (s.always_trans) return true;
+  if (s.sym_tile < 0) return false;
+  return (kt * (KB / ESZ)) / BT < s.sym_tile;  // below the diagonal: read the mirror block
+}
+
+template <int ESZ, int BT, int NPL, int NREG>
+__device__ __forceinline__ void load_stage(u32x4 (&r)[NPL][NREG], const OpSrc& s, int kt, int tid) {
+  using G = Geo<ESZ, BT>;
+  if (stage_is_trans<ESZ, BT>(s, kt)) {
+    const int k0 = kt * (KB / ESZ);
 #pragma unroll
-  for (int q = 0; q < CH; ++q) {
-    const int c = tid + 256 * q;
-    const int64_t off = int64_t(c >> 3) * ld * ESZ + int64_t(kt) * KB + (c & 7) * 16;
+    for (int q = 0; q < G::PER; ++q) {
+      const int blk = tid + 256 * q;
+      if (G::NB % 256 != 0 && blk >= G::NB) break;
+      const int rb = blk % G::RB, kc = blk / G::RB;   // row block, K chunk
 #pragma unroll
-    for (int pl = 0; pl < NPL; ++pl)
-      r[pl][q] = *reinterpret_cast<const u32x4*>(g + pl * plane * ESZ + off);
+      for (int e = 0; e < G::KPB; ++e) {
+        const int64_t off = int64_t(k0 + kc * G::KPB + e) * s.ld_b + rb * 16;
+#pragma unroll
+        for (int pl = 0; pl < NPL; ++pl) r[pl][q * G::KPB + e] = *(gu32x4*)(s.trans + pl * s.plane_b + off);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < G::CH; ++q) {
+      const int c = tid + 256 * q;
+      const int64_t off = int64_t(c >> 3) * s.ld_b + int64_t(kt) * KB + (c & 7) * 16;
+#pragma unroll
+      for (int pl = 0; pl < NPL; ++pl) r[pl][q] = *(gu32x4*)(s.direct + pl * s.plane_b + off);
+    }
   }
 }
 
-// Registers -> LDS (row pitch PITCH; the planes of one operand follow each other).
-template <int NPL, int CH>
-__device__ __forceinline__ void store_tile(const u32x4 (&r)[NPL][CH], char* lds, int tid) {
-  constexpr int OPB = CH * 32 * PITCH;  // CH*256/8 rows
+// 8x8 transpose of 16-bit values: in[e] holds k-value e of 8 consecutive
+// rows (two rows per dword); out[c] holds the 8 k-values of row c.
+__device__ __forceinline__ void transpose8x8_b16(const u32x4* in, u32x4* out) {
 #pragma unroll
-  for (int q = 0; q < CH; ++q) {
-    const int c = tid + 256 * q;
+  for (int c2 = 0; c2 < 4; ++c2) {
+    u32x4 even, odd;
 #pragma unroll
-    for (int pl = 0; pl < NPL; ++pl)
-      *reinterpret_cast<u32x4*>(lds + pl * OPB + (c >> 3) * PITCH + (c & 7) * 16) = r[pl][q];
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const uint32_t a = in[2 * e2][c2], b = in[2 * e2 + 1][c2];
+      even[e2] = __builtin_amdgcn_perm(b, a, 0x05040100u);   // a.lo, b.lo: row 2 c2
+      odd[e2] = __builtin_amdgcn_perm(b, a, 0x07060302u);    // a.hi, b.hi: row 2 c2 + 1
+    }
+    out[2 * c2] = even;
+    out[2 * c2 + 1] = odd;
   }
 }
 
-template <int PREC, int PHASE, int BT>
-__global__ __launch_bounds__(256) void ns_gemm_kernel(const MatDev* __restrict__ mats,
-                                                      const MatScal* __restrict__ scal,
-                                                      const int2* __restrict__ tiles, PhaseArgs pa) {
+template <int ESZ, int BT, int NPL, int NREG, int OPB>
+__device__ __forceinline__ void store_stage(const u32x4 (&r)[NPL][NREG], const OpSrc& s, int kt, char* lds,
+                                            int tid) {
+  using G = Geo<ESZ, BT>;
+  if (stage_is_trans<ESZ, BT>(s, kt)) {
+#pragma unroll
+    for (int q = 0; q < G::PER; ++q) {
+      const int blk = tid + 256 * q;
+      if (G::NB % 256 != 0 && blk >= G::NB) break;
+      const int rb = blk % G::RB, kc = blk / G::RB;
+#pragma unroll
+      for (int pl = 0; pl < NPL; ++pl) {
+        u32x4 t[G::KPB];
+        if constexpr (ESZ == 2) {
+          transpose8x8_b16(&r[pl][q * G::KPB], t);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            t[c] = u32x4{r[pl][q * 4 + 0][c], r[pl][q * 4 + 1][c], r[pl][q * 4 + 2][c], r[pl][q * 4 + 3][c]};
+        }
+#pragma unroll
+        for (int c = 0; c < G::KPB; ++c)
+          *reinterpret_cast<u32x4*>(lds + pl * OPB + lds_off(rb * G::KPB + c, kc)) = t[c];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < G::CH; ++q) {
+      const int c = tid + 256 * q;
+#pragma unroll
+      for (int pl = 0; pl < NPL; ++pl) *reinterpret_cast<u32x4*>(lds + pl * OPB + lds_off(c >> 3, c & 7)) = r[pl][q];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ tile
+
+// VAR: GRAM 1 = c != 0 (store A), 0 = c == 0 (store B = b A);
+//      COMB 1 = last step (write-back), 0 = store the next iterate.
+template <int PREC, int PHASE, int BT, int VAR>
+__device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __restrict__ scal, int mat,
+                                             int ti, int tj, const PhaseArgs& pa, char* smem) {
   constexpr int ESZ = Fmt<PREC>::esz;
   constexpr int NPL = Fmt<PREC>::npl;
+  using G = Geo<ESZ, BT>;
   constexpr int WT = BT / 2;               // wave tile edge
   constexpr int F = WT / 32;               // 32x32 MFMA blocks per wave edge
-  constexpr int CH = BT * (KB / 16) / 256; // 16-byte chunks per thread, per operand plane
   constexpr int OPB = BT * PITCH;          // LDS bytes of one operand plane
   constexpr int STAGE = 2 * NPL * OPB;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
-
-  const int bid = blockIdx.x;
-  const int2 te = tiles[(bid % NUM_XCD) * pa.per_xcd + bid / NUM_XCD];
-  if (te.x < 0) return;
-  const MatDev& md = mats[te.x];
-  const int ti = te.y >> 16, tj = te.y & 0xFFFF;
+  constexpr int KE = KB / ESZ;             // k-values per stage
+  constexpr int KS = ESZ == 2 ? 16 : 8;    // k-values per MFMA slab
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int wm = w & 1, wn = w >> 1;
+  const int wq = w & 1, wp = w >> 1;       // Q-side (columns) and P-side (rows) halves
 
-  const char* Pg;
-  const char* Qg;
-  int64_t ldP, ldQ, planeP, planeQ;
+  OpSrc sp, sq;
   int K;
   if constexpr (PHASE == PH_GRAM) {
-    Pg = Qg = reinterpret_cast<const char*>(md.X[pa.cur]);
-    ldP = ldQ = md.Np;
-    planeP = planeQ = md.plane_X;
+    const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
+    const int64_t ld = int64_t(md.Np) * ESZ;
+    sp = {x + int64_t(ti) * BT * ld, nullptr, ld, md.plane_X * ESZ, -1, 0};
+    sq = {x + int64_t(tj) * BT * ld, nullptr, ld, md.plane_X * ESZ, -1, 0};
     K = md.Np;
   } else if constexpr (PHASE == PH_POLY) {
-    Pg = Qg = reinterpret_cast<const char*>(md.A);
-    ldP = ldQ = md.Mp;
-    planeP = planeQ = md.plane_A;
+    const char* a = reinterpret_cast<const char*>(md.A);
+    const int64_t ld = int64_t(md.Mp) * ESZ;
+    sp = {a + int64_t(ti) * BT * ld, a + int64_t(ti) * BT * ESZ, ld, md.plane_A * ESZ, ti, 0};
+    sq = {a + int64_t(tj) * BT * ld, a + int64_t(tj) * BT * ESZ, ld, md.plane_A * ESZ, tj, 0};
     K = md.Mp;
   } else {
-    Pg = reinterpret_cast<const char*>(pa.c != 0.f ? md.B : md.A);
-    Qg = reinterpret_cast<const char*>(md.Xt[pa.cur]);
-    ldP = ldQ = md.Mp;
-    planeP = md.plane_A;
-    planeQ = md.plane_X;
+    const char* b = reinterpret_cast<const char*>(md.B);
+    const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
+    const int64_t lda = int64_t(md.Mp) * ESZ, ldx = int64_t(md.Np) * ESZ;
+    sp = {b + int64_t(ti) * BT * lda, b + int64_t(ti) * BT * ESZ, lda, md.plane_A * ESZ, ti, 0};
+    sq = {nullptr, x + int64_t(tj) * BT * ESZ, ldx, md.plane_X * ESZ, -1, 1};
     K = md.Mp;
   }
-  Pg += int64_t(ti) * BT * ldP * ESZ;
-  Qg += int64_t(tj) * BT * ldQ * ESZ;
-  const int nk = K * ESZ / KB;
+  const int nk = K / KE;
 
-  u32x4 rP[NPL][CH], rQ[NPL][CH];
-  f32x16 acc[F][F];
-#pragma unroll
-  for (int i = 0; i < F; ++i)
-#pragma unroll
-    for (int j = 0; j < F; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  // additive term alpha * D on the tile's own rows (POLY: (b/c) A, COMB: a X)
+  constexpr bool ADD = PHASE != PH_GRAM;
+  const float alpha = PHASE == PH_POLY ? pa.b / pa.c : pa.a;
+  const int prow0 = ti * BT + wp * WT;     // first P-side (output) row of this wave
 
-  load_tile<NPL, CH, ESZ>(rP, Pg, planeP, ldP, 0, tid);
-  load_tile<NPL, CH, ESZ>(rQ, Qg, planeQ, ldQ, 0, tid);
-  store_tile<NPL, CH>(rP, smem, tid);
-  store_tile<NPL, CH>(rQ, smem + NPL * OPB, tid);
+  u32x4 rp[NPL][G::NREG], rq[NPL][G::NREG];
+  f32x16 acc[F][F];                         // [fj][fi]
+#pragma clang loop unroll(full)
+  for (int j = 0; j < F; ++j)
+#pragma clang loop unroll(full)
+    for (int i = 0; i < F; ++i)
+#pragma clang loop unroll(full)
+      for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
+
+  load_stage<ESZ, BT, NPL, G::NREG>(rp, sp, 0, tid);
+  load_stage<ESZ, BT, NPL, G::NREG>(rq, sq, 0, tid);
+  store_stage<ESZ, BT, NPL, G::NREG, OPB>(rp, sp, 0, smem, tid);
+  store_stage<ESZ, BT, NPL, G::NREG, OPB>(rq, sq, 0, smem + NPL * OPB, tid);
   __syncthreads();
 
-  const int frag_off = (lane & 31) * PITCH + (lane >> 5) * 16;
+  const int hsel = lane >> 5;
+#pragma unroll 1
   for (int kt = 0; kt < nk; ++kt) {
     const int s = kt & 1;
     if (kt + 1 < nk) {
-      load_tile<NPL, CH, ESZ>(rP, Pg, planeP, ldP, kt + 1, tid);
-      load_tile<NPL, CH, ESZ>(rQ, Qg, planeQ, ldQ, kt + 1, tid);
+      load_stage<ESZ, BT, NPL, G::NREG>(rp, sp, kt + 1, tid);
+      load_stage<ESZ, BT, NPL, G::NREG>(rq, sq, kt + 1, tid);
     }
-    const char* sP = smem + s * STAGE;
-    const char* sQ = sP + NPL * OPB;
-#pragma unroll
-    for (int ks = 0; ks < KB / 32; ++ks) {
-      u32x4 af[F][NPL], bf[F][NPL];
-#pragma unroll
-      for (int f = 0; f < F; ++f)
-#pragma unroll
+    const char* lP = smem + s * STAGE;
+    const char* lQ = lP + NPL * OPB;
+#pragma clang loop unroll(full)
+    for (int ks = 0; ks < KE / KS; ++ks) {
+      const int ch = 2 * ks + hsel;           // this lane's 16-byte chunk of the slab
+      u32x4 qf[F][NPL], pf[F][NPL];
+#pragma clang loop unroll(full)
+      for (int f = 0; f < F; ++f) {
+        const int rq_ = wq * WT + f * 32 + (lane & 31);
+        const int rp_ = wp * WT + f * 32 + (lane & 31);
+#pragma clang loop unroll(full)
         for (int pl = 0; pl < NPL; ++pl) {
-          af[f][pl] = *reinterpret_cast<const u32x4*>(sP + pl * OPB + (wm * WT + f * 32) * PITCH + ks * 32 + frag_off);
-          bf[f][pl] = *reinterpret_cast<const u32x4*>(sQ + pl * OPB + (wn * WT + f * 32) * PITCH + ks * 32 + frag_off);
+          qf[f][pl] = *reinterpret_cast<const u32x4*>(lQ + pl * OPB + lds_off(rq_, ch));
+          pf[f][pl] = *reinterpret_cast<const u32x4*>(lP + pl * OPB + lds_off(rp_, ch));
         }
-#pragma unroll
-      for (int i = 0; i < F; ++i)
-#pragma unroll
-        for (int j = 0; j < F; ++j) mfma_step<PREC>(acc[i][j], af[i], bf[j]);
+      }
+#pragma clang loop unroll(full)
+      for (int j = 0; j < F; ++j)
+#pragma clang loop unroll(full)
+        for (int i = 0; i < F; ++i) mfma_step<PREC>(acc[j][i], qf[j], pf[i]);
+      if constexpr (ADD) {
+        // the k-slab [kk, kk + KS) meets the output rows of this wave's block fi
+        const int kk = kt * KE + ks * KS;
+        const int d = kk - prow0;
+        if (d >= 0 && d < WT) {
+          const int fi = d >> 5;
+          // this lane's row within the block is lane & 31; its k-values are
+          // kk + (KS / 2) h + e
+          const int pos = (lane & 31) - (d & 31) - (KS / 2) * hsel;
+          u32x4 id[2];
+          identity_frag<PREC>(id, pos, alpha);
+#pragma clang loop unroll(full)
+          for (int i = 0; i < F; ++i)
+            if (i == fi) {
+#pragma clang loop unroll(full)
+              for (int j = 0; j < F; ++j) mfma_identity<PREC>(acc[j][i], qf[j], id);
+            }
+        }
+      }
     }
     if (kt + 1 < nk) {
-      store_tile<NPL, CH>(rP, smem + (s ^ 1) * STAGE, tid);
-      store_tile<NPL, CH>(rQ, smem + (s ^ 1) * STAGE + NPL * OPB, tid);
+      store_stage<ESZ, BT, NPL, G::NREG, OPB>(rp, sp, kt + 1, smem + (s ^ 1) * STAGE, tid);
+      store_stage<ESZ, BT, NPL, G::NREG, OPB>(rq, sq, kt + 1, smem + (s ^ 1) * STAGE + NPL * OPB, tid);
     }
     __syncthreads();
   }
 
   // ---------------------------------------------------------------- epilogue
-  // The accumulators go through LDS (the loop above ended with a barrier, so
-  // the operand tiles are dead) and leave in two passes of 16-byte accesses:
-  // a row pass (tile rows, contiguous in the row-major output) and, where a
-  // transposed copy is needed, a column pass (tile columns, contiguous in
-  // the transposed output).
-  constexpr int SP = BT + 4;              // staging pitch in floats
-  static_assert(BT * SP * 4 <= 2 * STAGE, "staging tile does not fit");
-  constexpr int TPR = BT / 8;             // threads per row, 8 elements each
-  constexpr int RPP = 256 / TPR;          // rows per pass
-  float* stg = reinterpret_cast<float*>(smem);
-  {
-    const int half = lane >> 5;
-    const int lc = lane & 31;
-#pragma unroll
-    for (int i = 0; i < F; ++i)
-#pragma unroll
-      for (int j = 0; j < F; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          stg[(wm * WT + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3)) * SP + wn * WT + j * 32 + lc] =
-              acc[i][j][v];
-  }
-  __syncthreads();
-  const int pr = tid / TPR;
-  const int pc = (tid % TPR) * 8;
-  const int gi_base = ti * BT, gj_base = tj * BT;
-
+  // acc[fj][fi][4g + e] is output row ti*BT + wp*WT + 32 fi + (lane & 31),
+  // output column tj*BT + wq*WT + 32 fj + 8g + 4h + e.
+  const int orow = ti * BT + wp * WT + (lane & 31);
+  const int ocol = tj * BT + wq * WT + 4 * hsel;
   if constexpr (PHASE == PH_GRAM || PHASE == PH_POLY) {
-    const float gs = (PHASE == PH_GRAM && pa.first) ? scal[te.x].inv2 : 1.f;
-    void* out = (PHASE == PH_GRAM) ? md.A : md.B;
-    const int64_t ld = md.Mp;
-    const bool mirror = ti != tj;
-#pragma unroll 2
-    for (int r = pr; r < BT; r += RPP) {
-      float* sp = stg + r * SP + pc;
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = sp[e];
-      const int64_t idx = int64_t(gi_base + r) * ld + gj_base + pc;
-      if constexpr (PHASE == PH_GRAM) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = gs * v[e];
-      } else {
-        float av[8];
-        ld8<PREC>(md.A, md.plane_A, idx, av);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = pa.b * av[e] + pa.c * v[e];
-      }
-      st8<PREC>(out, md.plane_A, idx, v);
-      if (mirror) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sp[e] = v[e];
-      }
-    }
-    if (mirror) {
-      __syncthreads();
-#pragma unroll 2
-      for (int jl = pr; jl < BT; jl += RPP) {
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = stg[(pc + e) * SP + jl];
-        st8<PREC>(out, md.plane_A, int64_t(gj_base + jl) * ld + gi_base + pc, v);
-      }
-    }
+    void* out = (PHASE == PH_GRAM && VAR == 1) ? md.A : md.B;
+    const float sc = PHASE == PH_POLY ? pa.c
+                                      : (pa.first ? scal[mat].inv2 : 1.f) * (VAR == 1 ? 1.f : pa.b);
+#pragma clang loop unroll(full)
+    for (int j = 0; j < F; ++j)
+#pragma clang loop unroll(full)
+      for (int i = 0; i < F; ++i)
+#pragma clang loop unroll(full)
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+#pragma clang loop unroll(full)
+          for (int e = 0; e < 4; ++e) v[e] = sc * acc[j][i][4 * g + e];
+          st4<PREC>(out, md.plane_A, int64_t(orow + 32 * i) * md.Mp + ocol + 32 * j + 8 * g, v);
+        }
   } else {
-    const float s = pa.first ? scal[te.x].inv : 1.f;
-    const float cb = (pa.c != 0.f) ? 1.f : pa.b;
-    const void* xc = md.X[pa.cur];
-    const int64_t ldx = md.Np, ldt = md.Mp;
-    const bool tr = md.transposed != 0;
-    const float t = update_scale(pa.lr, pa.scale_rule, md.rows, md.cols);
-#pragma unroll 2
-    for (int r = pr; r < BT; r += RPP) {
-      float* sp = stg + r * SP + pc;
-      const int gi = gi_base + r, gj = gj_base + pc;
-      const int64_t idx = int64_t(gi) * ldx + gj;
-      float xv[8], v[8];
-      ld8<PREC>(xc, md.plane_X, idx, xv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = s * (pa.a * xv[e] + cb * sp[e]);
-      if (!pa.last) {
-        st8<PREC>(md.X[pa.cur ^ 1], md.plane_X, idx, v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sp[e] = v[e];
-      } else if (!tr) {
-        if (gi < md.m) write_back8(md, gi, gj, md.n, v, t);
+    const float s = pa.first ? scal[mat].inv : 1.f;
+    if constexpr (VAR == 0) {
+      void* xn = md.X[pa.cur ^ 1];
+#pragma clang loop unroll(full)
+      for (int j = 0; j < F; ++j)
+#pragma clang loop unroll(full)
+        for (int i = 0; i < F; ++i)
+#pragma clang loop unroll(full)
+          for (int g = 0; g < 4; ++g) {
+            float v[4];
+#pragma clang loop unroll(full)
+            for (int e = 0; e < 4; ++e) v[e] = s * acc[j][i][4 * g + e];
+            st4<PREC>(xn, md.plane_X, int64_t(orow + 32 * i) * md.Np + ocol + 32 * j + 8 * g, v);
+          }
+    } else {
+      const float t = update_scale(pa.lr, pa.scale_rule, md.rows, md.cols);
+      if (md.transposed == 0) {
+        // W = X': this lane's four consecutive columns are four consecutive W elements
+#pragma clang loop unroll(full)
+        for (int j = 0; j < F; ++j)
+#pragma clang loop unroll(full)
+          for (int i = 0; i < F; ++i)
+#pragma clang loop unroll(full)
+            for (int g = 0; g < 4; ++g) {
+              const int r = orow + 32 * i, c0 = ocol + 32 * j + 8 * g;
+              float v[4];
+#pragma clang loop unroll(full)
+              for (int e = 0; e < 4; ++e) v[e] = s * acc[j][i][4 * g + e];
+              if (r < md.m) write_back_n<4>(md, r, c0, md.n, v, t);
+            }
       } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sp[e] = v[e];
-      }
-    }
-    if (!pa.last || tr) {
-      __syncthreads();
-#pragma unroll 2
-      for (int jl = pr; jl < BT; jl += RPP) {
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = stg[(pc + e) * SP + jl];
-        const int gj = gj_base + jl, gi = gi_base + pc;
-        if (!pa.last) {
-          st8<PREC>(md.Xt[pa.cur ^ 1], md.plane_X, int64_t(gj) * ldt + gi, v);
-        } else if (gj < md.n) {
-          // tall matrix: natural row gj, natural columns gi .. gi+7
-          write_back8(md, gj, gi, md.m, v, t);
+        // W = X'^T: stage the binary32 update transposed through LDS, 128 output
+        // rows (= W columns) at a time, then read-modify-write 8-element W rows.
+        constexpr int NPASS = BT / 128;
+        constexpr int RP = BT / NPASS;        // output rows per pass
+        constexpr int SPT = RP + 4;           // staging pitch in floats: BT rows of RP floats
+        static_assert(BT * SPT * 4 <= 2 * STAGE, "staging does not fit");
+        float* stg = reinterpret_cast<float*>(smem);
+#pragma unroll 1
+        for (int pass = 0; pass < NPASS; ++pass) {
+          if (NPASS == 1 || wp == pass) {
+            const int rl = wp * WT - pass * RP + (lane & 31);
+#pragma clang loop unroll(full)
+            for (int j = 0; j < F; ++j)
+#pragma clang loop unroll(full)
+              for (int i = 0; i < F; ++i)
+#pragma clang loop unroll(full)
+                for (int g = 0; g < 4; ++g)
+#pragma clang loop unroll(full)
+                  for (int e = 0; e < 4; ++e) {
+                    const int cl = wq * WT + 32 * j + 8 * g + 4 * hsel + e;
+                    stg[cl * SPT + rl + 32 * i] = s * acc[j][i][4 * g + e];
+                  }
+          }
+          __syncthreads();
+          const int row_base = ti * BT + pass * RP;
+          for (int q = tid; q < BT * RP / 8; q += 256) {
+            const int cl = q / (RP / 8), r8 = (q % (RP / 8)) * 8;
+            const int nrow = tj * BT + cl;    // natural row = wide column
+            if (nrow >= md.n) continue;
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(stg + cl * SPT + r8);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(stg + cl * SPT + r8 + 4);
+            const float o[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            write_back_n<8>(md, nrow, row_base + r8, md.m, o, t);
+          }
+          __syncthreads();
         }
       }
     }
   }
 }
 
-template <int PREC, int PHASE>
+// Persistent grid: workgroup b serves XCD b % 8 and walks that XCD's tile
+// list from entry b / 8 with a stride of (grid / 8).
+template <int PREC, int PHASE, int BT, int VAR>
+__global__ __launch_bounds__(256) void ns_gemm_kernel(const MatDev* __restrict__ mats,
+                                                      const MatScal* __restrict__ scal,
+                                                      const int2* __restrict__ tiles, PhaseArgs pa) {
+  constexpr int NPL = Fmt<PREC>::npl;
+  constexpr int STAGE = 2 * NPL * BT * PITCH;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  const int xcd = blockIdx.x % NUM_XCD;
+  const int stride = gridDim.x / NUM_XCD;
+  const int2* list = tiles + int64_t(xcd) * pa.per_xcd;
+#pragma unroll 1
+  for (int slot = blockIdx.x / NUM_XCD; slot < pa.per_xcd; slot += stride) {
+    const int2 te = list[slot];
+    if (te.x < 0) break;  // lists are padded at their end only
+    ns_tile_body<PREC, PHASE, BT, VAR>(mats[te.x], scal, te.x, te.y >> 16, te.y & 0xFFFF, pa, smem);
+    __syncthreads();
+  }
+}
+
+template <int PREC, int PHASE, int VAR>
 hipError_t launch_one(const MatDev* mats, const MatScal* scal, const int2* tiles,
                       const PhaseArgs& pa, hipStream_t stream) {
-  const unsigned grid = unsigned(NUM_XCD) * unsigned(pa.per_xcd);
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((ns_gemm_kernel<PREC, PHASE, NS_TILE>), dim3(grid), dim3(256), 0, stream,
+  if (pa.per_xcd <= 0) return hipSuccess;
+  // resident workgroups per XCD: CUs per XCD times workgroups per CU (LDS-bound)
+  constexpr int per_cu = (ns_tile(PREC) == 256 || PREC == PREC_BF16X3) ? 1 : 2;
+  const int per_xcd = std::min(pa.per_xcd, pa.cus_per_xcd * per_cu);
+  const unsigned grid = unsigned(NUM_XCD) * unsigned(per_xcd);
+  hipLaunchKernelGGL((ns_gemm_kernel<PREC, PHASE, ns_tile(PREC), VAR>), dim3(grid), dim3(256), 0, stream,
                      mats, scal, tiles, pa);
   return hipGetLastError();
 }
@@ -479,9 +610,13 @@ template <int PREC>
 hipError_t launch_prec(int phase, const MatDev* mats, const MatScal* scal, const int2* tiles,
                        const PhaseArgs& pa, hipStream_t stream) {
   switch (phase) {
-    case PH_GRAM: return launch_one<PREC, PH_GRAM>(mats, scal, tiles, pa, stream);
-    case PH_POLY: return launch_one<PREC, PH_POLY>(mats, scal, tiles, pa, stream);
-    case PH_COMB: return launch_one<PREC, PH_COMB>(mats, scal, tiles, pa, stream);
+    case PH_GRAM:
+      return pa.c != 0.f ? launch_one<PREC, PH_GRAM, 1>(mats, scal, tiles, pa, stream)
+                         : launch_one<PREC, PH_GRAM, 0>(mats, scal, tiles, pa, stream);
+    case PH_POLY: return launch_one<PREC, PH_POLY, 0>(mats, scal, tiles, pa, stream);
+    case PH_COMB:
+      return pa.last ? launch_one<PREC, PH_COMB, 1>(mats, scal, tiles, pa, stream)
+                     : launch_one<PREC, PH_COMB, 0>(mats, scal, tiles, pa, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -217,16 +217,15 @@ def orthogonalise_bf16_storage(u, coeffs, steps: int, eps: float = EPS, rnd=None
 
     A bf16 GPU path cannot keep its intermediates in float64; it stores
     them in bfloat16 between the matrix products and accumulates each
-    product in binary32.  The points where values are stored, in order:
+    product in binary32.  The storage points, in order:
 
-      1. U (before scaling) is stored in bf16; 1/(||U||_F + eps) is applied
-         later as a scalar, with ||U||_F taken from the binary32 U.
-      2. A = s^2 (X X^T) is stored in bf16 (s = that scalar on the first
-         step, 1 afterwards).
-      3. B = b A + c (A A) is stored in bf16 when c != 0; when c == 0 no B
-         is formed and the product A X is scaled by b instead.
-      4. X_new = s (a X + B X) is stored in bf16, except after the last
-         step, whose value is the update O.
+      1. U (before scaling) is stored; 1/(||U||_F + eps) is applied later as
+         a scalar s, with ||U||_F taken from the binary32 U.
+      2. With G = s^2 X X^T (s on the first step, 1 afterwards):
+         c != 0: A = G is stored, then B = b A + c A A is stored;
+         c == 0: B = b G is stored.
+      3. X_new = s (a X + B X) is stored, except after the last step, whose
+         value is the update O.  a X is added in full precision.
 
     All arithmetic between the storage points is float64 here, so the
     result differs from a binary32-accumulating GPU only by accumulation
@@ -246,12 +245,13 @@ def orthogonalise_bf16_storage(u, coeffs, steps: int, eps: float = EPS, rnd=None
         o = s * x
         return o.T if tr else o
     for k in range(steps):
-        gram = np.asarray(rnd((s * s) * (x @ x.T)), dtype=np.float64)
+        gram = (s * s) * (x @ x.T)
         if c != 0.0:
-            poly = np.asarray(rnd(b * gram + c * (gram @ gram)), dtype=np.float64)
-            xn = s * (a * x + poly @ x)
+            a_st = np.asarray(rnd(gram), dtype=np.float64)
+            b_st = np.asarray(rnd(b * a_st + c * (a_st @ a_st)), dtype=np.float64)
         else:
-            xn = s * (a * x + b * (gram @ x))
+            b_st = np.asarray(rnd(b * gram), dtype=np.float64)
+        xn = s * (a * x + b_st @ x)
         s = 1.0
         x = xn if k == steps - 1 else np.asarray(rnd(xn), dtype=np.float64)
     return x.T if tr else x

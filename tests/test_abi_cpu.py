@@ -144,12 +144,15 @@ def test_valid_call_without_gpu_reports_hip_error(L):
 
 def test_workspace_bytes(L):
     one = mb.muon_workspace_bytes([(1536, 1536)])
-    # X, X' and their transposes (4 x 1536^2) plus A and B (2 x 1536^2), bf16
-    assert one == 6 * 1536 * 1536 * 2
+    # X and X' (2 x 1536^2) plus A and B (2 x 1536^2), bf16
+    assert one == 4 * 1536 * 1536 * 2
     tall = mb.muon_workspace_bytes([(6144, 1536)])
     wide = mb.muon_workspace_bytes([(1536, 6144)])
-    assert tall == wide == (4 * 1536 * 6144 + 2 * 1536 * 1536) * 2
+    assert tall == wide == (2 * 1536 * 6144 + 2 * 1536 * 1536) * 2
     assert mb.muon_workspace_bytes([(1536, 1536)], precision=mb.NS_BF16X3) == 2 * one
+    assert mb.muon_workspace_bytes([(1536, 1536)], precision=mb.NS_F32) == 2 * one
+    # padding to multiples of 256
+    assert mb.muon_workspace_bytes([(1, 300)]) == (2 * 256 * 512 + 2 * 256 * 256) * 2
     assert mb.muon_workspace_bytes([(0, 4)]) == 0
 
 
