@@ -28,9 +28,9 @@
 //    on or above the diagonal.  A consumer that needs a block below the
 //    diagonal stages the mirror block transposed.
 //  * Q in COMB reads X along its rows (the contraction index k is X's row
-//    index): each thread loads an 8 x 8 block (4 x 4 for float32), transposes
-//    it in registers and writes one 16-byte LDS chunk per row.  The same path
-//    serves the lower triangle of A and B.
+//    index): each thread loads 4 k-values of 8 rows (4 rows for float32),
+//    transposes them in registers and writes 8 bytes (16 for float32) per
+//    row into LDS.  The same path serves the lower triangle of A and B.
 //  * The additive terms a X and (b/c) A run on the matrix cores: where the
 //    k-slab meets the tile's own rows, extra MFMAs pair the Q fragment with
 //    a scaled identity fragment (for bf16 the scale is split into hi + lo, so
@@ -40,10 +40,11 @@
 //    ch of row r sits at chunk position ch ^ ((r >> 4) & 7).  Fragment reads
 //    (16 consecutive rows) and transposed writes (rows 8 apart) are then both
 //    free of bank conflicts.
-//  * Tiles: T x T per 256-thread workgroup (T = 256 for bf16, 128 for the
-//    split-bf16 and float32 formats), four waves in a 2 x 2 layout, each
-//    T/2 square; K staged 128 bytes per row, double-buffered through LDS
-//    with register staging.  Operands are zero-padded to a multiple of 256.
+//  * Tiles: 256 x 256 over eight waves (2 x 4, each 128 x 64) for bf16;
+//    128 x 128 over four waves (2 x 2, each 64 x 64) for the split-bf16 and
+//    float32 formats.  K is staged 128 bytes per row, double-buffered
+//    through LDS with register staging.  Operands are zero-padded to a
+//    multiple of 256.
 //  * Tile lists are split into one contiguous, cost-balanced segment per XCD;
 //    a persistent grid walks them, workgroup b on XCD b % 8 taking entries
 //    b/8, b/8 + grid/8, ... of that XCD's segment, so tiles that share
@@ -80,6 +81,16 @@ template <int PREC> struct Fmt;
 template <> struct Fmt<PREC_BF16> { static constexpr int esz = 2, npl = 1; };
 template <> struct Fmt<PREC_BF16X3> { static constexpr int esz = 2, npl = 2; };
 template <> struct Fmt<PREC_F32> { static constexpr int esz = 4, npl = 1; };
+
+// Tile shape per format: T x T tile, WP x WQ waves (rows x columns), NT threads.
+// bf16: 256 x 256 over eight waves (two per SIMD, each 128 x 64, 128
+// accumulator registers), so one wave's barrier or LDS wait overlaps the
+// other's matrix-core work.  The formats whose operands take twice the bytes
+// use 128 x 128 over four waves.
+template <int PREC> struct Cfg;
+template <> struct Cfg<PREC_BF16> { static constexpr int BT = 256, WP = 2, WQ = 4, NT = 512; };
+template <> struct Cfg<PREC_BF16X3> { static constexpr int BT = 128, WP = 2, WQ = 2, NT = 256; };
+template <> struct Cfg<PREC_F32> { static constexpr int BT = 128, WP = 2, WQ = 2, NT = 256; };
 
 __device__ __forceinline__ int lds_off(int r, int ch) { return r * PITCH + ((ch ^ ((r >> 4) & 7)) << 4); }
 
@@ -246,20 +257,22 @@ __device__ __forceinline__ void mfma_identity(f32x16& acc, const u32x4* q, const
 // ------------------------------------------------------------------ staging
 
 // Staging geometry of one operand of a T x T tile for one stage (KB bytes of K).
-//   direct: the operand's rows are K-contiguous; chunk c = tid + 256 q is
+//   direct: the operand's rows are K-contiguous; chunk c = tid + NT q is
 //           row c / 8, 16-byte chunk c % 8.  CH chunks per thread.
 //   trans:  the operand's element (row r, k) sits at memory (k, r), row
-//           stride ld; a block is KPB k-values x KPB rows (KPB = 16 / esz), one
-//           16-byte load per k-value, transposed in registers into one 16-byte
-//           chunk per row.  NB blocks per stage, PER per thread.
-template <int ESZ, int BT>
+//           stride ld.  A block is 4 consecutive k-values of RPB = 16 / esz
+//           consecutive rows: four 16-byte loads, transposed in registers into
+//           4 k-values per row (8 bytes for bf16: half an LDS chunk; 16 bytes
+//           for float32: a whole chunk).  NB blocks per stage, PER per thread.
+template <int ESZ, int BT, int NT>
 struct Geo {
-  static constexpr int CH = BT * (KB / 16) / 256;
-  static constexpr int KPB = 16 / ESZ;
-  static constexpr int RB = BT / KPB;
-  static constexpr int NB = RB * (KB / 16);
-  static constexpr int PER = (NB + 255) / 256;
-  static constexpr int NREG = (CH > PER * KPB) ? CH : PER * KPB;
+  static constexpr int CH = BT * (KB / 16) / NT;
+  static constexpr int RPB = 16 / ESZ;
+  static constexpr int RB = BT / RPB;
+  static constexpr int KG = KB / ESZ / 4;
+  static constexpr int NB = RB * KG;
+  static constexpr int PER = (NB + NT - 1) / NT;
+  static constexpr int NREG = (CH > PER * 4) ? CH : PER * 4;
 };
 
 // Where one operand of one tile comes from.
@@ -279,27 +292,27 @@ __device__ __forceinline__ bool stage_is_trans(const OpSrc& s, int kt) {
   return (kt * (KB / ESZ)) / BT < s.sym_tile;  // below the diagonal: read the mirror block
 }
 
-template <int ESZ, int BT, int NPL, int NREG>
+template <int ESZ, int BT, int NT, int NPL, int NREG>
 __device__ __forceinline__ void load_stage(u32x4 (&r)[NPL][NREG], const OpSrc& s, int kt, int tid) {
-  using G = Geo<ESZ, BT>;
+  using G = Geo<ESZ, BT, NT>;
   if (stage_is_trans<ESZ, BT>(s, kt)) {
     const int k0 = kt * (KB / ESZ);
 #pragma unroll
     for (int q = 0; q < G::PER; ++q) {
-      const int blk = tid + 256 * q;
-      if (G::NB % 256 != 0 && blk >= G::NB) break;
-      const int rb = blk % G::RB, kc = blk / G::RB;   // row block, K chunk
+      const int blk = tid + NT * q;
+      if (G::NB % NT != 0 && blk >= G::NB) break;
+      const int rb = blk % G::RB, kg = blk / G::RB;   // row block, group of 4 k-values
 #pragma unroll
-      for (int e = 0; e < G::KPB; ++e) {
-        const int64_t off = int64_t(k0 + kc * G::KPB + e) * s.ld_b + rb * 16;
+      for (int e = 0; e < 4; ++e) {
+        const int64_t off = int64_t(k0 + kg * 4 + e) * s.ld_b + rb * 16;
 #pragma unroll
-        for (int pl = 0; pl < NPL; ++pl) r[pl][q * G::KPB + e] = *(gu32x4*)(s.trans + pl * s.plane_b + off);
+        for (int pl = 0; pl < NPL; ++pl) r[pl][q * 4 + e] = *(gu32x4*)(s.trans + pl * s.plane_b + off);
       }
     }
   } else {
 #pragma unroll
     for (int q = 0; q < G::CH; ++q) {
-      const int c = tid + 256 * q;
+      const int c = tid + NT * q;
       const int64_t off = int64_t(c >> 3) * s.ld_b + int64_t(kt) * KB + (c & 7) * 16;
 #pragma unroll
       for (int pl = 0; pl < NPL; ++pl) r[pl][q] = *(gu32x4*)(s.direct + pl * s.plane_b + off);
@@ -307,52 +320,47 @@ __device__ __forceinline__ void load_stage(u32x4 (&r)[NPL][NREG], const OpSrc& s
   }
 }
 
-// 8x8 transpose of 16-bit values: in[e] holds k-value e of 8 consecutive
-// rows (two rows per dword); out[c] holds the 8 k-values of row c.
-__device__ __forceinline__ void transpose8x8_b16(const u32x4* in, u32x4* out) {
+// 4 x 8 transpose of 16-bit values: in[e] holds k-value e of 8 consecutive
+// rows (two rows per dword); out[c] holds the 4 k-values of row c.
+__device__ __forceinline__ void transpose4x8_b16(const u32x4* in, u32x2* out) {
 #pragma unroll
   for (int c2 = 0; c2 < 4; ++c2) {
-    u32x4 even, odd;
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const uint32_t a = in[2 * e2][c2], b = in[2 * e2 + 1][c2];
-      even[e2] = __builtin_amdgcn_perm(b, a, 0x05040100u);   // a.lo, b.lo: row 2 c2
-      odd[e2] = __builtin_amdgcn_perm(b, a, 0x07060302u);    // a.hi, b.hi: row 2 c2 + 1
-    }
-    out[2 * c2] = even;
-    out[2 * c2 + 1] = odd;
+    const uint32_t k0 = in[0][c2], k1 = in[1][c2], k2 = in[2][c2], k3 = in[3][c2];
+    out[2 * c2] = u32x2{__builtin_amdgcn_perm(k1, k0, 0x05040100u), __builtin_amdgcn_perm(k3, k2, 0x05040100u)};
+    out[2 * c2 + 1] = u32x2{__builtin_amdgcn_perm(k1, k0, 0x07060302u), __builtin_amdgcn_perm(k3, k2, 0x07060302u)};
   }
 }
 
-template <int ESZ, int BT, int NPL, int NREG, int OPB>
+template <int ESZ, int BT, int NT, int NPL, int NREG, int OPB>
 __device__ __forceinline__ void store_stage(const u32x4 (&r)[NPL][NREG], const OpSrc& s, int kt, char* lds,
                                             int tid) {
-  using G = Geo<ESZ, BT>;
+  using G = Geo<ESZ, BT, NT>;
   if (stage_is_trans<ESZ, BT>(s, kt)) {
 #pragma unroll
     for (int q = 0; q < G::PER; ++q) {
-      const int blk = tid + 256 * q;
-      if (G::NB % 256 != 0 && blk >= G::NB) break;
-      const int rb = blk % G::RB, kc = blk / G::RB;
+      const int blk = tid + NT * q;
+      if (G::NB % NT != 0 && blk >= G::NB) break;
+      const int rb = blk % G::RB, kg = blk / G::RB;
 #pragma unroll
       for (int pl = 0; pl < NPL; ++pl) {
-        u32x4 t[G::KPB];
         if constexpr (ESZ == 2) {
-          transpose8x8_b16(&r[pl][q * G::KPB], t);
+          u32x2 t[8];
+          transpose4x8_b16(&r[pl][q * 4], t);
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+            *reinterpret_cast<u32x2*>(lds + pl * OPB + lds_off(rb * 8 + c, kg >> 1) + ((kg & 1) << 3)) = t[c];
         } else {
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            t[c] = u32x4{r[pl][q * 4 + 0][c], r[pl][q * 4 + 1][c], r[pl][q * 4 + 2][c], r[pl][q * 4 + 3][c]};
+            *reinterpret_cast<u32x4*>(lds + pl * OPB + lds_off(rb * 4 + c, kg)) =
+                u32x4{r[pl][q * 4 + 0][c], r[pl][q * 4 + 1][c], r[pl][q * 4 + 2][c], r[pl][q * 4 + 3][c]};
         }
-#pragma unroll
-        for (int c = 0; c < G::KPB; ++c)
-          *reinterpret_cast<u32x4*>(lds + pl * OPB + lds_off(rb * G::KPB + c, kc)) = t[c];
       }
     }
   } else {
 #pragma unroll
     for (int q = 0; q < G::CH; ++q) {
-      const int c = tid + 256 * q;
+      const int c = tid + NT * q;
 #pragma unroll
       for (int pl = 0; pl < NPL; ++pl) *reinterpret_cast<u32x4*>(lds + pl * OPB + lds_off(c >> 3, c & 7)) = r[pl][q];
     }
@@ -363,14 +371,16 @@ __device__ __forceinline__ void store_stage(const u32x4 (&r)[NPL][NREG], const O
 
 // VAR: GRAM 1 = c != 0 (store A), 0 = c == 0 (store B = b A);
 //      COMB 1 = last step (write-back), 0 = store the next iterate.
-template <int PREC, int PHASE, int BT, int VAR>
+template <int PREC, int PHASE, int VAR>
 __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __restrict__ scal, int mat,
                                              int ti, int tj, const PhaseArgs& pa, char* smem) {
   constexpr int ESZ = Fmt<PREC>::esz;
   constexpr int NPL = Fmt<PREC>::npl;
-  using G = Geo<ESZ, BT>;
-  constexpr int WT = BT / 2;               // wave tile edge
-  constexpr int F = WT / 32;               // 32x32 MFMA blocks per wave edge
+  constexpr int BT = Cfg<PREC>::BT, NT = Cfg<PREC>::NT, WQN = Cfg<PREC>::WQ;
+  using G = Geo<ESZ, BT, NT>;
+  constexpr int WTP = BT / Cfg<PREC>::WP;  // wave tile rows (P side)
+  constexpr int WTQ = BT / WQN;            // wave tile columns (Q side)
+  constexpr int FP = WTP / 32, FQ = WTQ / 32;  // 32x32 MFMA blocks per wave
   constexpr int OPB = BT * PITCH;          // LDS bytes of one operand plane
   constexpr int STAGE = 2 * NPL * OPB;
   constexpr int KE = KB / ESZ;             // k-values per stage
@@ -378,7 +388,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int wq = w & 1, wp = w >> 1;       // Q-side (columns) and P-side (rows) halves
+  const int wq = w % WQN, wp = w / WQN;    // wave position: Q side (columns), P side (rows)
 
   OpSrc sp, sq;
   int K;
@@ -407,21 +417,21 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
   // additive term alpha * D on the tile's own rows (POLY: (b/c) A, COMB: a X)
   constexpr bool ADD = PHASE != PH_GRAM;
   const float alpha = PHASE == PH_POLY ? pa.b / pa.c : pa.a;
-  const int prow0 = ti * BT + wp * WT;     // first P-side (output) row of this wave
+  const int prow0 = ti * BT + wp * WTP;    // first P-side (output) row of this wave
 
   u32x4 rp[NPL][G::NREG], rq[NPL][G::NREG];
-  f32x16 acc[F][F];                         // [fj][fi]
+  f32x16 acc[FQ][FP];                       // [fj][fi]
 #pragma clang loop unroll(full)
-  for (int j = 0; j < F; ++j)
+  for (int j = 0; j < FQ; ++j)
 #pragma clang loop unroll(full)
-    for (int i = 0; i < F; ++i)
+    for (int i = 0; i < FP; ++i)
 #pragma clang loop unroll(full)
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
 
-  load_stage<ESZ, BT, NPL, G::NREG>(rp, sp, 0, tid);
-  load_stage<ESZ, BT, NPL, G::NREG>(rq, sq, 0, tid);
-  store_stage<ESZ, BT, NPL, G::NREG, OPB>(rp, sp, 0, smem, tid);
-  store_stage<ESZ, BT, NPL, G::NREG, OPB>(rq, sq, 0, smem + NPL * OPB, tid);
+  load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, sp, 0, tid);
+  load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, sq, 0, tid);
+  store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rp, sp, 0, smem, tid);
+  store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rq, sq, 0, smem + NPL * OPB, tid);
   __syncthreads();
 
   const int hsel = lane >> 5;
@@ -429,34 +439,38 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
   for (int kt = 0; kt < nk; ++kt) {
     const int s = kt & 1;
     if (kt + 1 < nk) {
-      load_stage<ESZ, BT, NPL, G::NREG>(rp, sp, kt + 1, tid);
-      load_stage<ESZ, BT, NPL, G::NREG>(rq, sq, kt + 1, tid);
+      load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, sp, kt + 1, tid);
+      load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, sq, kt + 1, tid);
     }
     const char* lP = smem + s * STAGE;
     const char* lQ = lP + NPL * OPB;
 #pragma clang loop unroll(full)
     for (int ks = 0; ks < KE / KS; ++ks) {
       const int ch = 2 * ks + hsel;           // this lane's 16-byte chunk of the slab
-      u32x4 qf[F][NPL], pf[F][NPL];
+      u32x4 qf[FQ][NPL], pf[FP][NPL];
 #pragma clang loop unroll(full)
-      for (int f = 0; f < F; ++f) {
-        const int rq_ = wq * WT + f * 32 + (lane & 31);
-        const int rp_ = wp * WT + f * 32 + (lane & 31);
+      for (int f = 0; f < FQ; ++f) {
+        const int rq_ = wq * WTQ + f * 32 + (lane & 31);
 #pragma clang loop unroll(full)
-        for (int pl = 0; pl < NPL; ++pl) {
+        for (int pl = 0; pl < NPL; ++pl)
           qf[f][pl] = *reinterpret_cast<const u32x4*>(lQ + pl * OPB + lds_off(rq_, ch));
-          pf[f][pl] = *reinterpret_cast<const u32x4*>(lP + pl * OPB + lds_off(rp_, ch));
-        }
       }
 #pragma clang loop unroll(full)
-      for (int j = 0; j < F; ++j)
+      for (int f = 0; f < FP; ++f) {
+        const int rp_ = wp * WTP + f * 32 + (lane & 31);
 #pragma clang loop unroll(full)
-        for (int i = 0; i < F; ++i) mfma_step<PREC>(acc[j][i], qf[j], pf[i]);
+        for (int pl = 0; pl < NPL; ++pl)
+          pf[f][pl] = *reinterpret_cast<const u32x4*>(lP + pl * OPB + lds_off(rp_, ch));
+      }
+#pragma clang loop unroll(full)
+      for (int j = 0; j < FQ; ++j)
+#pragma clang loop unroll(full)
+        for (int i = 0; i < FP; ++i) mfma_step<PREC>(acc[j][i], qf[j], pf[i]);
       if constexpr (ADD) {
         // the k-slab [kk, kk + KS) meets the output rows of this wave's block fi
         const int kk = kt * KE + ks * KS;
         const int d = kk - prow0;
-        if (d >= 0 && d < WT) {
+        if (d >= 0 && d < WTP) {
           const int fi = d >> 5;
           // this lane's row within the block is lane & 31; its k-values are
           // kk + (KS / 2) h + e
@@ -464,34 +478,34 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
           u32x4 id[2];
           identity_frag<PREC>(id, pos, alpha);
 #pragma clang loop unroll(full)
-          for (int i = 0; i < F; ++i)
+          for (int i = 0; i < FP; ++i)
             if (i == fi) {
 #pragma clang loop unroll(full)
-              for (int j = 0; j < F; ++j) mfma_identity<PREC>(acc[j][i], qf[j], id);
+              for (int j = 0; j < FQ; ++j) mfma_identity<PREC>(acc[j][i], qf[j], id);
             }
         }
       }
     }
     if (kt + 1 < nk) {
-      store_stage<ESZ, BT, NPL, G::NREG, OPB>(rp, sp, kt + 1, smem + (s ^ 1) * STAGE, tid);
-      store_stage<ESZ, BT, NPL, G::NREG, OPB>(rq, sq, kt + 1, smem + (s ^ 1) * STAGE + NPL * OPB, tid);
+      store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rp, sp, kt + 1, smem + (s ^ 1) * STAGE, tid);
+      store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rq, sq, kt + 1, smem + (s ^ 1) * STAGE + NPL * OPB, tid);
     }
     __syncthreads();
   }
 
   // ---------------------------------------------------------------- epilogue
-  // acc[fj][fi][4g + e] is output row ti*BT + wp*WT + 32 fi + (lane & 31),
-  // output column tj*BT + wq*WT + 32 fj + 8g + 4h + e.
-  const int orow = ti * BT + wp * WT + (lane & 31);
-  const int ocol = tj * BT + wq * WT + 4 * hsel;
+  // acc[fj][fi][4g + e] is output row ti*BT + wp*WTP + 32 fi + (lane & 31),
+  // output column tj*BT + wq*WTQ + 32 fj + 8g + 4h + e.
+  const int orow = ti * BT + wp * WTP + (lane & 31);
+  const int ocol = tj * BT + wq * WTQ + 4 * hsel;
   if constexpr (PHASE == PH_GRAM || PHASE == PH_POLY) {
     void* out = (PHASE == PH_GRAM && VAR == 1) ? md.A : md.B;
     const float sc = PHASE == PH_POLY ? pa.c
                                       : (pa.first ? scal[mat].inv2 : 1.f) * (VAR == 1 ? 1.f : pa.b);
 #pragma clang loop unroll(full)
-    for (int j = 0; j < F; ++j)
+    for (int j = 0; j < FQ; ++j)
 #pragma clang loop unroll(full)
-      for (int i = 0; i < F; ++i)
+      for (int i = 0; i < FP; ++i)
 #pragma clang loop unroll(full)
         for (int g = 0; g < 4; ++g) {
           float v[4];
@@ -504,9 +518,9 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     if constexpr (VAR == 0) {
       void* xn = md.X[pa.cur ^ 1];
 #pragma clang loop unroll(full)
-      for (int j = 0; j < F; ++j)
+      for (int j = 0; j < FQ; ++j)
 #pragma clang loop unroll(full)
-        for (int i = 0; i < F; ++i)
+        for (int i = 0; i < FP; ++i)
 #pragma clang loop unroll(full)
           for (int g = 0; g < 4; ++g) {
             float v[4];
@@ -519,9 +533,9 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       if (md.transposed == 0) {
         // W = X': this lane's four consecutive columns are four consecutive W elements
 #pragma clang loop unroll(full)
-        for (int j = 0; j < F; ++j)
+        for (int j = 0; j < FQ; ++j)
 #pragma clang loop unroll(full)
-          for (int i = 0; i < F; ++i)
+          for (int i = 0; i < FP; ++i)
 #pragma clang loop unroll(full)
             for (int g = 0; g < 4; ++g) {
               const int r = orow + 32 * i, c0 = ocol + 32 * j + 8 * g;
@@ -541,22 +555,22 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
 #pragma unroll 1
         for (int pass = 0; pass < NPASS; ++pass) {
           if (NPASS == 1 || wp == pass) {
-            const int rl = wp * WT - pass * RP + (lane & 31);
+            const int rl = wp * WTP - pass * RP + (lane & 31);
 #pragma clang loop unroll(full)
-            for (int j = 0; j < F; ++j)
+            for (int j = 0; j < FQ; ++j)
 #pragma clang loop unroll(full)
-              for (int i = 0; i < F; ++i)
+              for (int i = 0; i < FP; ++i)
 #pragma clang loop unroll(full)
                 for (int g = 0; g < 4; ++g)
 #pragma clang loop unroll(full)
                   for (int e = 0; e < 4; ++e) {
-                    const int cl = wq * WT + 32 * j + 8 * g + 4 * hsel + e;
+                    const int cl = wq * WTQ + 32 * j + 8 * g + 4 * hsel + e;
                     stg[cl * SPT + rl + 32 * i] = s * acc[j][i][4 * g + e];
                   }
           }
           __syncthreads();
           const int row_base = ti * BT + pass * RP;
-          for (int q = tid; q < BT * RP / 8; q += 256) {
+          for (int q = tid; q < BT * RP / 8; q += NT) {
             const int cl = q / (RP / 8), r8 = (q % (RP / 8)) * 8;
             const int nrow = tj * BT + cl;    // natural row = wide column
             if (nrow >= md.n) continue;
@@ -574,12 +588,12 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
 
 // Persistent grid: workgroup b serves XCD b % 8 and walks that XCD's tile
 // list from entry b / 8 with a stride of (grid / 8).
-template <int PREC, int PHASE, int BT, int VAR>
-__global__ __launch_bounds__(256) void ns_gemm_kernel(const MatDev* __restrict__ mats,
-                                                      const MatScal* __restrict__ scal,
-                                                      const int2* __restrict__ tiles, PhaseArgs pa) {
+template <int PREC, int PHASE, int VAR>
+__global__ __launch_bounds__(Cfg<PREC>::NT) void ns_gemm_kernel(const MatDev* __restrict__ mats,
+                                                                const MatScal* __restrict__ scal,
+                                                                const int2* __restrict__ tiles, PhaseArgs pa) {
   constexpr int NPL = Fmt<PREC>::npl;
-  constexpr int STAGE = 2 * NPL * BT * PITCH;
+  constexpr int STAGE = 2 * NPL * Cfg<PREC>::BT * PITCH;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   const int xcd = blockIdx.x % NUM_XCD;
   const int stride = gridDim.x / NUM_XCD;
@@ -588,7 +602,7 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(const MatDev* __restrict__
   for (int slot = blockIdx.x / NUM_XCD; slot < pa.per_xcd; slot += stride) {
     const int2 te = list[slot];
     if (te.x < 0) break;  // lists are padded at their end only
-    ns_tile_body<PREC, PHASE, BT, VAR>(mats[te.x], scal, te.x, te.y >> 16, te.y & 0xFFFF, pa, smem);
+    ns_tile_body<PREC, PHASE, VAR>(mats[te.x], scal, te.x, te.y >> 16, te.y & 0xFFFF, pa, smem);
     __syncthreads();
   }
 }
@@ -601,7 +615,8 @@ hipError_t launch_one(const MatDev* mats, const MatScal* scal, const int2* tiles
   constexpr int per_cu = (ns_tile(PREC) == 256 || PREC == PREC_BF16X3) ? 1 : 2;
   const int per_xcd = std::min(pa.per_xcd, pa.cus_per_xcd * per_cu);
   const unsigned grid = unsigned(NUM_XCD) * unsigned(per_xcd);
-  hipLaunchKernelGGL((ns_gemm_kernel<PREC, PHASE, ns_tile(PREC), VAR>), dim3(grid), dim3(256), 0, stream,
+  static_assert(Cfg<PREC>::BT == ns_tile(PREC), "tile size disagrees with the host's tile lists");
+  hipLaunchKernelGGL((ns_gemm_kernel<PREC, PHASE, VAR>), dim3(grid), dim3(Cfg<PREC>::NT), 0, stream,
                      mats, scal, tiles, pa);
   return hipGetLastError();
 }
