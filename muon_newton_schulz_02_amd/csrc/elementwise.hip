@@ -99,9 +99,9 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
   const int rows = md.rows, cols = md.cols;
   const int prec = md.prec;
   const bool tr = md.transposed != 0;
-  // X = U (wide) or X = U^T (tall), row stride Np
+  // X = U (wide) or X = U^T (tall), row stride ldx
   void* xw = md.X[0];
-  const int64_t ldx = md.Np;
+  const int64_t ldx = md.ldx;
   float ss = 0.f;
 
 #pragma unroll
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void writeback_direct_kernel(const MatDev* __r
   for (int e = threadIdx.x; e < ETILE * ETILE; e += 256) {
     const int row = tr0 + e / ETILE, col = tc0 + e % ETILE;
     if (row >= md.rows || col >= md.cols) continue;
-    const int64_t xi = tr ? int64_t(col) * md.Np + row : int64_t(row) * md.Np + col;
+    const int64_t xi = tr ? int64_t(col) * md.ldx + row : int64_t(row) * md.ldx + col;
     const float o = inv * load_ws(xw, md.plane_X, md.prec, xi);
     if (md.param) {
       const int64_t pi = int64_t(row) * md.ld_param + col;

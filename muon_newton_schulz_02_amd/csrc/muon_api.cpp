@@ -59,6 +59,7 @@ uint64_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int esz) {
 
 struct MatGeom {
   int64_t m, n, Mp, Np;
+  int64_t ldx, lda;  // workspace row strides (elements)
   bool transposed;
   int prec;
   int esz, npl;
@@ -72,11 +73,13 @@ MatGeom geom_of(const muon_matrix_desc& d) {
   g.n = std::max(d.rows, d.cols);
   g.Mp = round_up(g.m, PAD);
   g.Np = round_up(g.n, PAD);
+  g.ldx = g.Np + LDPAD;
+  g.lda = g.Mp + LDPAD;
   g.prec = d.precision;
   g.esz = g.prec == PREC_F32 ? 4 : 2;
   g.npl = g.prec == PREC_BF16X3 ? 2 : 1;
-  g.x_bytes = align256(size_t(g.Mp) * size_t(g.Np) * g.esz * g.npl);
-  g.a_bytes = align256(size_t(g.Mp) * size_t(g.Mp) * g.esz * g.npl);
+  g.x_bytes = align256(size_t(g.Mp) * size_t(g.ldx) * g.esz * g.npl);
+  g.a_bytes = align256(size_t(g.Mp) * size_t(g.lda) * g.esz * g.npl);
   return g;
 }
 
@@ -523,6 +526,8 @@ muon_status run(const Call& c) {
       m.n = int32_t(g.n);
       m.Mp = int32_t(g.Mp);
       m.Np = int32_t(g.Np);
+      m.ldx = int32_t(g.ldx);
+      m.lda = int32_t(g.lda);
       m.transposed = g.transposed ? 1 : 0;
       m.param_bf16 = (c.mode == MODE_STEP && d.param_dtype == MUON_DTYPE_BF16) ? 1 : 0;
       m.grad_bf16 = d.grad_dtype == MUON_DTYPE_BF16 ? 1 : 0;
@@ -541,8 +546,8 @@ muon_status run(const Call& c) {
       m.etile_cols = int32_t(cp / ETILE);
       etile_off[i + 1] = etile_off[i] + int32_t((rp / ETILE) * (cp / ETILE));
       if (c.mode != MODE_NORMS) {
-        m.plane_X = g.Mp * g.Np;
-        m.plane_A = g.Mp * g.Mp;
+        m.plane_X = g.Mp * g.ldx;
+        m.plane_A = g.Mp * g.lda;
         m.X[0] = ws + wo; wo += g.x_bytes;
         m.X[1] = ws + wo; wo += g.x_bytes;
         m.A = ws + wo; wo += g.a_bytes;

@@ -11,6 +11,9 @@ namespace muon {
 // the padding holds zeros, so the Newton-Schulz products run without bounds
 // checks: zero rows and columns contribute nothing and stay zero.
 constexpr int PAD = 256;
+// Workspace rows may hold LDPAD elements beyond the padded width (never
+// read); a pad of 64 was measured to change nothing on the d24 stack.
+constexpr int LDPAD = 0;
 // Elementwise tiles (momentum, transposed copy, norm partials).
 constexpr int ETILE = 64;
 // Dispatch order puts consecutive workgroups on different XCDs.
@@ -30,6 +33,7 @@ struct MatDev {
   int32_t rows, cols;     // natural shape
   int32_t m, n;           // wide shape
   int32_t Mp, Np;         // padded wide shape
+  int32_t ldx, lda;       // workspace row strides (elements) of X and of A, B
   int32_t transposed;     // rows > cols
   int32_t param_bf16, grad_bf16;
   int32_t vec_ok;         // grad/mom rows allow 4-element vector access

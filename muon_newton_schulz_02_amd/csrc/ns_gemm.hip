@@ -394,20 +394,20 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
   int K;
   if constexpr (PHASE == PH_GRAM) {
     const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
-    const int64_t ld = int64_t(md.Np) * ESZ;
+    const int64_t ld = int64_t(md.ldx) * ESZ;
     sp = {x + int64_t(ti) * BT * ld, nullptr, ld, md.plane_X * ESZ, -1, 0};
     sq = {x + int64_t(tj) * BT * ld, nullptr, ld, md.plane_X * ESZ, -1, 0};
     K = md.Np;
   } else if constexpr (PHASE == PH_POLY) {
     const char* a = reinterpret_cast<const char*>(md.A);
-    const int64_t ld = int64_t(md.Mp) * ESZ;
+    const int64_t ld = int64_t(md.lda) * ESZ;
     sp = {a + int64_t(ti) * BT * ld, a + int64_t(ti) * BT * ESZ, ld, md.plane_A * ESZ, ti, 0};
     sq = {a + int64_t(tj) * BT * ld, a + int64_t(tj) * BT * ESZ, ld, md.plane_A * ESZ, tj, 0};
     K = md.Mp;
   } else {
     const char* b = reinterpret_cast<const char*>(md.B);
     const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
-    const int64_t lda = int64_t(md.Mp) * ESZ, ldx = int64_t(md.Np) * ESZ;
+    const int64_t lda = int64_t(md.lda) * ESZ, ldx = int64_t(md.ldx) * ESZ;
     sp = {b + int64_t(ti) * BT * lda, b + int64_t(ti) * BT * ESZ, lda, md.plane_A * ESZ, ti, 0};
     sq = {nullptr, x + int64_t(tj) * BT * ESZ, ldx, md.plane_X * ESZ, -1, 1};
     K = md.Mp;
@@ -511,7 +511,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
           float v[4];
 #pragma clang loop unroll(full)
           for (int e = 0; e < 4; ++e) v[e] = sc * acc[j][i][4 * g + e];
-          st4<PREC>(out, md.plane_A, int64_t(orow + 32 * i) * md.Mp + ocol + 32 * j + 8 * g, v);
+          st4<PREC>(out, md.plane_A, int64_t(orow + 32 * i) * md.lda + ocol + 32 * j + 8 * g, v);
         }
   } else {
     const float s = pa.first ? scal[mat].inv : 1.f;
@@ -526,7 +526,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
             float v[4];
 #pragma clang loop unroll(full)
             for (int e = 0; e < 4; ++e) v[e] = s * acc[j][i][4 * g + e];
-            st4<PREC>(xn, md.plane_X, int64_t(orow + 32 * i) * md.Np + ocol + 32 * j + 8 * g, v);
+            st4<PREC>(xn, md.plane_X, int64_t(orow + 32 * i) * md.ldx + ocol + 32 * j + 8 * g, v);
           }
     } else {
       const float t = update_scale(pa.lr, pa.scale_rule, md.rows, md.cols);

@@ -143,16 +143,18 @@ def test_valid_call_without_gpu_reports_hip_error(L):
 
 
 def test_workspace_bytes(L):
+    # workspace rows carry LDPAD (0) elements beyond their padded width
+    pad = 0
     one = mb.muon_workspace_bytes([(1536, 1536)])
-    # X and X' (2 x 1536^2) plus A and B (2 x 1536^2), bf16
-    assert one == 4 * 1536 * 1536 * 2
+    # X and X' (2 x 1536 rows) plus A and B (2 x 1536 rows), bf16
+    assert one == 4 * 1536 * (1536 + pad) * 2
     tall = mb.muon_workspace_bytes([(6144, 1536)])
     wide = mb.muon_workspace_bytes([(1536, 6144)])
-    assert tall == wide == (2 * 1536 * 6144 + 2 * 1536 * 1536) * 2
+    assert tall == wide == (2 * 1536 * (6144 + pad) + 2 * 1536 * (1536 + pad)) * 2
     assert mb.muon_workspace_bytes([(1536, 1536)], precision=mb.NS_BF16X3) == 2 * one
     assert mb.muon_workspace_bytes([(1536, 1536)], precision=mb.NS_F32) == 2 * one
     # padding to multiples of 256
-    assert mb.muon_workspace_bytes([(1, 300)]) == (2 * 256 * 512 + 2 * 256 * 256) * 2
+    assert mb.muon_workspace_bytes([(1, 300)]) == (2 * 256 * (512 + pad) + 2 * 256 * (256 + pad)) * 2
     assert mb.muon_workspace_bytes([(0, 4)]) == 0
 
 
