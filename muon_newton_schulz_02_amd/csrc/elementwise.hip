@@ -48,17 +48,12 @@ __device__ inline void store4_ws(void* base, int64_t plane, int prec, int64_t id
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
   } else {
     uint16_t* p = reinterpret_cast<uint16_t*>(base);
-    uint16_t h[4], l[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      h[e] = float_to_bf16_bits(v[e]);
-      l[e] = float_to_bf16_bits(v[e] - bf16_bits_to_float(h[e]));
-    }
-    uint2 hv = make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
-    *reinterpret_cast<uint2*>(p + idx) = hv;
+    const uint32_t h01 = float2_to_bf16x2_bits(v[0], v[1]), h23 = float2_to_bf16x2_bits(v[2], v[3]);
+    *reinterpret_cast<uint2*>(p + idx) = make_uint2(h01, h23);
     if (prec == PREC_BF16X3) {
-      uint2 lv = make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
-      *reinterpret_cast<uint2*>(p + plane + idx) = lv;
+      const uint32_t l01 = float2_to_bf16x2_bits(v[0] - bf16_bits_to_float(h01), v[1] - bf16_bits_to_float(h01 >> 16));
+      const uint32_t l23 = float2_to_bf16x2_bits(v[2] - bf16_bits_to_float(h23), v[3] - bf16_bits_to_float(h23 >> 16));
+      *reinterpret_cast<uint2*>(p + plane + idx) = make_uint2(l01, l23);
     }
   }
 }

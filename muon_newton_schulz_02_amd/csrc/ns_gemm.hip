@@ -104,15 +104,12 @@ __device__ __forceinline__ void st4(void* base, int64_t plane, int64_t idx, cons
     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + idx) = f32x4{v[0], v[1], v[2], v[3]};
   } else {
     uint16_t* p = reinterpret_cast<uint16_t*>(base);
-    uint32_t h[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) h[e] = float_to_bf16_bits(v[e]);
-    *reinterpret_cast<u32x2*>(p + idx) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    const uint32_t h01 = float2_to_bf16x2_bits(v[0], v[1]), h23 = float2_to_bf16x2_bits(v[2], v[3]);
+    *reinterpret_cast<u32x2*>(p + idx) = u32x2{h01, h23};
     if constexpr (PREC == PREC_BF16X3) {
-      uint32_t l[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) l[e] = float_to_bf16_bits(v[e] - bf16_bits_to_float(h[e]));
-      *reinterpret_cast<u32x2*>(p + plane + idx) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+      const uint32_t l01 = float2_to_bf16x2_bits(v[0] - bf16_bits_to_float(h01), v[1] - bf16_bits_to_float(h01 >> 16));
+      const uint32_t l23 = float2_to_bf16x2_bits(v[2] - bf16_bits_to_float(h23), v[3] - bf16_bits_to_float(h23 >> 16));
+      *reinterpret_cast<u32x2*>(p + plane + idx) = u32x2{l01, l23};
     }
   }
 }
@@ -155,8 +152,7 @@ __device__ __forceinline__ void write_back_n(const MatDev& md, int row, int c0, 
 #pragma unroll
         for (int e = 0; e < NE / 2; ++e) {
           const float w0 = bf16_bits_to_float(raw[e] & 0xFFFFu), w1 = bf16_bits_to_float(raw[e] >> 16);
-          raw[e] = uint32_t(float_to_bf16_bits(w0 - t * o[2 * e])) |
-                   (uint32_t(float_to_bf16_bits(w1 - t * o[2 * e + 1])) << 16);
+          raw[e] = float2_to_bf16x2_bits(w0 - t * o[2 * e], w1 - t * o[2 * e + 1]);
         }
         if constexpr (NE == 8) {
           *reinterpret_cast<u32x4*>(pw) = u32x4{raw[0], raw[1], raw[2], raw[3]};

@@ -11,14 +11,18 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
   return __uint_as_float((h & 0xFFFFu) << 16);
 }
 
-// Round a binary32 value to bfloat16, nearest with ties to even; NaN stays a
-// (quiet) NaN, overflow goes to infinity.
-__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+// Round two binary32 values to bfloat16, nearest with ties to even (overflow
+// to infinity, NaN stays NaN), with the converter of the CDNA4 vector unit
+// (v_cvt_pk_bf16_f32); returns lo | hi << 16.  A test of every binary32 bit
+// pattern found it equal to the explicit rounding (add 0x7FFF plus the
+// lowest kept bit, truncate) on all non-NaN inputs.
+__device__ __forceinline__ uint32_t float2_to_bf16x2_bits(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) { return uint16_t(float2_to_bf16x2_bits(f, 0.f)); }
 
 // t = fl32(lr * s) with s from the scale rule: 0 none (s = 1),
 // 1 sqrt(max(1, rows/cols)), 2 0.2*sqrt(max(rows, cols)); s and the
