@@ -9,13 +9,17 @@ momenta resident in HBM before the timed region.  Prints one JSON line.
 
 The roofline object is for the kernel class with the largest share of the
 timed region; per-launch durations come from HIP events the library
-records around each launch on the launch stream (muon_timing_*).
+records around each launch on the launch stream (muon_timing_*).  Its
+traffic is the HBM bytes per launch from the rocprofv3 FETCH_SIZE /
+WRITE_SIZE summary under profiles/, reported only while the kernel sources
+hash to the values recorded there (null otherwise).
 The cpu_baseline is the CPU oracle timed on a bounded sample of the same
 workload on this host.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -162,12 +166,13 @@ def main():
         kernels[name] = entry
     dom = max(kernels, key=lambda x: kernels[x]["share"])
     d = kernels[dom]
+    traffic = measured_traffic(args.workload, dom)
     if d.get("bound") == "mfma":
         roofline = {"bound": "mfma", "kernel": dom, "achieved": d["tflops"], "peak": peak_mfma,
-                    "unit": "TFLOP/s", "frac": d["frac"], "traffic": None}
+                    "unit": "TFLOP/s", "frac": d["frac"], "traffic": traffic}
     else:
         roofline = {"bound": "hbm", "kernel": dom, "achieved": d.get("gbs"), "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": d.get("frac"), "traffic": None}
+                    "unit": "GB/s", "frac": d.get("frac"), "traffic": traffic}
     ns_ms = sum(kern[x][0] for x in ("gram", "poly", "combine")) / steps
     ns_exec = sum(alg.values())
     ns_chain = {"nominal_tflop_per_step": round(nominal / 1e12, 4),
@@ -204,6 +209,39 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ns_gemm_d24_bf16_hbm.md")
+CSRC = os.path.join(ROOT, "muon_newton_schulz_02_amd", "csrc")
+
+
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for nm in names:
+        with open(os.path.join(CSRC, nm), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE summary of
+    the d24 workload, or None when that summary was taken on other kernel sources (or another
+    workload)."""
+    if workload != "d24_bf16" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    line = None
+    with open(TRAFFIC_FILE) as f:
+        for ln in f:
+            if ln.strip().startswith("traffic:"):
+                line = ln.strip()[len("traffic:"):]
+    if line is None:
+        return None
+    kv = dict(tok.split("=", 1) for tok in line.split())
+    src = _src_hash("elementwise.hip", "numeric.h", "muon_internal.h") if kernel == "momentum" else \
+        _src_hash("ns_gemm.hip", "numeric.h", "muon_internal.h")
+    if src != kv.get("elementwise_src" if kernel == "momentum" else "gemm_src") or kernel not in kv:
+        return None
+    return float(kv[kernel])
 
 
 def cpu_baseline(wl, sample, sample_idx, kw, n_total):
