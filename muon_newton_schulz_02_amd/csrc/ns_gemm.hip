@@ -281,6 +281,19 @@ struct OpSrc {
   int always_trans;        // COMB's X operand
 };
 
+// Buffer resources over the two layouts of an operand: loads then take a
+// 32-bit per-thread offset (the same every stage) and a scalar stage offset,
+// with no per-load address arithmetic.  Word 3 = 0x00020000: raw 32-bit
+// data, no swizzle; the record count covers any workspace matrix.
+struct OpRsrc {
+  __amdgpu_buffer_rsrc_t direct, trans;
+};
+__device__ __forceinline__ OpRsrc op_rsrc(const OpSrc& s) {
+  constexpr int RECORDS = 0x7FFFFFFF;
+  return {__builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(s.direct), 0, RECORDS, 0x00020000),
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(s.trans), 0, RECORDS, 0x00020000)};
+}
+
 template <int ESZ, int BT>
 __device__ __forceinline__ bool stage_is_trans(const OpSrc& s, int kt) {
   if (s.always_trans) return true;
@@ -288,11 +301,14 @@ __device__ __forceinline__ bool stage_is_trans(const OpSrc& s, int kt) {
   return (kt * (KB / ESZ)) / BT < s.sym_tile;  // below the diagonal: read the mirror block
 }
 
-template <int ESZ, int BT, int NT, int NPL, int NREG>
-__device__ __forceinline__ void load_stage(u32x4 (&r)[NPL][NREG], const OpSrc& s, int kt, int tid) {
+// Loads number I0 .. I1 - 1 of this thread's loads of one operand of stage kt
+// (numbered q * 4 + e for the transposed layout, q for the direct one).
+template <int ESZ, int BT, int NT, int NPL, int NREG, int I0 = 0, int I1 = 1 << 20>
+__device__ __forceinline__ void load_stage(u32x4 (&r)[NPL][NREG], const OpSrc& s, const OpRsrc& rs, int kt,
+                                           int tid) {
   using G = Geo<ESZ, BT, NT>;
   if (stage_is_trans<ESZ, BT>(s, kt)) {
-    const int k0 = kt * (KB / ESZ);
+    const int sbase = int(int64_t(kt) * (KB / ESZ) * s.ld_b);
 #pragma unroll
     for (int q = 0; q < G::PER; ++q) {
       const int blk = tid + NT * q;
@@ -300,18 +316,25 @@ __device__ __forceinline__ void load_stage(u32x4 (&r)[NPL][NREG], const OpSrc& s
       const int rb = blk % G::RB, kg = blk / G::RB;   // row block, group of 4 k-values
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t off = int64_t(k0 + kg * 4 + e) * s.ld_b + rb * 16;
+        if (q * 4 + e < I0 || q * 4 + e >= I1) continue;
+        const int off = int((kg * 4 + e) * s.ld_b + rb * 16);
 #pragma unroll
-        for (int pl = 0; pl < NPL; ++pl) r[pl][q * 4 + e] = *(gu32x4*)(s.trans + pl * s.plane_b + off);
+        for (int pl = 0; pl < NPL; ++pl)
+          r[pl][q * 4 + e] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.trans, off, sbase + pl * int(s.plane_b), 0));
       }
     }
   } else {
+    const int sbase = kt * KB;
 #pragma unroll
     for (int q = 0; q < G::CH; ++q) {
+      if (q < I0 || q >= I1) continue;
       const int c = tid + NT * q;
-      const int64_t off = int64_t(c >> 3) * s.ld_b + int64_t(kt) * KB + (c & 7) * 16;
+      const int off = int((c >> 3) * s.ld_b + (c & 7) * 16);
 #pragma unroll
-      for (int pl = 0; pl < NPL; ++pl) r[pl][q] = *(gu32x4*)(s.direct + pl * s.plane_b + off);
+      for (int pl = 0; pl < NPL; ++pl)
+        r[pl][q] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.direct, off, sbase + pl * int(s.plane_b), 0));
     }
   }
 }
@@ -363,6 +386,38 @@ __device__ __forceinline__ void store_stage(const u32x4 (&r)[NPL][NREG], const O
   }
 }
 
+// Store a bf16 output tile (BT x BT at `out`, row stride ld bytes) through
+// LDS: every lane's four consecutive columns go to LDS as 8 bytes, then each
+// 32 lanes write 512 contiguous bytes of one row (stores straight from the
+// accumulators would put 16 bytes into each of 32 rows per instruction).
+// The k-loop has ended with a barrier, so the operand stages are free.
+template <int FQ, int FP, int WTP, int WTQ, int BT, int NT, int LDSB>
+__device__ __forceinline__ void store_tile_bf16(const f32x16 (&acc)[FQ][FP], float sc, char* out, int64_t ld,
+                                                char* smem, int wp, int wq, int lane, int tid) {
+  constexpr int EP = BT * 2 + 16;  // staging pitch in bytes
+  static_assert(BT * EP <= LDSB, "staging does not fit");
+  const int hsel = lane >> 5;
+#pragma clang loop unroll(full)
+  for (int j = 0; j < FQ; ++j)
+#pragma clang loop unroll(full)
+    for (int i = 0; i < FP; ++i)
+#pragma clang loop unroll(full)
+      for (int g = 0; g < 4; ++g) {
+        const int r = wp * WTP + 32 * i + (lane & 31), c = wq * WTQ + 32 * j + 8 * g + 4 * hsel;
+        const f32x16& a = acc[j][i];
+        *reinterpret_cast<u32x2*>(smem + r * EP + c * 2) =
+            u32x2{float2_to_bf16x2_bits(sc * a[4 * g], sc * a[4 * g + 1]),
+                  float2_to_bf16x2_bits(sc * a[4 * g + 2], sc * a[4 * g + 3])};
+      }
+  __syncthreads();
+  constexpr int CPR = BT * 2 / 16;  // 16-byte chunks per row
+#pragma unroll 4
+  for (int q = tid; q < BT * CPR; q += NT) {
+    const int r = q / CPR, c16 = q % CPR;
+    *reinterpret_cast<u32x4*>(out + int64_t(r) * ld + c16 * 16) = *reinterpret_cast<const u32x4*>(smem + r * EP + c16 * 16);
+  }
+}
+
 // ------------------------------------------------------------------ tile
 
 // VAR: GRAM 1 = c != 0 (store A), 0 = c == 0 (store B = b A);
@@ -409,6 +464,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     K = md.Mp;
   }
   const int nk = K / KE;
+  const OpRsrc rsp = op_rsrc(sp), rsq = op_rsrc(sq);
 
   // additive term alpha * D on the tile's own rows (POLY: (b/c) A, COMB: a X)
   constexpr bool ADD = PHASE != PH_GRAM;
@@ -424,8 +480,8 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
 #pragma clang loop unroll(full)
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
 
-  load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, sp, 0, tid);
-  load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, sq, 0, tid);
+  load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, sp, rsp, 0, tid);
+  load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, sq, rsq, 0, tid);
   store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rp, sp, 0, smem, tid);
   store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rq, sq, 0, smem + NPL * OPB, tid);
   __syncthreads();
@@ -434,14 +490,26 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
 #pragma unroll 1
   for (int kt = 0; kt < nk; ++kt) {
     const int s = kt & 1;
-    if (kt + 1 < nk) {
-      load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, sp, kt + 1, tid);
-      load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, sq, kt + 1, tid);
+    // The loads of stage kt + 1 go out a quarter before each k-slab (bf16:
+    // four slabs, four loads per operand), not in one burst: a burst of
+    // 64 loads per workgroup stalls every wave at issue.
+    constexpr bool SPREAD = PREC == PREC_BF16 && KE / KS == 4 && G::NREG == 4;
+    if (!SPREAD && kt + 1 < nk) {
+      load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, sp, rsp, kt + 1, tid);
+      load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, sq, rsq, kt + 1, tid);
     }
     const char* lP = smem + s * STAGE;
     const char* lQ = lP + NPL * OPB;
 #pragma clang loop unroll(full)
     for (int ks = 0; ks < KE / KS; ++ks) {
+      if constexpr (SPREAD) {
+        if (kt + 1 < nk) {
+          if (ks == 0) load_stage<ESZ, BT, NT, NPL, G::NREG, 0, 2>(rp, sp, rsp, kt + 1, tid);
+          if (ks == 1) load_stage<ESZ, BT, NT, NPL, G::NREG, 2, 4>(rp, sp, rsp, kt + 1, tid);
+          if (ks == 2) load_stage<ESZ, BT, NT, NPL, G::NREG, 0, 2>(rq, sq, rsq, kt + 1, tid);
+          if (ks == 3) load_stage<ESZ, BT, NT, NPL, G::NREG, 2, 4>(rq, sq, rsq, kt + 1, tid);
+        }
+      }
       const int ch = 2 * ks + hsel;           // this lane's 16-byte chunk of the slab
       u32x4 qf[FQ][NPL], pf[FP][NPL];
 #pragma clang loop unroll(full)
@@ -494,7 +562,14 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
   // output column tj*BT + wq*WTQ + 32 fj + 8g + 4h + e.
   const int orow = ti * BT + wp * WTP + (lane & 31);
   const int ocol = tj * BT + wq * WTQ + 4 * hsel;
-  if constexpr (PHASE == PH_GRAM || PHASE == PH_POLY) {
+  if constexpr ((PHASE == PH_GRAM || PHASE == PH_POLY) && PREC == PREC_BF16) {
+    char* out = reinterpret_cast<char*>((PHASE == PH_GRAM && VAR == 1) ? md.A : md.B);
+    const float sc = PHASE == PH_POLY ? pa.c
+                                      : (pa.first ? scal[mat].inv2 : 1.f) * (VAR == 1 ? 1.f : pa.b);
+    const int64_t ld = int64_t(md.lda) * 2;
+    store_tile_bf16<FQ, FP, WTP, WTQ, BT, NT, 2 * STAGE>(acc, sc, out + int64_t(ti) * BT * ld + int64_t(tj) * BT * 2,
+                                                       ld, smem, wp, wq, lane, tid);
+  } else if constexpr (PHASE == PH_GRAM || PHASE == PH_POLY) {
     void* out = (PHASE == PH_GRAM && VAR == 1) ? md.A : md.B;
     const float sc = PHASE == PH_POLY ? pa.c
                                       : (pa.first ? scal[mat].inv2 : 1.f) * (VAR == 1 ? 1.f : pa.b);
@@ -511,7 +586,11 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
         }
   } else {
     const float s = pa.first ? scal[mat].inv : 1.f;
-    if constexpr (VAR == 0) {
+    if constexpr (VAR == 0 && PREC == PREC_BF16) {
+      const int64_t ld = int64_t(md.ldx) * 2;
+      char* xn = reinterpret_cast<char*>(md.X[pa.cur ^ 1]) + int64_t(ti) * BT * ld + int64_t(tj) * BT * 2;
+      store_tile_bf16<FQ, FP, WTP, WTQ, BT, NT, 2 * STAGE>(acc, s, xn, ld, smem, wp, wq, lane, tid);
+    } else if constexpr (VAR == 0) {
       void* xn = md.X[pa.cur ^ 1];
 #pragma clang loop unroll(full)
       for (int j = 0; j < FQ; ++j)
