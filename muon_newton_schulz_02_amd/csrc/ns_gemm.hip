@@ -490,9 +490,10 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
 #pragma unroll 1
   for (int kt = 0; kt < nk; ++kt) {
     const int s = kt & 1;
-    // The loads of stage kt + 1 go out a quarter before each k-slab (bf16:
-    // four slabs, four loads per operand), not in one burst: a burst of
-    // 64 loads per workgroup stalls every wave at issue.
+    // The loads of stage kt + 1 go out in two halves, P's before k-slab 0 and
+    // Q's before k-slab 1 (bf16: four slabs), not in one burst: a burst of 64
+    // loads per workgroup stalls every wave at issue, while loads issued in
+    // the last slabs leave too little time before the stage's LDS stores.
     constexpr bool SPREAD = PREC == PREC_BF16 && KE / KS == 4 && G::NREG == 4;
     if (!SPREAD && kt + 1 < nk) {
       load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, sp, rsp, kt + 1, tid);
@@ -504,10 +505,8 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     for (int ks = 0; ks < KE / KS; ++ks) {
       if constexpr (SPREAD) {
         if (kt + 1 < nk) {
-          if (ks == 0) load_stage<ESZ, BT, NT, NPL, G::NREG, 0, 2>(rp, sp, rsp, kt + 1, tid);
-          if (ks == 1) load_stage<ESZ, BT, NT, NPL, G::NREG, 2, 4>(rp, sp, rsp, kt + 1, tid);
-          if (ks == 2) load_stage<ESZ, BT, NT, NPL, G::NREG, 0, 2>(rq, sq, rsq, kt + 1, tid);
-          if (ks == 3) load_stage<ESZ, BT, NT, NPL, G::NREG, 2, 4>(rq, sq, rsq, kt + 1, tid);
+          if (ks == 0) load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, sp, rsp, kt + 1, tid);
+          if (ks == 1) load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, sq, rsq, kt + 1, tid);
         }
       }
       const int ch = 2 * ks + hsel;           // this lane's 16-byte chunk of the slab
@@ -605,57 +604,61 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
           }
     } else {
       const float t = update_scale(pa.lr, pa.scale_rule, md.rows, md.cols);
-      if (md.transposed == 0) {
-        // W = X': this lane's four consecutive columns are four consecutive W elements
-#pragma clang loop unroll(full)
-        for (int j = 0; j < FQ; ++j)
-#pragma clang loop unroll(full)
-          for (int i = 0; i < FP; ++i)
-#pragma clang loop unroll(full)
-            for (int g = 0; g < 4; ++g) {
-              const int r = orow + 32 * i, c0 = ocol + 32 * j + 8 * g;
-              float v[4];
-#pragma clang loop unroll(full)
-              for (int e = 0; e < 4; ++e) v[e] = s * acc[j][i][4 * g + e];
-              if (r < md.m) write_back_n<4>(md, r, c0, md.n, v, t);
-            }
-      } else {
-        // W = X'^T: stage the binary32 update transposed through LDS, 128 output
-        // rows (= W columns) at a time, then read-modify-write 8-element W rows.
-        constexpr int NPASS = BT / 128;
-        constexpr int RP = BT / NPASS;        // output rows per pass
-        constexpr int SPT = RP + 4;           // staging pitch in floats: BT rows of RP floats
-        static_assert(BT * SPT * 4 <= 2 * STAGE, "staging does not fit");
-        float* stg = reinterpret_cast<float*>(smem);
+      // Stage the binary32 update through LDS, RP output rows per pass (as W's
+      // rows, or transposed when W = X'^T), then read-modify-write 8-element
+      // runs of W rows: 16-byte accesses, 512 contiguous bytes per 32 lanes.
+      constexpr int RP = WTP;                 // output rows per pass: one row of waves
+      constexpr int NPASS = BT / RP;
+      constexpr int SPN = BT + 4;             // pitch (floats): RP rows of BT floats
+      constexpr int SPT = RP + 4;             // pitch (floats): BT rows of RP floats (transposed)
+      static_assert(RP * SPN * 4 <= 2 * STAGE && BT * SPT * 4 <= 2 * STAGE, "staging does not fit");
+      float* stg = reinterpret_cast<float*>(smem);
+      const bool tr = md.transposed != 0;
 #pragma unroll 1
-        for (int pass = 0; pass < NPASS; ++pass) {
-          if (NPASS == 1 || wp == pass) {
-            const int rl = wp * WTP - pass * RP + (lane & 31);
+      for (int pass = 0; pass < NPASS; ++pass) {
+        if (wp == pass) {
+          const int rl = lane & 31;
 #pragma clang loop unroll(full)
-            for (int j = 0; j < FQ; ++j)
+          for (int j = 0; j < FQ; ++j)
 #pragma clang loop unroll(full)
-              for (int i = 0; i < FP; ++i)
+            for (int i = 0; i < FP; ++i)
 #pragma clang loop unroll(full)
-                for (int g = 0; g < 4; ++g)
+              for (int g = 0; g < 4; ++g) {
+                const int cl = wq * WTQ + 32 * j + 8 * g + 4 * hsel;
+                const f32x4 v = {s * acc[j][i][4 * g], s * acc[j][i][4 * g + 1], s * acc[j][i][4 * g + 2],
+                                 s * acc[j][i][4 * g + 3]};
+                if (tr) {
 #pragma clang loop unroll(full)
-                  for (int e = 0; e < 4; ++e) {
-                    const int cl = wq * WTQ + 32 * j + 8 * g + 4 * hsel + e;
-                    stg[cl * SPT + rl + 32 * i] = s * acc[j][i][4 * g + e];
-                  }
-          }
-          __syncthreads();
-          const int row_base = ti * BT + pass * RP;
+                  for (int e = 0; e < 4; ++e) stg[(cl + e) * SPT + rl + 32 * i] = v[e];
+                } else {
+                  *reinterpret_cast<f32x4*>(stg + (rl + 32 * i) * SPN + cl) = v;
+                }
+              }
+        }
+        __syncthreads();
+        const int row_base = ti * BT + pass * RP;  // first wide row of the pass
+        if (tr) {
           for (int q = tid; q < BT * RP / 8; q += NT) {
             const int cl = q / (RP / 8), r8 = (q % (RP / 8)) * 8;
-            const int nrow = tj * BT + cl;    // natural row = wide column
+            const int nrow = tj * BT + cl;  // natural row = wide column
             if (nrow >= md.n) continue;
             const f32x4 a0 = *reinterpret_cast<const f32x4*>(stg + cl * SPT + r8);
             const f32x4 a1 = *reinterpret_cast<const f32x4*>(stg + cl * SPT + r8 + 4);
             const float o[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             write_back_n<8>(md, nrow, row_base + r8, md.m, o, t);
           }
-          __syncthreads();
+        } else {
+          for (int q = tid; q < RP * BT / 8; q += NT) {
+            const int rl = q / (BT / 8), c8 = (q % (BT / 8)) * 8;
+            const int nrow = row_base + rl;
+            if (nrow >= md.m) continue;
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(stg + rl * SPN + c8);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(stg + rl * SPN + c8 + 4);
+            const float o[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            write_back_n<8>(md, nrow, tj * BT + c8, md.n, o, t);
+          }
         }
+        __syncthreads();
       }
     }
   }
