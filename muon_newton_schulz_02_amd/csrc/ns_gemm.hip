@@ -94,6 +94,12 @@ template <> struct Cfg<PREC_F32> { static constexpr int BT = 128, WP = 2, WQ = 2
 
 __device__ __forceinline__ int lds_off(int r, int ch) { return r * PITCH + ((ch ^ ((r >> 4) & 7)) << 4); }
 
+// Workgroup barrier for LDS reuse only: this wave's LDS accesses complete,
+// then s_barrier.  Unlike __syncthreads it does not wait for global stores
+// in flight, so a tile's output drains while the next tile loads; no tile of
+// a launch reads what another tile of that launch writes.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ------------------------------------------------------------------ storage
 
 // Four consecutive values of the working format at element idx (a multiple
@@ -409,7 +415,7 @@ __device__ __forceinline__ void store_tile_bf16(const f32x16 (&acc)[FQ][FP], flo
             u32x2{float2_to_bf16x2_bits(sc * a[4 * g], sc * a[4 * g + 1]),
                   float2_to_bf16x2_bits(sc * a[4 * g + 2], sc * a[4 * g + 3])};
       }
-  __syncthreads();
+  lds_barrier();
   constexpr int CPR = BT * 2 / 16;  // 16-byte chunks per row
 #pragma unroll 4
   for (int q = tid; q < BT * CPR; q += NT) {
@@ -484,7 +490,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
   load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, sq, rsq, 0, tid);
   store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rp, sp, 0, smem, tid);
   store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rq, sq, 0, smem + NPL * OPB, tid);
-  __syncthreads();
+  lds_barrier();
 
   const int hsel = lane >> 5;
 #pragma unroll 1
@@ -553,7 +559,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rp, sp, kt + 1, smem + (s ^ 1) * STAGE, tid);
       store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rq, sq, kt + 1, smem + (s ^ 1) * STAGE + NPL * OPB, tid);
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -635,7 +641,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
                 }
               }
         }
-        __syncthreads();
+        lds_barrier();
         const int row_base = ti * BT + pass * RP;  // first wide row of the pass
         if (tr) {
           for (int q = tid; q < BT * RP / 8; q += NT) {
@@ -658,7 +664,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
             write_back_n<8>(md, nrow, tj * BT + c8, md.n, o, t);
           }
         }
-        __syncthreads();
+        lds_barrier();
       }
     }
   }
@@ -681,7 +687,7 @@ __global__ __launch_bounds__(Cfg<PREC>::NT) void ns_gemm_kernel(const MatDev* __
     const int2 te = list[slot];
     if (te.x < 0) break;  // lists are padded at their end only
     ns_tile_body<PREC, PHASE, VAR>(mats[te.x], scal, te.x, te.y >> 16, te.y & 0xFFFF, pa, smem);
-    __syncthreads();
+    lds_barrier();
   }
 }
 
