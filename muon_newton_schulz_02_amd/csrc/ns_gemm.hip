@@ -610,61 +610,59 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
           }
     } else {
       const float t = update_scale(pa.lr, pa.scale_rule, md.rows, md.cols);
-      // Stage the binary32 update through LDS, RP output rows per pass (as W's
-      // rows, or transposed when W = X'^T), then read-modify-write 8-element
-      // runs of W rows: 16-byte accesses, 512 contiguous bytes per 32 lanes.
-      constexpr int RP = WTP;                 // output rows per pass: one row of waves
-      constexpr int NPASS = BT / RP;
-      constexpr int SPN = BT + 4;             // pitch (floats): RP rows of BT floats
-      constexpr int SPT = RP + 4;             // pitch (floats): BT rows of RP floats (transposed)
-      static_assert(RP * SPN * 4 <= 2 * STAGE && BT * SPT * 4 <= 2 * STAGE, "staging does not fit");
-      float* stg = reinterpret_cast<float*>(smem);
-      const bool tr = md.transposed != 0;
+      if (md.transposed == 0) {
+        // W = X': this lane's four consecutive columns are four consecutive W
+        // elements (staging these through LDS was measured slower)
+#pragma clang loop unroll(full)
+        for (int j = 0; j < FQ; ++j)
+#pragma clang loop unroll(full)
+          for (int i = 0; i < FP; ++i)
+#pragma clang loop unroll(full)
+            for (int g = 0; g < 4; ++g) {
+              const int r = orow + 32 * i, c0 = ocol + 32 * j + 8 * g;
+              float v[4];
+#pragma clang loop unroll(full)
+              for (int e = 0; e < 4; ++e) v[e] = s * acc[j][i][4 * g + e];
+              if (r < md.m) write_back_n<4>(md, r, c0, md.n, v, t);
+            }
+      } else {
+        // W = X'^T: stage the binary32 update transposed through LDS, one row of
+        // waves (RP output rows = W columns) per pass, then read-modify-write
+        // 8-element runs of W rows: 16-byte accesses, 512 bytes per 32 lanes.
+        constexpr int RP = WTP;               // output rows per pass
+        constexpr int NPASS = BT / RP;
+        constexpr int SPT = RP + 4;           // staging pitch in floats: BT rows of RP floats
+        static_assert(BT * SPT * 4 <= 2 * STAGE, "staging does not fit");
+        float* stg = reinterpret_cast<float*>(smem);
 #pragma unroll 1
-      for (int pass = 0; pass < NPASS; ++pass) {
-        if (wp == pass) {
-          const int rl = lane & 31;
+        for (int pass = 0; pass < NPASS; ++pass) {
+          if (wp == pass) {
+            const int rl = lane & 31;
 #pragma clang loop unroll(full)
-          for (int j = 0; j < FQ; ++j)
+            for (int j = 0; j < FQ; ++j)
 #pragma clang loop unroll(full)
-            for (int i = 0; i < FP; ++i)
+              for (int i = 0; i < FP; ++i)
 #pragma clang loop unroll(full)
-              for (int g = 0; g < 4; ++g) {
-                const int cl = wq * WTQ + 32 * j + 8 * g + 4 * hsel;
-                const f32x4 v = {s * acc[j][i][4 * g], s * acc[j][i][4 * g + 1], s * acc[j][i][4 * g + 2],
-                                 s * acc[j][i][4 * g + 3]};
-                if (tr) {
+                for (int g = 0; g < 4; ++g)
 #pragma clang loop unroll(full)
-                  for (int e = 0; e < 4; ++e) stg[(cl + e) * SPT + rl + 32 * i] = v[e];
-                } else {
-                  *reinterpret_cast<f32x4*>(stg + (rl + 32 * i) * SPN + cl) = v;
-                }
-              }
-        }
-        lds_barrier();
-        const int row_base = ti * BT + pass * RP;  // first wide row of the pass
-        if (tr) {
+                  for (int e = 0; e < 4; ++e) {
+                    const int cl = wq * WTQ + 32 * j + 8 * g + 4 * hsel + e;
+                    stg[cl * SPT + rl + 32 * i] = s * acc[j][i][4 * g + e];
+                  }
+          }
+          lds_barrier();
+          const int row_base = ti * BT + pass * RP;
           for (int q = tid; q < BT * RP / 8; q += NT) {
             const int cl = q / (RP / 8), r8 = (q % (RP / 8)) * 8;
-            const int nrow = tj * BT + cl;  // natural row = wide column
+            const int nrow = tj * BT + cl;    // natural row = wide column
             if (nrow >= md.n) continue;
             const f32x4 a0 = *reinterpret_cast<const f32x4*>(stg + cl * SPT + r8);
             const f32x4 a1 = *reinterpret_cast<const f32x4*>(stg + cl * SPT + r8 + 4);
             const float o[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             write_back_n<8>(md, nrow, row_base + r8, md.m, o, t);
           }
-        } else {
-          for (int q = tid; q < RP * BT / 8; q += NT) {
-            const int rl = q / (BT / 8), c8 = (q % (BT / 8)) * 8;
-            const int nrow = row_base + rl;
-            if (nrow >= md.m) continue;
-            const f32x4 a0 = *reinterpret_cast<const f32x4*>(stg + rl * SPN + c8);
-            const f32x4 a1 = *reinterpret_cast<const f32x4*>(stg + rl * SPN + c8 + 4);
-            const float o[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            write_back_n<8>(md, nrow, tj * BT + c8, md.n, o, t);
-          }
+          lds_barrier();
         }
-        lds_barrier();
       }
     }
   }
