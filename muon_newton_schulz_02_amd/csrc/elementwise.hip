@@ -38,29 +38,29 @@ __device__ inline int find_matrix(const int32_t* __restrict__ off, int count, in
 }
 
 __device__ inline float load_elem(const void* p, int64_t idx, int bf16) {
-  return bf16 ? bf16_bits_to_float(reinterpret_cast<const uint16_t*>(p)[idx])
-              : reinterpret_cast<const float*>(p)[idx];
+  return bf16 ? bf16_bits_to_float(gmem(reinterpret_cast<const uint16_t*>(p))[idx])
+              : gmem(reinterpret_cast<const float*>(p))[idx];
 }
 
 // Store four consecutive values of the Newton-Schulz working format.
 __device__ inline void store4_ws(void* base, int64_t plane, int prec, int64_t idx, const float v[4]) {
   if (prec == PREC_F32) {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+    *gmem(reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx)) = make_float4(v[0], v[1], v[2], v[3]);
   } else {
     uint16_t* p = reinterpret_cast<uint16_t*>(base);
     const uint32_t h01 = float2_to_bf16x2_bits(v[0], v[1]), h23 = float2_to_bf16x2_bits(v[2], v[3]);
-    *reinterpret_cast<uint2*>(p + idx) = make_uint2(h01, h23);
+    *gmem(reinterpret_cast<uint2*>(p + idx)) = make_uint2(h01, h23);
     if (prec == PREC_BF16X3) {
       const uint32_t l01 = float2_to_bf16x2_bits(v[0] - bf16_bits_to_float(h01), v[1] - bf16_bits_to_float(h01 >> 16));
       const uint32_t l23 = float2_to_bf16x2_bits(v[2] - bf16_bits_to_float(h23), v[3] - bf16_bits_to_float(h23 >> 16));
-      *reinterpret_cast<uint2*>(p + plane + idx) = make_uint2(l01, l23);
+      *gmem(reinterpret_cast<uint2*>(p + plane + idx)) = make_uint2(l01, l23);
     }
   }
 }
 
 __device__ inline float load_ws(const void* base, int64_t plane, int prec, int64_t idx) {
-  if (prec == PREC_F32) return reinterpret_cast<const float*>(base)[idx];
-  const uint16_t* p = reinterpret_cast<const uint16_t*>(base);
+  if (prec == PREC_F32) return gmem(reinterpret_cast<const float*>(base))[idx];
+  auto p = gmem(reinterpret_cast<const uint16_t*>(base));
   float v = bf16_bits_to_float(p[idx]);
   if (prec == PREC_BF16X3) v = v + bf16_bits_to_float(p[plane + idx]);
   return v;
@@ -111,13 +111,13 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
       const int64_t gi = int64_t(row) * md.ld_grad + col;
       if (full) {
         if (md.grad_bf16) {
-          uint2 raw = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(md.grad) + gi);
+          uint2 raw = *gmem(reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(md.grad) + gi));
           g[0] = bf16_bits_to_float(raw.x & 0xFFFFu);
           g[1] = bf16_bits_to_float(raw.x >> 16);
           g[2] = bf16_bits_to_float(raw.y & 0xFFFFu);
           g[3] = bf16_bits_to_float(raw.y >> 16);
         } else {
-          float4 raw = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(md.grad) + gi);
+          float4 raw = *gmem(reinterpret_cast<const float4*>(reinterpret_cast<const float*>(md.grad) + gi));
           g[0] = raw.x; g[1] = raw.y; g[2] = raw.z; g[3] = raw.w;
         }
       } else {
@@ -128,12 +128,12 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
       if (mode == 0) {
         const int64_t mi64 = int64_t(row) * md.ld_mom + col;
         if (full) {
-          float4 raw = *reinterpret_cast<const float4*>(md.mom + mi64);
+          float4 raw = *gmem(reinterpret_cast<const float4*>(md.mom + mi64));
           m[0] = raw.x; m[1] = raw.y; m[2] = raw.z; m[3] = raw.w;
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (col + e < cols) m[e] = md.mom[mi64 + e];
+            if (col + e < cols) m[e] = gmem(md.mom)[mi64 + e];
         }
         float mn[4];
 #pragma unroll
@@ -145,11 +145,11 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
           u[e] = nesterov ? (g[e] + bn) : mn[e];
         }
         if (full) {
-          *reinterpret_cast<float4*>(md.mom + mi64) = make_float4(mn[0], mn[1], mn[2], mn[3]);
+          *gmem(reinterpret_cast<float4*>(md.mom + mi64)) = make_float4(mn[0], mn[1], mn[2], mn[3]);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (col + e < cols) md.mom[mi64 + e] = mn[e];
+            if (col + e < cols) gmem(md.mom)[mi64 + e] = mn[e];
         }
       } else {
 #pragma unroll
@@ -237,15 +237,15 @@ __global__ __launch_bounds__(256) void writeback_direct_kernel(const MatDev* __r
     if (md.param) {
       const int64_t pi = int64_t(row) * md.ld_param + col;
       if (md.param_bf16) {
-        uint16_t* pw = reinterpret_cast<uint16_t*>(md.param);
+        auto pw = gmem(reinterpret_cast<uint16_t*>(md.param));
         const float w = bf16_bits_to_float(pw[pi]);
         pw[pi] = float_to_bf16_bits(w - t * o);
       } else {
-        float* pw = reinterpret_cast<float*>(md.param);
+        auto pw = gmem(reinterpret_cast<float*>(md.param));
         pw[pi] = pw[pi] - t * o;
       }
     }
-    if (md.upd) md.upd[int64_t(row) * md.ld_upd + col] = o;
+    if (md.upd) gmem(md.upd)[int64_t(row) * md.ld_upd + col] = o;
   }
 }
 

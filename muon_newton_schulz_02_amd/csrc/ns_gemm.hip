@@ -107,15 +107,15 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 template <int PREC>
 __device__ __forceinline__ void st4(void* base, int64_t plane, int64_t idx, const float* v) {
   if constexpr (PREC == PREC_F32) {
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + idx) = f32x4{v[0], v[1], v[2], v[3]};
+    *gmem(reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + idx)) = f32x4{v[0], v[1], v[2], v[3]};
   } else {
     uint16_t* p = reinterpret_cast<uint16_t*>(base);
     const uint32_t h01 = float2_to_bf16x2_bits(v[0], v[1]), h23 = float2_to_bf16x2_bits(v[2], v[3]);
-    *reinterpret_cast<u32x2*>(p + idx) = u32x2{h01, h23};
+    *gmem(reinterpret_cast<u32x2*>(p + idx)) = u32x2{h01, h23};
     if constexpr (PREC == PREC_BF16X3) {
       const uint32_t l01 = float2_to_bf16x2_bits(v[0] - bf16_bits_to_float(h01), v[1] - bf16_bits_to_float(h01 >> 16));
       const uint32_t l23 = float2_to_bf16x2_bits(v[2] - bf16_bits_to_float(h23), v[3] - bf16_bits_to_float(h23 >> 16));
-      *reinterpret_cast<u32x2*>(p + plane + idx) = u32x2{l01, l23};
+      *gmem(reinterpret_cast<u32x2*>(p + plane + idx)) = u32x2{l01, l23};
     }
   }
 }
@@ -125,14 +125,14 @@ __device__ __forceinline__ void write_back1(const MatDev& md, int row, int col, 
   if (md.param) {
     const int64_t pi = int64_t(row) * md.ld_param + col;
     if (md.param_bf16) {
-      uint16_t* pw = reinterpret_cast<uint16_t*>(md.param) + pi;
+      auto pw = gmem(reinterpret_cast<uint16_t*>(md.param) + pi);
       *pw = float_to_bf16_bits(bf16_bits_to_float(*pw) - t * o);
     } else {
-      float* pw = reinterpret_cast<float*>(md.param) + pi;
+      auto pw = gmem(reinterpret_cast<float*>(md.param) + pi);
       *pw = *pw - t * o;
     }
   }
-  if (md.upd) md.upd[int64_t(row) * md.ld_upd + col] = o;
+  if (md.upd) *gmem(md.upd + int64_t(row) * md.ld_upd + col) = o;
 }
 
 // The same for W[row][c0 .. c0+NE-1] (NE = 4 or 8, c0 a multiple of NE),
@@ -146,13 +146,13 @@ __device__ __forceinline__ void write_back_n(const MatDev& md, int row, int c0, 
     const int64_t pi = int64_t(row) * md.ld_param + c0;
     if (md.param) {
       if (md.param_bf16) {
-        uint16_t* pw = reinterpret_cast<uint16_t*>(md.param) + pi;
+        auto pw = gmem(reinterpret_cast<uint16_t*>(md.param) + pi);
         uint32_t raw[NE / 2];
         if constexpr (NE == 8) {
-          const u32x4 r4 = *reinterpret_cast<const u32x4*>(pw);
+          const u32x4 r4 = *reinterpret_cast<__attribute__((address_space(1))) const u32x4*>(pw);
           raw[0] = r4[0]; raw[1] = r4[1]; raw[2] = r4[2]; raw[3] = r4[3];
         } else {
-          const u32x2 r2 = *reinterpret_cast<const u32x2*>(pw);
+          const u32x2 r2 = *reinterpret_cast<__attribute__((address_space(1))) const u32x2*>(pw);
           raw[0] = r2[0]; raw[1] = r2[1];
         }
 #pragma unroll
@@ -161,12 +161,12 @@ __device__ __forceinline__ void write_back_n(const MatDev& md, int row, int c0, 
           raw[e] = float2_to_bf16x2_bits(w0 - t * o[2 * e], w1 - t * o[2 * e + 1]);
         }
         if constexpr (NE == 8) {
-          *reinterpret_cast<u32x4*>(pw) = u32x4{raw[0], raw[1], raw[2], raw[3]};
+          *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(pw) = u32x4{raw[0], raw[1], raw[2], raw[3]};
         } else {
-          *reinterpret_cast<u32x2*>(pw) = u32x2{raw[0], raw[1]};
+          *reinterpret_cast<__attribute__((address_space(1))) u32x2*>(pw) = u32x2{raw[0], raw[1]};
         }
       } else {
-        f32x4* pw = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(md.param) + pi);
+        auto pw = gmem(reinterpret_cast<f32x4*>(reinterpret_cast<float*>(md.param) + pi));
 #pragma unroll
         for (int h = 0; h < NE / 4; ++h) {
           f32x4 w = pw[h];
@@ -177,11 +177,11 @@ __device__ __forceinline__ void write_back_n(const MatDev& md, int row, int c0, 
       }
     }
     if (md.upd) {
-      float* pu = md.upd + int64_t(row) * md.ld_upd + c0;
+      auto pu = gmem(md.upd + int64_t(row) * md.ld_upd + c0);
       if (md.uvec_ok) {
 #pragma unroll
         for (int h = 0; h < NE / 4; ++h)
-          reinterpret_cast<f32x4*>(pu)[h] = f32x4{o[4 * h], o[4 * h + 1], o[4 * h + 2], o[4 * h + 3]};
+          reinterpret_cast<__attribute__((address_space(1))) f32x4*>(pu)[h] = f32x4{o[4 * h], o[4 * h + 1], o[4 * h + 2], o[4 * h + 3]};
       } else {
 #pragma unroll
         for (int e = 0; e < NE; ++e) pu[e] = o[e];
@@ -420,7 +420,7 @@ __device__ __forceinline__ void store_tile_bf16(const f32x16 (&acc)[FQ][FP], flo
 #pragma unroll 4
   for (int q = tid; q < BT * CPR; q += NT) {
     const int r = q / CPR, c16 = q % CPR;
-    *reinterpret_cast<u32x4*>(out + int64_t(r) * ld + c16 * 16) = *reinterpret_cast<const u32x4*>(smem + r * EP + c16 * 16);
+    *gmem(reinterpret_cast<u32x4*>(out + int64_t(r) * ld + c16 * 16)) = *reinterpret_cast<const u32x4*>(smem + r * EP + c16 * 16);
   }
 }
 

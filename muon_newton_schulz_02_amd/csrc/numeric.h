@@ -7,6 +7,15 @@
 
 namespace muon {
 
+// Global-memory view of a pointer: accesses through it compile to global_*
+// instructions, counted by vmcnt only.  Through a generic pointer they become
+// flat instructions, which also count in lgkmcnt, so that every wait for LDS
+// results would wait for the global traffic in flight as well.
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gmem(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
   return __uint_as_float((h & 0xFFFFu) << 16);
 }
