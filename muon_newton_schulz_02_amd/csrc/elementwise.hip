@@ -26,6 +26,9 @@
 
 namespace muon {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 namespace {
 
 __device__ inline int find_matrix(const int32_t* __restrict__ off, int count, int tile) {
@@ -45,15 +48,15 @@ __device__ inline float load_elem(const void* p, int64_t idx, int bf16) {
 // Store four consecutive values of the Newton-Schulz working format.
 __device__ inline void store4_ws(void* base, int64_t plane, int prec, int64_t idx, const float v[4]) {
   if (prec == PREC_F32) {
-    *gmem(reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx)) = make_float4(v[0], v[1], v[2], v[3]);
+    *gmem(reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + idx)) = f32x4{v[0], v[1], v[2], v[3]};
   } else {
     uint16_t* p = reinterpret_cast<uint16_t*>(base);
     const uint32_t h01 = float2_to_bf16x2_bits(v[0], v[1]), h23 = float2_to_bf16x2_bits(v[2], v[3]);
-    *gmem(reinterpret_cast<uint2*>(p + idx)) = make_uint2(h01, h23);
+    *gmem(reinterpret_cast<u32x2*>(p + idx)) = u32x2{h01, h23};
     if (prec == PREC_BF16X3) {
       const uint32_t l01 = float2_to_bf16x2_bits(v[0] - bf16_bits_to_float(h01), v[1] - bf16_bits_to_float(h01 >> 16));
       const uint32_t l23 = float2_to_bf16x2_bits(v[2] - bf16_bits_to_float(h23), v[3] - bf16_bits_to_float(h23 >> 16));
-      *gmem(reinterpret_cast<uint2*>(p + plane + idx)) = make_uint2(l01, l23);
+      *gmem(reinterpret_cast<u32x2*>(p + plane + idx)) = u32x2{l01, l23};
     }
   }
 }
@@ -111,14 +114,14 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
       const int64_t gi = int64_t(row) * md.ld_grad + col;
       if (full) {
         if (md.grad_bf16) {
-          uint2 raw = *gmem(reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(md.grad) + gi));
-          g[0] = bf16_bits_to_float(raw.x & 0xFFFFu);
-          g[1] = bf16_bits_to_float(raw.x >> 16);
-          g[2] = bf16_bits_to_float(raw.y & 0xFFFFu);
-          g[3] = bf16_bits_to_float(raw.y >> 16);
+          const u32x2 raw = *gmem(reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(md.grad) + gi));
+          g[0] = bf16_bits_to_float(raw[0] & 0xFFFFu);
+          g[1] = bf16_bits_to_float(raw[0] >> 16);
+          g[2] = bf16_bits_to_float(raw[1] & 0xFFFFu);
+          g[3] = bf16_bits_to_float(raw[1] >> 16);
         } else {
-          float4 raw = *gmem(reinterpret_cast<const float4*>(reinterpret_cast<const float*>(md.grad) + gi));
-          g[0] = raw.x; g[1] = raw.y; g[2] = raw.z; g[3] = raw.w;
+          const f32x4 raw = *gmem(reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(md.grad) + gi));
+          g[0] = raw[0]; g[1] = raw[1]; g[2] = raw[2]; g[3] = raw[3];
         }
       } else {
 #pragma unroll
@@ -128,8 +131,8 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
       if (mode == 0) {
         const int64_t mi64 = int64_t(row) * md.ld_mom + col;
         if (full) {
-          float4 raw = *gmem(reinterpret_cast<const float4*>(md.mom + mi64));
-          m[0] = raw.x; m[1] = raw.y; m[2] = raw.z; m[3] = raw.w;
+          const f32x4 raw = *gmem(reinterpret_cast<const f32x4*>(md.mom + mi64));
+          m[0] = raw[0]; m[1] = raw[1]; m[2] = raw[2]; m[3] = raw[3];
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
           u[e] = nesterov ? (g[e] + bn) : mn[e];
         }
         if (full) {
-          *gmem(reinterpret_cast<float4*>(md.mom + mi64)) = make_float4(mn[0], mn[1], mn[2], mn[3]);
+          *gmem(reinterpret_cast<f32x4*>(md.mom + mi64)) = f32x4{mn[0], mn[1], mn[2], mn[3]};
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
