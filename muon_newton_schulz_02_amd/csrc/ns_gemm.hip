@@ -53,6 +53,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "muon_internal.h"
 #include "numeric.h"
@@ -308,40 +309,33 @@ __device__ __forceinline__ bool stage_is_trans(const OpSrc& s, int kt) {
 }
 
 // Loads number I0 .. I1 - 1 of this thread's loads of one operand of stage kt
-// (numbered q * 4 + e for the transposed layout, q for the direct one).
+// (numbered q * 4 + e for the transposed layout, q for the direct one).  Both
+// layouts take NREG loads per thread; the layout is selected per load (buffer
+// resource, scalar and per-thread offset), not branched on: loads issued in
+// two branches into the same registers make the compiler wait for them at the
+// join.
 template <int ESZ, int BT, int NT, int NPL, int NREG, int I0 = 0, int I1 = 1 << 20>
 __device__ __forceinline__ void load_stage(u32x4 (&r)[NPL][NREG], const OpSrc& s, const OpRsrc& rs, int kt,
                                            int tid) {
   using G = Geo<ESZ, BT, NT>;
-  if (stage_is_trans<ESZ, BT>(s, kt)) {
-    const int sbase = int(int64_t(kt) * (KB / ESZ) * s.ld_b);
+  static_assert(G::PER * 4 == G::CH && G::CH == NREG, "both layouts take NREG loads per thread");
+  const bool tr = stage_is_trans<ESZ, BT>(s, kt);
+  const __amdgpu_buffer_rsrc_t rsrc = tr ? rs.trans : rs.direct;
+  const int sbase = tr ? int(int64_t(kt) * (KB / ESZ) * s.ld_b) : kt * KB;
 #pragma unroll
-    for (int q = 0; q < G::PER; ++q) {
-      const int blk = tid + NT * q;
-      if (G::NB % NT != 0 && blk >= G::NB) break;
-      const int rb = blk % G::RB, kg = blk / G::RB;   // row block, group of 4 k-values
+  for (int i = 0; i < NREG; ++i) {
+    if (i < I0 || i >= I1) continue;
+    // transposed: 16 bytes of memory row kg * 4 + e (k-value) at row block rb
+    const int blk = tid + NT * (i >> 2), e = i & 3;
+    const int rb = blk % G::RB, kg = blk / G::RB;
+    const int off_t = int((kg * 4 + e) * s.ld_b + rb * 16);
+    // direct: chunk c of the stage, 8 chunks of 16 bytes per row
+    const int c = tid + NT * i;
+    const int off_d = int((c >> 3) * s.ld_b + (c & 7) * 16);
+    const int off = tr ? off_t : off_d;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (q * 4 + e < I0 || q * 4 + e >= I1) continue;
-        const int off = int((kg * 4 + e) * s.ld_b + rb * 16);
-#pragma unroll
-        for (int pl = 0; pl < NPL; ++pl)
-          r[pl][q * 4 + e] = __builtin_bit_cast(
-              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.trans, off, sbase + pl * int(s.plane_b), 0));
-      }
-    }
-  } else {
-    const int sbase = kt * KB;
-#pragma unroll
-    for (int q = 0; q < G::CH; ++q) {
-      if (q < I0 || q >= I1) continue;
-      const int c = tid + NT * q;
-      const int off = int((c >> 3) * s.ld_b + (c & 7) * 16);
-#pragma unroll
-      for (int pl = 0; pl < NPL; ++pl)
-        r[pl][q] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.direct, off, sbase + pl * int(s.plane_b), 0));
-    }
+    for (int pl = 0; pl < NPL; ++pl)
+      r[pl][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, sbase + pl * int(s.plane_b), 0));
   }
 }
 
@@ -426,11 +420,44 @@ __device__ __forceinline__ void store_tile_bf16(const f32x16 (&acc)[FQ][FP], flo
 
 // ------------------------------------------------------------------ tile
 
+// The two operand sources of tile (ti, tj) of one phase; returns K.
+template <int PREC, int PHASE>
+__device__ __forceinline__ int tile_ops(const MatDev& md, int ti, int tj, const PhaseArgs& pa, OpSrc& sp, OpSrc& sq) {
+  constexpr int ESZ = Fmt<PREC>::esz;
+  constexpr int BT = Cfg<PREC>::BT;
+  if constexpr (PHASE == PH_GRAM) {
+    const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
+    const int64_t ld = int64_t(md.ldx) * ESZ;
+    sp = {x + int64_t(ti) * BT * ld, nullptr, ld, md.plane_X * ESZ, -1, 0};
+    sq = {x + int64_t(tj) * BT * ld, nullptr, ld, md.plane_X * ESZ, -1, 0};
+    return md.Np;
+  } else if constexpr (PHASE == PH_POLY) {
+    const char* a = reinterpret_cast<const char*>(md.A);
+    const int64_t ld = int64_t(md.lda) * ESZ;
+    sp = {a + int64_t(ti) * BT * ld, a + int64_t(ti) * BT * ESZ, ld, md.plane_A * ESZ, ti, 0};
+    sq = {a + int64_t(tj) * BT * ld, a + int64_t(tj) * BT * ESZ, ld, md.plane_A * ESZ, tj, 0};
+    return md.Mp;
+  } else {
+    const char* b = reinterpret_cast<const char*>(md.B);
+    const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
+    const int64_t lda = int64_t(md.lda) * ESZ, ldx = int64_t(md.ldx) * ESZ;
+    sp = {b + int64_t(ti) * BT * lda, b + int64_t(ti) * BT * ESZ, lda, md.plane_A * ESZ, ti, 0};
+    sq = {nullptr, x + int64_t(tj) * BT * ESZ, ldx, md.plane_X * ESZ, -1, 1};
+    return md.Mp;
+  }
+}
+
 // VAR: GRAM 1 = c != 0 (store A), 0 = c == 0 (store B = b A);
 //      COMB 1 = last step (write-back), 0 = store the next iterate.
-template <int PREC, int PHASE, int VAR>
+//
+// rp / rq hold this thread's part of the tile's stage 0 on entry (loaded
+// while the previous tile finished); during the last stage they receive the
+// next tile's stage 0 (when has_next), whose operand sources are np / nq.
+template <int PREC, int PHASE, int VAR, int NREG>
 __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __restrict__ scal, int mat,
-                                             int ti, int tj, const PhaseArgs& pa, char* smem) {
+                                             int ti, int tj, const PhaseArgs& pa, char* smem,
+                                             u32x4 (&rp)[Fmt<PREC>::npl][NREG], u32x4 (&rq)[Fmt<PREC>::npl][NREG],
+                                             bool has_next, const OpSrc& np, const OpSrc& nq) {
   constexpr int ESZ = Fmt<PREC>::esz;
   constexpr int NPL = Fmt<PREC>::npl;
   constexpr int BT = Cfg<PREC>::BT, NT = Cfg<PREC>::NT, WQN = Cfg<PREC>::WQ;
@@ -448,36 +475,17 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
   const int wq = w % WQN, wp = w / WQN;    // wave position: Q side (columns), P side (rows)
 
   OpSrc sp, sq;
-  int K;
-  if constexpr (PHASE == PH_GRAM) {
-    const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
-    const int64_t ld = int64_t(md.ldx) * ESZ;
-    sp = {x + int64_t(ti) * BT * ld, nullptr, ld, md.plane_X * ESZ, -1, 0};
-    sq = {x + int64_t(tj) * BT * ld, nullptr, ld, md.plane_X * ESZ, -1, 0};
-    K = md.Np;
-  } else if constexpr (PHASE == PH_POLY) {
-    const char* a = reinterpret_cast<const char*>(md.A);
-    const int64_t ld = int64_t(md.lda) * ESZ;
-    sp = {a + int64_t(ti) * BT * ld, a + int64_t(ti) * BT * ESZ, ld, md.plane_A * ESZ, ti, 0};
-    sq = {a + int64_t(tj) * BT * ld, a + int64_t(tj) * BT * ESZ, ld, md.plane_A * ESZ, tj, 0};
-    K = md.Mp;
-  } else {
-    const char* b = reinterpret_cast<const char*>(md.B);
-    const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
-    const int64_t lda = int64_t(md.lda) * ESZ, ldx = int64_t(md.ldx) * ESZ;
-    sp = {b + int64_t(ti) * BT * lda, b + int64_t(ti) * BT * ESZ, lda, md.plane_A * ESZ, ti, 0};
-    sq = {nullptr, x + int64_t(tj) * BT * ESZ, ldx, md.plane_X * ESZ, -1, 1};
-    K = md.Mp;
-  }
+  const int K = tile_ops<PREC, PHASE>(md, ti, tj, pa, sp, sq);
   const int nk = K / KE;
   const OpRsrc rsp = op_rsrc(sp), rsq = op_rsrc(sq);
+  const OpRsrc rnp = op_rsrc(np), rnq = op_rsrc(nq);
 
   // additive term alpha * D on the tile's own rows (POLY: (b/c) A, COMB: a X)
   constexpr bool ADD = PHASE != PH_GRAM;
   const float alpha = PHASE == PH_POLY ? pa.b / pa.c : pa.a;
   const int prow0 = ti * BT + wp * WTP;    // first P-side (output) row of this wave
 
-  u32x4 rp[NPL][G::NREG], rq[NPL][G::NREG];
+  static_assert(NREG == G::NREG, "staging registers");
   f32x16 acc[FQ][FP];                       // [fj][fi]
 #pragma clang loop unroll(full)
   for (int j = 0; j < FQ; ++j)
@@ -486,34 +494,42 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
 #pragma clang loop unroll(full)
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
 
-  load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, sp, rsp, 0, tid);
-  load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, sq, rsq, 0, tid);
   store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rp, sp, 0, smem, tid);
   store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rq, sq, 0, smem + NPL * OPB, tid);
   lds_barrier();
 
   const int hsel = lane >> 5;
-#pragma unroll 1
-  for (int kt = 0; kt < nk; ++kt) {
+  // The loads of stage kt + 1 go out in two halves, P's before k-slab 0 and
+  // Q's before k-slab 1 (bf16: four slabs), not in one burst: a burst of 64
+  // loads per workgroup stalls every wave at issue, while loads issued in the
+  // last slabs leave too little time before the stage's LDS stores.
+  constexpr bool SPREAD = PREC == PREC_BF16 && KE / KS == 4 && G::NREG == 4;
+  // One stage of the k-loop.  MORE: stage kt + 1 follows and is loaded; else
+  // (the last stage) the loads fetch the next tile's stage 0, if any, which
+  // then lands while this tile's epilogue runs.
+  auto stage = [&](const int kt, auto more_c) {
+    constexpr bool MORE = decltype(more_c)::value;
     const int s = kt & 1;
-    // The loads of stage kt + 1 go out in two halves, P's before k-slab 0 and
-    // Q's before k-slab 1 (bf16: four slabs), not in one burst: a burst of 64
-    // loads per workgroup stalls every wave at issue, while loads issued in
-    // the last slabs leave too little time before the stage's LDS stores.
-    constexpr bool SPREAD = PREC == PREC_BF16 && KE / KS == 4 && G::NREG == 4;
-    if (!SPREAD && kt + 1 < nk) {
-      load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, sp, rsp, kt + 1, tid);
-      load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, sq, rsq, kt + 1, tid);
+    const bool ld = MORE || has_next;
+    const int kl = MORE ? kt + 1 : 0;
+    const OpSrc& lp_ = MORE ? sp : np;
+    const OpSrc& lq_ = MORE ? sq : nq;
+    const OpRsrc& rlp = MORE ? rsp : rnp;
+    const OpRsrc& rlq = MORE ? rsq : rnq;
+    if (!SPREAD && ld) {
+      load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, lp_, rlp, kl, tid);
+      load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, lq_, rlq, kl, tid);
     }
     const char* lP = smem + s * STAGE;
     const char* lQ = lP + NPL * OPB;
 #pragma clang loop unroll(full)
     for (int ks = 0; ks < KE / KS; ++ks) {
       if constexpr (SPREAD) {
-        if (kt + 1 < nk) {
-          if (ks == 0) load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, sp, rsp, kt + 1, tid);
-          if (ks == 1) load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, sq, rsq, kt + 1, tid);
-        }
+        // the scheduling barriers keep the loads here: left free, the
+        // scheduler sinks them to the LDS stores at the end of the stage
+        if (ks == 0 && ld) load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, lp_, rlp, kl, tid);
+        if (ks == 1 && ld) load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, lq_, rlq, kl, tid);
+        if (ks < 2) __builtin_amdgcn_sched_barrier(0);
       }
       const int ch = 2 * ks + hsel;           // this lane's 16-byte chunk of the slab
       u32x4 qf[FQ][NPL], pf[FP][NPL];
@@ -555,12 +571,15 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
         }
       }
     }
-    if (kt + 1 < nk) {
+    if constexpr (MORE) {
       store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rp, sp, kt + 1, smem + (s ^ 1) * STAGE, tid);
       store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rq, sq, kt + 1, smem + (s ^ 1) * STAGE + NPL * OPB, tid);
     }
     lds_barrier();
-  }
+  };
+#pragma unroll 1
+  for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, std::true_type{});
+  stage(nk - 1, std::false_type{});
 
   // ---------------------------------------------------------------- epilogue
   // acc[fj][fi][4g + e] is output row ti*BT + wp*WTP + 32 fi + (lane & 31),
@@ -680,12 +699,29 @@ __global__ __launch_bounds__(Cfg<PREC>::NT) void ns_gemm_kernel(const MatDev* __
   const int xcd = blockIdx.x % NUM_XCD;
   const int stride = gridDim.x / NUM_XCD;
   const int2* list = tiles + int64_t(xcd) * pa.per_xcd;
+  using G = Geo<Fmt<PREC>::esz, Cfg<PREC>::BT, Cfg<PREC>::NT>;
+  u32x4 rp[NPL][G::NREG], rq[NPL][G::NREG];  // the next stage 0, carried across tiles
+  int slot = blockIdx.x / NUM_XCD;
+  // lists are padded at their end only
+  int2 te = slot < pa.per_xcd ? list[slot] : int2{-1, 0};
+  if (te.x >= 0) {
+    OpSrc sp, sq;
+    tile_ops<PREC, PHASE>(mats[te.x], te.y >> 16, te.y & 0xFFFF, pa, sp, sq);
+    const OpRsrc rsp = op_rsrc(sp), rsq = op_rsrc(sq);
+    load_stage<Fmt<PREC>::esz, Cfg<PREC>::BT, Cfg<PREC>::NT, NPL, G::NREG>(rp, sp, rsp, 0, threadIdx.x);
+    load_stage<Fmt<PREC>::esz, Cfg<PREC>::BT, Cfg<PREC>::NT, NPL, G::NREG>(rq, sq, rsq, 0, threadIdx.x);
+  }
 #pragma unroll 1
-  for (int slot = blockIdx.x / NUM_XCD; slot < pa.per_xcd; slot += stride) {
-    const int2 te = list[slot];
-    if (te.x < 0) break;  // lists are padded at their end only
-    ns_tile_body<PREC, PHASE, VAR>(mats[te.x], scal, te.x, te.y >> 16, te.y & 0xFFFF, pa, smem);
+  while (te.x >= 0) {
+    const int nslot = slot + stride;
+    const int2 tn = nslot < pa.per_xcd ? list[nslot] : int2{-1, 0};
+    OpSrc np = {}, nq = {};
+    if (tn.x >= 0) tile_ops<PREC, PHASE>(mats[tn.x], tn.y >> 16, tn.y & 0xFFFF, pa, np, nq);
+    ns_tile_body<PREC, PHASE, VAR, G::NREG>(mats[te.x], scal, te.x, te.y >> 16, te.y & 0xFFFF, pa, smem, rp, rq,
+                                            tn.x >= 0, np, nq);
     lds_barrier();
+    slot = nslot;
+    te = tn;
   }
 }
 
