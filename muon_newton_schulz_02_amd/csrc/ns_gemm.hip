@@ -88,11 +88,19 @@ template <> struct Fmt<PREC_F32> { static constexpr int esz = 4, npl = 1; };
 // accumulator registers), so one wave's barrier or LDS wait overlaps the
 // other's matrix-core work.  The formats whose operands take twice the bytes
 // use 128 x 128 over four waves.
+// The bf16 tiles run the software-pipelined k-loop with their own LDS layout
+// (and transposed-operand block order); the other formats stage one k-step at
+// a time in the swizzled layout.
+constexpr bool pipelined(int prec) { return prec == PREC_BF16; }
+
 template <int PREC> struct Cfg;
 template <> struct Cfg<PREC_BF16> { static constexpr int BT = 256, WP = 2, WQ = 4, NT = 512; };
 template <> struct Cfg<PREC_BF16X3> { static constexpr int BT = 128, WP = 2, WQ = 2, NT = 256; };
 template <> struct Cfg<PREC_F32> { static constexpr int BT = 128, WP = 2, WQ = 2, NT = 256; };
 
+// LDS operand layout of the split-bf16 and binary32 tiles: row r at r * PITCH,
+// 16-byte chunk ch at 16 (ch ^ ((r >> 4) & 7)).  (The bf16 tiles use their
+// own, unswizzled layout.)
 __device__ __forceinline__ int lds_off(int r, int ch) { return r * PITCH + ((ch ^ ((r >> 4) & 7)) << 4); }
 
 // Workgroup barrier for LDS reuse only: this wave's LDS accesses complete,
@@ -314,28 +322,29 @@ __device__ __forceinline__ bool stage_is_trans(const OpSrc& s, int kt) {
 // resource, scalar and per-thread offset), not branched on: loads issued in
 // two branches into the same registers make the compiler wait for them at the
 // join.
-template <int ESZ, int BT, int NT, int NPL, int NREG, int I0 = 0, int I1 = 1 << 20>
+template <int ESZ, int BT, int NT, int NPL, int NREG, bool KG_FAST = false, int I0 = 0, int I1 = 1 << 20>
 __device__ __forceinline__ void load_stage(u32x4 (&r)[NPL][NREG], const OpSrc& s, const OpRsrc& rs, int kt,
                                            int tid) {
   using G = Geo<ESZ, BT, NT>;
-  static_assert(G::PER * 4 == G::CH && G::CH == NREG, "both layouts take NREG loads per thread");
+  static_assert(G::PER == 1 && G::CH == 4 && NREG == 4 && G::NB == NT, "one block or four chunks per thread");
   const bool tr = stage_is_trans<ESZ, BT>(s, kt);
   const __amdgpu_buffer_rsrc_t rsrc = tr ? rs.trans : rs.direct;
-  const int sbase = tr ? int(int64_t(kt) * (KB / ESZ) * s.ld_b) : kt * KB;
+  const int ld = int(s.ld_b);
+  // transposed: block (row block rb, k-group kg), loads e = 0..3 are memory
+  // rows 4 kg + e, 16 bytes at row block rb (consecutive threads take
+  // consecutive k-groups if KG_FAST, else consecutive row blocks); direct:
+  // chunk tid + NT i is row tid / 8 + (NT / 8) i, 16-byte chunk tid % 8
+  const int rb = KG_FAST ? tid / G::KG : tid % G::RB, kg = KG_FAST ? tid % G::KG : tid / G::RB;
+  const int off = tr ? (kg * 4) * ld + rb * 16 : (tid >> 3) * ld + (tid & 7) * 16;
+  const int step = tr ? ld : (NT / 8) * ld;
+  const int sbase = tr ? kt * (KB / ESZ) * ld : kt * KB;
 #pragma unroll
   for (int i = 0; i < NREG; ++i) {
     if (i < I0 || i >= I1) continue;
-    // transposed: 16 bytes of memory row kg * 4 + e (k-value) at row block rb
-    const int blk = tid + NT * (i >> 2), e = i & 3;
-    const int rb = blk % G::RB, kg = blk / G::RB;
-    const int off_t = int((kg * 4 + e) * s.ld_b + rb * 16);
-    // direct: chunk c of the stage, 8 chunks of 16 bytes per row
-    const int c = tid + NT * i;
-    const int off_d = int((c >> 3) * s.ld_b + (c & 7) * 16);
-    const int off = tr ? off_t : off_d;
 #pragma unroll
     for (int pl = 0; pl < NPL; ++pl)
-      r[pl][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, sbase + pl * int(s.plane_b), 0));
+      r[pl][i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, sbase + i * step + pl * int(s.plane_b), 0));
   }
 }
 
@@ -494,71 +503,68 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
 #pragma clang loop unroll(full)
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
 
-  store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rp, sp, 0, smem, tid);
-  store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rq, sq, 0, smem + NPL * OPB, tid);
-  lds_barrier();
-
   const int hsel = lane >> 5;
-  // The loads of stage kt + 1 go out in two halves, P's before k-slab 0 and
-  // Q's before k-slab 1 (bf16: four slabs), not in one burst: a burst of 64
-  // loads per workgroup stalls every wave at issue, while loads issued in the
-  // last slabs leave too little time before the stage's LDS stores.
-  constexpr bool SPREAD = PREC == PREC_BF16 && KE / KS == 4 && G::NREG == 4;
-  // One stage of the k-loop.  MORE: stage kt + 1 follows and is loaded; else
-  // (the last stage) the loads fetch the next tile's stage 0, if any, which
-  // then lands while this tile's epilogue runs.
-  auto stage = [&](const int kt, auto more_c) {
-    constexpr bool MORE = decltype(more_c)::value;
-    const int s = kt & 1;
-    const bool ld = MORE || has_next;
-    const int kl = MORE ? kt + 1 : 0;
-    const OpSrc& lp_ = MORE ? sp : np;
-    const OpSrc& lq_ = MORE ? sq : nq;
-    const OpRsrc& rlp = MORE ? rsp : rnp;
-    const OpRsrc& rlq = MORE ? rsq : rnq;
-    if (!SPREAD && ld) {
-      load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, lp_, rlp, kl, tid);
-      load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, lq_, rlq, kl, tid);
-    }
-    const char* lP = smem + s * STAGE;
-    const char* lQ = lP + NPL * OPB;
+  // bf16: software-pipelined k-loop (below); the other formats: one stage at a time.
+  constexpr bool PIPE = pipelined(PREC);
+  static_assert(!PIPE || (KE / KS == 4 && G::NREG == 4 && G::PER == 1 && G::CH == 4 && NPL == 1), "pipelined geometry");
+  if constexpr (PIPE) {
+    // Per stage kt (LDS buffer kt & 1), four k-slabs; slab s runs its MFMAs on
+    // fragment set F[s & 1] while the LDS reads of slab s + 1 fill the other
+    // set, so matrix-core and LDS work overlap inside each wave.  Stage kt + 1
+    // goes into the other buffer from registers during slabs 0-2 (P: halves in
+    // slabs 0 and 1, Q: slabs 1 and 2), the registers then take stage kt + 2
+    // from memory (P after slab 1, Q after slab 2), and one barrier after slab
+    // 2 publishes stage kt + 1, whose first slab is read during slab 3.  The
+    // barrier also ends every read of this stage's buffer before the next
+    // stage starts overwriting it.  The last two stages load the next tile's
+    // stage 0 instead (or, without a next tile, this tile's again, unused).
+    //
+    // LDS: P buffer b at b OPB, Q buffer b at (2 + b) OPB, so that with the
+    // buffer fixed at compile time (stages unrolled by two; nk is a multiple
+    // of 4) every fragment address is one per-lane register plus an
+    // immediate.  Operand row r sits at r * PITCH, its 16-byte k-chunk ch at
+    // 16 ch, unswizzled: the LDS serves a ds_read_b128 in four groups of 16
+    // lanes (lanes 0-31 and 32-63 apart; within each half, the lanes whose
+    // index bits 2-4 have even parity, then odd), and a fragment read (32
+    // consecutive rows, one chunk per half-wave) at this 144-byte pitch puts
+    // every group on 16 distinct bank quads: 4.5 clk per instruction, against
+    // 8 when rows 16-31 take other chunks than rows 0-15 (measured).
+    constexpr int NF = FQ + FP;
+    constexpr int QOFF = 2 * OPB;
+    static_assert(2 * QOFF <= 2 * STAGE, "LDS layout");
+    u32x4 F[2][NF];
+    char* const lds = smem;
+    const int fragP = (wp * WTP + (lane & 31)) * PITCH + hsel * 16;
+    const int fragQ = QOFF + (wq * WTQ + (lane & 31)) * PITCH + hsel * 16;
+    const int stD = (tid >> 3) * PITCH + (tid & 7) * 16;               // direct chunk tid, + q (NT / 8) rows
+    // transposed block: k-group kg = tid % 16, row block rb = tid / 16, so
+    // that the 16 lanes of a ds_write_b64 group (16 k-groups of one row)
+    // hit 16 distinct bank pairs; the loads then fetch 64 contiguous bytes
+    // per memory row and instruction
+    const int stT = (tid / G::KG) * 8 * PITCH + (tid % G::KG) * 8;
+    auto read_frags = [&](u32x4 (&f)[NF], auto buf_c, int ks) {
+      constexpr int BUF = decltype(buf_c)::value;
 #pragma clang loop unroll(full)
-    for (int ks = 0; ks < KE / KS; ++ks) {
-      if constexpr (SPREAD) {
-        // the scheduling barriers keep the loads here: left free, the
-        // scheduler sinks them to the LDS stores at the end of the stage
-        if (ks == 0 && ld) load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, lp_, rlp, kl, tid);
-        if (ks == 1 && ld) load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, lq_, rlq, kl, tid);
-        if (ks < 2) __builtin_amdgcn_sched_barrier(0);
-      }
-      const int ch = 2 * ks + hsel;           // this lane's 16-byte chunk of the slab
-      u32x4 qf[FQ][NPL], pf[FP][NPL];
+      for (int x = 0; x < FQ; ++x)
+        f[x] = *reinterpret_cast<const u32x4*>(lds + fragQ + BUF * OPB + x * 32 * PITCH + ks * 32);
 #pragma clang loop unroll(full)
-      for (int f = 0; f < FQ; ++f) {
-        const int rq_ = wq * WTQ + f * 32 + (lane & 31);
-#pragma clang loop unroll(full)
-        for (int pl = 0; pl < NPL; ++pl)
-          qf[f][pl] = *reinterpret_cast<const u32x4*>(lQ + pl * OPB + lds_off(rq_, ch));
-      }
-#pragma clang loop unroll(full)
-      for (int f = 0; f < FP; ++f) {
-        const int rp_ = wp * WTP + f * 32 + (lane & 31);
-#pragma clang loop unroll(full)
-        for (int pl = 0; pl < NPL; ++pl)
-          pf[f][pl] = *reinterpret_cast<const u32x4*>(lP + pl * OPB + lds_off(rp_, ch));
-      }
+      for (int x = 0; x < FP; ++x)
+        f[FQ + x] = *reinterpret_cast<const u32x4*>(lds + fragP + BUF * OPB + x * 32 * PITCH + ks * 32);
+    };
+    auto mfma_half = [&](const u32x4 (&f)[NF], int h) {
 #pragma clang loop unroll(full)
       for (int j = 0; j < FQ; ++j)
 #pragma clang loop unroll(full)
-        for (int i = 0; i < FP; ++i) mfma_step<PREC>(acc[j][i], qf[j], pf[i]);
+        for (int i = 2 * h; i < 2 * h + 2; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[j]),
+                                                              __builtin_bit_cast(bf16x8, f[FQ + i]), acc[j][i], 0, 0, 0);
+    };
+    auto identity_add = [&](const u32x4 (&f)[NF], int kt, int ks) {
       if constexpr (ADD) {
-        // the k-slab [kk, kk + KS) meets the output rows of this wave's block fi
         const int kk = kt * KE + ks * KS;
         const int d = kk - prow0;
         if (d >= 0 && d < WTP) {
           const int fi = d >> 5;
-          // this lane's row within the block is lane & 31; its k-values are
-          // kk + (KS / 2) h + e
           const int pos = (lane & 31) - (d & 31) - (KS / 2) * hsel;
           u32x4 id[2];
           identity_frag<PREC>(id, pos, alpha);
@@ -566,20 +572,195 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
           for (int i = 0; i < FP; ++i)
             if (i == fi) {
 #pragma clang loop unroll(full)
-              for (int j = 0; j < FQ; ++j) mfma_identity<PREC>(acc[j][i], qf[j], id);
+              for (int j = 0; j < FQ; ++j) mfma_identity<PREC>(acc[j][i], &f[j], id);
             }
         }
       }
-    }
-    if constexpr (MORE) {
-      store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rp, sp, kt + 1, smem + (s ^ 1) * STAGE, tid);
-      store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rq, sq, kt + 1, smem + (s ^ 1) * STAGE + NPL * OPB, tid);
-    }
+    };
+    // half H of one operand's part of stage kt, from registers to LDS at byte
+    // offset BASE (the operand's buffer)
+    auto store_half = [&](const u32x4 (&r)[NPL][G::NREG], const OpSrc& src, int kt, auto base_c, auto h_c) {
+      constexpr int BASE = decltype(base_c)::value;
+      constexpr int H = decltype(h_c)::value;
+      if (stage_is_trans<ESZ, BT>(src, kt)) {
+        u32x2 t[8];
+        transpose4x8_b16(&r[0][0], t);
+#pragma unroll
+        for (int c = 4 * H; c < 4 * H + 4; ++c) *reinterpret_cast<u32x2*>(lds + stT + BASE + c * PITCH) = t[c];
+      } else {
+#pragma unroll
+        for (int q = 2 * H; q < 2 * H + 2; ++q)
+          *reinterpret_cast<u32x4*>(lds + stD + BASE + q * (NT / 8) * PITCH) = r[0][q];
+      }
+    };
+    const OpSrc& xp = has_next ? np : sp;   // the next tile's sources (or this tile's)
+    const OpSrc& xq = has_next ? nq : sq;
+    const OpRsrc rxp = op_rsrc(xp), rxq = op_rsrc(xq);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    store_half(rp, sp, 0, I0{}, I0{});
+    store_half(rp, sp, 0, I0{}, I1{});
+    store_half(rq, sq, 0, std::integral_constant<int, QOFF>{}, I0{});
+    store_half(rq, sq, 0, std::integral_constant<int, QOFF>{}, I1{});
     lds_barrier();
-  };
+    load_stage<ESZ, BT, NT, NPL, G::NREG, true>(rp, sp, rsp, 1, tid);
+    load_stage<ESZ, BT, NT, NPL, G::NREG, true>(rq, sq, rsq, 1, tid);
+    read_frags(F[0], I0{}, 0);
+
+    // MODE 0: store stage kt + 1, load stage kt + 2 of this tile; 1: store
+    // stage kt + 1, load the next tile's stage 0; 2: the last stage.
+    auto stage = [&](const int kt, auto buf_c, auto mode_c) {
+      constexpr int BUF = decltype(buf_c)::value;
+      constexpr int MODE = decltype(mode_c)::value;
+      using CUR = std::integral_constant<int, BUF>;
+      using NXT = std::integral_constant<int, BUF ^ 1>;
+      using NP = std::integral_constant<int, (BUF ^ 1) * OPB>;
+      using NQ = std::integral_constant<int, QOFF + (BUF ^ 1) * OPB>;
+      // slab 0
+      read_frags(F[1], CUR{}, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(F[0], 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MODE != 2) store_half(rp, sp, kt + 1, NP{}, I0{});
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(F[0], 1);
+      identity_add(F[0], kt, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // slab 1
+      read_frags(F[0], CUR{}, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(F[1], 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MODE != 2) {
+        store_half(rp, sp, kt + 1, NP{}, I1{});
+        store_half(rq, sq, kt + 1, NQ{}, I0{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(F[1], 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MODE == 0) load_stage<ESZ, BT, NT, NPL, G::NREG, true>(rp, sp, rsp, kt + 2, tid);
+      if constexpr (MODE == 1) load_stage<ESZ, BT, NT, NPL, G::NREG, true>(rp, xp, rxp, 0, tid);
+      __builtin_amdgcn_sched_barrier(0);
+      identity_add(F[1], kt, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // slab 2
+      read_frags(F[1], CUR{}, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(F[0], 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MODE != 2) store_half(rq, sq, kt + 1, NQ{}, I1{});
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(F[0], 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MODE == 0) load_stage<ESZ, BT, NT, NPL, G::NREG, true>(rq, sq, rsq, kt + 2, tid);
+      if constexpr (MODE == 1) load_stage<ESZ, BT, NT, NPL, G::NREG, true>(rq, xq, rxq, 0, tid);
+      __builtin_amdgcn_sched_barrier(0);
+      identity_add(F[0], kt, 2);
+      lds_barrier();
+      // slab 3
+      if constexpr (MODE != 2) read_frags(F[0], NXT{}, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(F[1], 0);
+      mfma_half(F[1], 1);
+      identity_add(F[1], kt, 3);
+      __builtin_amdgcn_sched_barrier(0);
+    };
 #pragma unroll 1
-  for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, std::true_type{});
-  stage(nk - 1, std::false_type{});
+    for (int kt = 0; kt + 2 < nk; kt += 2) {
+      stage(kt, I0{}, I0{});
+      stage(kt + 1, I1{}, I0{});
+    }
+    stage(nk - 2, I0{}, I1{});
+    stage(nk - 1, I1{}, std::integral_constant<int, 2>{});
+    lds_barrier();
+  } else {
+    store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rp, sp, 0, smem, tid);
+    store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rq, sq, 0, smem + NPL * OPB, tid);
+    lds_barrier();
+
+    // The loads of stage kt + 1 go out in two halves, P's before k-slab 0 and
+    // Q's before k-slab 1 (bf16: four slabs), not in one burst: a burst of 64
+    // loads per workgroup stalls every wave at issue, while loads issued in the
+    // last slabs leave too little time before the stage's LDS stores.
+    constexpr bool SPREAD = PREC == PREC_BF16 && KE / KS == 4 && G::NREG == 4;
+    // One stage of the k-loop.  MORE: stage kt + 1 follows and is loaded; else
+    // (the last stage) the loads fetch the next tile's stage 0, if any, which
+    // then lands while this tile's epilogue runs.
+    auto stage = [&](const int kt, auto more_c) {
+      constexpr bool MORE = decltype(more_c)::value;
+      const int s = kt & 1;
+      const bool ld = MORE || has_next;
+      const int kl = MORE ? kt + 1 : 0;
+      const OpSrc& lp_ = MORE ? sp : np;
+      const OpSrc& lq_ = MORE ? sq : nq;
+      const OpRsrc& rlp = MORE ? rsp : rnp;
+      const OpRsrc& rlq = MORE ? rsq : rnq;
+      if (!SPREAD && ld) {
+        load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, lp_, rlp, kl, tid);
+        load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, lq_, rlq, kl, tid);
+      }
+      const char* lP = smem + s * STAGE;
+      const char* lQ = lP + NPL * OPB;
+  #pragma clang loop unroll(full)
+      for (int ks = 0; ks < KE / KS; ++ks) {
+        if constexpr (SPREAD) {
+          // the scheduling barriers keep the loads here: left free, the
+          // scheduler sinks them to the LDS stores at the end of the stage
+          if (ks == 0 && ld) load_stage<ESZ, BT, NT, NPL, G::NREG>(rp, lp_, rlp, kl, tid);
+          if (ks == 1 && ld) load_stage<ESZ, BT, NT, NPL, G::NREG>(rq, lq_, rlq, kl, tid);
+          if (ks < 2) __builtin_amdgcn_sched_barrier(0);
+        }
+        const int ch = 2 * ks + hsel;           // this lane's 16-byte chunk of the slab
+        u32x4 qf[FQ][NPL], pf[FP][NPL];
+  #pragma clang loop unroll(full)
+        for (int f = 0; f < FQ; ++f) {
+          const int rq_ = wq * WTQ + f * 32 + (lane & 31);
+  #pragma clang loop unroll(full)
+          for (int pl = 0; pl < NPL; ++pl)
+            qf[f][pl] = *reinterpret_cast<const u32x4*>(lQ + pl * OPB + lds_off(rq_, ch));
+        }
+  #pragma clang loop unroll(full)
+        for (int f = 0; f < FP; ++f) {
+          const int rp_ = wp * WTP + f * 32 + (lane & 31);
+  #pragma clang loop unroll(full)
+          for (int pl = 0; pl < NPL; ++pl)
+            pf[f][pl] = *reinterpret_cast<const u32x4*>(lP + pl * OPB + lds_off(rp_, ch));
+        }
+  #pragma clang loop unroll(full)
+        for (int j = 0; j < FQ; ++j)
+  #pragma clang loop unroll(full)
+          for (int i = 0; i < FP; ++i) mfma_step<PREC>(acc[j][i], qf[j], pf[i]);
+        if constexpr (ADD) {
+          // the k-slab [kk, kk + KS) meets the output rows of this wave's block fi
+          const int kk = kt * KE + ks * KS;
+          const int d = kk - prow0;
+          if (d >= 0 && d < WTP) {
+            const int fi = d >> 5;
+            // this lane's row within the block is lane & 31; its k-values are
+            // kk + (KS / 2) h + e
+            const int pos = (lane & 31) - (d & 31) - (KS / 2) * hsel;
+            u32x4 id[2];
+            identity_frag<PREC>(id, pos, alpha);
+  #pragma clang loop unroll(full)
+            for (int i = 0; i < FP; ++i)
+              if (i == fi) {
+  #pragma clang loop unroll(full)
+                for (int j = 0; j < FQ; ++j) mfma_identity<PREC>(acc[j][i], qf[j], id);
+              }
+          }
+        }
+      }
+      if constexpr (MORE) {
+        store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rp, sp, kt + 1, smem + (s ^ 1) * STAGE, tid);
+        store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rq, sq, kt + 1, smem + (s ^ 1) * STAGE + NPL * OPB, tid);
+      }
+      lds_barrier();
+    };
+  #pragma unroll 1
+    for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, std::true_type{});
+    stage(nk - 1, std::false_type{});
+  }
 
   // ---------------------------------------------------------------- epilogue
   // acc[fj][fi][4g + e] is output row ti*BT + wp*WTP + 32 fi + (lane & 31),
@@ -708,8 +889,9 @@ __global__ __launch_bounds__(Cfg<PREC>::NT) void ns_gemm_kernel(const MatDev* __
     OpSrc sp, sq;
     tile_ops<PREC, PHASE>(mats[te.x], te.y >> 16, te.y & 0xFFFF, pa, sp, sq);
     const OpRsrc rsp = op_rsrc(sp), rsq = op_rsrc(sq);
-    load_stage<Fmt<PREC>::esz, Cfg<PREC>::BT, Cfg<PREC>::NT, NPL, G::NREG>(rp, sp, rsp, 0, threadIdx.x);
-    load_stage<Fmt<PREC>::esz, Cfg<PREC>::BT, Cfg<PREC>::NT, NPL, G::NREG>(rq, sq, rsq, 0, threadIdx.x);
+    constexpr bool KGF = pipelined(PREC);
+    load_stage<Fmt<PREC>::esz, Cfg<PREC>::BT, Cfg<PREC>::NT, NPL, G::NREG, KGF>(rp, sp, rsp, 0, threadIdx.x);
+    load_stage<Fmt<PREC>::esz, Cfg<PREC>::BT, Cfg<PREC>::NT, NPL, G::NREG, KGF>(rq, sq, rsq, 0, threadIdx.x);
   }
 #pragma unroll 1
   while (te.x >= 0) {
