@@ -348,6 +348,33 @@ __device__ __forceinline__ void load_stage(u32x4 (&r)[NPL][NREG], const OpSrc& s
   }
 }
 
+// The bf16 iterate as COMBINE's second operand, in k-row form: the stage's
+// KB / 2 memory rows (k-values) of 2 BT bytes each, chunk tid + NT i = k-row
+// tid / 32 + (NT / 32) i, 16-byte piece tid % 32: whole 512-byte rows per
+// 32 lanes.
+template <int BT, int NT>
+__device__ __forceinline__ void load_krow(u32x4 (&r)[1][4], const OpSrc& s, const OpRsrc& rs, int kt, int tid) {
+  static_assert(BT * 2 == 32 * 16, "one k-row is 32 chunks");
+  const int ld = int(s.ld_b);
+  const int off = (tid >> 5) * ld + (tid & 31) * 16;
+  const int sbase = kt * (KB / 2) * ld;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[0][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.trans, off, sbase + i * (NT / 32) * ld, 0));
+}
+
+// Operand OPD (0: P, 1: Q) of stage kt into registers, in the form the
+// tile's k-loop stages it.
+template <int PREC, int PHASE, int OPD>
+__device__ __forceinline__ void load_operand(u32x4 (&r)[Fmt<PREC>::npl][4], const OpSrc& s, const OpRsrc& rs, int kt,
+                                             int tid) {
+  constexpr int ESZ = Fmt<PREC>::esz, BT = Cfg<PREC>::BT, NT = Cfg<PREC>::NT;
+  if constexpr (pipelined(PREC) && PHASE == PH_COMB && OPD == 1)
+    load_krow<BT, NT>(r, s, rs, kt, tid);
+  else
+    load_stage<ESZ, BT, NT, Fmt<PREC>::npl, 4, pipelined(PREC)>(r, s, rs, kt, tid);
+}
+
 // 4 x 8 transpose of 16-bit values: in[e] holds k-value e of 8 consecutive
 // rows (two rows per dword); out[c] holds the 4 k-values of row c.
 __device__ __forceinline__ void transpose4x8_b16(const u32x4* in, u32x2* out) {
@@ -427,6 +454,41 @@ __device__ __forceinline__ void store_tile_bf16(const f32x16 (&acc)[FQ][FP], flo
   }
 }
 
+// The transpose of the same tile (its mirror block, at `out`): the values go
+// to LDS transposed, two bytes at a time (32 lanes hold 32 consecutive rows
+// of one column: 64 contiguous bytes of a transposed row), then whole rows
+// leave as above.  Called after store_tile_bf16, whose staging it reuses.
+template <int FQ, int FP, int WTP, int WTQ, int BT, int NT, int LDSB>
+__device__ __forceinline__ void store_tile_bf16_mirror(const f32x16 (&acc)[FQ][FP], float sc, char* out, int64_t ld,
+                                                       char* smem, int wp, int wq, int lane, int tid) {
+  constexpr int EP = BT * 2 + 16;
+  static_assert(BT * EP <= LDSB, "staging does not fit");
+  const int hsel = lane >> 5;
+  lds_barrier();   // every lane's copy-out of the direct staging is done
+#pragma clang loop unroll(full)
+  for (int j = 0; j < FQ; ++j)
+#pragma clang loop unroll(full)
+    for (int i = 0; i < FP; ++i)
+#pragma clang loop unroll(full)
+      for (int g = 0; g < 4; ++g) {
+        const int r = wp * WTP + 32 * i + (lane & 31), c = wq * WTQ + 32 * j + 8 * g + 4 * hsel;
+        const f32x16& a = acc[j][i];
+        const uint32_t v01 = float2_to_bf16x2_bits(sc * a[4 * g], sc * a[4 * g + 1]);
+        const uint32_t v23 = float2_to_bf16x2_bits(sc * a[4 * g + 2], sc * a[4 * g + 3]);
+        *reinterpret_cast<uint16_t*>(smem + (c + 0) * EP + r * 2) = uint16_t(v01);
+        *reinterpret_cast<uint16_t*>(smem + (c + 1) * EP + r * 2) = uint16_t(v01 >> 16);
+        *reinterpret_cast<uint16_t*>(smem + (c + 2) * EP + r * 2) = uint16_t(v23);
+        *reinterpret_cast<uint16_t*>(smem + (c + 3) * EP + r * 2) = uint16_t(v23 >> 16);
+      }
+  lds_barrier();
+  constexpr int CPR = BT * 2 / 16;
+#pragma unroll 4
+  for (int q = tid; q < BT * CPR; q += NT) {
+    const int r = q / CPR, c16 = q % CPR;
+    *gmem(reinterpret_cast<u32x4*>(out + int64_t(r) * ld + c16 * 16)) = *reinterpret_cast<const u32x4*>(smem + r * EP + c16 * 16);
+  }
+}
+
 // ------------------------------------------------------------------ tile
 
 // The two operand sources of tile (ti, tj) of one phase; returns K.
@@ -443,14 +505,18 @@ __device__ __forceinline__ int tile_ops(const MatDev& md, int ti, int tj, const 
   } else if constexpr (PHASE == PH_POLY) {
     const char* a = reinterpret_cast<const char*>(md.A);
     const int64_t ld = int64_t(md.lda) * ESZ;
-    sp = {a + int64_t(ti) * BT * ld, a + int64_t(ti) * BT * ESZ, ld, md.plane_A * ESZ, ti, 0};
-    sq = {a + int64_t(tj) * BT * ld, a + int64_t(tj) * BT * ESZ, ld, md.plane_A * ESZ, tj, 0};
+    // bf16: GRAM stored A whole (each tile and its mirror), so both operands
+    // are read as rows; the other formats read blocks below the diagonal
+    // through their mirror block
+    const int sym = pipelined(PREC) ? -1 : 0;
+    sp = {a + int64_t(ti) * BT * ld, a + int64_t(ti) * BT * ESZ, ld, md.plane_A * ESZ, sym < 0 ? -1 : ti, 0};
+    sq = {a + int64_t(tj) * BT * ld, a + int64_t(tj) * BT * ESZ, ld, md.plane_A * ESZ, sym < 0 ? -1 : tj, 0};
     return md.Mp;
   } else {
     const char* b = reinterpret_cast<const char*>(md.B);
     const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
     const int64_t lda = int64_t(md.lda) * ESZ, ldx = int64_t(md.ldx) * ESZ;
-    sp = {b + int64_t(ti) * BT * lda, b + int64_t(ti) * BT * ESZ, lda, md.plane_A * ESZ, ti, 0};
+    sp = {b + int64_t(ti) * BT * lda, b + int64_t(ti) * BT * ESZ, lda, md.plane_A * ESZ, pipelined(PREC) ? -1 : ti, 0};
     sq = {nullptr, x + int64_t(tj) * BT * ESZ, ldx, md.plane_X * ESZ, -1, 1};
     return md.Mp;
   }
@@ -529,14 +595,29 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     // consecutive rows, one chunk per half-wave) at this 144-byte pitch puts
     // every group on 16 distinct bank quads: 4.5 clk per instruction, against
     // 8 when rows 16-31 take other chunks than rows 0-15 (measured).
+    //
+    // COMBINE's second operand (the iterate, read along its columns) is
+    // staged in k-row form: LDS row k holds the stage's k-row as in memory
+    // (512 bytes) at a KP = 544-byte pitch, stored with whole-row loads and
+    // ds_write_b128, and its fragments come from ds_read_b64_tr_b16, which
+    // gives lane j of each 16-lane group element j % 4 of the 8 bytes read by
+    // lane 4 e + j / 4 of the group as its value e: with lane 4 e + m pointing
+    // at k-row k0 + e, columns n0 + 4 m .. + 3, lane j receives k-values
+    // k0 .. k0 + 3 of column n0 + j.  The 16 lanes of a read cover 4 rows x 32
+    // bytes, on distinct banks at this pitch.
     constexpr int NF = FQ + FP;
     constexpr int QOFF = 2 * OPB;
-    static_assert(2 * QOFF <= 2 * STAGE, "LDS layout");
+    constexpr bool QK = PHASE == PH_COMB;
+    constexpr int KP = 544;
+    static_assert(2 * QOFF <= 2 * STAGE && KE * KP <= OPB, "LDS layout");
     u32x4 F[2][NF];
     char* const lds = smem;
     const int fragP = (wp * WTP + (lane & 31)) * PITCH + hsel * 16;
-    const int fragQ = QOFF + (wq * WTQ + (lane & 31)) * PITCH + hsel * 16;
+    const int fragQ = QK ? QOFF + (8 * hsel + ((lane & 15) >> 2)) * KP +
+                               2 * (wq * WTQ + 16 * ((lane >> 4) & 1) + 4 * (lane & 3))
+                         : QOFF + (wq * WTQ + (lane & 31)) * PITCH + hsel * 16;
     const int stD = (tid >> 3) * PITCH + (tid & 7) * 16;               // direct chunk tid, + q (NT / 8) rows
+    const int stK = (tid >> 5) * KP + (tid & 31) * 16;                 // k-row piece tid, + i (NT / 32) k-rows
     // transposed block: k-group kg = tid % 16, row block rb = tid / 16, so
     // that the 16 lanes of a ds_write_b64 group (16 k-groups of one row)
     // hit 16 distinct bank pairs; the loads then fetch 64 contiguous bytes
@@ -544,9 +625,22 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     const int stT = (tid / G::KG) * 8 * PITCH + (tid % G::KG) * 8;
     auto read_frags = [&](u32x4 (&f)[NF], auto buf_c, int ks) {
       constexpr int BUF = decltype(buf_c)::value;
+      if constexpr (QK) {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 ls16x4;
+        typedef __attribute__((address_space(3))) char lchar;
 #pragma clang loop unroll(full)
-      for (int x = 0; x < FQ; ++x)
-        f[x] = *reinterpret_cast<const u32x4*>(lds + fragQ + BUF * OPB + x * 32 * PITCH + ks * 32);
+        for (int x = 0; x < FQ; ++x) {
+          lchar* a = (lchar*)(lds + fragQ + BUF * OPB + x * 64 + ks * 16 * KP);
+          const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4*)a));
+          const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4*)(a + 4 * KP)));
+          f[x] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+      } else {
+#pragma clang loop unroll(full)
+        for (int x = 0; x < FQ; ++x)
+          f[x] = *reinterpret_cast<const u32x4*>(lds + fragQ + BUF * OPB + x * 32 * PITCH + ks * 32);
+      }
 #pragma clang loop unroll(full)
       for (int x = 0; x < FP; ++x)
         f[FQ + x] = *reinterpret_cast<const u32x4*>(lds + fragP + BUF * OPB + x * 32 * PITCH + ks * 32);
@@ -582,7 +676,11 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     auto store_half = [&](const u32x4 (&r)[NPL][G::NREG], const OpSrc& src, int kt, auto base_c, auto h_c) {
       constexpr int BASE = decltype(base_c)::value;
       constexpr int H = decltype(h_c)::value;
-      if (stage_is_trans<ESZ, BT>(src, kt)) {
+      if constexpr (QK && BASE >= QOFF) {
+#pragma unroll
+        for (int i = 2 * H; i < 2 * H + 2; ++i)
+          *reinterpret_cast<u32x4*>(lds + stK + BASE + i * (NT / 32) * KP) = r[0][i];
+      } else if (stage_is_trans<ESZ, BT>(src, kt)) {
         u32x2 t[8];
         transpose4x8_b16(&r[0][0], t);
 #pragma unroll
@@ -604,8 +702,8 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     store_half(rq, sq, 0, std::integral_constant<int, QOFF>{}, I0{});
     store_half(rq, sq, 0, std::integral_constant<int, QOFF>{}, I1{});
     lds_barrier();
-    load_stage<ESZ, BT, NT, NPL, G::NREG, true>(rp, sp, rsp, 1, tid);
-    load_stage<ESZ, BT, NT, NPL, G::NREG, true>(rq, sq, rsq, 1, tid);
+    load_operand<PREC, PHASE, 0>(rp, sp, rsp, 1, tid);
+    load_operand<PREC, PHASE, 1>(rq, sq, rsq, 1, tid);
     read_frags(F[0], I0{}, 0);
 
     // MODE 0: store stage kt + 1, load stage kt + 2 of this tile; 1: store
@@ -639,8 +737,8 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(F[1], 1);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (MODE == 0) load_stage<ESZ, BT, NT, NPL, G::NREG, true>(rp, sp, rsp, kt + 2, tid);
-      if constexpr (MODE == 1) load_stage<ESZ, BT, NT, NPL, G::NREG, true>(rp, xp, rxp, 0, tid);
+      if constexpr (MODE == 0) load_operand<PREC, PHASE, 0>(rp, sp, rsp, kt + 2, tid);
+      if constexpr (MODE == 1) load_operand<PREC, PHASE, 0>(rp, xp, rxp, 0, tid);
       __builtin_amdgcn_sched_barrier(0);
       identity_add(F[1], kt, 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -653,8 +751,8 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(F[0], 1);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (MODE == 0) load_stage<ESZ, BT, NT, NPL, G::NREG, true>(rq, sq, rsq, kt + 2, tid);
-      if constexpr (MODE == 1) load_stage<ESZ, BT, NT, NPL, G::NREG, true>(rq, xq, rxq, 0, tid);
+      if constexpr (MODE == 0) load_operand<PREC, PHASE, 1>(rq, sq, rsq, kt + 2, tid);
+      if constexpr (MODE == 1) load_operand<PREC, PHASE, 1>(rq, xq, rxq, 0, tid);
       __builtin_amdgcn_sched_barrier(0);
       identity_add(F[0], kt, 2);
       lds_barrier();
@@ -774,6 +872,10 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     const int64_t ld = int64_t(md.lda) * 2;
     store_tile_bf16<FQ, FP, WTP, WTQ, BT, NT, 2 * STAGE>(acc, sc, out + int64_t(ti) * BT * ld + int64_t(tj) * BT * 2,
                                                        ld, smem, wp, wq, lane, tid);
+    // the symmetric product is stored whole: the mirror block too
+    if (ti != tj)
+      store_tile_bf16_mirror<FQ, FP, WTP, WTQ, BT, NT, 2 * STAGE>(
+          acc, sc, out + int64_t(tj) * BT * ld + int64_t(ti) * BT * 2, ld, smem, wp, wq, lane, tid);
   } else if constexpr (PHASE == PH_GRAM || PHASE == PH_POLY) {
     void* out = (PHASE == PH_GRAM && VAR == 1) ? md.A : md.B;
     const float sc = PHASE == PH_POLY ? pa.c
@@ -889,9 +991,8 @@ __global__ __launch_bounds__(Cfg<PREC>::NT) void ns_gemm_kernel(const MatDev* __
     OpSrc sp, sq;
     tile_ops<PREC, PHASE>(mats[te.x], te.y >> 16, te.y & 0xFFFF, pa, sp, sq);
     const OpRsrc rsp = op_rsrc(sp), rsq = op_rsrc(sq);
-    constexpr bool KGF = pipelined(PREC);
-    load_stage<Fmt<PREC>::esz, Cfg<PREC>::BT, Cfg<PREC>::NT, NPL, G::NREG, KGF>(rp, sp, rsp, 0, threadIdx.x);
-    load_stage<Fmt<PREC>::esz, Cfg<PREC>::BT, Cfg<PREC>::NT, NPL, G::NREG, KGF>(rq, sq, rsq, 0, threadIdx.x);
+    load_operand<PREC, PHASE, 0>(rp, sp, rsp, 0, threadIdx.x);
+    load_operand<PREC, PHASE, 1>(rq, sq, rsq, 0, threadIdx.x);
   }
 #pragma unroll 1
   while (te.x >= 0) {
