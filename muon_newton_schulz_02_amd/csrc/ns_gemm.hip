@@ -598,17 +598,18 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     //
     // COMBINE's second operand (the iterate, read along its columns) is
     // staged in k-row form: LDS row k holds the stage's k-row as in memory
-    // (512 bytes) at a KP = 544-byte pitch, stored with whole-row loads and
+    // (512 bytes) at a KP = 576-byte pitch, stored with whole-row loads and
     // ds_write_b128, and its fragments come from ds_read_b64_tr_b16, which
     // gives lane j of each 16-lane group element j % 4 of the 8 bytes read by
     // lane 4 e + j / 4 of the group as its value e: with lane 4 e + m pointing
     // at k-row k0 + e, columns n0 + 4 m .. + 3, lane j receives k-values
     // k0 .. k0 + 3 of column n0 + j.  The 16 lanes of a read cover 4 rows x 32
-    // bytes, on distinct banks at this pitch.
+    // bytes, the 32 lanes of a half-wave 4 rows x 64 bytes: distinct banks at
+    // this pitch.
     constexpr int NF = FQ + FP;
     constexpr int QOFF = 2 * OPB;
     constexpr bool QK = PHASE == PH_COMB;
-    constexpr int KP = 544;
+    constexpr int KP = 576;
     static_assert(2 * QOFF <= 2 * STAGE && KE * KP <= OPB, "LDS layout");
     u32x4 F[2][NF];
     char* const lds = smem;
@@ -913,20 +914,42 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     } else {
       const float t = update_scale(pa.lr, pa.scale_rule, md.rows, md.cols);
       if (md.transposed == 0) {
-        // W = X': this lane's four consecutive columns are four consecutive W
-        // elements (staging these through LDS was measured slower)
+        // W = X': stage the binary32 update through LDS, one row of waves (RP
+        // output rows = W rows) per pass, then read-modify-write 8-element
+        // runs of W rows: 16-byte accesses, 512 bytes per 32 lanes.
+        constexpr int RP = WTP;
+        constexpr int NPASS = BT / RP;
+        constexpr int SPN = BT + 4;           // staging pitch in floats: RP rows of BT floats
+        static_assert(RP * SPN * 4 <= 2 * STAGE, "staging does not fit");
+        float* stg = reinterpret_cast<float*>(smem);
+#pragma unroll 1
+        for (int pass = 0; pass < NPASS; ++pass) {
+          if (wp == pass) {
 #pragma clang loop unroll(full)
-        for (int j = 0; j < FQ; ++j)
+            for (int j = 0; j < FQ; ++j)
 #pragma clang loop unroll(full)
-          for (int i = 0; i < FP; ++i)
+              for (int i = 0; i < FP; ++i)
 #pragma clang loop unroll(full)
-            for (int g = 0; g < 4; ++g) {
-              const int r = orow + 32 * i, c0 = ocol + 32 * j + 8 * g;
-              float v[4];
-#pragma clang loop unroll(full)
-              for (int e = 0; e < 4; ++e) v[e] = s * acc[j][i][4 * g + e];
-              if (r < md.m) write_back_n<4>(md, r, c0, md.n, v, t);
-            }
+                for (int g = 0; g < 4; ++g) {
+                  const int rl = 32 * i + (lane & 31), c = wq * WTQ + 32 * j + 8 * g + 4 * hsel;
+                  const f32x16& a = acc[j][i];
+                  *reinterpret_cast<f32x4*>(stg + rl * SPN + c) =
+                      f32x4{s * a[4 * g], s * a[4 * g + 1], s * a[4 * g + 2], s * a[4 * g + 3]};
+                }
+          }
+          lds_barrier();
+          const int row_base = ti * BT + pass * RP;
+          for (int q = tid; q < RP * BT / 8; q += NT) {
+            const int rl = q / (BT / 8), c8 = (q % (BT / 8)) * 8;
+            const int row = row_base + rl;
+            if (row >= md.m) continue;
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(stg + rl * SPN + c8);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(stg + rl * SPN + c8 + 4);
+            const float o[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            write_back_n<8>(md, row, tj * BT + c8, md.n, o, t);
+          }
+          lds_barrier();
+        }
       } else {
         // W = X'^T: stage the binary32 update transposed through LDS, one row of
         // waves (RP output rows = W columns) per pass, then read-modify-write
