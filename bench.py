@@ -52,7 +52,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="d24_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=2, help="layers in the oracle's sample")
+    ap.add_argument("--cpu-layers", type=int, default=6,
+                    help="layers in the oracle's sample (about 10-15 s of host work for d24)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device once (a plain copy kernel "
                          "of known size, to scale HBM byte counters)")
