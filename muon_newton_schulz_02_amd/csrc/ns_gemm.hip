@@ -369,10 +369,22 @@ template <int PREC, int PHASE, int OPD>
 __device__ __forceinline__ void load_operand(u32x4 (&r)[Fmt<PREC>::npl][4], const OpSrc& s, const OpRsrc& rs, int kt,
                                              int tid) {
   constexpr int ESZ = Fmt<PREC>::esz, BT = Cfg<PREC>::BT, NT = Cfg<PREC>::NT;
-  if constexpr (pipelined(PREC) && PHASE == PH_COMB && OPD == 1)
-    load_krow<BT, NT>(r, s, rs, kt, tid);
-  else
-    load_stage<ESZ, BT, NT, Fmt<PREC>::npl, 4, pipelined(PREC)>(r, s, rs, kt, tid);
+  if constexpr (pipelined(PREC)) {
+    // row form (chunk tid + NT i: row tid / 8 + (NT / 8) i, 16 bytes at 16 (tid % 8))
+    // or k-row form (k-row tid / 32 + (NT / 32) i, 16 bytes at 16 (tid % 32))
+    static_assert(ESZ == 2 && BT * 2 == 32 * 16, "bf16 256-wide stages");
+    const bool tr = stage_is_trans<ESZ, BT>(s, kt);
+    const __amdgpu_buffer_rsrc_t rsrc = tr ? rs.trans : rs.direct;
+    const int ld = int(s.ld_b);
+    const int off = tr ? (tid >> 5) * ld + (tid & 31) * 16 : (tid >> 3) * ld + (tid & 7) * 16;
+    const int step = tr ? (NT / 32) * ld : (NT / 8) * ld;
+    const int sbase = tr ? kt * (KB / 2) * ld : kt * KB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[0][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, sbase + i * step, 0));
+  } else {
+    load_stage<ESZ, BT, NT, Fmt<PREC>::npl, 4>(r, s, rs, kt, tid);
+  }
 }
 
 // 4 x 8 transpose of 16-bit values: in[e] holds k-value e of 8 consecutive
@@ -505,18 +517,15 @@ __device__ __forceinline__ int tile_ops(const MatDev& md, int ti, int tj, const 
   } else if constexpr (PHASE == PH_POLY) {
     const char* a = reinterpret_cast<const char*>(md.A);
     const int64_t ld = int64_t(md.lda) * ESZ;
-    // bf16: GRAM stored A whole (each tile and its mirror), so both operands
-    // are read as rows; the other formats read blocks below the diagonal
-    // through their mirror block
-    const int sym = pipelined(PREC) ? -1 : 0;
-    sp = {a + int64_t(ti) * BT * ld, a + int64_t(ti) * BT * ESZ, ld, md.plane_A * ESZ, sym < 0 ? -1 : ti, 0};
-    sq = {a + int64_t(tj) * BT * ld, a + int64_t(tj) * BT * ESZ, ld, md.plane_A * ESZ, sym < 0 ? -1 : tj, 0};
+    // blocks below the diagonal are read through their mirror block
+    sp = {a + int64_t(ti) * BT * ld, a + int64_t(ti) * BT * ESZ, ld, md.plane_A * ESZ, ti, 0};
+    sq = {a + int64_t(tj) * BT * ld, a + int64_t(tj) * BT * ESZ, ld, md.plane_A * ESZ, tj, 0};
     return md.Mp;
   } else {
     const char* b = reinterpret_cast<const char*>(md.B);
     const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
     const int64_t lda = int64_t(md.lda) * ESZ, ldx = int64_t(md.ldx) * ESZ;
-    sp = {b + int64_t(ti) * BT * lda, b + int64_t(ti) * BT * ESZ, lda, md.plane_A * ESZ, pipelined(PREC) ? -1 : ti, 0};
+    sp = {b + int64_t(ti) * BT * lda, b + int64_t(ti) * BT * ESZ, lda, md.plane_A * ESZ, ti, 0};
     sq = {nullptr, x + int64_t(tj) * BT * ESZ, ldx, md.plane_X * ESZ, -1, 1};
     return md.Mp;
   }
@@ -608,43 +617,47 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     // this pitch.
     constexpr int NF = FQ + FP;
     constexpr int QOFF = 2 * OPB;
-    constexpr bool QK = PHASE == PH_COMB;
     constexpr int KP = 576;
     static_assert(2 * QOFF <= 2 * STAGE && KE * KP <= OPB, "LDS layout");
     u32x4 F[2][NF];
     char* const lds = smem;
+    // per-lane fragment offsets: row form (32 rows, one chunk per half-wave)
+    // and k-row form (ds_read_b64_tr_b16: lane 4 e + m of each 16-lane group
+    // points at k-row e, columns 4 m .. 4 m + 3 of its 16)
+    const int kfr = (8 * hsel + ((lane & 15) >> 2)) * KP + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
     const int fragP = (wp * WTP + (lane & 31)) * PITCH + hsel * 16;
-    const int fragQ = QK ? QOFF + (8 * hsel + ((lane & 15) >> 2)) * KP +
-                               2 * (wq * WTQ + 16 * ((lane >> 4) & 1) + 4 * (lane & 3))
-                         : QOFF + (wq * WTQ + (lane & 31)) * PITCH + hsel * 16;
-    const int stD = (tid >> 3) * PITCH + (tid & 7) * 16;               // direct chunk tid, + q (NT / 8) rows
+    const int fragPk = kfr + 2 * wp * WTP;
+    const int fragQ = QOFF + (wq * WTQ + (lane & 31)) * PITCH + hsel * 16;
+    const int fragQk = QOFF + kfr + 2 * wq * WTQ;
+    const int stD = (tid >> 3) * PITCH + (tid & 7) * 16;               // row-form chunk tid, + q (NT / 8) rows
     const int stK = (tid >> 5) * KP + (tid & 31) * 16;                 // k-row piece tid, + i (NT / 32) k-rows
-    // transposed block: k-group kg = tid % 16, row block rb = tid / 16, so
-    // that the 16 lanes of a ds_write_b64 group (16 k-groups of one row)
-    // hit 16 distinct bank pairs; the loads then fetch 64 contiguous bytes
-    // per memory row and instruction
-    const int stT = (tid / G::KG) * 8 * PITCH + (tid % G::KG) * 8;
-    auto read_frags = [&](u32x4 (&f)[NF], auto buf_c, int ks) {
+    auto read_frags = [&](u32x4 (&f)[NF], auto buf_c, int ks, bool ptr, bool qtr) {
       constexpr int BUF = decltype(buf_c)::value;
-      if constexpr (QK) {
-        typedef short s16x4 __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) s16x4 ls16x4;
-        typedef __attribute__((address_space(3))) char lchar;
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) s16x4 ls16x4;
+      typedef __attribute__((address_space(3))) char lchar;
+      auto tr_pair = [&](int off) {
+        lchar* a = (lchar*)(lds + off);
+        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4*)a));
+        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4*)(a + 4 * KP)));
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
+      if (qtr) {
 #pragma clang loop unroll(full)
-        for (int x = 0; x < FQ; ++x) {
-          lchar* a = (lchar*)(lds + fragQ + BUF * OPB + x * 64 + ks * 16 * KP);
-          const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4*)a));
-          const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4*)(a + 4 * KP)));
-          f[x] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        }
+        for (int x = 0; x < FQ; ++x) f[x] = tr_pair(fragQk + BUF * OPB + x * 64 + ks * 16 * KP);
       } else {
 #pragma clang loop unroll(full)
         for (int x = 0; x < FQ; ++x)
           f[x] = *reinterpret_cast<const u32x4*>(lds + fragQ + BUF * OPB + x * 32 * PITCH + ks * 32);
       }
+      if (ptr) {
 #pragma clang loop unroll(full)
-      for (int x = 0; x < FP; ++x)
-        f[FQ + x] = *reinterpret_cast<const u32x4*>(lds + fragP + BUF * OPB + x * 32 * PITCH + ks * 32);
+        for (int x = 0; x < FP; ++x) f[FQ + x] = tr_pair(fragPk + BUF * OPB + x * 64 + ks * 16 * KP);
+      } else {
+#pragma clang loop unroll(full)
+        for (int x = 0; x < FP; ++x)
+          f[FQ + x] = *reinterpret_cast<const u32x4*>(lds + fragP + BUF * OPB + x * 32 * PITCH + ks * 32);
+      }
     };
     auto mfma_half = [&](const u32x4 (&f)[NF], int h) {
 #pragma clang loop unroll(full)
@@ -673,23 +686,15 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       }
     };
     // half H of one operand's part of stage kt, from registers to LDS at byte
-    // offset BASE (the operand's buffer)
+    // offset BASE (the operand's buffer), in row or k-row form
     auto store_half = [&](const u32x4 (&r)[NPL][G::NREG], const OpSrc& src, int kt, auto base_c, auto h_c) {
       constexpr int BASE = decltype(base_c)::value;
       constexpr int H = decltype(h_c)::value;
-      if constexpr (QK && BASE >= QOFF) {
+      const bool tr = stage_is_trans<ESZ, BT>(src, kt);
 #pragma unroll
-        for (int i = 2 * H; i < 2 * H + 2; ++i)
-          *reinterpret_cast<u32x4*>(lds + stK + BASE + i * (NT / 32) * KP) = r[0][i];
-      } else if (stage_is_trans<ESZ, BT>(src, kt)) {
-        u32x2 t[8];
-        transpose4x8_b16(&r[0][0], t);
-#pragma unroll
-        for (int c = 4 * H; c < 4 * H + 4; ++c) *reinterpret_cast<u32x2*>(lds + stT + BASE + c * PITCH) = t[c];
-      } else {
-#pragma unroll
-        for (int q = 2 * H; q < 2 * H + 2; ++q)
-          *reinterpret_cast<u32x4*>(lds + stD + BASE + q * (NT / 8) * PITCH) = r[0][q];
+      for (int i = 2 * H; i < 2 * H + 2; ++i) {
+        const int off = tr ? stK + i * (NT / 32) * KP : stD + i * (NT / 8) * PITCH;
+        *reinterpret_cast<u32x4*>(lds + BASE + off) = r[0][i];
       }
     };
     const OpSrc& xp = has_next ? np : sp;   // the next tile's sources (or this tile's)
@@ -705,7 +710,8 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     lds_barrier();
     load_operand<PREC, PHASE, 0>(rp, sp, rsp, 1, tid);
     load_operand<PREC, PHASE, 1>(rq, sq, rsq, 1, tid);
-    read_frags(F[0], I0{}, 0);
+    auto ktr = [&](const OpSrc& src, int kt) { return stage_is_trans<ESZ, BT>(src, kt); };
+    read_frags(F[0], I0{}, 0, ktr(sp, 0), ktr(sq, 0));
 
     // MODE 0: store stage kt + 1, load stage kt + 2 of this tile; 1: store
     // stage kt + 1, load the next tile's stage 0; 2: the last stage.
@@ -717,7 +723,8 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       using NP = std::integral_constant<int, (BUF ^ 1) * OPB>;
       using NQ = std::integral_constant<int, QOFF + (BUF ^ 1) * OPB>;
       // slab 0
-      read_frags(F[1], CUR{}, 1);
+      const bool ptr = ktr(sp, kt), qtr = ktr(sq, kt);
+      read_frags(F[1], CUR{}, 1, ptr, qtr);
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(F[0], 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -727,7 +734,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       identity_add(F[0], kt, 0);
       __builtin_amdgcn_sched_barrier(0);
       // slab 1
-      read_frags(F[0], CUR{}, 2);
+      read_frags(F[0], CUR{}, 2, ptr, qtr);
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(F[1], 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -744,7 +751,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       identity_add(F[1], kt, 1);
       __builtin_amdgcn_sched_barrier(0);
       // slab 2
-      read_frags(F[1], CUR{}, 3);
+      read_frags(F[1], CUR{}, 3, ptr, qtr);
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(F[0], 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -758,7 +765,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       identity_add(F[0], kt, 2);
       lds_barrier();
       // slab 3
-      if constexpr (MODE != 2) read_frags(F[0], NXT{}, 0);
+      if constexpr (MODE != 2) read_frags(F[0], NXT{}, 0, ktr(sp, kt + 1), ktr(sq, kt + 1));
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(F[1], 0);
       mfma_half(F[1], 1);
@@ -873,10 +880,6 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     const int64_t ld = int64_t(md.lda) * 2;
     store_tile_bf16<FQ, FP, WTP, WTQ, BT, NT, 2 * STAGE>(acc, sc, out + int64_t(ti) * BT * ld + int64_t(tj) * BT * 2,
                                                        ld, smem, wp, wq, lane, tid);
-    // the symmetric product is stored whole: the mirror block too
-    if (ti != tj)
-      store_tile_bf16_mirror<FQ, FP, WTP, WTQ, BT, NT, 2 * STAGE>(
-          acc, sc, out + int64_t(tj) * BT * ld + int64_t(ti) * BT * 2, ld, smem, wp, wq, lane, tid);
   } else if constexpr (PHASE == PH_GRAM || PHASE == PH_POLY) {
     void* out = (PHASE == PH_GRAM && VAR == 1) ? md.A : md.B;
     const float sc = PHASE == PH_POLY ? pa.c
