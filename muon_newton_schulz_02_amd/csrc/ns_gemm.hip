@@ -201,6 +201,56 @@ __device__ __forceinline__ void write_back_n(const MatDev& md, int row, int c0, 
   for (int e = 0; e < NE && e < cnt; ++e) write_back1(md, row, c0 + e, o[e], t);
 }
 
+// Read-modify-write of PER 8-element runs of W per thread (run k: chunk
+// tid + NT k), their binary32 update values in LDS.  run(q, so, row, col,
+// rok, ncols) names run q: LDS float offset, W row and first column, whether
+// the row exists, and the column count.  For bf16 W with 16-byte aligned rows
+// and no update export, the loads of B runs go out before their stores, so
+// their latencies overlap (a load is not moved above an earlier store to the
+// same array by the compiler).
+template <int PER, int B, int NT, class Run>
+__device__ __forceinline__ void write_back_runs(const MatDev& md, const float* stg, int tid, float t, Run run) {
+  static_assert(PER % B == 0, "batches");
+  const bool fast = md.param != nullptr && md.param_bf16 && md.wvec_ok && md.upd == nullptr;
+#pragma unroll 1
+  for (int k0 = 0; k0 < PER; k0 += B) {
+    u32x4 w[B];
+    bool full[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      int so, row, col, ncols;
+      bool rok;
+      run(tid + NT * (k0 + k), so, row, col, rok, ncols);
+      full[k] = fast && rok && col + 8 <= ncols;
+      if (full[k])
+        w[k] = *gmem(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(md.param) +
+                                                    int64_t(row) * md.ld_param + col));
+    }
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      int so, row, col, ncols;
+      bool rok;
+      run(tid + NT * (k0 + k), so, row, col, rok, ncols);
+      if (!rok) continue;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(stg + so);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(stg + so + 4);
+      const float o[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      if (full[k]) {
+        uint32_t raw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float w0 = bf16_bits_to_float(w[k][e] & 0xFFFFu), w1 = bf16_bits_to_float(w[k][e] >> 16);
+          raw[e] = float2_to_bf16x2_bits(w0 - t * o[2 * e], w1 - t * o[2 * e + 1]);
+        }
+        *gmem(reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(md.param) + int64_t(row) * md.ld_param + col)) =
+            u32x4{raw[0], raw[1], raw[2], raw[3]};
+      } else {
+        write_back_n<8>(md, row, col, ncols, o, t);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ MFMA
 
 // acc += A operand (Q side) x B operand (P side) over one k-slab.
@@ -942,15 +992,17 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
           }
           lds_barrier();
           const int row_base = ti * BT + pass * RP;
-          for (int q = tid; q < RP * BT / 8; q += NT) {
+          static_assert((RP * BT / 8) % NT == 0, "runs per thread");
+          constexpr int PER = RP * BT / 8 / NT;
+          write_back_runs<PER, (PER >= 4 ? 4 : PER), NT>(md, stg, tid, t,
+                                                         [&](int q, int& so, int& row, int& col, bool& rok, int& ncols) {
             const int rl = q / (BT / 8), c8 = (q % (BT / 8)) * 8;
-            const int row = row_base + rl;
-            if (row >= md.m) continue;
-            const f32x4 a0 = *reinterpret_cast<const f32x4*>(stg + rl * SPN + c8);
-            const f32x4 a1 = *reinterpret_cast<const f32x4*>(stg + rl * SPN + c8 + 4);
-            const float o[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            write_back_n<8>(md, row, tj * BT + c8, md.n, o, t);
-          }
+            so = rl * SPN + c8;
+            row = row_base + rl;
+            col = tj * BT + c8;
+            rok = row < md.m;
+            ncols = md.n;
+          });
           lds_barrier();
         }
       } else {
@@ -980,15 +1032,17 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
           }
           lds_barrier();
           const int row_base = ti * BT + pass * RP;
-          for (int q = tid; q < BT * RP / 8; q += NT) {
+          static_assert((BT * RP / 8) % NT == 0, "runs per thread");
+          constexpr int PER = BT * RP / 8 / NT;
+          write_back_runs<PER, (PER >= 4 ? 4 : PER), NT>(md, stg, tid, t,
+                                                         [&](int q, int& so, int& row, int& col, bool& rok, int& ncols) {
             const int cl = q / (RP / 8), r8 = (q % (RP / 8)) * 8;
-            const int nrow = tj * BT + cl;    // natural row = wide column
-            if (nrow >= md.n) continue;
-            const f32x4 a0 = *reinterpret_cast<const f32x4*>(stg + cl * SPT + r8);
-            const f32x4 a1 = *reinterpret_cast<const f32x4*>(stg + cl * SPT + r8 + 4);
-            const float o[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            write_back_n<8>(md, nrow, row_base + r8, md.m, o, t);
-          }
+            so = cl * SPT + r8;
+            row = tj * BT + cl;               // natural row = wide column
+            col = row_base + r8;
+            rok = row < md.n;
+            ncols = md.m;
+          });
           lds_barrier();
         }
       }
