@@ -372,7 +372,7 @@ __device__ __forceinline__ bool stage_is_trans(const OpSrc& s, int kt) {
 // resource, scalar and per-thread offset), not branched on: loads issued in
 // two branches into the same registers make the compiler wait for them at the
 // join.
-template <int ESZ, int BT, int NT, int NPL, int NREG, bool KG_FAST = false, int I0 = 0, int I1 = 1 << 20>
+template <int ESZ, int BT, int NT, int NPL, int NREG, int I0 = 0, int I1 = 1 << 20>
 __device__ __forceinline__ void load_stage(u32x4 (&r)[NPL][NREG], const OpSrc& s, const OpRsrc& rs, int kt,
                                            int tid) {
   using G = Geo<ESZ, BT, NT>;
@@ -381,10 +381,10 @@ __device__ __forceinline__ void load_stage(u32x4 (&r)[NPL][NREG], const OpSrc& s
   const __amdgpu_buffer_rsrc_t rsrc = tr ? rs.trans : rs.direct;
   const int ld = int(s.ld_b);
   // transposed: block (row block rb, k-group kg), loads e = 0..3 are memory
-  // rows 4 kg + e, 16 bytes at row block rb (consecutive threads take
-  // consecutive k-groups if KG_FAST, else consecutive row blocks); direct:
-  // chunk tid + NT i is row tid / 8 + (NT / 8) i, 16-byte chunk tid % 8
-  const int rb = KG_FAST ? tid / G::KG : tid % G::RB, kg = KG_FAST ? tid % G::KG : tid / G::RB;
+  // rows 4 kg + e, 16 bytes at row block rb (consecutive threads, consecutive
+  // row blocks); direct: chunk tid + NT i is row tid / 8 + (NT / 8) i,
+  // 16-byte chunk tid % 8
+  const int rb = tid % G::RB, kg = tid / G::RB;
   const int off = tr ? (kg * 4) * ld + rb * 16 : (tid >> 3) * ld + (tid & 7) * 16;
   const int step = tr ? ld : (NT / 8) * ld;
   const int sbase = tr ? kt * (KB / ESZ) * ld : kt * KB;
@@ -396,21 +396,6 @@ __device__ __forceinline__ void load_stage(u32x4 (&r)[NPL][NREG], const OpSrc& s
       r[pl][i] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, sbase + i * step + pl * int(s.plane_b), 0));
   }
-}
-
-// The bf16 iterate as COMBINE's second operand, in k-row form: the stage's
-// KB / 2 memory rows (k-values) of 2 BT bytes each, chunk tid + NT i = k-row
-// tid / 32 + (NT / 32) i, 16-byte piece tid % 32: whole 512-byte rows per
-// 32 lanes.
-template <int BT, int NT>
-__device__ __forceinline__ void load_krow(u32x4 (&r)[1][4], const OpSrc& s, const OpRsrc& rs, int kt, int tid) {
-  static_assert(BT * 2 == 32 * 16, "one k-row is 32 chunks");
-  const int ld = int(s.ld_b);
-  const int off = (tid >> 5) * ld + (tid & 31) * 16;
-  const int sbase = kt * (KB / 2) * ld;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[0][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.trans, off, sbase + i * (NT / 32) * ld, 0));
 }
 
 // Operand OPD (0: P, 1: Q) of stage kt into registers, in the form the
@@ -509,41 +494,6 @@ __device__ __forceinline__ void store_tile_bf16(const f32x16 (&acc)[FQ][FP], flo
       }
   lds_barrier();
   constexpr int CPR = BT * 2 / 16;  // 16-byte chunks per row
-#pragma unroll 4
-  for (int q = tid; q < BT * CPR; q += NT) {
-    const int r = q / CPR, c16 = q % CPR;
-    *gmem(reinterpret_cast<u32x4*>(out + int64_t(r) * ld + c16 * 16)) = *reinterpret_cast<const u32x4*>(smem + r * EP + c16 * 16);
-  }
-}
-
-// The transpose of the same tile (its mirror block, at `out`): the values go
-// to LDS transposed, two bytes at a time (32 lanes hold 32 consecutive rows
-// of one column: 64 contiguous bytes of a transposed row), then whole rows
-// leave as above.  Called after store_tile_bf16, whose staging it reuses.
-template <int FQ, int FP, int WTP, int WTQ, int BT, int NT, int LDSB>
-__device__ __forceinline__ void store_tile_bf16_mirror(const f32x16 (&acc)[FQ][FP], float sc, char* out, int64_t ld,
-                                                       char* smem, int wp, int wq, int lane, int tid) {
-  constexpr int EP = BT * 2 + 16;
-  static_assert(BT * EP <= LDSB, "staging does not fit");
-  const int hsel = lane >> 5;
-  lds_barrier();   // every lane's copy-out of the direct staging is done
-#pragma clang loop unroll(full)
-  for (int j = 0; j < FQ; ++j)
-#pragma clang loop unroll(full)
-    for (int i = 0; i < FP; ++i)
-#pragma clang loop unroll(full)
-      for (int g = 0; g < 4; ++g) {
-        const int r = wp * WTP + 32 * i + (lane & 31), c = wq * WTQ + 32 * j + 8 * g + 4 * hsel;
-        const f32x16& a = acc[j][i];
-        const uint32_t v01 = float2_to_bf16x2_bits(sc * a[4 * g], sc * a[4 * g + 1]);
-        const uint32_t v23 = float2_to_bf16x2_bits(sc * a[4 * g + 2], sc * a[4 * g + 3]);
-        *reinterpret_cast<uint16_t*>(smem + (c + 0) * EP + r * 2) = uint16_t(v01);
-        *reinterpret_cast<uint16_t*>(smem + (c + 1) * EP + r * 2) = uint16_t(v01 >> 16);
-        *reinterpret_cast<uint16_t*>(smem + (c + 2) * EP + r * 2) = uint16_t(v23);
-        *reinterpret_cast<uint16_t*>(smem + (c + 3) * EP + r * 2) = uint16_t(v23 >> 16);
-      }
-  lds_barrier();
-  constexpr int CPR = BT * 2 / 16;
 #pragma unroll 4
   for (int q = tid; q < BT * CPR; q += NT) {
     const int r = q / CPR, c16 = q % CPR;
@@ -655,10 +605,12 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     // every group on 16 distinct bank quads: 4.5 clk per instruction, against
     // 8 when rows 16-31 take other chunks than rows 0-15 (measured).
     //
-    // COMBINE's second operand (the iterate, read along its columns) is
-    // staged in k-row form: LDS row k holds the stage's k-row as in memory
-    // (512 bytes) at a KP = 576-byte pitch, stored with whole-row loads and
-    // ds_write_b128, and its fragments come from ds_read_b64_tr_b16, which
+    // Operands read along their memory columns (COMBINE's iterate, and the
+    // blocks of A and B below the diagonal, read through their mirror block)
+    // are staged in k-row form, chosen per stage: LDS row k holds the stage's
+    // k-row as in memory (512 bytes) at a KP = 576-byte pitch, stored with
+    // whole-row loads and ds_write_b128, and their fragments come from
+    // ds_read_b64_tr_b16, which
     // gives lane j of each 16-lane group element j % 4 of the 8 bytes read by
     // lane 4 e + j / 4 of the group as its value e: with lane 4 e + m pointing
     // at k-row k0 + e, columns n0 + 4 m .. + 3, lane j receives k-values
