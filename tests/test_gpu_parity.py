@@ -49,6 +49,23 @@ def test_ragged_shapes(prec, steps, coeffs):
                    param_bf16=pdt == torch.bfloat16)
 
 
+MULTI_TILE = [(700, 1100), (1100, 700), (769, 769)]
+
+
+@pytest.mark.parametrize("prec", [mb.NS_BF16X3, mb.NS_BF16])
+def test_multi_tile_shapes(prec):
+    """Three or more 256-row tiles per symmetric product: blocks below the diagonal
+    are read through their mirror in several k-ranges, with ragged edges."""
+    _announce(f"multi-tile prec={prec}")
+    pdt = torch.bfloat16 if prec == mb.NS_BF16 else torch.float32
+    ws, gs, ms = _inputs(MULTI_TILE, 29, pdt, torch.bfloat16)
+    lr = f32(0.02)
+    w1, m1, o1 = run_step(ws, gs, ms, lr=lr, beta=0.95, nesterov=True, coeffs=MUON, steps=5, precision=prec)
+    for i in range(len(MULTI_TILE)):
+        check_step(to_np(ws[i]), to_np(gs[i]), to_np(ms[i]), w1[i], m1[i], o1[i], lr=lr, beta=0.95,
+                   nesterov=True, coeffs=MUON, steps=5, tol=PREC_TOL[prec], param_bf16=pdt == torch.bfloat16)
+
+
 @pytest.mark.parametrize("nesterov", [0, 1])
 @pytest.mark.parametrize("pdt,gdt", [(torch.float32, torch.float32), (torch.bfloat16, torch.float32),
                                      (torch.float32, torch.bfloat16)])
