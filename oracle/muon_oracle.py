@@ -39,6 +39,17 @@ named R<n> below and listed with its reason in the design notes.
   R7  scale rules: NONE s = 1; SQRT_ASPECT s = sqrt(max(1, rows/cols));
       RMS_MATCH s = 0.2*sqrt(max(rows, cols)).
 
+Update variants (the pages describe none of them; they are the forms
+commonly used with Muon, offered as options):
+  R8  EMA momentum: M <- beta*M + (1-beta)*g, with (1-beta) rounded to
+      binary32 and each product and sum rounded once; its Nesterov
+      direction is U = (1-beta)*g + beta*M_new.
+  R9  a Newton-Schulz schedule: step k uses its own triple (a_k, b_k, c_k).
+  R10 decoupled weight decay: W <- rnd(fl32(fl32(W*d) - fl32(t*O))) with
+      d = fl32(1 - fl32(lr*wd)); wd = 0 gives d = 1 and R6 exactly.
+  R11 a per-matrix learning rate and a per-matrix scale s replace lr and the
+      scale rule of R6/R7 for that matrix.
+
 Parity of every function here is pinned by tests/test_oracle_pins.py
 against closed forms, invariants, exact rational arithmetic and LAPACK; see
 that file for which pin covers which function.
@@ -92,8 +103,12 @@ def split_bf16x2(x) -> tuple[np.ndarray, np.ndarray]:
 # the step, one stage at a time
 # ---------------------------------------------------------------------------
 
-def momentum(m, g, beta: float, nesterov: bool):
-    """Momentum buffer update and the update direction U ([P3]; R1-R3).
+MOMENTUM_HEAVY_BALL = 0
+MOMENTUM_EMA = 1
+
+
+def momentum(m, g, beta: float, nesterov: bool, kind: int = MOMENTUM_HEAVY_BALL):
+    """Momentum buffer update and the update direction U ([P3]; R1-R3, R8).
 
     m: float32 buffer, g: gradient (bf16 values held in float32, or float32).
     Returns (m_new, u), both float32.  numpy float32 arithmetic rounds each
@@ -102,9 +117,15 @@ def momentum(m, g, beta: float, nesterov: bool):
     m = np.asarray(m, dtype=np.float32)
     g = np.asarray(g, dtype=np.float32)
     b = np.float32(beta)
-    m_new = (b * m) + g
+    if kind == MOMENTUM_HEAVY_BALL:
+        gin = g
+    elif kind == MOMENTUM_EMA:
+        gin = (np.float32(1.0) - b) * g
+    else:
+        raise ValueError(f"unknown momentum kind {kind}")
+    m_new = (b * m) + gin
     if nesterov:
-        u = g + (b * m_new)
+        u = gin + (b * m_new)
     else:
         u = m_new.copy()
     return m_new, u
@@ -132,15 +153,26 @@ def orient(x):
     return x, False
 
 
+def schedule(coeffs, steps: int) -> list:
+    """The triple of each of `steps` steps: one triple for all (a, b, c), or a
+    sequence of `steps` triples (R9)."""
+    c = np.asarray(coeffs, dtype=np.float64)
+    if c.shape == (3,):
+        return [tuple(float(v) for v in c)] * steps
+    if c.shape != (steps, 3):
+        raise ValueError(f"a schedule needs {steps} triples, got shape {c.shape}")
+    return [tuple(float(v) for v in row) for row in c]
+
+
 def newton_schulz(x0, coeffs, steps: int) -> np.ndarray:
     """`steps` polynomial Newton-Schulz steps on a wide float64 matrix ([P4], [H]).
 
     Each step forms the Gram matrix A = X X^T, the polynomial B = b A + c A A
-    and the new iterate X <- a X + B X.  All in float64.
+    and the new iterate X <- a X + B X.  All in float64.  `coeffs` is one
+    triple or a schedule of `steps` triples (R9).
     """
-    a, b, c = (float(v) for v in coeffs)
     x = np.array(x0, dtype=np.float64)
-    for _ in range(steps):
+    for a, b, c in schedule(coeffs, steps):
         gram = x @ x.T
         poly = b * gram + c * (gram @ gram)
         x = a * x + poly @ x
@@ -165,8 +197,9 @@ def scale_factor(rule: int, rows: int, cols: int) -> float:
     raise ValueError(f"unknown scale rule {rule}")
 
 
-def write_back(w, o, lr: float, s: float, param_bf16: bool) -> np.ndarray:
-    """W <- rnd(fl32(W - fl32(t*O))) with t = fl32(lr*s) (R6).
+def write_back(w, o, lr: float, s: float, param_bf16: bool, weight_decay: float = 0.0) -> np.ndarray:
+    """W <- rnd(fl32(fl32(W*d) - fl32(t*O))) with t = fl32(lr*s) and
+    d = fl32(1 - fl32(lr*wd)) (R6, R10; wd = 0 leaves W*d = W exactly).
 
     o is rounded to binary32 first (the update leaves the GPU's epilogue in
     binary32); returns float32 values (bf16-representable when param_bf16).
@@ -174,6 +207,9 @@ def write_back(w, o, lr: float, s: float, param_bf16: bool) -> np.ndarray:
     t = np.float32(np.float64(lr) * np.float64(s))
     w32 = np.asarray(w, dtype=np.float32)
     o32 = np.asarray(o, dtype=np.float32)
+    if weight_decay != 0.0:
+        d = np.float32(1.0) - np.float32(np.float32(lr) * np.float32(weight_decay))
+        w32 = w32 * d
     out = w32 - (t * o32)
     return to_bf16(out) if param_bf16 else out
 
@@ -191,15 +227,19 @@ class StepResult:
 
 
 def muon_step(w, g, m, *, lr, beta, nesterov, coeffs, steps, scale_rule=SCALE_NONE,
-              param_bf16=False, eps=EPS, storage="fp64") -> StepResult:
+              param_bf16=False, eps=EPS, storage="fp64", momentum_kind=MOMENTUM_HEAVY_BALL,
+              weight_decay=0.0, scale=None) -> StepResult:
     """One Muon step on one matrix: momentum, normalise, Newton-Schulz, write-back.
 
     storage="fp64" is the reference definition.  storage="bf16" evaluates the
     same step with the intermediates rounded where a bf16 GPU path stores
     them (see `orthogonalise_bf16_storage`); it is an aid for separating the
     bf16 storage error from other error, not a different method.
+    Variants: momentum_kind (R8), a schedule in `coeffs` (R9), weight_decay
+    (R10), and `scale` replacing the scale rule (R11; `lr` is per matrix
+    already, one matrix per call).
     """
-    m_new, u = momentum(m, g, beta, nesterov)
+    m_new, u = momentum(m, g, beta, nesterov, momentum_kind)
     if storage == "fp64":
         o = orthogonalise(u, coeffs, steps, eps)
     elif storage == "bf16":
@@ -207,8 +247,8 @@ def muon_step(w, g, m, *, lr, beta, nesterov, coeffs, steps, scale_rule=SCALE_NO
     else:
         raise ValueError(storage)
     rows, cols = np.asarray(w).shape
-    s = scale_factor(scale_rule, rows, cols)
-    w_new = write_back(w, o, lr, s, param_bf16)
+    s = scale_factor(scale_rule, rows, cols) if scale is None else float(scale)
+    w_new = write_back(w, o, lr, s, param_bf16, weight_decay)
     return StepResult(w=w_new, m=m_new, o=o, u=u)
 
 
@@ -235,7 +275,7 @@ def orthogonalise_bf16_storage(u, coeffs, steps: int, eps: float = EPS, rnd=None
     """
     if rnd is None:
         rnd = to_bf16
-    a, b, c = (float(v) for v in coeffs)
+    triples = schedule(coeffs, steps)
     u32 = np.asarray(u, dtype=np.float32)
     xw, tr = orient(u32)
     inv = 1.0 / (frobenius_norm(u32) + eps)
@@ -245,6 +285,7 @@ def orthogonalise_bf16_storage(u, coeffs, steps: int, eps: float = EPS, rnd=None
         o = s * x
         return o.T if tr else o
     for k in range(steps):
+        a, b, c = triples[k]
         gram = (s * s) * (x @ x.T)
         if c != 0.0:
             a_st = np.asarray(rnd(gram), dtype=np.float64)

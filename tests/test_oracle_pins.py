@@ -404,3 +404,133 @@ def test_lm38_stack_matches_page_heads():
     kv = gold["kv_heads"] * head_dim
     assert {(s.rows, s.cols) for s in wl.specs} == {(q, q), (q, kv), (q, 4 * q), (4 * q, q)}
     assert wl.elements < gold["total_params_billion"] * 1e9
+
+
+# ---------------------------------------------------------------------------
+# update variants (R8-R11)
+# ---------------------------------------------------------------------------
+
+# an arbitrary five-step schedule of quintic triples (steep first, then milder)
+SCHEDULE5 = [(4.0848, -6.8946, 2.9270), (3.9505, -6.3029, 2.6377), (3.7418, -5.5913, 2.3037),
+             (2.8769, -3.1427, 1.2046), (2.8366, -3.0525, 1.2012)]
+
+
+def test_schedule_spectral_closed_form():
+    # X0 = U diag(s) V^T: step k maps every singular value through its own
+    # polynomial p_k, so the schedule acts as the composition p_K o ... o p_1.
+    rng = np.random.default_rng(77)
+    rows, cols = 30, 50
+    uu = random_orthonormal(rng, rows, rows)
+    vv = random_orthonormal(rng, cols, rows)
+    s = rng.uniform(0.02, 1.0, rows)
+    g = (uu * s) @ vv.T
+    sig = s / (np.linalg.norm(s) + orc.EPS)
+    for t in SCHEDULE5:
+        sig = scalar_map(t, 1, sig)
+    ref = (uu * sig) @ vv.T
+    o = orc.orthogonalise(g, SCHEDULE5, len(SCHEDULE5))
+    assert orc.rel_frobenius(o, ref) < 1e-10
+    # the transposed (tall) matrix gives the transposed result
+    o_t = orc.orthogonalise(g.T, SCHEDULE5, len(SCHEDULE5))
+    assert np.max(np.abs(o_t - o.T)) < 1e-12
+
+
+def test_schedule_of_one_triple_is_that_triple():
+    rng = np.random.default_rng(78)
+    g = rng.standard_normal((20, 33))
+    a = orc.orthogonalise(g, MUON, 4)
+    b = orc.orthogonalise(g, [MUON] * 4, 4)
+    assert np.array_equal(a, b)
+    with pytest.raises(ValueError):
+        orc.orthogonalise(g, [MUON] * 3, 4)
+
+
+def test_schedule_exact_rational_2x2():
+    # the rational rotation case of test_exact_rational_2x2 with two different triples
+    sched = [CUBIC, TEXTBOOK]
+    r = _fmat([[Fraction(3, 5), Fraction(-4, 5)], [Fraction(4, 5), Fraction(3, 5)]])
+    g = _fmul(r, _fmat([[3, 0], [0, 4]]))
+    sv = []
+    for sig in (Fraction(3, 5), Fraction(4, 5)):
+        for t in sched:
+            sig = _exact_scalar_map(t, 1, sig)
+        sv.append(sig)
+    ref = _as_np(_fmul(r, _fmat([[sv[0], 0], [0, sv[1]]])))
+    o = orc.newton_schulz(_as_np(g) / 5.0, sched, 2)
+    assert np.max(np.abs(o - ref)) < 1e-14
+
+
+def test_bf16_emulation_schedule_reduces_to_definition():
+    rng = np.random.default_rng(79)
+    u = rng.standard_normal((24, 40)).astype(np.float32)
+    sched = SCHEDULE5
+    a = orc.orthogonalise_bf16_storage(u, sched, len(sched), rnd=lambda v: np.asarray(v, np.float64))
+    b = orc.orthogonalise(u, sched, len(sched))
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+def test_ema_momentum_exact_cases():
+    # beta = 0.5, 0.75: 1 - beta and every product and sum below are exact in
+    # binary32, so M' = beta M + (1 - beta) g and U hold exactly.
+    m = np.array([4.0, -8.0, 0.0, 1.5], np.float32)
+    g = np.array([2.0, 6.0, -3.0, 0.5], np.float32)
+    for beta in (0.5, 0.75):
+        mn, u = orc.momentum(m, g, beta, False, orc.MOMENTUM_EMA)
+        exp = beta * m.astype(np.float64) + (1 - beta) * g.astype(np.float64)
+        assert np.array_equal(mn, exp.astype(np.float32))
+        assert np.array_equal(u, mn)
+        mn2, u2 = orc.momentum(m, g, beta, True, orc.MOMENTUM_EMA)
+        assert np.array_equal(mn2, mn)
+        exp_u = (1 - beta) * g.astype(np.float64) + beta * exp
+        assert np.array_equal(u2, exp_u.astype(np.float32))
+    # beta = 0: the buffer becomes g; g = 0: the buffer decays as heavy-ball's
+    mn, _ = orc.momentum(m, g, 0.0, False, orc.MOMENTUM_EMA)
+    assert np.array_equal(mn, g)
+    z = np.zeros_like(g)
+    assert np.array_equal(orc.momentum(m, z, 0.9, False, orc.MOMENTUM_EMA)[0],
+                          orc.momentum(m, z, 0.9, False, orc.MOMENTUM_HEAVY_BALL)[0])
+
+
+def test_ema_momentum_same_direction_from_zero():
+    # from M0 = 0 both forms give U proportional to g: the normalised update is the same
+    rng = np.random.default_rng(80)
+    g = rng.standard_normal((16, 24)).astype(np.float32)
+    w = (rng.standard_normal((16, 24)) * 0.02).astype(np.float32)
+    m0 = np.zeros_like(g)
+    kw = dict(lr=0.02, beta=0.95, nesterov=True, coeffs=MUON, steps=5)
+    hb = orc.muon_step(w, g, m0, **kw)
+    ema = orc.muon_step(w, g, m0, momentum_kind=orc.MOMENTUM_EMA, **kw)
+    assert orc.rel_frobenius(ema.o, hb.o) < 1e-6
+    assert np.array_equal(ema.m, (np.float32(1) - np.float32(0.95)) * g)
+
+
+def test_weight_decay_closed_form():
+    # zero gradient and momentum: O = 0, so W' = rnd(W * d) with d = 1 - lr*wd;
+    # lr = 0.5, wd = 0.5 makes d = 0.75 exact, and W below times 0.75 is exact
+    w = np.array([[4.0, -8.0, 0.5], [1.0, 2.0, -16.0]], np.float32)
+    z = np.zeros_like(w)
+    for bf in (False, True):
+        r = orc.muon_step(w, z, z, lr=0.5, beta=0.9, nesterov=True, coeffs=MUON, steps=5,
+                          param_bf16=bf, weight_decay=0.5)
+        assert np.array_equal(r.w, 0.75 * w)
+    # wd = 0 is the step without decay, bit for bit
+    rng = np.random.default_rng(81)
+    g = rng.standard_normal((6, 9)).astype(np.float32)
+    w2 = (rng.standard_normal((6, 9)) * 0.02).astype(np.float32)
+    kw = dict(lr=0.02, beta=0.95, nesterov=True, coeffs=MUON, steps=3, param_bf16=True)
+    m0 = np.zeros_like(g)
+    assert np.array_equal(orc.muon_step(w2, g, m0, **kw).w, orc.muon_step(w2, g, m0, weight_decay=0.0, **kw).w)
+
+
+def test_scale_override_equals_rule():
+    rng = np.random.default_rng(82)
+    g = rng.standard_normal((12, 30)).astype(np.float32)
+    w = (rng.standard_normal((12, 30)) * 0.02).astype(np.float32)
+    z = np.zeros_like(g)
+    kw = dict(lr=0.02, beta=0.95, nesterov=True, coeffs=MUON, steps=3, param_bf16=True)
+    for rule in (orc.SCALE_SQRT_ASPECT, orc.SCALE_RMS_MATCH):
+        s = orc.scale_factor(rule, 12, 30)
+        assert np.array_equal(orc.muon_step(w, g, z, scale_rule=rule, **kw).w,
+                              orc.muon_step(w, g, z, scale=s, **kw).w)
+    # lr = 0 leaves W unchanged (without decay)
+    assert np.array_equal(orc.muon_step(w, g, z, **{**kw, "lr": 0.0}).w, orc.to_bf16(w))
