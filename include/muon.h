@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 1
+#define MUON_ABI_VERSION 2
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -92,6 +92,41 @@ typedef enum muon_scale_rule {
 typedef struct muon_ns_coeffs {
   float a, b, c;
 } muon_ns_coeffs;
+
+/* Momentum forms (muon_step_options.momentum_kind).
+ *   HEAVY_BALL  M <- beta*M + G; Nesterov U = G + beta*M (the default).
+ *   EMA         M <- beta*M + (1-beta)*G with (1-beta) rounded to binary32;
+ *               Nesterov U = (1-beta)*G + beta*M.  Every product and sum is
+ *               rounded once in binary32.                                 */
+typedef enum muon_momentum_kind {
+  MUON_MOMENTUM_HEAVY_BALL = 0,
+  MUON_MOMENTUM_EMA = 1
+} muon_momentum_kind;
+
+/* Update variants of muon_step_batched_v2.  The pages describe none of
+ * them; they are the forms commonly used with Muon.  A zero-initialised
+ * struct (or a NULL pointer) gives muon_step_batched bit for bit.
+ *
+ * ns_schedule       host array of ns_steps finite triples, step k using
+ *                   entry k (a step with c = 0 skips its A*A product); NULL:
+ *                   ns_coeffs at every step.
+ * weight_decay      decoupled weight decay wd, finite and >= 0:
+ *                   W <- rnd(fl32(fl32(W*d) - fl32(t*O))), d = fl32(1 -
+ *                   fl32(lr_i*wd)); 0 leaves the write-back unchanged.
+ * momentum_kind     a muon_momentum_kind.
+ * lr_per_matrix     host array of `count` finite learning rates replacing
+ *                   lr for matrix i (in t and d), or NULL.
+ * scale_per_matrix  host array of `count` finite scales s_i replacing the
+ *                   scale rule for matrix i (t = fl32(lr_i*s_i), the product
+ *                   in binary64), or NULL.
+ * The arrays are read during the call and not kept.                        */
+typedef struct muon_step_options {
+  const muon_ns_coeffs* ns_schedule;
+  float weight_decay;
+  int32_t momentum_kind;
+  const float* lr_per_matrix;
+  const float* scale_per_matrix;
+} muon_step_options;
 
 /* One 2-D matrix.  rows, cols in [1, 65536]; ld_* >= cols.
  * param_dtype and grad_dtype: MUON_DTYPE_F32 or MUON_DTYPE_BF16;
@@ -139,6 +174,18 @@ muon_status muon_step_batched_ex(void* const* params, const void* const* grads,
                                  muon_ns_coeffs ns_coeffs, int32_t ns_steps,
                                  int32_t scale_rule, float* const* updates_out,
                                  void* stream);
+
+/* muon_step_batched_ex with the update variants of `options` (may be NULL,
+ * see muon_step_options).  Per-matrix learning rates, scales or a weight
+ * decay add one small host-to-device copy (8 bytes per matrix) on `stream`.
+ * Errors as muon_step_batched, and INVALID_ARGUMENT for an option out of
+ * its range.                                                              */
+muon_status muon_step_batched_v2(void* const* params, const void* const* grads,
+                                 void* const* momenta, const muon_matrix_desc* shapes,
+                                 int32_t count, float lr, float beta, int32_t nesterov,
+                                 muon_ns_coeffs ns_coeffs, int32_t ns_steps,
+                                 int32_t scale_rule, const muon_step_options* options,
+                                 float* const* updates_out, void* stream);
 
 /* Newton-Schulz orthogonalisation only: x_out[i] = NS^ns_steps(x / (||x||_F
  * + 1e-7)) for x = x_in[i] (rows x cols, grad_dtype, row stride ld_grad),

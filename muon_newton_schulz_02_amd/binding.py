@@ -60,6 +60,19 @@ class NsCoeffs(ctypes.Structure):
     _fields_ = [("a", ctypes.c_float), ("b", ctypes.c_float), ("c", ctypes.c_float)]
 
 
+MOMENTUM_HEAVY_BALL = 0
+MOMENTUM_EMA = 1
+
+
+class StepOptions(ctypes.Structure):
+    """muon_step_options (include/muon.h)."""
+    _fields_ = [
+        ("ns_schedule", ctypes.POINTER(NsCoeffs)), ("weight_decay", ctypes.c_float),
+        ("momentum_kind", ctypes.c_int32), ("lr_per_matrix", ctypes.POINTER(ctypes.c_float)),
+        ("scale_per_matrix", ctypes.POINTER(ctypes.c_float)),
+    ]
+
+
 _VP = ctypes.c_void_p
 _PP = ctypes.POINTER(ctypes.c_void_p)
 _lib = None
@@ -86,6 +99,9 @@ def lib() -> ctypes.CDLL:
     L.muon_step_batched.restype = i32
     L.muon_step_batched_ex.argtypes = [_PP, _PP, _PP, D, i32, f32, f32, i32, NsCoeffs, i32, i32, _PP, _VP]
     L.muon_step_batched_ex.restype = i32
+    L.muon_step_batched_v2.argtypes = [_PP, _PP, _PP, D, i32, f32, f32, i32, NsCoeffs, i32, i32,
+                                       ctypes.POINTER(StepOptions), _PP, _VP]
+    L.muon_step_batched_v2.restype = i32
     L.muon_ns_batched.argtypes = [_PP, _PP, D, i32, NsCoeffs, i32, _VP]
     L.muon_ns_batched.restype = i32
     L.muon_frobenius_norms.argtypes = [_PP, D, i32, _VP, _VP]
@@ -246,6 +262,38 @@ def muon_step_batched(params, grads=None, momenta=None, *, lr, beta, nesterov, n
         status = lib().muon_step_batched_ex(args.params, args.grads, args.momenta, args.descs, args.count,
                                             float(lr), float(beta), int(nesterov), co, int(ns_steps),
                                             int(scale_rule), args.updates, st)
+    _check(status)
+
+
+def muon_step_batched_v2(params, grads=None, momenta=None, *, lr, beta, nesterov, ns_coeffs, ns_steps,
+                         scale_rule=SCALE_NONE, precision=NS_BF16, stream=None, updates_out=None,
+                         ns_schedule=None, weight_decay=0.0, momentum_kind=MOMENTUM_HEAVY_BALL,
+                         lr_per_matrix=None, scale_per_matrix=None):
+    """muon_step_batched with the update variants of muon_step_options."""
+    args = params if isinstance(params, StepArgs) else StepArgs(params, grads, momenta, precision, updates_out)
+    a, b, c = ns_coeffs
+    co = NsCoeffs(float(a), float(b), float(c))
+    opt = StepOptions()
+    keep = []
+    if ns_schedule is not None:
+        if len(ns_schedule) != int(ns_steps):
+            raise ValueError("ns_schedule needs one triple per step")
+        arr = (NsCoeffs * max(len(ns_schedule), 1))(*[NsCoeffs(*(float(v) for v in t)) for t in ns_schedule])
+        keep.append(arr)
+        opt.ns_schedule = ctypes.cast(arr, ctypes.POINTER(NsCoeffs))
+    opt.weight_decay = float(weight_decay)
+    opt.momentum_kind = int(momentum_kind)
+    for name, vals in (("lr_per_matrix", lr_per_matrix), ("scale_per_matrix", scale_per_matrix)):
+        if vals is not None:
+            if len(vals) != args.count:
+                raise ValueError(f"{name} needs one value per matrix")
+            arr = (ctypes.c_float * max(len(vals), 1))(*[float(v) for v in vals])
+            keep.append(arr)
+            setattr(opt, name, ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)))
+    status = lib().muon_step_batched_v2(args.params, args.grads, args.momenta, args.descs, args.count,
+                                        float(lr), float(beta), int(nesterov), co, int(ns_steps),
+                                        int(scale_rule), ctypes.byref(opt), args.updates, _stream_handle(stream))
+    del keep
     _check(status)
 
 

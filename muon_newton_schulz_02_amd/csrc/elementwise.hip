@@ -82,7 +82,7 @@ __device__ inline float wave_sum(float v) {
 __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict__ mats,
                                                        const int32_t* __restrict__ etile_off,
                                                        int32_t count, float beta, int32_t nesterov,
-                                                       int32_t mode, float* __restrict__ partials) {
+                                                       int32_t ema, int32_t mode, float* __restrict__ partials) {
   __shared__ float tile[ETILE][ETILE + 1];
   __shared__ float red[4];
   const int b = blockIdx.x;
@@ -141,11 +141,13 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
         float mn[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // binary32, one rounding per operation (contraction is off here)
+          // binary32, one rounding per operation (contraction is off here);
+          // EMA form: the gradient enters as fl32((1 - beta) * g)
+          const float gi = ema ? (1.f - beta) * g[e] : g[e];
           const float bm = beta * m[e];
-          mn[e] = bm + g[e];
+          mn[e] = bm + gi;
           const float bn = beta * mn[e];
-          u[e] = nesterov ? (g[e] + bn) : mn[e];
+          u[e] = nesterov ? (gi + bn) : mn[e];
         }
         if (full) {
           *gmem(reinterpret_cast<f32x4*>(md.mom + mi64)) = f32x4{mn[0], mn[1], mn[2], mn[3]};
@@ -221,7 +223,8 @@ __global__ __launch_bounds__(256) void writeback_direct_kernel(const MatDev* __r
                                                                const int32_t* __restrict__ etile_off,
                                                                int32_t count,
                                                                const MatScal* __restrict__ scal,
-                                                               float lr, int32_t scale_rule) {
+                                                               float lr, int32_t scale_rule,
+                                                               const float2* __restrict__ wb) {
   const int b = blockIdx.x;
   const int mi = find_matrix(etile_off, count, b);
   const MatDev& md = mats[mi];
@@ -231,7 +234,8 @@ __global__ __launch_bounds__(256) void writeback_direct_kernel(const MatDev* __r
   const bool tr = md.transposed != 0;
   const void* xw = md.X[0];
   const float inv = scal[mi].inv;
-  const float t = update_scale(lr, scale_rule, md.rows, md.cols);
+  const float t = wb ? wb[mi].x : update_scale(lr, scale_rule, md.rows, md.cols);
+  const float d = wb ? wb[mi].y : 1.f;
   for (int e = threadIdx.x; e < ETILE * ETILE; e += 256) {
     const int row = tr0 + e / ETILE, col = tc0 + e % ETILE;
     if (row >= md.rows || col >= md.cols) continue;
@@ -242,10 +246,10 @@ __global__ __launch_bounds__(256) void writeback_direct_kernel(const MatDev* __r
       if (md.param_bf16) {
         auto pw = gmem(reinterpret_cast<uint16_t*>(md.param));
         const float w = bf16_bits_to_float(pw[pi]);
-        pw[pi] = float_to_bf16_bits(w - t * o);
+        pw[pi] = float_to_bf16_bits(w * d - t * o);
       } else {
         auto pw = gmem(reinterpret_cast<float*>(md.param));
-        pw[pi] = pw[pi] - t * o;
+        pw[pi] = pw[pi] * d - t * o;
       }
     }
     if (md.upd) gmem(md.upd)[int64_t(row) * md.ld_upd + col] = o;
@@ -253,11 +257,11 @@ __global__ __launch_bounds__(256) void writeback_direct_kernel(const MatDev* __r
 }
 
 hipError_t launch_momentum(const MatDev* mats, const int32_t* etile_off, int32_t count,
-                           int64_t total_tiles, float beta, int32_t nesterov, int32_t mode,
+                           int64_t total_tiles, float beta, int32_t nesterov, int32_t ema, int32_t mode,
                            float* partials, hipStream_t stream) {
   if (total_tiles <= 0) return hipSuccess;
   hipLaunchKernelGGL(momentum_kernel, dim3(unsigned(total_tiles)), dim3(256), 0, stream, mats,
-                     etile_off, count, beta, nesterov, mode, partials);
+                     etile_off, count, beta, nesterov, ema, mode, partials);
   return hipGetLastError();
 }
 
@@ -271,10 +275,10 @@ hipError_t launch_norm_finalize(const int32_t* etile_off, int32_t count, const f
 
 hipError_t launch_writeback_direct(const MatDev* mats, const int32_t* etile_off, int32_t count,
                                    int64_t total_tiles, const MatScal* scal, float lr,
-                                   int32_t scale_rule, hipStream_t stream) {
+                                   int32_t scale_rule, const float2* wb, hipStream_t stream) {
   if (total_tiles <= 0) return hipSuccess;
   hipLaunchKernelGGL(writeback_direct_kernel, dim3(unsigned(total_tiles)), dim3(256), 0, stream,
-                     mats, etile_off, count, scal, lr, scale_rule);
+                     mats, etile_off, count, scal, lr, scale_rule, wb);
   return hipGetLastError();
 }
 

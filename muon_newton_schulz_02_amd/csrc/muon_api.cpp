@@ -158,6 +158,7 @@ struct Plan {
   int32_t* d_etile_off = nullptr;
   MatScal* d_scal = nullptr;
   float* d_partials = nullptr;
+  float2* d_wb = nullptr;        // per-matrix write-back scalars {t, d}, filled per call when used
   struct Group {
     int prec;
     int2* tiles[3];
@@ -315,6 +316,8 @@ muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vec
   off = align256(off + sizeof(MatScal) * count);
   const size_t off_part = off;
   off = align256(off + sizeof(float) * size_t(std::max<int64_t>(etile_off[count], 1)));
+  const size_t off_wb = off;
+  off = align256(off + sizeof(float2) * count);
   std::vector<size_t> off_lists;
   for (auto& l : lists) {
     off_lists.push_back(off);
@@ -343,6 +346,7 @@ muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vec
   plan->d_etile_off = reinterpret_cast<int32_t*>(base + off_etile);
   plan->d_scal = reinterpret_cast<MatScal*>(base + off_scal);
   plan->d_partials = reinterpret_cast<float*>(base + off_part);
+  plan->d_wb = reinterpret_cast<float2*>(base + off_wb);
   size_t li = 0;
   for (auto& g : groups)
     for (int ph = 0; ph < 3; ++ph) g.tiles[ph] = reinterpret_cast<int2*>(base + off_lists[li++]);
@@ -367,9 +371,23 @@ struct Call {
   muon_ns_coeffs co;
   int32_t ns_steps;
   int32_t scale_rule;
+  const muon_step_options* opt;  // update variants (MODE_STEP), or null
   float* norms_out;
   hipStream_t stream;
 };
+
+// Scale s of the update from the rule, in binary64 (the device computes the
+// same in update_scale).
+double rule_scale(int rule, int64_t rows, int64_t cols) {
+  if (rule == MUON_SCALE_SQRT_ASPECT) return std::sqrt(std::max(1.0, double(rows) / double(cols)));
+  if (rule == MUON_SCALE_RMS_MATCH) return 0.2 * std::sqrt(double(std::max(rows, cols)));
+  return 1.0;
+}
+
+// Whether the write-back takes per-matrix scalars from the host.
+bool per_matrix_wb(const Call& c) {
+  return c.opt && (c.opt->weight_decay != 0.f || c.opt->lr_per_matrix || c.opt->scale_per_matrix);
+}
 
 muon_status validate_call(const Call& c) {
   if (c.count < 0 || c.count > MAX_COUNT)
@@ -384,6 +402,24 @@ muon_status validate_call(const Call& c) {
     if (c.nesterov != 0 && c.nesterov != 1) return fail(MUON_ERR_INVALID_ARGUMENT, "nesterov must be 0 or 1");
     if (c.scale_rule < MUON_SCALE_NONE || c.scale_rule > MUON_SCALE_RMS_MATCH)
       return fail(MUON_ERR_INVALID_ARGUMENT, "unknown scale_rule %d", c.scale_rule);
+  }
+  if (c.opt && c.mode == MODE_STEP) {
+    const muon_step_options& o = *c.opt;
+    if (!std::isfinite(o.weight_decay) || o.weight_decay < 0.f)
+      return fail(MUON_ERR_INVALID_ARGUMENT, "weight_decay must be finite and >= 0");
+    if (o.momentum_kind != MUON_MOMENTUM_HEAVY_BALL && o.momentum_kind != MUON_MOMENTUM_EMA)
+      return fail(MUON_ERR_INVALID_ARGUMENT, "unknown momentum_kind %d", o.momentum_kind);
+    if (o.ns_schedule)
+      for (int32_t k = 0; k < c.ns_steps; ++k)
+        if (!std::isfinite(o.ns_schedule[k].a) || !std::isfinite(o.ns_schedule[k].b) ||
+            !std::isfinite(o.ns_schedule[k].c))
+          return fail(MUON_ERR_INVALID_ARGUMENT, "ns_schedule[%d] is not finite", k);
+    for (int32_t i = 0; i < c.count; ++i) {
+      if (o.lr_per_matrix && !std::isfinite(o.lr_per_matrix[i]))
+        return fail(MUON_ERR_INVALID_ARGUMENT, "lr_per_matrix[%d] is not finite", i);
+      if (o.scale_per_matrix && !std::isfinite(o.scale_per_matrix[i]))
+        return fail(MUON_ERR_INVALID_ARGUMENT, "scale_per_matrix[%d] is not finite", i);
+    }
   }
   if (c.mode == MODE_NS && !c.updates) return fail(MUON_ERR_INVALID_ARGUMENT, "x_out is NULL");
   if (c.mode == MODE_NORMS && !c.norms_out) return fail(MUON_ERR_INVALID_ARGUMENT, "norms_out is NULL");
@@ -574,10 +610,28 @@ muon_status run(const Call& c) {
   // ------------------------------------------------------------ launches
   hipError_t e = hipSuccess;
   const int kmode = c.mode == MODE_STEP ? 0 : (c.mode == MODE_NS ? 1 : 2);
-  e = timed(MUON_KC_MOMENTUM, c.stream, [&] {
-    return launch_momentum(plan->d_mats, plan->d_etile_off, plan->count, plan->total_etiles, c.beta,
-                           c.nesterov, kmode, plan->d_partials, c.stream);
-  });
+  const int32_t ema = (c.mode == MODE_STEP && c.opt && c.opt->momentum_kind == MUON_MOMENTUM_EMA) ? 1 : 0;
+  // per-matrix write-back scalars t_i = fl32(lr_i * s_i), d_i = fl32(1 - fl32(lr_i * wd))
+  const float2* wb = nullptr;
+  if (c.mode == MODE_STEP && per_matrix_wb(c)) {
+    std::vector<float2> hwb(size_t(c.count));
+    for (int32_t i = 0; i < c.count; ++i) {
+      const float lr_i = c.opt->lr_per_matrix ? c.opt->lr_per_matrix[i] : c.lr;
+      const double s_i = c.opt->scale_per_matrix ? double(c.opt->scale_per_matrix[i])
+                                                 : rule_scale(c.scale_rule, c.shapes[i].rows, c.shapes[i].cols);
+      const float decay = c.opt->weight_decay;
+      const float lw = lr_i * decay;
+      hwb[size_t(i)] = make_float2(float(double(lr_i) * s_i), decay != 0.f ? 1.f - lw : 1.f);
+    }
+    // pageable source: the copy takes the data before the call returns
+    e = hipMemcpyAsync(plan->d_wb, hwb.data(), sizeof(float2) * size_t(c.count), hipMemcpyHostToDevice, c.stream);
+    wb = plan->d_wb;
+  }
+  if (e == hipSuccess)
+    e = timed(MUON_KC_MOMENTUM, c.stream, [&] {
+      return launch_momentum(plan->d_mats, plan->d_etile_off, plan->count, plan->total_etiles, c.beta,
+                             c.nesterov, ema, kmode, plan->d_partials, c.stream);
+    });
   if (e == hipSuccess)
     e = timed(MUON_KC_NORM, c.stream, [&] {
       return launch_norm_finalize(plan->d_etile_off, plan->count, plan->d_partials, plan->d_scal,
@@ -587,14 +641,16 @@ muon_status run(const Call& c) {
     if (c.ns_steps == 0) {
       e = timed(MUON_KC_WRITEBACK, c.stream, [&] {
         return launch_writeback_direct(plan->d_mats, plan->d_etile_off, plan->count, plan->total_etiles,
-                                       plan->d_scal, c.lr, c.scale_rule, c.stream);
+                                       plan->d_scal, c.lr, c.scale_rule, wb, c.stream);
       });
     } else {
       for (int it = 0; it < c.ns_steps && e == hipSuccess; ++it) {
+        const muon_ns_coeffs co = (c.opt && c.opt->ns_schedule) ? c.opt->ns_schedule[it] : c.co;
         PhaseArgs pa;
-        pa.a = c.co.a;
-        pa.b = c.co.b;
-        pa.c = c.co.c;
+        pa.a = co.a;
+        pa.b = co.b;
+        pa.c = co.c;
+        pa.wb = wb;
         pa.lr = c.lr;
         pa.cur = it & 1;
         pa.first = it == 0;
@@ -603,7 +659,7 @@ muon_status run(const Call& c) {
         pa.cus_per_xcd = ds.cus_per_xcd;
         for (const auto& g : plan->groups) {
           for (int ph = 0; ph < 3 && e == hipSuccess; ++ph) {
-            if (ph == PH_POLY && c.co.c == 0.f) continue;  // GRAM already formed B = b A
+            if (ph == PH_POLY && co.c == 0.f) continue;  // GRAM already formed B = b A
             pa.per_xcd = g.per_xcd[ph];
             e = timed(MUON_KC_GRAM + ph, c.stream, [&] {
               return launch_ns_phase(g.prec, ph, plan->d_mats, plan->d_scal, g.tiles[ph], pa, c.stream);
@@ -651,6 +707,30 @@ muon_status muon_step_batched_ex(void* const* params, const void* const* grads, 
   c.co = ns_coeffs;
   c.ns_steps = ns_steps;
   c.scale_rule = scale_rule;
+  c.stream = reinterpret_cast<hipStream_t>(stream);
+  return run(c);
+}
+
+muon_status muon_step_batched_v2(void* const* params, const void* const* grads, void* const* momenta,
+                                 const muon_matrix_desc* shapes, int32_t count, float lr, float beta,
+                                 int32_t nesterov, muon_ns_coeffs ns_coeffs, int32_t ns_steps,
+                                 int32_t scale_rule, const muon_step_options* options,
+                                 float* const* updates_out, void* stream) {
+  Call c{};
+  c.mode = MODE_STEP;
+  c.params = params;
+  c.grads = grads;
+  c.momenta = momenta;
+  c.updates = updates_out;
+  c.shapes = shapes;
+  c.count = count;
+  c.lr = lr;
+  c.beta = beta;
+  c.nesterov = nesterov;
+  c.co = ns_coeffs;
+  c.ns_steps = ns_steps;
+  c.scale_rule = scale_rule;
+  c.opt = options;
   c.stream = reinterpret_cast<hipStream_t>(stream);
   return run(c);
 }

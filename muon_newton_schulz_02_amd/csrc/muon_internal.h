@@ -59,6 +59,7 @@ struct PhaseArgs {
   int32_t scale_rule;
   int32_t per_xcd;        // tile-list entries per XCD
   int32_t cus_per_xcd;    // compute units per XCD (persistent grid size)
+  const float2* wb;       // per matrix {t = fl32(lr*s), decay d}, or null: t from lr and the rule, d = 1
 };
 
 // Per-matrix scalars written by the norm finalize kernel.
@@ -71,13 +72,13 @@ struct MatScal {
 
 // Launchers (defined in the .hip files).  All enqueue on `stream`.
 hipError_t launch_momentum(const MatDev* mats, const int32_t* etile_off, int32_t count,
-                           int64_t total_tiles, float beta, int32_t nesterov, int32_t mode,
+                           int64_t total_tiles, float beta, int32_t nesterov, int32_t ema, int32_t mode,
                            float* partials, hipStream_t stream);
 hipError_t launch_norm_finalize(const int32_t* etile_off, int32_t count, const float* partials,
                                 MatScal* scal, float* norms_out, hipStream_t stream);
 hipError_t launch_writeback_direct(const MatDev* mats, const int32_t* etile_off, int32_t count,
                                    int64_t total_tiles, const MatScal* scal, float lr,
-                                   int32_t scale_rule, hipStream_t stream);
+                                   int32_t scale_rule, const float2* wb, hipStream_t stream);
 enum Phase : int { PH_GRAM = 0, PH_POLY = 1, PH_COMB = 2 };
 hipError_t launch_ns_phase(int prec, int phase, const MatDev* mats, const MatScal* scal,
                            const int2* tiles, const PhaseArgs& args, hipStream_t stream);

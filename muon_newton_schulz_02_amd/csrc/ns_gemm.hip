@@ -129,16 +129,18 @@ __device__ __forceinline__ void st4(void* base, int64_t plane, int64_t idx, cons
   }
 }
 
-// W[row][col] <- rnd(W - t*o), and the optional binary32 export of o.
-__device__ __forceinline__ void write_back1(const MatDev& md, int row, int col, float o, float t) {
+// W[row][col] <- rnd(W*d - t*o) (each operation rounded to binary32; d = 1
+// without weight decay, and W*1 = W exactly), and the optional binary32
+// export of o.
+__device__ __forceinline__ void write_back1(const MatDev& md, int row, int col, float o, float t, float d) {
   if (md.param) {
     const int64_t pi = int64_t(row) * md.ld_param + col;
     if (md.param_bf16) {
       auto pw = gmem(reinterpret_cast<uint16_t*>(md.param) + pi);
-      *pw = float_to_bf16_bits(bf16_bits_to_float(*pw) - t * o);
+      *pw = float_to_bf16_bits(bf16_bits_to_float(*pw) * d - t * o);
     } else {
       auto pw = gmem(reinterpret_cast<float*>(md.param) + pi);
-      *pw = *pw - t * o;
+      *pw = *pw * d - t * o;
     }
   }
   if (md.upd) *gmem(md.upd + int64_t(row) * md.ld_upd + col) = o;
@@ -148,7 +150,7 @@ __device__ __forceinline__ void write_back1(const MatDev& md, int row, int col, 
 // columns below ncols only.  wvec_ok promises 16-byte aligned rows.
 template <int NE>
 __device__ __forceinline__ void write_back_n(const MatDev& md, int row, int c0, int ncols, const float* o,
-                                             float t) {
+                                             float t, float d) {
   const int cnt = ncols - c0;
   if (cnt <= 0) return;
   if (cnt >= NE && md.wvec_ok) {
@@ -167,7 +169,7 @@ __device__ __forceinline__ void write_back_n(const MatDev& md, int row, int c0, 
 #pragma unroll
         for (int e = 0; e < NE / 2; ++e) {
           const float w0 = bf16_bits_to_float(raw[e] & 0xFFFFu), w1 = bf16_bits_to_float(raw[e] >> 16);
-          raw[e] = float2_to_bf16x2_bits(w0 - t * o[2 * e], w1 - t * o[2 * e + 1]);
+          raw[e] = float2_to_bf16x2_bits(w0 * d - t * o[2 * e], w1 * d - t * o[2 * e + 1]);
         }
         if constexpr (NE == 8) {
           *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(pw) = u32x4{raw[0], raw[1], raw[2], raw[3]};
@@ -180,7 +182,7 @@ __device__ __forceinline__ void write_back_n(const MatDev& md, int row, int c0, 
         for (int h = 0; h < NE / 4; ++h) {
           f32x4 w = pw[h];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = w[e] - t * o[4 * h + e];
+          for (int e = 0; e < 4; ++e) w[e] = w[e] * d - t * o[4 * h + e];
           pw[h] = w;
         }
       }
@@ -198,7 +200,7 @@ __device__ __forceinline__ void write_back_n(const MatDev& md, int row, int c0, 
     }
     return;
   }
-  for (int e = 0; e < NE && e < cnt; ++e) write_back1(md, row, c0 + e, o[e], t);
+  for (int e = 0; e < NE && e < cnt; ++e) write_back1(md, row, c0 + e, o[e], t, d);
 }
 
 // Read-modify-write of PER 8-element runs of W per thread (run k: chunk
@@ -209,7 +211,7 @@ __device__ __forceinline__ void write_back_n(const MatDev& md, int row, int c0, 
 // their latencies overlap (a load is not moved above an earlier store to the
 // same array by the compiler).
 template <int PER, int B, int NT, class Run>
-__device__ __forceinline__ void write_back_runs(const MatDev& md, const float* stg, int tid, float t, Run run) {
+__device__ __forceinline__ void write_back_runs(const MatDev& md, const float* stg, int tid, float t, float d, Run run) {
   static_assert(PER % B == 0, "batches");
   const bool fast = md.param != nullptr && md.param_bf16 && md.wvec_ok && md.upd == nullptr;
 #pragma unroll 1
@@ -240,12 +242,12 @@ __device__ __forceinline__ void write_back_runs(const MatDev& md, const float* s
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float w0 = bf16_bits_to_float(w[k][e] & 0xFFFFu), w1 = bf16_bits_to_float(w[k][e] >> 16);
-          raw[e] = float2_to_bf16x2_bits(w0 - t * o[2 * e], w1 - t * o[2 * e + 1]);
+          raw[e] = float2_to_bf16x2_bits(w0 * d - t * o[2 * e], w1 * d - t * o[2 * e + 1]);
         }
         *gmem(reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(md.param) + int64_t(row) * md.ld_param + col)) =
             u32x4{raw[0], raw[1], raw[2], raw[3]};
       } else {
-        write_back_n<8>(md, row, col, ncols, o, t);
+        write_back_n<8>(md, row, col, ncols, o, t, d);
       }
     }
   }
@@ -917,7 +919,10 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
             st4<PREC>(xn, md.plane_X, int64_t(orow + 32 * i) * md.ldx + ocol + 32 * j + 8 * g, v);
           }
     } else {
-      const float t = update_scale(pa.lr, pa.scale_rule, md.rows, md.cols);
+      // t = fl32(lr*s) and the decay factor d: per matrix from the host when
+      // given (per-matrix lr or scale, weight decay), else from lr and the rule
+      const float t = pa.wb ? pa.wb[mat].x : update_scale(pa.lr, pa.scale_rule, md.rows, md.cols);
+      const float d = pa.wb ? pa.wb[mat].y : 1.f;
       if (md.transposed == 0) {
         // W = X': stage the binary32 update through LDS, one row of waves (RP
         // output rows = W rows) per pass, then read-modify-write 8-element
@@ -946,7 +951,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
           const int row_base = ti * BT + pass * RP;
           static_assert((RP * BT / 8) % NT == 0, "runs per thread");
           constexpr int PER = RP * BT / 8 / NT;
-          write_back_runs<PER, (PER >= 4 ? 4 : PER), NT>(md, stg, tid, t,
+          write_back_runs<PER, (PER >= 4 ? 4 : PER), NT>(md, stg, tid, t, d,
                                                          [&](int q, int& so, int& row, int& col, bool& rok, int& ncols) {
             const int rl = q / (BT / 8), c8 = (q % (BT / 8)) * 8;
             so = rl * SPN + c8;
@@ -986,7 +991,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
           const int row_base = ti * BT + pass * RP;
           static_assert((BT * RP / 8) % NT == 0, "runs per thread");
           constexpr int PER = BT * RP / 8 / NT;
-          write_back_runs<PER, (PER >= 4 ? 4 : PER), NT>(md, stg, tid, t,
+          write_back_runs<PER, (PER >= 4 ? 4 : PER), NT>(md, stg, tid, t, d,
                                                          [&](int q, int& so, int& row, int& col, bool& rok, int& ncols) {
             const int cl = q / (RP / 8), r8 = (q % (RP / 8)) * 8;
             so = cl * SPT + r8;

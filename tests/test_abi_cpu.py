@@ -20,7 +20,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = mb.exported_names()
-    assert len(names) == 11
+    assert len(names) == 12
     out = subprocess.run(["nm", "-D", "--defined-only", mb.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert mb.muon_abi_version() == 1
+    assert mb.muon_abi_version() == 2
     assert mb.muon_status_string(mb.MUON_OK) == "MUON_OK"
     assert mb.muon_status_string(mb.MUON_ERR_ALIAS) == "MUON_ERR_ALIAS"
     assert mb.muon_status_string(99) == "MUON_ERR_UNKNOWN"
@@ -103,6 +103,61 @@ def test_descriptor_errors(L, field, value, status):
 def test_scalar_errors(L, kw, status):
     p, g, m = _ptrs(0, 16, 32)
     assert _call(L, [_desc(16, 32)], [p], [g], [m], **kw) == status
+
+
+def _call_v2(L, opt, steps=5, n=1):
+    descs = [_desc(16, 32) for _ in range(n)]
+    ptrs = [_ptrs(i, 16, 32) for i in range(n)]
+    D = (mb.MatrixDesc * n)(*descs)
+    return L.muon_step_batched_v2(mb._ptr_array([p for p, _, _ in ptrs]), mb._ptr_array([g for _, g, _ in ptrs]),
+                                  mb._ptr_array([m for _, _, m in ptrs]), D, n, 0.02, 0.95, 1,
+                                  mb.NsCoeffs(3.4445, -4.775, 2.0315), steps, 0, opt, None, None)
+
+
+def _opt(**kw):
+    o = mb.StepOptions()
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def _floats(*v):
+    arr = (ctypes.c_float * len(v))(*v)
+    return ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)), arr
+
+
+@pytest.mark.parametrize("case", ["kind", "wd_neg", "wd_nan", "schedule_nan", "lr_nan", "scale_inf"])
+def test_option_errors(L, case):
+    keep = []
+    if case == "kind":
+        o = _opt(momentum_kind=2)
+    elif case == "wd_neg":
+        o = _opt(weight_decay=-0.1)
+    elif case == "wd_nan":
+        o = _opt(weight_decay=float("nan"))
+    elif case == "schedule_nan":
+        sched = (mb.NsCoeffs * 5)(*([mb.NsCoeffs(3.4445, -4.775, 2.0315)] * 4 + [mb.NsCoeffs(float("nan"), 0, 0)]))
+        keep.append(sched)
+        o = _opt(ns_schedule=ctypes.cast(sched, ctypes.POINTER(mb.NsCoeffs)))
+    elif case == "lr_nan":
+        ptr, arr = _floats(0.02, float("nan"))
+        keep.append(arr)
+        o = _opt(lr_per_matrix=ptr)
+    else:
+        ptr, arr = _floats(1.0, float("inf"))
+        keep.append(arr)
+        o = _opt(scale_per_matrix=ptr)
+    assert _call_v2(L, ctypes.byref(o), n=2) == mb.MUON_ERR_INVALID_ARGUMENT
+    assert mb.muon_last_error() != ""
+
+
+def test_option_schedule_only_read_for_its_steps(L):
+    # a schedule of 2 valid triples with ns_steps = 2 passes validation (the
+    # call then fails only for want of a GPU, or runs on one)
+    sched = (mb.NsCoeffs * 2)(mb.NsCoeffs(3.4445, -4.775, 2.0315), mb.NsCoeffs(1.5, -0.5, 0.0))
+    o = _opt(ns_schedule=ctypes.cast(sched, ctypes.POINTER(mb.NsCoeffs)), weight_decay=0.1, momentum_kind=1)
+    assert _call_v2(L, ctypes.byref(o), steps=2) != mb.MUON_ERR_INVALID_ARGUMENT
+    assert _call_v2(L, None) != mb.MUON_ERR_INVALID_ARGUMENT
 
 
 def test_null_and_alignment(L):
