@@ -41,13 +41,13 @@ named R<n> below and listed with its reason in the design notes.
 
 Update variants (the pages describe none of them; they are the forms
 commonly used with Muon, offered as options):
-  R8  EMA momentum: M <- beta*M + (1-beta)*g, with (1-beta) rounded to
+  R14 EMA momentum: M <- beta*M + (1-beta)*g, with (1-beta) rounded to
       binary32 and each product and sum rounded once; its Nesterov
       direction is U = (1-beta)*g + beta*M_new.
-  R9  a Newton-Schulz schedule: step k uses its own triple (a_k, b_k, c_k).
-  R10 decoupled weight decay: W <- rnd(fl32(fl32(W*d) - fl32(t*O))) with
+  R15 a Newton-Schulz schedule: step k uses its own triple (a_k, b_k, c_k).
+  R16 decoupled weight decay: W <- rnd(fl32(fl32(W*d) - fl32(t*O))) with
       d = fl32(1 - fl32(lr*wd)); wd = 0 gives d = 1 and R6 exactly.
-  R11 a per-matrix learning rate and a per-matrix scale s replace lr and the
+  R17 a per-matrix learning rate and a per-matrix scale s replace lr and the
       scale rule of R6/R7 for that matrix.
 
 Parity of every function here is pinned by tests/test_oracle_pins.py
@@ -108,7 +108,7 @@ MOMENTUM_EMA = 1
 
 
 def momentum(m, g, beta: float, nesterov: bool, kind: int = MOMENTUM_HEAVY_BALL):
-    """Momentum buffer update and the update direction U ([P3]; R1-R3, R8).
+    """Momentum buffer update and the update direction U ([P3]; R1-R3, R14).
 
     m: float32 buffer, g: gradient (bf16 values held in float32, or float32).
     Returns (m_new, u), both float32.  numpy float32 arithmetic rounds each
@@ -155,7 +155,7 @@ def orient(x):
 
 def schedule(coeffs, steps: int) -> list:
     """The triple of each of `steps` steps: one triple for all (a, b, c), or a
-    sequence of `steps` triples (R9)."""
+    sequence of `steps` triples (R15)."""
     c = np.asarray(coeffs, dtype=np.float64)
     if c.shape == (3,):
         return [tuple(float(v) for v in c)] * steps
@@ -169,7 +169,7 @@ def newton_schulz(x0, coeffs, steps: int) -> np.ndarray:
 
     Each step forms the Gram matrix A = X X^T, the polynomial B = b A + c A A
     and the new iterate X <- a X + B X.  All in float64.  `coeffs` is one
-    triple or a schedule of `steps` triples (R9).
+    triple or a schedule of `steps` triples (R15).
     """
     x = np.array(x0, dtype=np.float64)
     for a, b, c in schedule(coeffs, steps):
@@ -199,7 +199,7 @@ def scale_factor(rule: int, rows: int, cols: int) -> float:
 
 def write_back(w, o, lr: float, s: float, param_bf16: bool, weight_decay: float = 0.0) -> np.ndarray:
     """W <- rnd(fl32(fl32(W*d) - fl32(t*O))) with t = fl32(lr*s) and
-    d = fl32(1 - fl32(lr*wd)) (R6, R10; wd = 0 leaves W*d = W exactly).
+    d = fl32(1 - fl32(lr*wd)) (R6, R16; wd = 0 leaves W*d = W exactly).
 
     o is rounded to binary32 first (the update leaves the GPU's epilogue in
     binary32); returns float32 values (bf16-representable when param_bf16).
@@ -235,8 +235,8 @@ def muon_step(w, g, m, *, lr, beta, nesterov, coeffs, steps, scale_rule=SCALE_NO
     same step with the intermediates rounded where a bf16 GPU path stores
     them (see `orthogonalise_bf16_storage`); it is an aid for separating the
     bf16 storage error from other error, not a different method.
-    Variants: momentum_kind (R8), a schedule in `coeffs` (R9), weight_decay
-    (R10), and `scale` replacing the scale rule (R11; `lr` is per matrix
+    Variants: momentum_kind (R14), a schedule in `coeffs` (R15), weight_decay
+    (R16), and `scale` replacing the scale rule (R17; `lr` is per matrix
     already, one matrix per call).
     """
     m_new, u = momentum(m, g, beta, nesterov, momentum_kind)

@@ -407,7 +407,7 @@ def test_lm38_stack_matches_page_heads():
 
 
 # ---------------------------------------------------------------------------
-# update variants (R8-R11)
+# update variants (R14-R17)
 # ---------------------------------------------------------------------------
 
 # an arbitrary five-step schedule of quintic triples (steep first, then milder)
