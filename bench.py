@@ -14,7 +14,9 @@ traffic is the HBM bytes per launch from the rocprofv3 FETCH_SIZE /
 WRITE_SIZE summary under profiles/, reported only while the kernel sources
 hash to the values recorded there (null otherwise).
 The cpu_baseline is the CPU oracle timed on a bounded sample of the same
-workload on this host.
+workload on this host.  The `adamw` object times the other half of the
+hybrid optimizer, AdamW on the d24 parameters that are not transformer
+matrices; it is reported beside the Muon step and not counted in `value`.
 """
 from __future__ import annotations
 
@@ -54,6 +56,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=6,
                     help="layers in the oracle's sample (about 10-15 s of host work for d24)")
+    ap.add_argument("--no-adamw", action="store_true",
+                    help="skip timing the AdamW half of the hybrid optimizer (d24 non-matrix parameters)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device once (a plain copy kernel "
                          "of known size, to scale HBM byte counters)")
@@ -183,6 +187,10 @@ def main():
                 "algorithmic_tflops": round(ns_exec / (ns_ms * 1e-3) / 1e12, 2),
                 "algorithmic_frac": round(ns_exec / (ns_ms * 1e-3) / 1e12 / peak_mfma, 4)}
 
+    adamw = None
+    if not args.no_adamw and args.workload == "d24_bf16":
+        adamw = time_adamw(args, mb, wlm, torch, dev, stream)
+
     # ------------------------------------------------------------ CPU oracle
     cpu = None
     if sample:
@@ -207,9 +215,60 @@ def main():
         "roofline": roofline,
         "ns_chain": ns_chain,
         "kernels": kernels,
+        "adamw": adamw,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def time_adamw(args, mb, wlm, torch, dev, stream):
+    """Time muon_adamw_batched on the d24 AdamW set (the parameters Muon does
+    not take), `args.steps` calls after `args.warmup`, with the step number
+    advancing; reported beside the Muon step, not part of its value."""
+    wl = wlm.adamw_workload()
+    print(f"[bench] generating {wl.name}: {len(wl.specs)} tensors, {wl.elements} elements", file=sys.stderr,
+          flush=True)
+    ps, gs, ms, vs = [], [], [], []
+    for i in range(len(wl.specs)):
+        p, m, v = wlm.adamw_state(wl, i, dev)
+        ps.append(p)
+        ms.append(m)
+        vs.append(v)
+        gs.append(wlm.adamw_gradient(wl, i, 0, dev))
+    aargs = mb.AdamwArgs(ps, gs, ms, vs)
+    kw = dict(lr=wl.lr[0], beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps, lr_per_tensor=wl.lr_per_tensor(),
+              wd_per_tensor=wl.wd_per_tensor(), stream=stream)
+    t = wl.step
+    for _ in range(args.warmup):
+        mb.muon_adamw_batched(aargs, step=t, **kw)
+        t += 1
+    torch.cuda.synchronize()
+    mb.muon_timing_enable(True)
+    mb.muon_timing_read()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        mb.muon_adamw_batched(aargs, step=t, **kw)
+        t += 1
+    stop.record(stream)
+    torch.cuda.synchronize()
+    kern = mb.muon_timing_read()
+    mb.muon_timing_enable(False)
+    ms_call = start.elapsed_time(stop) / args.steps
+    k_ms, k_n = kern["adamw"]
+    avg = k_ms / max(k_n, 1)
+    bpe = 2 * (ps[0].element_size() + 4 + 4) + gs[0].element_size()   # p, m, v read and written; g read
+    alg_bytes = wl.elements * bpe
+    gbs = alg_bytes / (avg * 1e-3) / 1e9
+    print(f"[bench] adamw: {ms_call:.3f} ms/call, kernel {avg:.3f} ms, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    del aargs, ps, gs, ms, vs
+    return {"workload": "d24 non-matrix parameters: lm_head, token embedding and 12 value embeddings "
+                        "(32768x1536 each) + 2 x 24 scalars, bf16 p and g, fp32 moments",
+            "elements": wl.elements, "tensors": len(wl.specs), "ms_per_call": round(ms_call, 4),
+            "kernel_avg_ms": round(avg, 5), "bytes_per_element": bpe, "algorithmic_gb": round(alg_bytes / 1e9, 3),
+            "bound": "hbm", "gbs": round(gbs, 1), "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic("d24_bf16", "adamw")}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ns_gemm_d24_bf16_hbm.md")
@@ -238,9 +297,13 @@ def measured_traffic(workload, kernel):
     if line is None:
         return None
     kv = dict(tok.split("=", 1) for tok in line.split())
-    src = _src_hash("elementwise.hip", "numeric.h", "muon_internal.h") if kernel == "momentum" else \
-        _src_hash("ns_gemm.hip", "numeric.h", "muon_internal.h")
-    if src != kv.get("elementwise_src" if kernel == "momentum" else "gemm_src") or kernel not in kv:
+    if kernel == "momentum":
+        src, key = _src_hash("elementwise.hip", "numeric.h", "muon_internal.h"), "elementwise_src"
+    elif kernel == "adamw":
+        src, key = _src_hash("adamw.hip", "numeric.h", "muon_internal.h"), "adamw_src"
+    else:
+        src, key = _src_hash("ns_gemm.hip", "numeric.h", "muon_internal.h"), "gemm_src"
+    if src != kv.get(key) or kernel not in kv:
         return None
     return float(kv[kernel])
 

@@ -21,8 +21,9 @@
  * table 符号与约定, row "Muon", defines it as an optimizer for matrix
  * parameters that orthogonalises the momentum; "开发者千美元训3.8B模型
  * 击败GPT-2" (aiproducthub.cn), paragraph 影响, says the orthogonalisation
- * is Newton-Schulz and that every non-matrix parameter goes to AdamW (so
- * this ABI accepts 2-D matrices only).  The polynomial form of the
+ * is Newton-Schulz and that every non-matrix parameter goes to AdamW (the
+ * Muon entry points take 2-D matrices; muon_adamw_batched below updates
+ * the other parameters).  The polynomial form of the
  * iteration is the textbook one (N. J. Higham, Functions of Matrices,
  * ch. 8); the momentum form, eps, orientation and scale rules are readings
  * the pages leave open, stated at each declaration below.
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 2
+#define MUON_ABI_VERSION 3
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -202,6 +203,72 @@ muon_status muon_ns_batched(const void* const* x_in, float* const* x_out,
 muon_status muon_frobenius_norms(const void* const* x_in, const muon_matrix_desc* shapes,
                                  int32_t count, float* norms_out, void* stream);
 
+/* ---------------------------------------------------------------------
+ * AdamW for the parameters that are not given to Muon (embeddings, the
+ * output head, scalars): "开发者千美元训3.8B模型 击败GPT-2" (aiproducthub.cn),
+ * paragraph 影响, pairs Muon with AdamW for every other parameter.  The
+ * update is Adam's (D. P. Kingma and J. Ba, "Adam: A Method for Stochastic
+ * Optimization", Algorithm 1) with decoupled weight decay (I. Loshchilov and
+ * F. Hutter, "Decoupled Weight Decay Regularization", Algorithm 2).  Per
+ * element, in binary32 with one rounding per operation, no fused
+ * multiply-add, division and square root correctly rounded:
+ *
+ *   m <- beta1*m + c1*g           c1 = fl32(1 - beta1)
+ *   v <- beta2*v + c2*(g*g)       c2 = fl32(1 - beta2)
+ *   u  = (m / bc1) / (sqrt(v / bc2) + eps)
+ *                                 bc_k = fl32(1 - beta_k^t), beta^t in binary64
+ *   p <- rnd(fl32(p*d) - fl32(lr*u))
+ *                                 d = fl32(1 - fl32(lr*wd)); rnd: to the
+ *                                 parameter type (bfloat16 to nearest-even)
+ * --------------------------------------------------------------------- */
+
+/* One tensor: numel contiguous elements (any shape, flattened).
+ * param_dtype, grad_dtype: MUON_DTYPE_F32 or MUON_DTYPE_BF16; the moment
+ * buffers are binary32.  numel in [0, 2^40]; 0 skips the tensor.          */
+typedef struct muon_adamw_desc {
+  int64_t numel;
+  int32_t param_dtype;
+  int32_t grad_dtype;
+} muon_adamw_desc;
+
+/* Hyperparameters of one AdamW step.
+ * lr            finite learning rate (binary32).
+ * beta1, beta2  in [0, 1).
+ * eps           finite, >= 0 (eps = 0 with v = 0 gives NaN, as the formula).
+ * weight_decay  finite, >= 0.
+ * step          t >= 1, the number of this step (bias corrections).
+ * lr_per_tensor NULL, or a host array of `count` finite rates replacing lr.
+ * wd_per_tensor NULL, or a host array of `count` finite decays >= 0
+ *               replacing weight_decay.
+ * The arrays are read during the call and not kept.                        */
+typedef struct muon_adamw_hparams {
+  float lr;
+  float beta1, beta2;
+  float eps;
+  float weight_decay;
+  int64_t step;
+  const float* lr_per_tensor;
+  const float* wd_per_tensor;
+} muon_adamw_hparams;
+
+/* One AdamW step on `count` tensors in one launch.
+ *
+ * params[i]      numel elements (param_dtype), updated in place.
+ * grads[i]       numel elements (grad_dtype), read only.
+ * exp_avg[i]     numel binary32 first moments m, updated in place.
+ * exp_avg_sq[i]  numel binary32 second moments v, updated in place.
+ * Pointers must be aligned to their element size; 16-byte alignment of
+ * all four (8-byte for bfloat16) takes the vector path.  Every result is
+ * bit-exact to the formula above.  count == 0 is a no-op returning MUON_OK.
+ * Per-tensor rates add one small host-to-device copy (8 bytes per tensor)
+ * on `stream`.  Errors: INVALID_ARGUMENT (null pointer, bad size or
+ * hyperparameter), UNSUPPORTED (dtype, alignment, size cap), ALIAS (a
+ * written buffer overlaps any other buffer), OUT_OF_MEMORY, HIP.          */
+muon_status muon_adamw_batched(void* const* params, const void* const* grads,
+                               float* const* exp_avg, float* const* exp_avg_sq,
+                               const muon_adamw_desc* tensors, int32_t count,
+                               const muon_adamw_hparams* hparams, void* stream);
+
 /* Kernel classes of the launch sequence, for muon_timing_read.            */
 typedef enum muon_kernel_class {
   MUON_KC_MOMENTUM = 0,  /* momentum / Nesterov + U copies + norm partials  */
@@ -210,7 +277,8 @@ typedef enum muon_kernel_class {
   MUON_KC_POLY = 3,      /* B = b A + c A A                                */
   MUON_KC_COMBINE = 4,   /* X = a X + B X (last step: write-back)          */
   MUON_KC_WRITEBACK = 5, /* write-back when ns_steps == 0                  */
-  MUON_KC_COUNT = 6
+  MUON_KC_ADAMW = 6,     /* muon_adamw_batched                             */
+  MUON_KC_COUNT = 7
 } muon_kernel_class;
 
 /* Measurement hook.  While enabled (enable = 1), every launch the library

@@ -73,6 +73,20 @@ class StepOptions(ctypes.Structure):
     ]
 
 
+class AdamwDesc(ctypes.Structure):
+    """muon_adamw_desc (include/muon.h)."""
+    _fields_ = [("numel", ctypes.c_int64), ("param_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32)]
+
+
+class AdamwHparams(ctypes.Structure):
+    """muon_adamw_hparams (include/muon.h)."""
+    _fields_ = [
+        ("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+        ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int64),
+        ("lr_per_tensor", ctypes.POINTER(ctypes.c_float)), ("wd_per_tensor", ctypes.POINTER(ctypes.c_float)),
+    ]
+
+
 _VP = ctypes.c_void_p
 _PP = ctypes.POINTER(ctypes.c_void_p)
 _lib = None
@@ -102,6 +116,9 @@ def lib() -> ctypes.CDLL:
     L.muon_step_batched_v2.argtypes = [_PP, _PP, _PP, D, i32, f32, f32, i32, NsCoeffs, i32, i32,
                                        ctypes.POINTER(StepOptions), _PP, _VP]
     L.muon_step_batched_v2.restype = i32
+    L.muon_adamw_batched.argtypes = [_PP, _PP, _PP, _PP, ctypes.POINTER(AdamwDesc), i32,
+                                     ctypes.POINTER(AdamwHparams), _VP]
+    L.muon_adamw_batched.restype = i32
     L.muon_ns_batched.argtypes = [_PP, _PP, D, i32, NsCoeffs, i32, _VP]
     L.muon_ns_batched.restype = i32
     L.muon_frobenius_norms.argtypes = [_PP, D, i32, _VP, _VP]
@@ -147,7 +164,7 @@ def muon_release_workspace() -> None:
     _check(lib().muon_release_workspace())
 
 
-KERNEL_CLASSES = ("momentum", "norm", "gram", "poly", "combine", "writeback")
+KERNEL_CLASSES = ("momentum", "norm", "gram", "poly", "combine", "writeback", "adamw")
 
 
 def muon_timing_enable(enable: bool) -> None:
@@ -300,6 +317,57 @@ def muon_step_batched_v2(params, grads=None, momenta=None, *, lr, beta, nesterov
 def muon_step_batched_ex(params, grads, momenta, updates_out, **kw):
     """muon_step_batched that also exports the binary32 update O of each matrix."""
     return muon_step_batched(params, grads, momenta, updates_out=updates_out, **kw)
+
+
+class AdamwArgs:
+    """Pointer and descriptor arrays of a fixed list of AdamW tensors, built
+    once and reused by every call on the same tensors."""
+
+    def __init__(self, params, grads, exp_avg, exp_avg_sq):
+        n = len(params)
+        if len(grads) != n or len(exp_avg) != n or len(exp_avg_sq) != n:
+            raise ValueError("params, grads, exp_avg and exp_avg_sq must have the same length")
+        self.count = n
+        self.descs = (AdamwDesc * max(n, 1))()
+        for i, (p, g, m, v) in enumerate(zip(params, grads, exp_avg, exp_avg_sq)):
+            for name, t in (("param", p), ("grad", g), ("exp_avg", m), ("exp_avg_sq", v)):
+                if not t.is_contiguous():
+                    raise ValueError(f"tensor {i}: {name} must be contiguous")
+            if not (p.numel() == g.numel() == m.numel() == v.numel()):
+                raise ValueError(f"tensor {i}: param, grad and moments differ in size")
+            if m.dtype != torch.float32 or v.dtype != torch.float32:
+                raise TypeError(f"tensor {i}: the moments must be float32")
+            d = self.descs[i]
+            d.numel = int(p.numel())
+            d.param_dtype = dtype_code(p.dtype)
+            d.grad_dtype = dtype_code(g.dtype)
+        self.params = _ptr_array([t.data_ptr() for t in params])
+        self.grads = _ptr_array([t.data_ptr() for t in grads])
+        self.exp_avg = _ptr_array([t.data_ptr() for t in exp_avg])
+        self.exp_avg_sq = _ptr_array([t.data_ptr() for t in exp_avg_sq])
+        self._keep = (params, grads, exp_avg, exp_avg_sq)
+
+
+def muon_adamw_batched(params, grads=None, exp_avg=None, exp_avg_sq=None, *, lr, beta1, beta2, eps,
+                       weight_decay=0.0, step, lr_per_tensor=None, wd_per_tensor=None, stream=None):
+    """One AdamW step on lists of contiguous tensors (or on a prebuilt AdamwArgs)."""
+    args = params if isinstance(params, AdamwArgs) else AdamwArgs(params, grads, exp_avg, exp_avg_sq)
+    hp = AdamwHparams()
+    hp.lr, hp.beta1, hp.beta2, hp.eps = float(lr), float(beta1), float(beta2), float(eps)
+    hp.weight_decay = float(weight_decay)
+    hp.step = int(step)
+    keep = []
+    for name, vals in (("lr_per_tensor", lr_per_tensor), ("wd_per_tensor", wd_per_tensor)):
+        if vals is not None:
+            if len(vals) != args.count:
+                raise ValueError(f"{name} needs one value per tensor")
+            arr = (ctypes.c_float * max(len(vals), 1))(*[float(v) for v in vals])
+            keep.append(arr)
+            setattr(hp, name, ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)))
+    status = lib().muon_adamw_batched(args.params, args.grads, args.exp_avg, args.exp_avg_sq, args.descs,
+                                      args.count, ctypes.byref(hp), _stream_handle(stream))
+    del keep
+    _check(status)
 
 
 def muon_ns_batched(x_in, x_out, *, ns_coeffs, ns_steps, precision=NS_BF16, stream=None):

@@ -1,0 +1,173 @@
+// AdamW for the parameters the hybrid optimizer does not give to Muon
+// (embeddings, the output head, scalars): "开发者千美元训3.8B模型 击败GPT-2"
+// (aiproducthub.cn), paragraph 影响, names the pairing; the update is Adam's
+// (D. P. Kingma and J. Ba, "Adam: A Method for Stochastic Optimization",
+// Algorithm 1) with the weight decay decoupled from the gradient
+// (I. Loshchilov and F. Hutter, "Decoupled Weight Decay Regularization",
+// Algorithm 2).
+//
+// Per element, in binary32 with one rounding per operation, no fused
+// multiply-add, division and square root correctly rounded:
+//   m <- b1*m + c1*g ; v <- b2*v + c2*(g*g)
+//   u  = (m / bc1) / (sqrt(v / bc2) + eps)
+//   p <- rnd(p*d - lr*u)
+// with c1, c2, bc1, bc2, d binary32 constants formed on the host.
+//
+// One grid covers every tensor of the call: tensor i owns the workgroups
+// [chunk_off[i], chunk_off[i+1]), each of which updates CHUNK consecutive
+// elements.  The work is HBM-bound (22 bytes per element for bf16 p and g);
+// each thread keeps four groups of four elements in flight, and every load
+// and store instruction of a wave covers one contiguous run of memory.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "muon_internal.h"
+#include "numeric.h"
+
+#pragma clang fp contract(off)
+
+namespace muon {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+namespace {
+
+constexpr int ADAMW_THREADS = 256;
+constexpr int ADAMW_GROUPS = ADAMW_CHUNK / (4 * ADAMW_THREADS);
+static_assert(ADAMW_GROUPS * 4 * ADAMW_THREADS == ADAMW_CHUNK, "chunk is a whole number of groups");
+
+__device__ inline int find_tensor(const int32_t* __restrict__ off, int count, int chunk) {
+  int lo = 0, hi = count;  // off[lo] <= chunk < off[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= chunk) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ inline void adamw_elem(float& p, float g, float& m, float& v, float lr, float d, const AdamwConsts& k) {
+  m = k.b1 * m + k.c1 * g;
+  v = k.b2 * v + k.c2 * (g * g);
+  // '/' and __builtin_sqrtf are correctly rounded for binary32 in HIP
+  // device code unless relaxed by compiler flags, which this library does
+  // not pass
+  const float mh = m / k.bc1;
+  const float vh = v / k.bc2;
+  const float u = mh / (__builtin_sqrtf(vh) + k.eps);
+  p = p * d - lr * u;
+}
+
+template <bool PBF>
+__device__ inline void load4_param(const void* base, int64_t e, float p[4]) {
+  if (PBF) {
+    const u32x2 raw = *gmem(reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(base) + e));
+    p[0] = bf16_bits_to_float(raw[0]);
+    p[1] = bf16_bits_to_float(raw[0] >> 16);
+    p[2] = bf16_bits_to_float(raw[1]);
+    p[3] = bf16_bits_to_float(raw[1] >> 16);
+  } else {
+    const f32x4 raw = *gmem(reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + e));
+    p[0] = raw[0]; p[1] = raw[1]; p[2] = raw[2]; p[3] = raw[3];
+  }
+}
+
+__device__ inline float load1(const void* base, int64_t e, bool bf) {
+  return bf ? bf16_bits_to_float(gmem(reinterpret_cast<const uint16_t*>(base))[e])
+            : gmem(reinterpret_cast<const float*>(base))[e];
+}
+
+// One workgroup's chunk of a tensor whose parameter and gradient types are
+// PBF and GBF (true: bfloat16).
+template <bool PBF, bool GBF>
+__device__ inline void adamw_chunk(const AdamwTensor& t, int64_t base, float lr, float d, const AdamwConsts& k) {
+  const int tid = threadIdx.x;
+  const int64_t n = t.numel;
+  float p[ADAMW_GROUPS][4], g[ADAMW_GROUPS][4], m[ADAMW_GROUPS][4], v[ADAMW_GROUPS][4];
+  bool full[ADAMW_GROUPS];
+#pragma unroll
+  for (int q = 0; q < ADAMW_GROUPS; ++q) {
+    const int64_t e = base + int64_t(q) * (4 * ADAMW_THREADS) + 4 * tid;
+    full[q] = t.vec_ok && e + 4 <= n;
+    if (full[q]) {
+      load4_param<PBF>(t.p, e, p[q]);
+      load4_param<GBF>(t.g, e, g[q]);
+      const f32x4 mr = *gmem(reinterpret_cast<const f32x4*>(t.m + e));
+      const f32x4 vr = *gmem(reinterpret_cast<const f32x4*>(t.v + e));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { m[q][j] = mr[j]; v[q][j] = vr[j]; }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool in = e + j < n;
+        p[q][j] = in ? load1(t.p, e + j, PBF) : 0.f;
+        g[q][j] = in ? load1(t.g, e + j, GBF) : 0.f;
+        m[q][j] = in ? gmem(t.m)[e + j] : 0.f;
+        v[q][j] = in ? gmem(t.v)[e + j] : 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < ADAMW_GROUPS; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) adamw_elem(p[q][j], g[q][j], m[q][j], v[q][j], lr, d, k);
+#pragma unroll
+  for (int q = 0; q < ADAMW_GROUPS; ++q) {
+    const int64_t e = base + int64_t(q) * (4 * ADAMW_THREADS) + 4 * tid;
+    if (full[q]) {
+      if (PBF) {
+        const uint32_t h01 = float2_to_bf16x2_bits(p[q][0], p[q][1]);
+        const uint32_t h23 = float2_to_bf16x2_bits(p[q][2], p[q][3]);
+        *gmem(reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(t.p) + e)) = u32x2{h01, h23};
+      } else {
+        *gmem(reinterpret_cast<f32x4*>(reinterpret_cast<float*>(t.p) + e)) =
+            f32x4{p[q][0], p[q][1], p[q][2], p[q][3]};
+      }
+      *gmem(reinterpret_cast<f32x4*>(t.m + e)) = f32x4{m[q][0], m[q][1], m[q][2], m[q][3]};
+      *gmem(reinterpret_cast<f32x4*>(t.v + e)) = f32x4{v[q][0], v[q][1], v[q][2], v[q][3]};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (e + j >= n) continue;
+        if (PBF) gmem(reinterpret_cast<uint16_t*>(t.p))[e + j] = float_to_bf16_bits(p[q][j]);
+        else gmem(reinterpret_cast<float*>(t.p))[e + j] = p[q][j];
+        gmem(t.m)[e + j] = m[q][j];
+        gmem(t.v)[e + j] = v[q][j];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(ADAMW_THREADS) void adamw_kernel(const AdamwTensor* __restrict__ tensors,
+                                                              const int32_t* __restrict__ chunk_off,
+                                                              int32_t count, const float2* __restrict__ rates,
+                                                              float lr, float d, AdamwConsts k) {
+  const int b = blockIdx.x;
+  const int ti = find_tensor(chunk_off, count, b);
+  const AdamwTensor t = tensors[ti];
+  const int64_t base = int64_t(b - chunk_off[ti]) * ADAMW_CHUNK;
+  if (rates) {
+    const float2 r = rates[ti];
+    lr = r.x;
+    d = r.y;
+  }
+  if (t.p_bf16) {
+    if (t.g_bf16) adamw_chunk<true, true>(t, base, lr, d, k);
+    else adamw_chunk<true, false>(t, base, lr, d, k);
+  } else {
+    if (t.g_bf16) adamw_chunk<false, true>(t, base, lr, d, k);
+    else adamw_chunk<false, false>(t, base, lr, d, k);
+  }
+}
+
+hipError_t launch_adamw(const AdamwTensor* tensors, const int32_t* chunk_off, int32_t count, int64_t total_chunks,
+                        const float2* rates, float lr, float d, const AdamwConsts& k, hipStream_t stream) {
+  if (total_chunks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(adamw_kernel, dim3(uint32_t(total_chunks)), dim3(ADAMW_THREADS), 0, stream, tensors, chunk_off,
+                     count, rates, lr, d, k);
+  return hipGetLastError();
+}
+
+}  // namespace muon

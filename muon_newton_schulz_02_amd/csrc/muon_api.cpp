@@ -168,11 +168,26 @@ struct Plan {
   hipEvent_t last_use = nullptr;
 };
 
+// Launch plan of an AdamW call: the device table of its non-empty tensors
+// and their first workgroups.
+struct AdamwPlan {
+  std::vector<uint64_t> key;
+  int32_t count = 0;              // tensors with numel > 0
+  int64_t total_chunks = 0;
+  std::vector<int32_t> kept;      // caller index of each tensor in the table
+  void* dmem = nullptr;
+  AdamwTensor* d_tensors = nullptr;
+  int32_t* d_chunk_off = nullptr;
+  float2* d_rates = nullptr;      // per tensor {lr, d}, filled per call when used
+  hipEvent_t last_use = nullptr;
+};
+
 struct DeviceState {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   int cus_per_xcd = 0;
-  std::list<Plan*> plans;  // most recently used first
+  std::list<Plan*> plans;              // most recently used first
+  std::list<AdamwPlan*> adamw_plans;   // most recently used first
 };
 
 std::mutex g_mu;
@@ -223,9 +238,20 @@ void free_plan(Plan* p) {
   delete p;
 }
 
+void free_adamw_plan(AdamwPlan* p) {
+  if (p->last_use) {
+    hipEventSynchronize(p->last_use);
+    hipEventDestroy(p->last_use);
+  }
+  if (p->dmem) hipFree(p->dmem);
+  delete p;
+}
+
 void drop_plans(DeviceState& ds) {
   for (Plan* p : ds.plans) free_plan(p);
   ds.plans.clear();
+  for (AdamwPlan* p : ds.adamw_plans) free_adamw_plan(p);
+  ds.adamw_plans.clear();
 }
 
 // Split each matrix's tiles over the XCDs: matrices in order, tiles of one
@@ -674,6 +700,229 @@ muon_status run(const Call& c) {
   return MUON_OK;
 }
 
+// ------------------------------------------------------------------ AdamW
+constexpr int64_t MAX_ADAMW_NUMEL = int64_t(1) << 40;
+
+struct AdamwCall {
+  void* const* params;
+  const void* const* grads;
+  float* const* m;
+  float* const* v;
+  const muon_adamw_desc* tensors;
+  int32_t count;
+  const muon_adamw_hparams* hp;
+  hipStream_t stream;
+};
+
+bool finite_f(float x) { return std::isfinite(x); }
+
+muon_status validate_adamw(const AdamwCall& c) {
+  if (c.count < 0 || c.count > MAX_COUNT)
+    return fail(MUON_ERR_INVALID_ARGUMENT, "count %d out of [0, %d]", c.count, MAX_COUNT);
+  if (!c.hp) return fail(MUON_ERR_INVALID_ARGUMENT, "hparams is NULL");
+  const muon_adamw_hparams& h = *c.hp;
+  if (!finite_f(h.lr)) return fail(MUON_ERR_INVALID_ARGUMENT, "lr must be finite");
+  if (!(h.beta1 >= 0.f && h.beta1 < 1.f) || !(h.beta2 >= 0.f && h.beta2 < 1.f))
+    return fail(MUON_ERR_INVALID_ARGUMENT, "beta1 and beta2 must lie in [0, 1)");
+  if (!finite_f(h.eps) || h.eps < 0.f) return fail(MUON_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (!finite_f(h.weight_decay) || h.weight_decay < 0.f)
+    return fail(MUON_ERR_INVALID_ARGUMENT, "weight_decay must be finite and >= 0");
+  if (h.step < 1) return fail(MUON_ERR_INVALID_ARGUMENT, "step must be >= 1 (got %lld)", (long long)h.step);
+  if (c.count == 0) return MUON_OK;
+  if (!c.params || !c.grads || !c.m || !c.v || !c.tensors)
+    return fail(MUON_ERR_INVALID_ARGUMENT, "a pointer array is NULL");
+  for (int32_t i = 0; i < c.count; ++i) {
+    if (h.lr_per_tensor && !finite_f(h.lr_per_tensor[i]))
+      return fail(MUON_ERR_INVALID_ARGUMENT, "tensor %d: lr_per_tensor is not finite", i);
+    if (h.wd_per_tensor && (!finite_f(h.wd_per_tensor[i]) || h.wd_per_tensor[i] < 0.f))
+      return fail(MUON_ERR_INVALID_ARGUMENT, "tensor %d: wd_per_tensor must be finite and >= 0", i);
+  }
+  std::vector<Interval> iv;
+  iv.reserve(size_t(c.count) * 4);
+  int64_t chunks = 0;
+  for (int32_t i = 0; i < c.count; ++i) {
+    const muon_adamw_desc& d = c.tensors[i];
+    if (d.numel < 0 || d.numel > MAX_ADAMW_NUMEL)
+      return fail(d.numel < 0 ? MUON_ERR_INVALID_ARGUMENT : MUON_ERR_UNSUPPORTED,
+                  "tensor %d: numel %lld out of [0, 2^40]", i, (long long)d.numel);
+    if (d.param_dtype != MUON_DTYPE_F32 && d.param_dtype != MUON_DTYPE_BF16)
+      return fail(MUON_ERR_UNSUPPORTED, "tensor %d: param_dtype %d is not F32 or BF16", i, d.param_dtype);
+    if (d.grad_dtype != MUON_DTYPE_F32 && d.grad_dtype != MUON_DTYPE_BF16)
+      return fail(MUON_ERR_UNSUPPORTED, "tensor %d: grad_dtype %d is not F32 or BF16", i, d.grad_dtype);
+    if (d.numel == 0) continue;
+    const int pe = dtype_size(d.param_dtype), ge = dtype_size(d.grad_dtype);
+    muon_status st;
+    if ((st = check_ptr(c.params[i], pe, i, "param")) != MUON_OK) return st;
+    if ((st = check_ptr(c.grads[i], ge, i, "grad")) != MUON_OK) return st;
+    if ((st = check_ptr(c.m[i], 4, i, "exp_avg")) != MUON_OK) return st;
+    if ((st = check_ptr(c.v[i], 4, i, "exp_avg_sq")) != MUON_OK) return st;
+    const uint64_t n = uint64_t(d.numel);
+    auto add = [&](const void* ptr, uint64_t bytes, bool w, const char* what) {
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+      iv.push_back({lo, lo + bytes, w, int(i), what});
+    };
+    add(c.params[i], n * pe, true, "param");
+    add(c.grads[i], n * ge, false, "grad");
+    add(c.m[i], n * 4, true, "exp_avg");
+    add(c.v[i], n * 4, true, "exp_avg_sq");
+    chunks += (d.numel + ADAMW_CHUNK - 1) / ADAMW_CHUNK;
+    if (chunks > int64_t(INT32_MAX))
+      return fail(MUON_ERR_UNSUPPORTED, "more than 2^31 - 1 workgroups of %d elements", ADAMW_CHUNK);
+  }
+  return check_alias_fast(iv);
+}
+
+muon_status build_adamw_plan(AdamwPlan* plan, const AdamwCall& c) {
+  std::vector<AdamwTensor> ht;
+  std::vector<int32_t> off(1, 0);
+  for (int32_t i = 0; i < c.count; ++i) {
+    const muon_adamw_desc& d = c.tensors[i];
+    if (d.numel == 0) continue;
+    AdamwTensor t;
+    memset(&t, 0, sizeof(t));
+    t.p = c.params[i];
+    t.g = c.grads[i];
+    t.m = c.m[i];
+    t.v = c.v[i];
+    t.numel = d.numel;
+    t.p_bf16 = d.param_dtype == MUON_DTYPE_BF16;
+    t.g_bf16 = d.grad_dtype == MUON_DTYPE_BF16;
+    auto al = [](const void* p, int bytes) { return reinterpret_cast<uintptr_t>(p) % uintptr_t(bytes) == 0; };
+    t.vec_ok = al(t.p, 4 * dtype_size(d.param_dtype)) && al(t.g, 4 * dtype_size(d.grad_dtype)) && al(t.m, 16) &&
+               al(t.v, 16);
+    ht.push_back(t);
+    plan->kept.push_back(i);
+    off.push_back(off.back() + int32_t((d.numel + ADAMW_CHUNK - 1) / ADAMW_CHUNK));
+  }
+  const int32_t n = int32_t(ht.size());
+  plan->count = n;
+  plan->total_chunks = off.back();
+  if (n == 0) return MUON_OK;
+  size_t bytes = 0;
+  const size_t o_t = bytes;
+  bytes = align256(bytes + sizeof(AdamwTensor) * n);
+  const size_t o_off = bytes;
+  bytes = align256(bytes + sizeof(int32_t) * (n + 1));
+  const size_t o_rates = bytes;
+  bytes = align256(bytes + sizeof(float2) * n);
+  void* dmem = nullptr;
+  if (hipMalloc(&dmem, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MUON_ERR_OUT_OF_MEMORY, "AdamW plan allocation of %zu bytes failed", bytes);
+  }
+  std::vector<char> host(bytes, 0);
+  memcpy(host.data() + o_t, ht.data(), sizeof(AdamwTensor) * n);
+  memcpy(host.data() + o_off, off.data(), sizeof(int32_t) * (n + 1));
+  if (hipMemcpyAsync(dmem, host.data(), bytes, hipMemcpyHostToDevice, c.stream) != hipSuccess ||
+      hipStreamSynchronize(c.stream) != hipSuccess) {
+    hipFree(dmem);
+    return fail(MUON_ERR_HIP, "AdamW plan upload failed: %s", hipGetErrorString(hipGetLastError()));
+  }
+  char* base = reinterpret_cast<char*>(dmem);
+  plan->dmem = dmem;
+  plan->d_tensors = reinterpret_cast<AdamwTensor*>(base + o_t);
+  plan->d_chunk_off = reinterpret_cast<int32_t*>(base + o_off);
+  plan->d_rates = reinterpret_cast<float2*>(base + o_rates);
+  if (hipEventCreateWithFlags(&plan->last_use, hipEventDisableTiming) != hipSuccess) {
+    plan->last_use = nullptr;
+    return fail(MUON_ERR_HIP, "hipEventCreate failed");
+  }
+  return MUON_OK;
+}
+
+// d = fl32(1 - fl32(lr*wd)), each operation rounded to binary32 (this file
+// is compiled without contraction).
+float decay_factor(float lr, float wd) {
+  const float lw = lr * wd;
+  return 1.0f - lw;
+}
+
+muon_status run_adamw(const AdamwCall& c) {
+  t_last_error.clear();
+  muon_status st = validate_adamw(c);
+  if (st != MUON_OK) return st;
+  bool any = false;
+  for (int32_t i = 0; i < c.count && !any; ++i) any = c.tensors[i].numel > 0;
+  if (!any) return MUON_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MUON_ERR_HIP, "hipGetDevice failed (no HIP device?)");
+  }
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState& ds = g_dev[dev];
+
+  std::vector<uint64_t> key;
+  key.reserve(size_t(c.count) * 6 + 1);
+  key.push_back(uint64_t(c.count));
+  for (int32_t i = 0; i < c.count; ++i) {
+    const muon_adamw_desc& d = c.tensors[i];
+    const bool live = d.numel > 0;
+    key.push_back(uint64_t(d.numel));
+    key.push_back((uint64_t(uint32_t(d.param_dtype)) << 32) | uint32_t(d.grad_dtype));
+    key.push_back(live ? reinterpret_cast<uint64_t>(c.params[i]) : 0);
+    key.push_back(live ? reinterpret_cast<uint64_t>(c.grads[i]) : 0);
+    key.push_back(live ? reinterpret_cast<uint64_t>(c.m[i]) : 0);
+    key.push_back(live ? reinterpret_cast<uint64_t>(c.v[i]) : 0);
+  }
+  AdamwPlan* plan = nullptr;
+  for (auto it = ds.adamw_plans.begin(); it != ds.adamw_plans.end(); ++it) {
+    if ((*it)->key == key) {
+      plan = *it;
+      ds.adamw_plans.erase(it);
+      ds.adamw_plans.push_front(plan);
+      break;
+    }
+  }
+  if (!plan) {
+    plan = new AdamwPlan;
+    plan->key = key;
+    st = build_adamw_plan(plan, c);
+    if (st != MUON_OK) {
+      free_adamw_plan(plan);
+      return st;
+    }
+    ds.adamw_plans.push_front(plan);
+    while (ds.adamw_plans.size() > MAX_PLANS) {
+      free_adamw_plan(ds.adamw_plans.back());
+      ds.adamw_plans.pop_back();
+    }
+  }
+  if (plan->count == 0) return MUON_OK;
+
+  const muon_adamw_hparams& h = *c.hp;
+  AdamwConsts k;
+  k.b1 = h.beta1;
+  k.b2 = h.beta2;
+  k.c1 = 1.0f - h.beta1;
+  k.c2 = 1.0f - h.beta2;
+  k.bc1 = float(1.0 - std::pow(double(h.beta1), double(h.step)));
+  k.bc2 = float(1.0 - std::pow(double(h.beta2), double(h.step)));
+  k.eps = h.eps;
+  const float2* rates = nullptr;
+  hipError_t e = hipSuccess;
+  if (h.lr_per_tensor || h.wd_per_tensor) {
+    std::vector<float2> hr(plan->count);
+    for (int32_t j = 0; j < plan->count; ++j) {
+      const int32_t i = plan->kept[j];
+      const float lr = h.lr_per_tensor ? h.lr_per_tensor[i] : h.lr;
+      const float wd = h.wd_per_tensor ? h.wd_per_tensor[i] : h.weight_decay;
+      hr[j] = make_float2(lr, decay_factor(lr, wd));
+    }
+    e = hipMemcpyAsync(plan->d_rates, hr.data(), sizeof(float2) * hr.size(), hipMemcpyHostToDevice, c.stream);
+    rates = plan->d_rates;
+  }
+  if (e == hipSuccess) {
+    e = timed(MUON_KC_ADAMW, c.stream, [&] {
+      return launch_adamw(plan->d_tensors, plan->d_chunk_off, plan->count, plan->total_chunks, rates, h.lr,
+                          decay_factor(h.lr, h.weight_decay), k, c.stream);
+    });
+  }
+  if (e != hipSuccess) return fail(MUON_ERR_HIP, "AdamW launch failed: %s", hipGetErrorString(e));
+  hipEventRecord(plan->last_use, c.stream);
+  return MUON_OK;
+}
+
 }  // namespace
 }  // namespace muon
 
@@ -760,6 +1009,13 @@ muon_status muon_frobenius_norms(const void* const* x_in, const muon_matrix_desc
   c.norms_out = norms_out;
   c.stream = reinterpret_cast<hipStream_t>(stream);
   return run(c);
+}
+
+muon_status muon_adamw_batched(void* const* params, const void* const* grads, float* const* exp_avg,
+                               float* const* exp_avg_sq, const muon_adamw_desc* tensors, int32_t count,
+                               const muon_adamw_hparams* hparams, void* stream) {
+  AdamwCall c{params, grads, exp_avg, exp_avg_sq, tensors, count, hparams, reinterpret_cast<hipStream_t>(stream)};
+  return run_adamw(c);
 }
 
 muon_status muon_timing_enable(int32_t enable) {

@@ -70,6 +70,28 @@ struct MatScal {
   float pad;
 };
 
+// One tensor of an AdamW call: numel contiguous elements.
+struct AdamwTensor {
+  void* p;                // param dtype, updated in place
+  const void* g;          // grad dtype
+  float* m;               // first moment
+  float* v;               // second moment
+  int64_t numel;
+  int32_t p_bf16, g_bf16;
+  int32_t vec_ok;         // every pointer allows 4-element vector access
+  int32_t pad;
+};
+// Elements per AdamW workgroup.
+constexpr int ADAMW_CHUNK = 4096;
+
+// Binary32 constants of an AdamW step (formed on the host).
+struct AdamwConsts {
+  float b1, b2;           // beta1, beta2
+  float c1, c2;           // fl32(1 - beta)
+  float bc1, bc2;         // fl32(1 - beta^t)
+  float eps;
+};
+
 // Launchers (defined in the .hip files).  All enqueue on `stream`.
 hipError_t launch_momentum(const MatDev* mats, const int32_t* etile_off, int32_t count,
                            int64_t total_tiles, float beta, int32_t nesterov, int32_t ema, int32_t mode,
@@ -80,6 +102,8 @@ hipError_t launch_writeback_direct(const MatDev* mats, const int32_t* etile_off,
                                    int64_t total_tiles, const MatScal* scal, float lr,
                                    int32_t scale_rule, const float2* wb, hipStream_t stream);
 enum Phase : int { PH_GRAM = 0, PH_POLY = 1, PH_COMB = 2 };
+hipError_t launch_adamw(const AdamwTensor* tensors, const int32_t* chunk_off, int32_t count, int64_t total_chunks,
+                        const float2* rates, float lr, float d, const AdamwConsts& k, hipStream_t stream);
 hipError_t launch_ns_phase(int prec, int phase, const MatDev* mats, const MatScal* scal,
                            const int2* tiles, const PhaseArgs& args, hipStream_t stream);
 

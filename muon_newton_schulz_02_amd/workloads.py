@@ -27,6 +27,20 @@ Workloads (shapes from the pages where they give them):
   the orthonormal factors of Student-t(3) matrices; 10 quintic steps on the
   split-bf16 (BF16X3) path.
 
+AdamW inputs (the non-matrix half of the hybrid optimizer):
+
+* ``d24_adamw_bf16``  the d24 parameters that are not transformer matrices.
+  The page gives 1,384,124,976 parameters in all, 679,481,856 in transformer
+  matrices and 50,331,648 in the output head (vocab 32768 x 1536); the
+  remaining 654,311,472 = 13 x 32768 x 1536 + 48 are read as the token
+  embedding plus 12 value embeddings ("Karpathy 只花 $72 就訓練出 GPT-2…",
+  section 那些讓 600 倍加速成為可能的技術, names value embeddings and
+  learnable residual scalars) and two scalars per layer.  The head, the 13
+  embeddings and two 24-element scalar tensors: 704,643,120 elements.
+  bf16 p and g; p ~ N(0, 0.02^2) (scalars 1 + N(0, 0.01^2)), g ~ N(0,
+  1e-3^2), m ~ N(0, 1e-3^2), v = (N(0, 1e-3^2))^2, as at a step well into
+  training (t = 100).
+
 Every tensor is drawn from a torch.Generator seeded from (workload seed,
 matrix index, step, purpose), on the device asked for; CPU and GPU
 generators give different streams, so a test that compares against the
@@ -234,3 +248,69 @@ def random_matrix(rows, cols, seed, dtype=torch.float32, device="cpu", std=1.0):
     """A plain seeded N(0, std^2) matrix for edge-case and shape tests."""
     gen = _gen(device, seed, rows * 131 + cols, 0, 3)
     return _normal((rows, cols), device, gen, std).to(dtype)
+
+
+# ---------------------------------------------------------------- AdamW inputs
+
+@dataclass(frozen=True)
+class AdamwSpec:
+    numel: int
+    name: str
+    group: int      # index into AdamwWorkload.lr / .wd
+
+
+@dataclass
+class AdamwWorkload:
+    name: str
+    specs: list
+    param_dtype: torch.dtype
+    grad_dtype: torch.dtype
+    lr: tuple           # per group: head, embeddings, scalars
+    wd: tuple
+    beta1: float = 0.9
+    beta2: float = 0.95
+    eps: float = 1e-8
+    step: int = 100
+    seed: int = 13
+
+    @property
+    def elements(self) -> int:
+        return sum(s.numel for s in self.specs)
+
+    def lr_per_tensor(self):
+        return [self.lr[s.group] for s in self.specs]
+
+    def wd_per_tensor(self):
+        return [self.wd[s.group] for s in self.specs]
+
+
+def adamw_workload(name: str = "d24_adamw_bf16", vocab: int = 32768, width: int = 1536, layers: int = 24,
+                   value_embeddings: int = 12) -> AdamwWorkload:
+    """The AdamW tensors of the d24 model (see the module docstring); the
+    keyword arguments shrink it for parity runs.  The rates are illustrative
+    (the pages give none): three groups, decay on the head only."""
+    if name != "d24_adamw_bf16":
+        raise KeyError(name)
+    table = vocab * width
+    specs = [AdamwSpec(table, "lm_head", 0), AdamwSpec(table, "wte", 1)]
+    specs += [AdamwSpec(table, f"value_embed{i}", 1) for i in range(value_embeddings)]
+    specs += [AdamwSpec(layers, "resid_lambdas", 2), AdamwSpec(layers, "x0_lambdas", 2)]
+    return AdamwWorkload(name, specs, torch.bfloat16, torch.bfloat16, lr=(4e-3, 2e-2, 5e-3), wd=(0.1, 0.0, 0.0))
+
+
+def adamw_state(wl: AdamwWorkload, idx: int, device="cpu"):
+    """(p, m, v) of tensor `idx`: p in the parameter dtype, m and v float32."""
+    spec = wl.specs[idx]
+    gen = _gen(device, wl.seed, idx, 0, 4)
+    if spec.group == 2:
+        p = _normal((spec.numel,), device, gen, 0.01).add_(1.0)
+    else:
+        p = _normal((spec.numel,), device, gen, 0.02)
+    m = _normal((spec.numel,), device, gen, 1e-3)
+    v = _normal((spec.numel,), device, gen, 1e-3).square_()
+    return p.to(wl.param_dtype), m, v
+
+
+def adamw_gradient(wl: AdamwWorkload, idx: int, step: int = 0, device="cpu") -> torch.Tensor:
+    spec = wl.specs[idx]
+    return _normal((spec.numel,), device, _gen(device, wl.seed, idx, step, 5), 1e-3).to(wl.grad_dtype)

@@ -20,7 +20,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = mb.exported_names()
-    assert len(names) == 12
+    assert len(names) == 13
     out = subprocess.run(["nm", "-D", "--defined-only", mb.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert mb.muon_abi_version() == 2
+    assert mb.muon_abi_version() == 3
     assert mb.muon_status_string(mb.MUON_OK) == "MUON_OK"
     assert mb.muon_status_string(mb.MUON_ERR_ALIAS) == "MUON_ERR_ALIAS"
     assert mb.muon_status_string(99) == "MUON_ERR_UNKNOWN"
@@ -219,3 +219,101 @@ def test_python_binding_rejects_bad_tensors():
         mb.StepArgs([w], [w], [w])
     with pytest.raises(ValueError):
         mb.StepArgs([torch.zeros(4)], [torch.zeros(4)], [torch.zeros(4)])
+
+
+# ------------------------------------------------------------------ AdamW
+
+def _adamw_desc(numel, pdt=mb.DTYPE_BF16, gdt=mb.DTYPE_BF16):
+    d = mb.AdamwDesc()
+    d.numel, d.param_dtype, d.grad_dtype = numel, pdt, gdt
+    return d
+
+
+def _hp(**kw):
+    h = mb.AdamwHparams()
+    h.lr, h.beta1, h.beta2, h.eps, h.weight_decay, h.step = 1e-3, 0.9, 0.95, 1e-8, 0.0, 1
+    keep = []
+    for k, v in kw.items():
+        if k in ("lr_per_tensor", "wd_per_tensor"):
+            ptr, arr = _floats(*v)
+            keep.append(arr)
+            setattr(h, k, ptr)
+        else:
+            setattr(h, k, v)
+    h._keep = keep
+    return h
+
+
+def _adamw_ptrs(i):
+    p = BASE + 0x40000000 + i * 0x10000000
+    return p, p + 0x1000000, p + 0x2000000, p + 0x3000000
+
+
+def _call_adamw(L, descs, ptrs, hp):
+    n = len(descs)
+    D = (mb.AdamwDesc * max(n, 1))(*descs)
+    cols = list(zip(*ptrs)) if ptrs else ([], [], [], [])
+    arrs = [mb._ptr_array(list(c)) for c in cols]
+    return L.muon_adamw_batched(arrs[0], arrs[1], arrs[2], arrs[3], D, n,
+                                None if hp is None else ctypes.byref(hp), None)
+
+
+def test_adamw_count_zero_and_empty_tensors(L):
+    assert _call_adamw(L, [], [], _hp()) == mb.MUON_OK
+    # tensors of zero elements are skipped (their pointers are not read)
+    assert _call_adamw(L, [_adamw_desc(0), _adamw_desc(0)], [(0, 0, 0, 0), (0, 0, 0, 0)], _hp()) == mb.MUON_OK
+    assert _call_adamw(L, [_adamw_desc(16)], [_adamw_ptrs(0)], None) == mb.MUON_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [
+    dict(lr=float("nan")), dict(lr=float("inf")), dict(beta1=1.0), dict(beta2=-0.1), dict(beta1=float("nan")),
+    dict(eps=-1e-8), dict(eps=float("nan")), dict(weight_decay=-0.1), dict(weight_decay=float("inf")),
+    dict(step=0), dict(step=-3), dict(lr_per_tensor=(1e-3, float("nan"))), dict(wd_per_tensor=(0.0, -0.5)),
+])
+def test_adamw_hparam_errors(L, kw):
+    st = _call_adamw(L, [_adamw_desc(16), _adamw_desc(16)], [_adamw_ptrs(0), _adamw_ptrs(1)], _hp(**kw))
+    assert st == mb.MUON_ERR_INVALID_ARGUMENT
+    assert mb.muon_last_error() != ""
+
+
+@pytest.mark.parametrize("desc,status", [
+    (dict(numel=-1), mb.MUON_ERR_INVALID_ARGUMENT),
+    (dict(numel=(1 << 40) + 1), mb.MUON_ERR_UNSUPPORTED),
+    (dict(pdt=7), mb.MUON_ERR_UNSUPPORTED),
+    (dict(gdt=-1), mb.MUON_ERR_UNSUPPORTED),
+])
+def test_adamw_desc_errors(L, desc, status):
+    d = _adamw_desc(desc.get("numel", 16), desc.get("pdt", mb.DTYPE_BF16), desc.get("gdt", mb.DTYPE_BF16))
+    assert _call_adamw(L, [d], [_adamw_ptrs(0)], _hp()) == status
+
+
+def test_adamw_pointer_errors_and_aliases(L):
+    p, g, m, v = _adamw_ptrs(0)
+    d = _adamw_desc(16)
+    assert _call_adamw(L, [d], [(0, g, m, v)], _hp()) == mb.MUON_ERR_INVALID_ARGUMENT
+    assert _call_adamw(L, [d], [(p, g, m, 0)], _hp()) == mb.MUON_ERR_INVALID_ARGUMENT
+    assert _call_adamw(L, [d], [(p + 1, g, m, v)], _hp()) == mb.MUON_ERR_UNSUPPORTED
+    assert _call_adamw(L, [d], [(p, g, m + 2, v)], _hp()) == mb.MUON_ERR_UNSUPPORTED
+    # second moment overlapping the first
+    assert _call_adamw(L, [d], [(p, g, m, m + 60)], _hp()) == mb.MUON_ERR_ALIAS
+    # the gradient of tensor 1 inside the parameter of tensor 0 (bf16: 32 bytes)
+    p1, g1, m1, v1 = _adamw_ptrs(1)
+    assert _call_adamw(L, [d, d], [(p, g, m, v), (p1, p + 30, m1, v1)], _hp()) == mb.MUON_ERR_ALIAS
+    assert _call_adamw(L, [d, d], [(p, g, m, v), (p1, p + 32, m1, v1)], _hp()) != mb.MUON_ERR_ALIAS
+    # two tensors reading one gradient pass validation
+    assert _call_adamw(L, [d, d], [(p, g, m, v), (p1, g, m1, v1)], _hp()) != mb.MUON_ERR_ALIAS
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU error path")
+def test_adamw_valid_call_without_gpu_reports_hip_error(L):
+    assert _call_adamw(L, [_adamw_desc(16)], [_adamw_ptrs(0)], _hp(weight_decay=0.1, step=7)) == mb.MUON_ERR_HIP
+
+
+def test_adamw_binding_rejects_bad_tensors():
+    p = torch.zeros(8, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        mb.AdamwArgs([p], [p], [p.float().half()], [p.float()])
+    with pytest.raises(ValueError):
+        mb.AdamwArgs([p], [p], [torch.zeros(7)], [torch.zeros(8)])
+    with pytest.raises(ValueError):
+        mb.AdamwArgs([torch.zeros(4, 4).t()], [torch.zeros(16)], [torch.zeros(16)], [torch.zeros(16)])

@@ -161,3 +161,20 @@ def test_bf16_parameter_ties_round_to_even():
     assert np.array_equal(p32, np.array([1 + 2 ** -8, 1 + 2 ** -7 + 2 ** -8, 1 + 2 ** -8], np.float32))
     pbf, _, _ = orc.adamw(p, g, z, z, param_bf16=True, **kw)
     assert np.array_equal(pbf, np.array([1.0, 1.0 + 2 ** -6, 1.0], np.float32))
+
+
+def test_d24_adamw_workload_matches_the_page_counts():
+    # the page's total, transformer-matrix and head counts leave 13 tables of
+    # vocab x width plus 48 scalars; the AdamW workload is those plus the head
+    import json
+    import os
+
+    from muon_newton_schulz_02_amd import workloads as wlm
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "d24_shapes.json")))
+    rest = g["total_params"] - g["transformer_matrices"] - g["lm_head"]
+    table = g["vocab"] * g["width"]
+    assert table == g["lm_head"]
+    assert rest == 13 * table + 2 * g["layers"]
+    wl = wlm.adamw_workload()
+    assert wl.elements == rest + g["lm_head"]
+    assert sum(s.numel == table for s in wl.specs) == 14

@@ -1,0 +1,172 @@
+"""AdamW on the GPU (muon_adamw_batched) against the CPU oracle: parameters
+and both moments bit for bit, on ragged sizes that span several workgroups,
+every parameter/gradient type pair, unaligned tensors (the element path),
+several consecutive steps, per-tensor rates, and the full d24 AdamW set on
+sampled elements."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from muon_newton_schulz_02_amd import binding as mb
+from muon_newton_schulz_02_amd import workloads as wlm
+
+from gpu_helpers import bits, to_np
+
+pytestmark = pytest.mark.gpu
+
+CHUNK = 4096    # elements per workgroup
+SIZES = [1, 3, 4, 5, 4095, 4096, 4097, 3 * 4096 + 17, 100003]
+HP = dict(beta1=0.9, beta2=0.95, eps=1e-8)
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _host_inputs(seed, sizes, pdt, gdt):
+    gen = torch.Generator().manual_seed(seed)
+    ps = [(torch.randn(n, generator=gen) * 0.02).to(pdt) for n in sizes]
+    gs = [(torch.randn(n, generator=gen) * 1e-3).to(gdt) for n in sizes]
+    ms = [torch.randn(n, generator=gen) * 1e-3 for n in sizes]
+    vs = [(torch.randn(n, generator=gen) * 1e-3).square() for n in sizes]
+    return ps, gs, ms, vs
+
+
+def _check(p0, g0, m0, v0, p1, m1, v1, *, lr, wd, step, param_bf16, what):
+    rp, rm, rv = orc.adamw(to_np(p0), to_np(g0), to_np(m0), to_np(v0), lr=lr, weight_decay=wd, step=step,
+                           param_bf16=param_bf16, **HP)
+    assert np.array_equal(bits(to_np(m1)), bits(rm)), f"{what}: exp_avg"
+    assert np.array_equal(bits(to_np(v1)), bits(rv)), f"{what}: exp_avg_sq"
+    assert np.array_equal(bits(to_np(p1)), bits(rp)), f"{what}: param"
+
+
+@pytest.mark.parametrize("pdt,gdt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.float32),
+                                     (torch.bfloat16, torch.float32), (torch.float32, torch.bfloat16)])
+def test_ragged_sizes_three_steps(pdt, gdt):
+    _announce(f"adamw ragged pdt={pdt} gdt={gdt}")
+    ps, gs, ms, vs = _host_inputs(7, SIZES, pdt, gdt)
+    p_d = [p.cuda() for p in ps]
+    m_d = [m.cuda() for m in ms]
+    v_d = [v.cuda() for v in vs]
+    args = None
+    for step in (1, 2, 3):
+        g_host = gs if step == 1 else _host_inputs(7 + step, SIZES, pdt, gdt)[1]
+        g_d = [g.cuda() for g in g_host]
+        before = [(p.cpu(), m.cpu(), v.cpu()) for p, m, v in zip(p_d, m_d, v_d)]
+        args = mb.AdamwArgs(p_d, g_d, m_d, v_d)
+        mb.muon_adamw_batched(args, lr=1e-3, weight_decay=0.1, step=step, **HP)
+        torch.cuda.synchronize()
+        for i, n in enumerate(SIZES):
+            _check(*before[i][:1], g_host[i], *before[i][1:], p_d[i], m_d[i], v_d[i], lr=1e-3, wd=0.1, step=step,
+                   param_bf16=pdt == torch.bfloat16, what=f"step {step} numel {n}")
+
+
+def test_per_tensor_rates_and_empty_tensors():
+    _announce("adamw per-tensor rates")
+    sizes = [5000, 0, 8192, 31, 0, 12289]
+    ps, gs, ms, vs = _host_inputs(11, sizes, torch.bfloat16, torch.bfloat16)
+    lrs = [1e-3, 5.0, 0.0, 3e-2, 5.0, 2e-4]
+    wds = [0.0, 1.0, 0.5, 0.1, 1.0, 0.01]
+    p_d, g_d, m_d, v_d = ([t.cuda() for t in ts] for ts in (ps, gs, ms, vs))
+    mb.muon_adamw_batched(p_d, g_d, m_d, v_d, lr=9.0, weight_decay=9.0, step=5, lr_per_tensor=lrs,
+                          wd_per_tensor=wds, **HP)
+    torch.cuda.synchronize()
+    for i, n in enumerate(sizes):
+        _check(ps[i], gs[i], ms[i], vs[i], p_d[i], m_d[i], v_d[i], lr=np.float32(lrs[i]), wd=np.float32(wds[i]),
+               step=5, param_bf16=True, what=f"tensor {i} numel {n}")
+
+
+def test_unaligned_tensors_take_the_element_path():
+    _announce("adamw unaligned views")
+    n = 3 * CHUNK + 5
+    ps, gs, ms, vs = _host_inputs(17, [n + 1], torch.bfloat16, torch.float32)
+    # views starting one element in: 2-byte and 4-byte aligned, not 8 or 16
+    p_full, g_full, m_full, v_full = (t[0].cuda() for t in (ps, gs, ms, vs))
+    p_d, g_d, m_d, v_d = p_full[1:], g_full[1:], m_full[1:], v_full[1:]
+    head = (p_full[0].item(), m_full[0].item(), v_full[0].item())
+    mb.muon_adamw_batched([p_d], [g_d], [m_d], [v_d], lr=2e-3, weight_decay=0.05, step=9, **HP)
+    torch.cuda.synchronize()
+    _check(ps[0][1:], gs[0][1:], ms[0][1:], vs[0][1:], p_d, m_d, v_d, lr=2e-3, wd=0.05, step=9, param_bf16=True,
+           what="unaligned")
+    assert (p_full[0].item(), m_full[0].item(), v_full[0].item()) == head
+
+
+def test_special_values():
+    _announce("adamw special values")
+    n = CHUNK + 3
+    z = torch.zeros(n)
+    p = (torch.randn(n, generator=torch.Generator().manual_seed(3)) * 0.02).to(torch.bfloat16)
+    # g = m = v = 0: u = 0, p <- p (1 - lr wd)
+    p_d, g_d, m_d, v_d = p.cuda(), z.to(torch.bfloat16).cuda(), z.cuda(), z.cuda()
+    mb.muon_adamw_batched([p_d], [g_d], [m_d], [v_d], lr=0.5, weight_decay=0.5, step=1, **HP)
+    torch.cuda.synchronize()
+    _check(p, z.to(torch.bfloat16), z, z, p_d, m_d, v_d, lr=0.5, wd=0.5, step=1, param_bf16=True, what="zero grad")
+    # eps = 0, first step: sign descent
+    g = torch.randn(n, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16)
+    p32 = p.float()
+    p_d, g_d, m_d, v_d = p32.cuda(), g.cuda(), z.cuda(), z.cuda()
+    mb.muon_adamw_batched([p_d], [g_d], [m_d], [v_d], lr=2.0 ** -10, beta1=0.5, beta2=0.9375, eps=0.0, step=1)
+    torch.cuda.synchronize()
+    expect = p32.numpy() - np.float32(2.0 ** -10) * np.sign(g.float().numpy())
+    nz = g.float().numpy() != 0
+    assert np.array_equal(bits(to_np(p_d)[nz]), bits(expect[nz]))
+
+
+def test_deterministic_and_stream_ordered():
+    _announce("adamw determinism")
+    sizes = [70001, 4096]
+    ps, gs, ms, vs = _host_inputs(23, sizes, torch.bfloat16, torch.bfloat16)
+    outs = []
+    for _ in range(2):
+        p_d, g_d, m_d, v_d = ([t.cuda() for t in ts] for ts in (ps, gs, ms, vs))
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            mb.muon_adamw_batched(p_d, g_d, m_d, v_d, lr=1e-3, weight_decay=0.1, step=4, stream=s, **HP)
+        s.synchronize()
+        outs.append([to_np(t) for t in p_d + m_d + v_d])
+    for a, b in zip(*outs):
+        assert np.array_equal(bits(a), bits(b))
+
+
+def test_d24_adamw_full_size_sampled():
+    # the d24 AdamW set at full size (704,643,120 elements), in the launch
+    # configuration the benchmark times; the oracle checks sampled elements,
+    # chunk edges and tensor ends included
+    _announce("adamw d24 full size, sampled")
+    wl = wlm.adamw_workload()
+    dev = "cuda"
+    p_d, m_d, v_d, g_d = [], [], [], []
+    for i in range(len(wl.specs)):
+        p, m, v = wlm.adamw_state(wl, i, dev)
+        p_d.append(p)
+        m_d.append(m)
+        v_d.append(v)
+        g_d.append(wlm.adamw_gradient(wl, i, 0, dev))
+    rng = np.random.default_rng(29)
+    samples = []
+    for i, spec in enumerate(wl.specs):
+        n = spec.numel
+        if n <= 4096:
+            idx = np.arange(n)
+        else:
+            edges = np.array([0, 1, 3, 4, CHUNK - 1, CHUNK, CHUNK + 1, n - 5, n - 4, n - 1])
+            idx = np.unique(np.concatenate([edges, rng.integers(0, n, 20000)]))
+        it = torch.from_numpy(idx).to(dev)
+        samples.append((idx, [t[it].cpu() for t in (p_d[i], g_d[i], m_d[i], v_d[i])]))
+    args = mb.AdamwArgs(p_d, g_d, m_d, v_d)
+    mb.muon_adamw_batched(args, lr=wl.lr[0], beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps, step=wl.step,
+                          lr_per_tensor=wl.lr_per_tensor(), wd_per_tensor=wl.wd_per_tensor())
+    torch.cuda.synchronize()
+    for i, (idx, (p0, g0, m0, v0)) in enumerate(samples):
+        it = torch.from_numpy(idx).to(dev)
+        rp, rm, rv = orc.adamw(to_np(p0), to_np(g0), to_np(m0), to_np(v0), lr=np.float32(wl.lr_per_tensor()[i]),
+                               beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
+                               weight_decay=np.float32(wl.wd_per_tensor()[i]), step=wl.step, param_bf16=True)
+        assert np.array_equal(bits(to_np(m_d[i][it])), bits(rm)), f"{wl.specs[i].name}: exp_avg"
+        assert np.array_equal(bits(to_np(v_d[i][it])), bits(rv)), f"{wl.specs[i].name}: exp_avg_sq"
+        assert np.array_equal(bits(to_np(p_d[i][it])), bits(rp)), f"{wl.specs[i].name}: param"
+    assert all(torch.isfinite(p.float()).all().item() for p in p_d)
