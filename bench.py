@@ -190,6 +190,10 @@ def main():
     adamw = None
     if not args.no_adamw and args.workload == "d24_bf16":
         adamw = time_adamw(args, mb, wlm, torch, dev, stream)
+    copy_gbs = hbm_copy_gbs(torch, dev, stream)
+    for entry in [kernels.get("momentum"), adamw]:
+        if entry and entry.get("gbs"):
+            entry["frac_of_copy"] = round(entry["gbs"] / copy_gbs, 4)
 
     # ------------------------------------------------------------ CPU oracle
     cpu = None
@@ -216,9 +220,29 @@ def main():
         "ns_chain": ns_chain,
         "kernels": kernels,
         "adamw": adamw,
+        "hbm_copy_gbs": round(copy_gbs, 1),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def hbm_copy_gbs(torch, dev, stream, nbytes=1 << 30, reps=5):
+    """Achievable HBM bandwidth for a read + write stream: torch's device copy
+    of `nbytes`, bytes read plus bytes written per second."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    gbs = 2.0 * nbytes * reps / (start.elapsed_time(stop) * 1e-3) / 1e9
+    print(f"[bench] device copy: {gbs:.0f} GB/s (read + write)", file=sys.stderr, flush=True)
+    del src, dst
+    return gbs
 
 
 def time_adamw(args, mb, wlm, torch, dev, stream):

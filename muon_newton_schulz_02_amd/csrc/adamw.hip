@@ -18,6 +18,9 @@
 // elements.  The work is HBM-bound (22 bytes per element for bf16 p and g);
 // each thread keeps four groups of four elements in flight, and every load
 // and store instruction of a wave covers one contiguous run of memory.
+// Every byte is touched once, so the vector path loads and stores with the
+// nontemporal hint (measured: 5.7 TB/s against 5.3 TB/s with the default
+// cache policy, on the d24 non-matrix set).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -61,7 +64,8 @@ __device__ inline void adamw_elem(float& p, float g, float& m, float& v, float l
 template <bool PBF>
 __device__ inline void load4_param(const void* base, int64_t e, float p[4]) {
   if (PBF) {
-    const u32x2 raw = *gmem(reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(base) + e));
+    const u32x2 raw =
+        __builtin_nontemporal_load(gmem(reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(base) + e)));
     p[0] = bf16_bits_to_float(raw[0]);
     p[1] = bf16_bits_to_float(raw[0] >> 16);
     p[2] = bf16_bits_to_float(raw[1]);
@@ -92,8 +96,8 @@ __device__ inline void adamw_chunk(const AdamwTensor& t, int64_t base, float lr,
     if (full[q]) {
       load4_param<PBF>(t.p, e, p[q]);
       load4_param<GBF>(t.g, e, g[q]);
-      const f32x4 mr = *gmem(reinterpret_cast<const f32x4*>(t.m + e));
-      const f32x4 vr = *gmem(reinterpret_cast<const f32x4*>(t.v + e));
+      const f32x4 mr = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4*>(t.m + e)));
+      const f32x4 vr = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4*>(t.v + e)));
 #pragma unroll
       for (int j = 0; j < 4; ++j) { m[q][j] = mr[j]; v[q][j] = vr[j]; }
     } else {
@@ -118,13 +122,16 @@ __device__ inline void adamw_chunk(const AdamwTensor& t, int64_t base, float lr,
       if (PBF) {
         const uint32_t h01 = float2_to_bf16x2_bits(p[q][0], p[q][1]);
         const uint32_t h23 = float2_to_bf16x2_bits(p[q][2], p[q][3]);
-        *gmem(reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(t.p) + e)) = u32x2{h01, h23};
+        __builtin_nontemporal_store(u32x2{h01, h23},
+                                    gmem(reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(t.p) + e)));
       } else {
         *gmem(reinterpret_cast<f32x4*>(reinterpret_cast<float*>(t.p) + e)) =
             f32x4{p[q][0], p[q][1], p[q][2], p[q][3]};
       }
-      *gmem(reinterpret_cast<f32x4*>(t.m + e)) = f32x4{m[q][0], m[q][1], m[q][2], m[q][3]};
-      *gmem(reinterpret_cast<f32x4*>(t.v + e)) = f32x4{v[q][0], v[q][1], v[q][2], v[q][3]};
+      __builtin_nontemporal_store(f32x4{m[q][0], m[q][1], m[q][2], m[q][3]},
+                                  gmem(reinterpret_cast<f32x4*>(t.m + e)));
+      __builtin_nontemporal_store(f32x4{v[q][0], v[q][1], v[q][2], v[q][3]},
+                                  gmem(reinterpret_cast<f32x4*>(t.v + e)));
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {

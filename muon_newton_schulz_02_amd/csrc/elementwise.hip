@@ -6,6 +6,9 @@
 //    through an LDS transpose for tall matrices) in the Newton-Schulz storage
 //    format, zero-filling the padding; writes one binary32 sum of u^2 per
 //    64x64 tile (wavefront shuffles, then LDS across the four waves).
+//    G and M are touched once per step, so their vector loads and the M
+//    store carry the nontemporal hint (measured 4 % faster); U is read
+//    again by the Newton-Schulz products and is stored normally.
 //  * norm_finalize_kernel: sums a matrix's tile partials in a fixed order
 //    and forms 1/(||U||_F + eps).
 //  * writeback_direct_kernel: the write-back when no Newton-Schulz step is
@@ -114,13 +117,15 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
       const int64_t gi = int64_t(row) * md.ld_grad + col;
       if (full) {
         if (md.grad_bf16) {
-          const u32x2 raw = *gmem(reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(md.grad) + gi));
+          const u32x2 raw = __builtin_nontemporal_load(
+              gmem(reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(md.grad) + gi)));
           g[0] = bf16_bits_to_float(raw[0] & 0xFFFFu);
           g[1] = bf16_bits_to_float(raw[0] >> 16);
           g[2] = bf16_bits_to_float(raw[1] & 0xFFFFu);
           g[3] = bf16_bits_to_float(raw[1] >> 16);
         } else {
-          const f32x4 raw = *gmem(reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(md.grad) + gi));
+          const f32x4 raw = __builtin_nontemporal_load(
+              gmem(reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(md.grad) + gi)));
           g[0] = raw[0]; g[1] = raw[1]; g[2] = raw[2]; g[3] = raw[3];
         }
       } else {
@@ -131,7 +136,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
       if (mode == 0) {
         const int64_t mi64 = int64_t(row) * md.ld_mom + col;
         if (full) {
-          const f32x4 raw = *gmem(reinterpret_cast<const f32x4*>(md.mom + mi64));
+          const f32x4 raw = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4*>(md.mom + mi64)));
           m[0] = raw[0]; m[1] = raw[1]; m[2] = raw[2]; m[3] = raw[3];
         } else {
 #pragma unroll
@@ -150,7 +155,8 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
           u[e] = nesterov ? (gi + bn) : mn[e];
         }
         if (full) {
-          *gmem(reinterpret_cast<f32x4*>(md.mom + mi64)) = f32x4{mn[0], mn[1], mn[2], mn[3]};
+          __builtin_nontemporal_store(f32x4{mn[0], mn[1], mn[2], mn[3]},
+                                      gmem(reinterpret_cast<f32x4*>(md.mom + mi64)));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
