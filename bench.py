@@ -13,6 +13,9 @@ records around each launch on the launch stream (muon_timing_*).  Its
 traffic is the HBM bytes per launch from the rocprofv3 FETCH_SIZE /
 WRITE_SIZE summary under profiles/, reported only while the kernel sources
 hash to the values recorded there (null otherwise).
+`roofline.measured_peak` is the achievable rate on the same box: the
+library's register-only MFMA loop (`muon_mfma_probe`) for the products, a
+torch device copy for HBM-bound kernels.
 The cpu_baseline is the CPU oracle timed on a bounded sample of the same
 workload on this host.  The `adamw` object times the other half of the
 hybrid optimizer, AdamW on the d24 parameters that are not transformer
@@ -53,6 +56,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="d24_bf16")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="truncate the layer stack (d24_bf16 with 3 layers is one GPU's share of 8: "
+                         "12 x 1536^2 + 3 up + 3 down)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=6,
                     help="layers in the oracle's sample (about 10-15 s of host work for d24)")
@@ -81,7 +87,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    wl = wlm.workload(args.workload)
+    wl = wlm.workload(args.workload, layers=args.layers)
     n = len(wl.specs)
     print(f"[bench] generating {args.workload}: {n} matrices, {wl.elements} elements", file=sys.stderr,
           flush=True)
@@ -110,20 +116,21 @@ def main():
 
     mb.muon_timing_enable(True)
     mb.muon_timing_read()  # clear
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         mb.muon_step_batched(sargs, **kw, stream=stream)
-    stop.record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern = mb.muon_timing_read()
     mb.muon_timing_enable(False)
-    ms_total = start.elapsed_time(stop)
+    ms_total = marks[0].elapsed_time(marks[-1])
     ms_step = ms_total / args.steps
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    pct = {f"p{q}": round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)}
     print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (event), wall {wall / args.steps * 1e3:.3f} ms",
           file=sys.stderr, flush=True)
 
@@ -171,7 +178,7 @@ def main():
         kernels[name] = entry
     dom = max(kernels, key=lambda x: kernels[x]["share"])
     d = kernels[dom]
-    traffic = measured_traffic(args.workload, dom)
+    traffic = measured_traffic(args.workload if args.layers is None else None, dom)
     if d.get("bound") == "mfma":
         roofline = {"bound": "mfma", "kernel": dom, "achieved": d["tflops"], "peak": peak_mfma,
                     "unit": "TFLOP/s", "frac": d["frac"], "traffic": traffic}
@@ -188,9 +195,18 @@ def main():
                 "algorithmic_frac": round(ns_exec / (ns_ms * 1e-3) / 1e12 / peak_mfma, 4)}
 
     adamw = None
-    if not args.no_adamw and args.workload == "d24_bf16":
+    if not args.no_adamw and args.workload == "d24_bf16" and args.layers is None:
         adamw = time_adamw(args, mb, wlm, torch, dev, stream)
     copy_gbs = hbm_copy_gbs(torch, dev, stream)
+    mfma_tflops = mfma_probe_tflops(mb, torch, dev, stream)
+    if roofline["bound"] == "hbm":
+        roofline["measured_peak"] = round(copy_gbs, 1)
+    elif wl.precision != mb.NS_F32:   # the probe measures the bf16 rate
+        roofline["measured_peak"] = round(mfma_tflops, 1)
+    if roofline.get("measured_peak") and roofline.get("achieved"):
+        roofline["frac_of_measured"] = round(roofline["achieved"] / roofline["measured_peak"], 4)
+    if wl.precision != mb.NS_F32:
+        ns_chain["algorithmic_frac_of_measured"] = round(ns_exec / (ns_ms * 1e-3) / 1e12 / mfma_tflops, 4)
     for entry in [kernels.get("momentum"), adamw]:
         if entry and entry.get("gbs"):
             entry["frac_of_copy"] = round(entry["gbs"] / copy_gbs, 4)
@@ -208,12 +224,14 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms_percentiles": pct,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wl.precision == mb.NS_BF16 else ("f32" if wl.precision == mb.NS_F32 else "bf16x3"),
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT.get(args.workload, args.workload), "name": args.workload,
+        "config": {"workload": WORKLOAD_TEXT.get(args.workload, args.workload) if args.layers is None else
+                   f"{args.workload} truncated to {args.layers} layers", "name": args.workload,
                    "matrices": n, "elements": elems, "ns_steps": k, "coeffs": list(wl.coeffs),
                    "matrices_per_s": round(n * 1e3 / ms_step, 1), "parallelism": "1 GPU"},
         "roofline": roofline,
@@ -221,9 +239,26 @@ def main():
         "kernels": kernels,
         "adamw": adamw,
         "hbm_copy_gbs": round(copy_gbs, 1),
+        "mfma_probe_tflops": round(mfma_tflops, 1),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def mfma_probe_tflops(mb, torch, dev, stream, iterations=200000):
+    """Achievable dense bf16 MFMA rate: the library's register-only MFMA loop
+    on every SIMD, timed with events (about 30 ms)."""
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    mb.muon_mfma_probe(1000, sink, stream=stream)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    flops = mb.muon_mfma_probe(iterations, sink, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    tf = flops / (start.elapsed_time(stop) * 1e-3) / 1e12
+    print(f"[bench] mfma probe: {tf:.0f} TFLOP/s dense bf16", file=sys.stderr, flush=True)
+    return tf
 
 
 def hbm_copy_gbs(torch, dev, stream, nbytes=1 << 30, reps=5):

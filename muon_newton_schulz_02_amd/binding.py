@@ -119,6 +119,8 @@ def lib() -> ctypes.CDLL:
     L.muon_adamw_batched.argtypes = [_PP, _PP, _PP, _PP, ctypes.POINTER(AdamwDesc), i32,
                                      ctypes.POINTER(AdamwHparams), _VP]
     L.muon_adamw_batched.restype = i32
+    L.muon_mfma_probe.argtypes = [ctypes.c_int64, _VP, ctypes.POINTER(ctypes.c_double), _VP]
+    L.muon_mfma_probe.restype = i32
     L.muon_ns_batched.argtypes = [_PP, _PP, D, i32, NsCoeffs, i32, _VP]
     L.muon_ns_batched.restype = i32
     L.muon_frobenius_norms.argtypes = [_PP, D, i32, _VP, _VP]
@@ -368,6 +370,15 @@ def muon_adamw_batched(params, grads=None, exp_avg=None, exp_avg_sq=None, *, lr,
                                       args.count, ctypes.byref(hp), _stream_handle(stream))
     del keep
     _check(status)
+
+
+def muon_mfma_probe(iterations: int, sink: torch.Tensor, stream=None) -> float:
+    """Enqueue the MFMA-rate probe; returns its floating-point operation count."""
+    if sink.dtype != torch.float32 or sink.numel() < 1:
+        raise ValueError("sink must be a float32 device tensor of at least one element")
+    flops = ctypes.c_double(0.0)
+    _check(lib().muon_mfma_probe(int(iterations), sink.data_ptr(), ctypes.byref(flops), _stream_handle(stream)))
+    return float(flops.value)
 
 
 def muon_ns_batched(x_in, x_out, *, ns_coeffs, ns_steps, precision=NS_BF16, stream=None):

@@ -1018,6 +1018,24 @@ muon_status muon_adamw_batched(void* const* params, const void* const* grads, fl
   return run_adamw(c);
 }
 
+muon_status muon_mfma_probe(int64_t iterations, float* sink, double* flops_out, void* stream) {
+  t_last_error.clear();
+  if (iterations < 1 || iterations > (int64_t(1) << 30))
+    return fail(MUON_ERR_INVALID_ARGUMENT, "iterations %lld out of [1, 2^30]", (long long)iterations);
+  if (!sink || !flops_out) return fail(MUON_ERR_INVALID_ARGUMENT, "sink or flops_out is NULL");
+  if (reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+    return fail(MUON_ERR_UNSUPPORTED, "sink is not aligned to 4 bytes");
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return fail(MUON_ERR_HIP, "cannot query the current device");
+  }
+  const hipError_t e = launch_mfma_probe(iterations, cus, sink, flops_out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MUON_ERR_HIP, "probe launch failed: %s", hipGetErrorString(e));
+  return MUON_OK;
+}
+
 muon_status muon_timing_enable(int32_t enable) {
   std::lock_guard<std::mutex> lock(g_mu);
   t_last_error.clear();

@@ -104,6 +104,7 @@ hipError_t launch_writeback_direct(const MatDev* mats, const int32_t* etile_off,
 enum Phase : int { PH_GRAM = 0, PH_POLY = 1, PH_COMB = 2 };
 hipError_t launch_adamw(const AdamwTensor* tensors, const int32_t* chunk_off, int32_t count, int64_t total_chunks,
                         const float2* rates, float lr, float d, const AdamwConsts& k, hipStream_t stream);
+hipError_t launch_mfma_probe(int64_t iterations, int32_t cus, float* sink, double* flops, hipStream_t stream);
 hipError_t launch_ns_phase(int prec, int phase, const MatDev* mats, const MatScal* scal,
                            const int2* tiles, const PhaseArgs& args, hipStream_t stream);
 

@@ -20,7 +20,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = mb.exported_names()
-    assert len(names) == 13
+    assert len(names) == 14
     out = subprocess.run(["nm", "-D", "--defined-only", mb.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -317,3 +317,13 @@ def test_adamw_binding_rejects_bad_tensors():
         mb.AdamwArgs([p], [p], [torch.zeros(7)], [torch.zeros(8)])
     with pytest.raises(ValueError):
         mb.AdamwArgs([torch.zeros(4, 4).t()], [torch.zeros(16)], [torch.zeros(16)], [torch.zeros(16)])
+
+
+def test_mfma_probe_argument_errors(L):
+    flops = ctypes.c_double(0.0)
+    sink = BASE
+    assert L.muon_mfma_probe(0, sink, ctypes.byref(flops), None) == mb.MUON_ERR_INVALID_ARGUMENT
+    assert L.muon_mfma_probe((1 << 30) + 1, sink, ctypes.byref(flops), None) == mb.MUON_ERR_INVALID_ARGUMENT
+    assert L.muon_mfma_probe(10, None, ctypes.byref(flops), None) == mb.MUON_ERR_INVALID_ARGUMENT
+    assert L.muon_mfma_probe(10, sink, None, None) == mb.MUON_ERR_INVALID_ARGUMENT
+    assert L.muon_mfma_probe(10, sink + 2, ctypes.byref(flops), None) == mb.MUON_ERR_UNSUPPORTED
