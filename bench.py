@@ -133,6 +133,15 @@ def main():
     pct = {f"p{q}": round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)}
     print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (event), wall {wall / args.steps * 1e3:.3f} ms",
           file=sys.stderr, flush=True)
+    # the same steps again without the per-launch events of the timing hook
+    # (they add a few microseconds per launch, visible on the small workloads)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        mb.muon_step_batched(sargs, **kw, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step_plain = e0.elapsed_time(e1) / args.steps
 
     if args.copy_calibration:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)
@@ -225,6 +234,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "step_ms_percentiles": pct,
+        "ms_per_step_without_kernel_events": round(ms_step_plain, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
