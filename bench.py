@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=6,
                     help="layers in the oracle's sample (about 10-15 s of host work for d24)")
+    ap.add_argument("--launch-mode", choices=("auto", "grids", "chain"), default="auto",
+                    help="Newton-Schulz launches: the library's choice, one grid per phase, or one persistent chain")
     ap.add_argument("--no-adamw", action="store_true",
                     help="skip timing the AdamW half of the hybrid optimizer (d24 non-matrix parameters)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -110,8 +112,16 @@ def main():
     kw = dict(lr=float(np.float32(wl.lr)), beta=wl.beta, nesterov=int(wl.nesterov), ns_coeffs=wl.coeffs,
               ns_steps=wl.ns_steps, scale_rule=wl.scale_rule)
     stream = torch.cuda.current_stream()
+    mode = {"auto": mb.LAUNCH_AUTO, "grids": mb.LAUNCH_PHASE_GRIDS, "chain": mb.LAUNCH_CHAIN}[args.launch_mode]
+
+    def step():
+        if mode == mb.LAUNCH_AUTO:
+            mb.muon_step_batched(sargs, **kw, stream=stream)
+        else:
+            mb.muon_step_batched_v2(sargs, **kw, stream=stream, launch_mode=mode)
+
     for _ in range(args.warmup):
-        mb.muon_step_batched(sargs, **kw, stream=stream)
+        step()
     torch.cuda.synchronize()
 
     mb.muon_timing_enable(True)
@@ -121,7 +131,7 @@ def main():
     t0 = time.perf_counter()
     marks[0].record(stream)
     for i in range(args.steps):
-        mb.muon_step_batched(sargs, **kw, stream=stream)
+        step()
         marks[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -138,7 +148,7 @@ def main():
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
-        mb.muon_step_batched(sargs, **kw, stream=stream)
+        step()
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step_plain = e0.elapsed_time(e1) / args.steps
@@ -177,8 +187,9 @@ def main():
         avg_ms = tot_ms / launches
         entry = {"launches_per_step": launches / steps, "avg_ms": round(avg_ms, 5),
                  "share": round(tot_ms / ms_total, 4)}
-        if name in alg:
-            flops_launch = alg[name] / k
+        if name in alg or name == "chain":
+            # one chain launch runs every step of the Newton-Schulz iteration
+            flops_launch = sum(alg.values()) if name == "chain" else alg[name] / k
             tf = flops_launch / (avg_ms * 1e-3) / 1e12
             entry.update({"bound": "mfma", "tflops": round(tf, 2), "frac": round(tf / peak_mfma, 4)})
         elif name == "momentum":
@@ -194,7 +205,7 @@ def main():
     else:
         roofline = {"bound": "hbm", "kernel": dom, "achieved": d.get("gbs"), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": d.get("frac"), "traffic": traffic}
-    ns_ms = sum(kern[x][0] for x in ("gram", "poly", "combine")) / steps
+    ns_ms = sum(kern[x][0] for x in ("gram", "poly", "combine", "chain")) / steps
     ns_exec = sum(alg.values())
     ns_chain = {"nominal_tflop_per_step": round(nominal / 1e12, 4),
                 "ms_per_step": round(ns_ms, 4),
@@ -243,7 +254,8 @@ def main():
         "config": {"workload": WORKLOAD_TEXT.get(args.workload, args.workload) if args.layers is None else
                    f"{args.workload} truncated to {args.layers} layers", "name": args.workload,
                    "matrices": n, "elements": elems, "ns_steps": k, "coeffs": list(wl.coeffs),
-                   "matrices_per_s": round(n * 1e3 / ms_step, 1), "parallelism": "1 GPU"},
+                   "matrices_per_s": round(n * 1e3 / ms_step, 1), "parallelism": "1 GPU",
+                   "launch_mode": args.launch_mode},
         "roofline": roofline,
         "ns_chain": ns_chain,
         "kernels": kernels,

@@ -46,6 +46,11 @@
  *     them on one stream or serialise them.
  *   - Nothing crosses the ABI as an exception; errors are status codes with
  *     a thread-local message from muon_last_error().
+ *   - The persistent chain (muon_launch_mode) bounds every dependency wait;
+ *     a wait that gives up (only possible when the GPU cannot hold the whole
+ *     grid at once) skips its tile and raises a flag, and the next call on
+ *     that device returns MUON_ERR_HIP saying the earlier results are
+ *     invalid.
  */
 #ifndef MUON_MI355X_H
 #define MUON_MI355X_H
@@ -104,6 +109,23 @@ typedef enum muon_momentum_kind {
   MUON_MOMENTUM_EMA = 1
 } muon_momentum_kind;
 
+/* How the Newton-Schulz steps are launched (muon_step_options.launch_mode).
+ *   AUTO         PHASE_GRIDS (the faster of the two on every workload
+ *                measured on MI355X).
+ *   PHASE_GRIDS  one persistent grid per phase and step over all matrices.
+ *   CHAIN        one persistent grid for every phase of every step: per-XCD
+ *                queues of (step, phase, matrix, tile) items, each waiting
+ *                on per-(matrix, phase) completion counts; ns_steps <= 16.
+ *                It keeps each step's A, B and iterate in buffers of their
+ *                own (a second workspace, (k - 1) iterates and 2k Gram-sized
+ *                matrices per matrix for k steps).
+ * Every mode gives the same results bit for bit.                            */
+typedef enum muon_launch_mode {
+  MUON_LAUNCH_AUTO = 0,
+  MUON_LAUNCH_PHASE_GRIDS = 1,
+  MUON_LAUNCH_CHAIN = 2
+} muon_launch_mode;
+
 /* Update variants of muon_step_batched_v2.  The pages describe none of
  * them; they are the forms commonly used with Muon.  A zero-initialised
  * struct (or a NULL pointer) gives muon_step_batched bit for bit.
@@ -120,6 +142,7 @@ typedef enum muon_momentum_kind {
  * scale_per_matrix  host array of `count` finite scales s_i replacing the
  *                   scale rule for matrix i (t = fl32(lr_i*s_i), the product
  *                   in binary64), or NULL.
+ * launch_mode       a muon_launch_mode.
  * The arrays are read during the call and not kept.                        */
 typedef struct muon_step_options {
   const muon_ns_coeffs* ns_schedule;
@@ -127,6 +150,7 @@ typedef struct muon_step_options {
   int32_t momentum_kind;
   const float* lr_per_matrix;
   const float* scale_per_matrix;
+  int32_t launch_mode;
 } muon_step_options;
 
 /* One 2-D matrix.  rows, cols in [1, 65536]; ld_* >= cols.
@@ -278,7 +302,8 @@ typedef enum muon_kernel_class {
   MUON_KC_COMBINE = 4,   /* X = a X + B X (last step: write-back)          */
   MUON_KC_WRITEBACK = 5, /* write-back when ns_steps == 0                  */
   MUON_KC_ADAMW = 6,     /* muon_adamw_batched                             */
-  MUON_KC_COUNT = 7
+  MUON_KC_CHAIN = 7,     /* the persistent chain (all steps, one launch)   */
+  MUON_KC_COUNT = 8
 } muon_kernel_class;
 
 /* Measurement hook.  While enabled (enable = 1), every launch the library

@@ -165,6 +165,21 @@ struct Plan {
     int32_t per_xcd[3];
   };
   std::vector<Group> groups;
+  // persistent chains (one per precision group), built on first use
+  struct Chain {
+    int prec = 0;
+    std::vector<uint64_t> key;     // steps, c == 0 pattern, chain workspace
+    void* dmem = nullptr;
+    MatDev* d_imats = nullptr;     // per (step, matrix) descriptors
+    ChainItem* d_items = nullptr;
+    int32_t* d_xcd_off = nullptr;
+    PhaseArgs* d_steps = nullptr;
+    int32_t* d_sync = nullptr;
+    int32_t nsync = 0;
+    int32_t per_xcd_max = 0;
+  };
+  std::vector<Chain> chains;
+  std::vector<MatDev> host_mats;   // host copy of d_mats (the chain derives its descriptors from it)
   hipEvent_t last_use = nullptr;
 };
 
@@ -185,6 +200,9 @@ struct AdamwPlan {
 struct DeviceState {
   void* ws = nullptr;
   size_t ws_bytes = 0;
+  void* chain_ws = nullptr;            // per-step buffers of the persistent chain
+  size_t chain_ws_bytes = 0;
+  int32_t* fail_flag = nullptr;        // pinned host word the chain raises when a wait times out
   int cus_per_xcd = 0;
   std::list<Plan*> plans;              // most recently used first
   std::list<AdamwPlan*> adamw_plans;   // most recently used first
@@ -235,6 +253,8 @@ void free_plan(Plan* p) {
     hipEventDestroy(p->last_use);
   }
   if (p->dmem) hipFree(p->dmem);
+  for (auto& ch : p->chains)
+    if (ch.dmem) hipFree(ch.dmem);
   delete p;
 }
 
@@ -285,17 +305,48 @@ std::vector<int2> xcd_lists(const std::vector<TileSrc>& src, int32_t* per_xcd) {
   return out;
 }
 
-muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vector<int32_t>& etile_off,
-                       hipStream_t stream) {
-  const int32_t count = int32_t(hm.size());
-  // order the matrices by decreasing Newton-Schulz cost so large ones start first
-  std::vector<int> order(count);
-  for (int i = 0; i < count; ++i) order[i] = i;
+// Matrices by decreasing Newton-Schulz cost, so large ones start first.
+std::vector<int> cost_order(const std::vector<MatDev>& hm) {
+  std::vector<int> order(hm.size());
+  for (size_t i = 0; i < hm.size(); ++i) order[i] = int(i);
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
     const double ca = double(hm[a].Mp) * hm[a].Mp * hm[a].Np;
     const double cb = double(hm[b].Mp) * hm[b].Mp * hm[b].Np;
     return ca > cb;
   });
+  return order;
+}
+
+// The tiles of one phase over the matrices of one precision, in `order`:
+// a grouped raster (bands of GROUP_M tile rows walked column by column) so
+// that tiles in flight together share row and column operand panels; GRAM
+// and POLY take the tiles on or above the diagonal.  Cost = K.
+std::vector<TileSrc> phase_tiles(const std::vector<MatDev>& hm, const std::vector<int>& order, int prec, int ph) {
+  std::vector<TileSrc> src;
+  for (int i : order) {
+    const MatDev& m = hm[i];
+    if (m.prec != prec) continue;
+    const int T = ns_tile(prec);
+    const int GROUP_M = T == 256 ? 4 : 8;
+    const int tm = m.Mp / T, tn = m.Np / T;
+    if (ph == PH_COMB) {
+      for (int g0 = 0; g0 < tm; g0 += GROUP_M)
+        for (int b = 0; b < tn; ++b)
+          for (int a = g0; a < std::min(tm, g0 + GROUP_M); ++a) src.push_back({i, a, b, double(m.Mp)});
+    } else {
+      const double k = ph == PH_GRAM ? double(m.Np) : double(m.Mp);
+      for (int g0 = 0; g0 < tm; g0 += GROUP_M)
+        for (int b = g0; b < tm; ++b)
+          for (int a = g0; a < std::min(tm, g0 + GROUP_M) && a <= b; ++a) src.push_back({i, a, b, k});
+    }
+  }
+  return src;
+}
+
+muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vector<int32_t>& etile_off,
+                       hipStream_t stream) {
+  const int32_t count = int32_t(hm.size());
+  const std::vector<int> order = cost_order(hm);
   std::vector<int> precs;
   for (const auto& m : hm)
     if (std::find(precs.begin(), precs.end(), m.prec) == precs.end()) precs.push_back(m.prec);
@@ -307,27 +358,7 @@ muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vec
     Plan::Group g;
     g.prec = prec;
     for (int ph = 0; ph < 3; ++ph) {
-      std::vector<TileSrc> src;
-      for (int i : order) {
-        const MatDev& m = hm[i];
-        if (m.prec != prec) continue;
-        const int T = ns_tile(prec);
-        const int GROUP_M = T == 256 ? 4 : 8;  // tile rows per raster band
-        const int tm = m.Mp / T, tn = m.Np / T;
-        // grouped raster: bands of GROUP_M tile rows, walked column by column,
-        // so tiles in flight together share row and column operand panels
-        if (ph == PH_COMB) {
-          for (int g0 = 0; g0 < tm; g0 += GROUP_M)
-            for (int b = 0; b < tn; ++b)
-              for (int a = g0; a < std::min(tm, g0 + GROUP_M); ++a) src.push_back({i, a, b, double(m.Mp)});
-        } else {
-          const double k = ph == PH_GRAM ? double(m.Np) : double(m.Mp);
-          for (int g0 = 0; g0 < tm; g0 += GROUP_M)
-            for (int b = g0; b < tm; ++b)
-              for (int a = g0; a < std::min(tm, g0 + GROUP_M) && a <= b; ++a) src.push_back({i, a, b, k});
-        }
-      }
-      lists.push_back(xcd_lists(src, &g.per_xcd[ph]));
+      lists.push_back(xcd_lists(phase_tiles(hm, order, prec, ph), &g.per_xcd[ph]));
       g.tiles[ph] = nullptr;
     }
     groups.push_back(g);
@@ -377,10 +408,158 @@ muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vec
   for (auto& g : groups)
     for (int ph = 0; ph < 3; ++ph) g.tiles[ph] = reinterpret_cast<int2*>(base + off_lists[li++]);
   plan->groups = groups;
+  plan->host_mats = hm;
+  plan->chains.resize(groups.size());
+  for (size_t gi = 0; gi < groups.size(); ++gi) plan->chains[gi].prec = groups[gi].prec;
   if (hipEventCreateWithFlags(&plan->last_use, hipEventDisableTiming) != hipSuccess) {
     plan->last_use = nullptr;
     return fail(MUON_ERR_HIP, "hipEventCreate failed");
   }
+  return MUON_OK;
+}
+
+// ------------------------------------------------------------ chain plan
+// Whether AUTO may pick the persistent chain and CHAIN is accepted.
+constexpr bool kChainEnabled = true;
+
+int per_cu_blocks(int prec) { return (ns_tile(prec) == 256 || prec == PREC_BF16X3) ? 1 : 2; }
+
+// GRAM tiles per precision of the call's shapes (the phase that fills the
+// grid least in the d24-like stacks).
+std::map<int, int64_t> gram_tiles(const muon_matrix_desc* shapes, int32_t count) {
+  std::map<int, int64_t> t;
+  for (int32_t i = 0; i < count; ++i) {
+    const MatGeom g = geom_of(shapes[i]);
+    const int64_t tm = g.Mp / ns_tile(g.prec);
+    t[g.prec] += tm * (tm + 1) / 2;
+  }
+  return t;
+}
+
+// Chain workspace of one matrix for k steps: iterates X_1 .. X_{k-1} (X_0 is
+// the momentum kernel's output in the main workspace) and A, B per step.
+size_t chain_bytes(const MatGeom& g, int k) { return size_t(k - 1) * g.x_bytes + size_t(2 * k) * g.a_bytes; }
+
+// Builds the persistent chain of precision group `gi` for `k` steps whose
+// c == 0 pattern is `cmask` (bit it set: step it has c == 0, so POLY is
+// skipped and GRAM stores B = b A).  `use` marks the matrices of the call
+// that take the chain; their step buffers start at `chain_ws`.
+muon_status build_chain(Plan* plan, size_t gi, int k, uint32_t cmask, char* chain_ws,
+                        const std::vector<MatGeom>& geo, hipStream_t stream) {
+  Plan::Chain& ch = plan->chains[gi];
+  if (ch.dmem) {
+    hipFree(ch.dmem);
+    ch.dmem = nullptr;
+  }
+  const int prec = ch.prec;
+  const std::vector<MatDev>& hm = plan->host_mats;
+  const int32_t count = int32_t(hm.size());
+  // per (step, matrix) descriptors with the step's own buffers
+  std::vector<MatDev> im(size_t(k) * count);
+  size_t wo = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const bool mine = hm[i].prec == prec;
+    char* base = chain_ws + wo;
+    if (mine) wo += chain_bytes(geo[i], k);
+    for (int it = 0; it < k; ++it) {
+      MatDev m = hm[i];
+      if (mine) {
+        auto xbuf = [&](int j) -> void* { return j == 0 ? hm[i].X[0] : base + size_t(j - 1) * geo[i].x_bytes; };
+        m.X[0] = xbuf(it);
+        m.X[1] = it + 1 < k ? xbuf(it + 1) : nullptr;
+        m.A = base + size_t(k - 1) * geo[i].x_bytes + size_t(2 * it) * geo[i].a_bytes;
+        m.B = reinterpret_cast<char*>(m.A) + geo[i].a_bytes;
+      }
+      im[size_t(it) * count + i] = m;
+    }
+  }
+  // work items: phase instances in order, each split into XCD-local runs
+  const std::vector<int> order = cost_order(hm);
+  // done counter of (step, phase, matrix): index into the counters that
+  // follow the CHAIN_SYNC_HEAD words of queue heads and abort flag
+  auto counter = [&](int it, int ph, int mat) { return (it * 3 + ph) * count + mat; };
+  std::vector<std::vector<ChainItem>> q(NUM_XCD);
+  std::vector<int32_t> ntiles(size_t(3) * count, 0);   // tiles per (phase, matrix)
+  for (int ph = 0; ph < 3; ++ph)
+    for (const TileSrc& t : phase_tiles(hm, order, prec, ph)) ++ntiles[size_t(ph) * count + t.mat];
+  for (int it = 0; it < k; ++it) {
+    const bool cz = (cmask >> it) & 1u;
+    for (int ph = 0; ph < 3; ++ph) {
+      if (ph == PH_POLY && cz) continue;
+      int32_t per = 0;
+      const std::vector<int2> lists = xcd_lists(phase_tiles(hm, order, prec, ph), &per);
+      for (int x = 0; x < NUM_XCD; ++x)
+        for (int32_t j = 0; j < per; ++j) {
+          const int2 e = lists[size_t(x) * per + j];
+          if (e.x < 0) continue;
+          const int mat = e.x;
+          ChainItem ci;
+          ci.desc = it * count + mat;
+          ci.mat = mat;
+          ci.step = it;
+          ci.tile = e.y;
+          ci.signal = counter(it, ph, mat);
+          if (ph == PH_GRAM) {
+            ci.kind = cz ? CHAIN_GRAM_B : CHAIN_GRAM_A;
+            ci.wait = it == 0 ? -1 : counter(it - 1, PH_COMB, mat);
+            ci.need = it == 0 ? 0 : ntiles[size_t(PH_COMB) * count + mat];
+          } else if (ph == PH_POLY) {
+            ci.kind = CHAIN_POLY;
+            ci.wait = counter(it, PH_GRAM, mat);
+            ci.need = ntiles[size_t(PH_GRAM) * count + mat];
+          } else {
+            ci.kind = it == k - 1 ? CHAIN_COMB_LAST : CHAIN_COMB;
+            const int prev = cz ? PH_GRAM : PH_POLY;
+            ci.wait = counter(it, prev, mat);
+            ci.need = ntiles[size_t(prev) * count + mat];
+          }
+          q[x].push_back(ci);
+        }
+    }
+  }
+  std::vector<int32_t> xoff(NUM_XCD + 1, 0);
+  int32_t mx = 0;
+  for (int x = 0; x < NUM_XCD; ++x) {
+    xoff[x + 1] = xoff[x] + int32_t(q[x].size());
+    mx = std::max(mx, int32_t(q[x].size()));
+  }
+  const int32_t nitems = xoff[NUM_XCD];
+  const int32_t nsync = CHAIN_SYNC_HEAD + 3 * k * count;
+  size_t off = 0;
+  const size_t o_im = off;
+  off = align256(off + sizeof(MatDev) * im.size());
+  const size_t o_items = off;
+  off = align256(off + sizeof(ChainItem) * std::max(nitems, 1));
+  const size_t o_xoff = off;
+  off = align256(off + sizeof(int32_t) * (NUM_XCD + 1));
+  const size_t o_steps = off;
+  off = align256(off + sizeof(PhaseArgs) * MAX_CHAIN_STEPS);
+  const size_t o_sync = off;
+  off = align256(off + sizeof(int32_t) * nsync);
+  void* dmem = nullptr;
+  if (hipMalloc(&dmem, off) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MUON_ERR_OUT_OF_MEMORY, "chain plan allocation of %zu bytes failed", off);
+  }
+  std::vector<char> host(off, 0);
+  memcpy(host.data() + o_im, im.data(), sizeof(MatDev) * im.size());
+  for (int x = 0; x < NUM_XCD; ++x)
+    memcpy(host.data() + o_items + sizeof(ChainItem) * xoff[x], q[x].data(), sizeof(ChainItem) * q[x].size());
+  memcpy(host.data() + o_xoff, xoff.data(), sizeof(int32_t) * (NUM_XCD + 1));
+  if (hipMemcpyAsync(dmem, host.data(), off, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    hipFree(dmem);
+    return fail(MUON_ERR_HIP, "chain plan upload failed: %s", hipGetErrorString(hipGetLastError()));
+  }
+  char* b = reinterpret_cast<char*>(dmem);
+  ch.dmem = dmem;
+  ch.d_imats = reinterpret_cast<MatDev*>(b + o_im);
+  ch.d_items = reinterpret_cast<ChainItem*>(b + o_items);
+  ch.d_xcd_off = reinterpret_cast<int32_t*>(b + o_xoff);
+  ch.d_steps = reinterpret_cast<PhaseArgs*>(b + o_steps);
+  ch.d_sync = reinterpret_cast<int32_t*>(b + o_sync);
+  ch.nsync = nsync;
+  ch.per_xcd_max = mx;
   return MUON_OK;
 }
 
@@ -435,6 +614,12 @@ muon_status validate_call(const Call& c) {
       return fail(MUON_ERR_INVALID_ARGUMENT, "weight_decay must be finite and >= 0");
     if (o.momentum_kind != MUON_MOMENTUM_HEAVY_BALL && o.momentum_kind != MUON_MOMENTUM_EMA)
       return fail(MUON_ERR_INVALID_ARGUMENT, "unknown momentum_kind %d", o.momentum_kind);
+    if (o.launch_mode < MUON_LAUNCH_AUTO || o.launch_mode > MUON_LAUNCH_CHAIN)
+      return fail(MUON_ERR_INVALID_ARGUMENT, "unknown launch_mode %d", o.launch_mode);
+    if (o.launch_mode == MUON_LAUNCH_CHAIN && !kChainEnabled)
+      return fail(MUON_ERR_UNSUPPORTED, "the persistent chain is switched off in this build");
+    if (o.launch_mode == MUON_LAUNCH_CHAIN && c.ns_steps > MAX_CHAIN_STEPS)
+      return fail(MUON_ERR_UNSUPPORTED, "the persistent chain takes at most %d Newton-Schulz steps", MAX_CHAIN_STEPS);
     if (o.ns_schedule)
       for (int32_t k = 0; k < c.ns_steps; ++k)
         if (!std::isfinite(o.ns_schedule[k].a) || !std::isfinite(o.ns_schedule[k].b) ||
@@ -516,6 +701,43 @@ muon_status run(const Call& c) {
     ds.cus_per_xcd = std::max(1, cus / NUM_XCD);
   }
 
+  // a persistent chain of an earlier call whose dependency wait timed out
+  if (!ds.fail_flag) {
+    void* f = nullptr;
+    if (hipHostMalloc(&f, sizeof(int32_t), hipHostMallocCoherent) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MUON_ERR_OUT_OF_MEMORY, "pinned failure flag allocation failed");
+    }
+    ds.fail_flag = reinterpret_cast<int32_t*>(f);
+    *ds.fail_flag = 0;
+  }
+  if (__atomic_load_n(ds.fail_flag, __ATOMIC_ACQUIRE) != 0) {
+    __atomic_store_n(ds.fail_flag, 0, __ATOMIC_RELEASE);
+    return fail(MUON_ERR_HIP, "an earlier persistent Newton-Schulz launch on this device gave up waiting for a "
+                "dependency; the results of that call are invalid");
+  }
+
+  // which precision groups run as one persistent chain
+  std::map<int, bool> use_chain;
+  size_t chain_need = 0;
+  if (c.mode != MODE_NORMS && c.ns_steps >= 1) {
+    const int32_t lm = (c.mode == MODE_STEP && c.opt) ? c.opt->launch_mode : MUON_LAUNCH_AUTO;
+    for (const auto& kv : gram_tiles(c.shapes, c.count)) {
+      const int64_t resident = int64_t(NUM_XCD) * ds.cus_per_xcd * per_cu_blocks(kv.first);
+      bool u = false;
+      // AUTO keeps the per-phase grids: measured on MI355X, the chain is
+      // slower on every workload tried (it gives up the grids' cross-tile
+      // prefetch of stage 0, pays a release per tile, and spills more)
+      (void)resident;
+      if (kChainEnabled && c.ns_steps <= MAX_CHAIN_STEPS) u = lm == MUON_LAUNCH_CHAIN;
+      use_chain[kv.first] = u;
+    }
+    for (int32_t i = 0; i < c.count; ++i) {
+      const MatGeom g = geom_of(c.shapes[i]);
+      if (use_chain[g.prec]) chain_need += chain_bytes(g, c.ns_steps);
+    }
+  }
+
   // workspace
   const size_t need = c.mode == MODE_NORMS ? 0 : workspace_bytes(c.shapes, c.count);
   if (need > ds.ws_bytes) {
@@ -533,6 +755,22 @@ muon_status run(const Call& c) {
     }
     ds.ws = p;
     ds.ws_bytes = need;
+  }
+  if (chain_need > ds.chain_ws_bytes) {
+    if (hipDeviceSynchronize() != hipSuccess) {
+      return fail(MUON_ERR_HIP, "hipDeviceSynchronize failed: %s", hipGetErrorString(hipGetLastError()));
+    }
+    drop_plans(ds);
+    if (ds.chain_ws) hipFree(ds.chain_ws);
+    ds.chain_ws = nullptr;
+    ds.chain_ws_bytes = 0;
+    void* p = nullptr;
+    if (hipMalloc(&p, chain_need) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MUON_ERR_OUT_OF_MEMORY, "chain workspace allocation of %zu bytes failed", chain_need);
+    }
+    ds.chain_ws = p;
+    ds.chain_ws_bytes = chain_need;
   }
 
   // plan key
@@ -670,8 +908,52 @@ muon_status run(const Call& c) {
                                        plan->d_scal, c.lr, c.scale_rule, wb, c.stream);
       });
     } else {
+      // step coefficients and the c == 0 pattern
+      std::vector<muon_ns_coeffs> cos(size_t(c.ns_steps));
+      uint32_t cmask = 0;
+      for (int it = 0; it < c.ns_steps; ++it) {
+        cos[size_t(it)] = (c.opt && c.opt->ns_schedule) ? c.opt->ns_schedule[it] : c.co;
+        if (cos[size_t(it)].c == 0.f && it < 32) cmask |= 1u << it;
+      }
+      // precision groups that run as one persistent chain
+      std::vector<MatGeom> geo;
+      for (size_t gi = 0; gi < plan->groups.size() && e == hipSuccess; ++gi) {
+        const int prec = plan->groups[gi].prec;
+        if (!use_chain[prec]) continue;
+        Plan::Chain& ch = plan->chains[gi];
+        const std::vector<uint64_t> ckey = {uint64_t(c.ns_steps), uint64_t(cmask),
+                                            reinterpret_cast<uint64_t>(ds.chain_ws)};
+        if (ch.key != ckey || !ch.dmem) {
+          if (geo.empty())
+            for (int32_t i = 0; i < c.count; ++i) geo.push_back(geom_of(c.shapes[i]));
+          // chain buffers of the earlier precision groups come first
+          size_t base = 0;
+          for (int32_t i = 0; i < c.count; ++i)
+            if (geo[i].prec < prec && use_chain[geo[i].prec]) base += chain_bytes(geo[i], c.ns_steps);
+          ch.key.clear();
+          st = build_chain(plan, gi, c.ns_steps, cmask, reinterpret_cast<char*>(ds.chain_ws) + base, geo, c.stream);
+          if (st != MUON_OK) return st;
+          ch.key = ckey;
+        }
+        ChainArgs ca;
+        memset(&ca, 0, sizeof(ca));
+        for (int it = 0; it < c.ns_steps; ++it) {
+          ca.a[it] = cos[size_t(it)].a;
+          ca.b[it] = cos[size_t(it)].b;
+          ca.c[it] = cos[size_t(it)].c;
+        }
+        ca.lr = c.lr;
+        ca.steps = c.ns_steps;
+        ca.scale_rule = c.scale_rule;
+        ca.cus_per_xcd = ds.cus_per_xcd;
+        ca.wb = wb;
+        e = timed(MUON_KC_CHAIN, c.stream, [&] {
+          return launch_ns_chain(prec, ch.d_imats, plan->d_scal, ch.d_items, ch.d_xcd_off, ch.per_xcd_max,
+                                 ch.d_steps, ch.d_sync, ch.nsync, ds.fail_flag, ca, c.stream);
+        });
+      }
       for (int it = 0; it < c.ns_steps && e == hipSuccess; ++it) {
-        const muon_ns_coeffs co = (c.opt && c.opt->ns_schedule) ? c.opt->ns_schedule[it] : c.co;
+        const muon_ns_coeffs co = cos[size_t(it)];
         PhaseArgs pa;
         pa.a = co.a;
         pa.b = co.b;
@@ -684,6 +966,7 @@ muon_status run(const Call& c) {
         pa.scale_rule = c.scale_rule;
         pa.cus_per_xcd = ds.cus_per_xcd;
         for (const auto& g : plan->groups) {
+          if (use_chain[g.prec]) continue;
           for (int ph = 0; ph < 3 && e == hipSuccess; ++ph) {
             if (ph == PH_POLY && co.c == 0.f) continue;  // GRAM already formed B = b A
             pa.per_xcd = g.per_xcd[ph];
@@ -1093,6 +1376,11 @@ muon_status muon_release_workspace(void) {
     if (kv.second.ws) hipFree(kv.second.ws);
     kv.second.ws = nullptr;
     kv.second.ws_bytes = 0;
+    if (kv.second.chain_ws) hipFree(kv.second.chain_ws);
+    kv.second.chain_ws = nullptr;
+    kv.second.chain_ws_bytes = 0;
+    if (kv.second.fail_flag) hipHostFree(kv.second.fail_flag);
+    kv.second.fail_flag = nullptr;
   }
   if (have_dev) hipSetDevice(cur);
   g_dev.clear();

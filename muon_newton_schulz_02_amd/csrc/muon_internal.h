@@ -92,6 +92,20 @@ struct AdamwConsts {
   float eps;
 };
 
+// One work item of the persistent Newton-Schulz chain: a tile of one phase
+// of one step of one matrix.
+enum ChainKind : int { CHAIN_GRAM_B = 0, CHAIN_GRAM_A = 1, CHAIN_POLY = 2, CHAIN_COMB = 3, CHAIN_COMB_LAST = 4 };
+struct ChainItem {
+  int32_t desc;           // descriptor of (step, matrix): buffers of that step
+  int32_t mat;            // matrix index (norm scalars, write-back table)
+  int32_t kind;           // ChainKind
+  int32_t step;           // Newton-Schulz step (index of its PhaseArgs)
+  int32_t tile;           // ti << 16 | tj
+  int32_t wait;           // done counter to wait for, -1 for none
+  int32_t need;           // its complete value
+  int32_t signal;         // done counter of this item's phase instance
+};
+
 // Launchers (defined in the .hip files).  All enqueue on `stream`.
 hipError_t launch_momentum(const MatDev* mats, const int32_t* etile_off, int32_t count,
                            int64_t total_tiles, float beta, int32_t nesterov, int32_t ema, int32_t mode,
@@ -105,6 +119,29 @@ enum Phase : int { PH_GRAM = 0, PH_POLY = 1, PH_COMB = 2 };
 hipError_t launch_adamw(const AdamwTensor* tensors, const int32_t* chunk_off, int32_t count, int64_t total_chunks,
                         const float2* rates, float lr, float d, const AdamwConsts& k, hipStream_t stream);
 hipError_t launch_mfma_probe(int64_t iterations, int32_t cus, float* sink, double* flops, hipStream_t stream);
+// Chain sync words: NUM_XCD queue heads, an abort word, padding, then the
+// completion counters.
+constexpr int CHAIN_SYNC_HEAD = 16;
+
+// Per-call scalars of a chain launch: the step coefficients and the
+// write-back parameters (PhaseArgs of each step are formed on the device
+// from these, so no host copy precedes the launch).
+constexpr int MAX_CHAIN_STEPS = 16;
+struct ChainArgs {
+  float a[MAX_CHAIN_STEPS], b[MAX_CHAIN_STEPS], c[MAX_CHAIN_STEPS];
+  float lr;
+  int32_t steps;
+  int32_t scale_rule;
+  int32_t cus_per_xcd;
+  const float2* wb;
+};
+
+// Zeroes sync[0, nsync) (heads, abort word, completion counters) and writes
+// the PhaseArgs of each step into `steps`, then runs the chain;
+// per_xcd_max is the longest XCD queue.
+hipError_t launch_ns_chain(int prec, const MatDev* imats, const MatScal* scal, const ChainItem* items,
+                           const int32_t* xcd_off, int32_t per_xcd_max, PhaseArgs* steps, int32_t* sync,
+                           int32_t nsync, int32_t* fail, const ChainArgs& args, hipStream_t stream);
 hipError_t launch_ns_phase(int prec, int phase, const MatDev* mats, const MatScal* scal,
                            const int2* tiles, const PhaseArgs& args, hipStream_t stream);
 

@@ -126,6 +126,16 @@ def _floats(*v):
     return ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)), arr
 
 
+def test_launch_mode_errors(L):
+    assert _call_v2(L, ctypes.byref(_opt(launch_mode=3))) == mb.MUON_ERR_INVALID_ARGUMENT
+    assert _call_v2(L, ctypes.byref(_opt(launch_mode=-1))) == mb.MUON_ERR_INVALID_ARGUMENT
+    # the chain takes at most 16 steps; the per-phase grids take any number
+    assert _call_v2(L, ctypes.byref(_opt(launch_mode=mb.LAUNCH_CHAIN)), steps=17) == mb.MUON_ERR_UNSUPPORTED
+    assert _call_v2(L, ctypes.byref(_opt(launch_mode=mb.LAUNCH_CHAIN)), steps=16) != mb.MUON_ERR_UNSUPPORTED
+    assert _call_v2(L, ctypes.byref(_opt(launch_mode=mb.LAUNCH_PHASE_GRIDS)), steps=17) \
+        not in (mb.MUON_ERR_UNSUPPORTED, mb.MUON_ERR_INVALID_ARGUMENT)
+
+
 @pytest.mark.parametrize("case", ["kind", "wd_neg", "wd_nan", "schedule_nan", "lr_nan", "scale_inf"])
 def test_option_errors(L, case):
     keep = []
