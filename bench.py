@@ -383,7 +383,7 @@ def measured_traffic(workload, kernel):
     elif kernel == "adamw":
         src, key = _src_hash("adamw.hip", "numeric.h", "muon_internal.h"), "adamw_src"
     else:
-        src, key = _src_hash("ns_gemm.hip", "numeric.h", "muon_internal.h"), "gemm_src"
+        src, key = _src_hash("ns_gemm.hip", "ns_tile.h", "numeric.h", "muon_internal.h"), "gemm_src"
     if src != kv.get(key) or kernel not in kv:
         return None
     return float(kv[kernel])
