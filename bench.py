@@ -64,6 +64,8 @@ def parse():
                     help="layers in the oracle's sample (about 10-15 s of host work for d24)")
     ap.add_argument("--launch-mode", choices=("auto", "grids", "chain"), default="auto",
                     help="Newton-Schulz launches: the library's choice, one grid per phase, or one persistent chain")
+    ap.add_argument("--tile-mode", choices=("auto", "large", "small"), default="auto",
+                    help="bf16 tile size of the Newton-Schulz products: the library's choice, 256 or 128")
     ap.add_argument("--no-adamw", action="store_true",
                     help="skip timing the AdamW half of the hybrid optimizer (d24 non-matrix parameters)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -113,12 +115,13 @@ def main():
               ns_steps=wl.ns_steps, scale_rule=wl.scale_rule)
     stream = torch.cuda.current_stream()
     mode = {"auto": mb.LAUNCH_AUTO, "grids": mb.LAUNCH_PHASE_GRIDS, "chain": mb.LAUNCH_CHAIN}[args.launch_mode]
+    tiles = {"auto": mb.TILES_AUTO, "large": mb.TILES_LARGE, "small": mb.TILES_SMALL}[args.tile_mode]
 
     def step():
-        if mode == mb.LAUNCH_AUTO:
+        if mode == mb.LAUNCH_AUTO and tiles == mb.TILES_AUTO:
             mb.muon_step_batched(sargs, **kw, stream=stream)
         else:
-            mb.muon_step_batched_v2(sargs, **kw, stream=stream, launch_mode=mode)
+            mb.muon_step_batched_v2(sargs, **kw, stream=stream, launch_mode=mode, tile_mode=tiles)
 
     for _ in range(args.warmup):
         step()
@@ -255,7 +258,7 @@ def main():
                    f"{args.workload} truncated to {args.layers} layers", "name": args.workload,
                    "matrices": n, "elements": elems, "ns_steps": k, "coeffs": list(wl.coeffs),
                    "matrices_per_s": round(n * 1e3 / ms_step, 1), "parallelism": "1 GPU",
-                   "launch_mode": args.launch_mode},
+                   "launch_mode": args.launch_mode, "tile_mode": args.tile_mode},
         "roofline": roofline,
         "ns_chain": ns_chain,
         "kernels": kernels,

@@ -126,6 +126,19 @@ typedef enum muon_launch_mode {
   MUON_LAUNCH_CHAIN = 2
 } muon_launch_mode;
 
+/* Tile size of the bf16 Newton-Schulz products (muon_step_options.tile_mode).
+ *   AUTO   128 x 128 when the stack has fewer 256 x 256 GRAM tiles than the
+ *          GPU has resident workgroups (GPT-2-small-sized stacks), else 256.
+ *   LARGE  256 x 256 tiles, eight waves, software-pipelined k-loop.
+ *   SMALL  128 x 128 tiles, four waves, one-stage k-loop.
+ * The working format is bf16 either way; split-bf16 and fp32 always use
+ * 128 x 128 tiles.                                                          */
+typedef enum muon_tile_mode {
+  MUON_TILES_AUTO = 0,
+  MUON_TILES_LARGE = 1,
+  MUON_TILES_SMALL = 2
+} muon_tile_mode;
+
 /* Update variants of muon_step_batched_v2.  The pages describe none of
  * them; they are the forms commonly used with Muon.  A zero-initialised
  * struct (or a NULL pointer) gives muon_step_batched bit for bit.
@@ -143,6 +156,7 @@ typedef enum muon_launch_mode {
  *                   scale rule for matrix i (t = fl32(lr_i*s_i), the product
  *                   in binary64), or NULL.
  * launch_mode       a muon_launch_mode.
+ * tile_mode         a muon_tile_mode.
  * The arrays are read during the call and not kept.                        */
 typedef struct muon_step_options {
   const muon_ns_coeffs* ns_schedule;
@@ -151,6 +165,7 @@ typedef struct muon_step_options {
   const float* lr_per_matrix;
   const float* scale_per_matrix;
   int32_t launch_mode;
+  int32_t tile_mode;
 } muon_step_options;
 
 /* One 2-D matrix.  rows, cols in [1, 65536]; ld_* >= cols.

@@ -70,7 +70,13 @@ class StepOptions(ctypes.Structure):
         ("ns_schedule", ctypes.POINTER(NsCoeffs)), ("weight_decay", ctypes.c_float),
         ("momentum_kind", ctypes.c_int32), ("lr_per_matrix", ctypes.POINTER(ctypes.c_float)),
         ("scale_per_matrix", ctypes.POINTER(ctypes.c_float)), ("launch_mode", ctypes.c_int32),
+        ("tile_mode", ctypes.c_int32),
     ]
+
+
+TILES_AUTO = 0
+TILES_LARGE = 1
+TILES_SMALL = 2
 
 
 LAUNCH_AUTO = 0
@@ -292,7 +298,8 @@ def muon_step_batched(params, grads=None, momenta=None, *, lr, beta, nesterov, n
 def muon_step_batched_v2(params, grads=None, momenta=None, *, lr, beta, nesterov, ns_coeffs, ns_steps,
                          scale_rule=SCALE_NONE, precision=NS_BF16, stream=None, updates_out=None,
                          ns_schedule=None, weight_decay=0.0, momentum_kind=MOMENTUM_HEAVY_BALL,
-                         lr_per_matrix=None, scale_per_matrix=None, launch_mode=LAUNCH_AUTO):
+                         lr_per_matrix=None, scale_per_matrix=None, launch_mode=LAUNCH_AUTO,
+                         tile_mode=TILES_AUTO):
     """muon_step_batched with the update variants of muon_step_options."""
     args = params if isinstance(params, StepArgs) else StepArgs(params, grads, momenta, precision, updates_out)
     a, b, c = ns_coeffs
@@ -308,6 +315,7 @@ def muon_step_batched_v2(params, grads=None, momenta=None, *, lr, beta, nesterov
     opt.weight_decay = float(weight_decay)
     opt.momentum_kind = int(momentum_kind)
     opt.launch_mode = int(launch_mode)
+    opt.tile_mode = int(tile_mode)
     for name, vals in (("lr_per_matrix", lr_per_matrix), ("scale_per_matrix", scale_per_matrix)):
         if vals is not None:
             if len(vals) != args.count:

@@ -424,16 +424,11 @@ constexpr bool kChainEnabled = true;
 
 int per_cu_blocks(int prec) { return (ns_tile(prec) == 256 || prec == PREC_BF16X3) ? 1 : 2; }
 
-// GRAM tiles per precision of the call's shapes (the phase that fills the
-// grid least in the d24-like stacks).
-std::map<int, int64_t> gram_tiles(const muon_matrix_desc* shapes, int32_t count) {
-  std::map<int, int64_t> t;
-  for (int32_t i = 0; i < count; ++i) {
-    const MatGeom g = geom_of(shapes[i]);
-    const int64_t tm = g.Mp / ns_tile(g.prec);
-    t[g.prec] += tm * (tm + 1) / 2;
-  }
-  return t;
+// GRAM tiles of a matrix in working format `prec` (the phase that fills
+// the grid least in the d24-like stacks).
+int64_t gram_tiles_of(const muon_matrix_desc& d, int prec) {
+  const int64_t tm = geom_of(d).Mp / ns_tile(prec);
+  return tm * (tm + 1) / 2;
 }
 
 // Chain workspace of one matrix for k steps: iterates X_1 .. X_{k-1} (X_0 is
@@ -616,6 +611,8 @@ muon_status validate_call(const Call& c) {
       return fail(MUON_ERR_INVALID_ARGUMENT, "unknown momentum_kind %d", o.momentum_kind);
     if (o.launch_mode < MUON_LAUNCH_AUTO || o.launch_mode > MUON_LAUNCH_CHAIN)
       return fail(MUON_ERR_INVALID_ARGUMENT, "unknown launch_mode %d", o.launch_mode);
+    if (o.tile_mode < MUON_TILES_AUTO || o.tile_mode > MUON_TILES_SMALL)
+      return fail(MUON_ERR_INVALID_ARGUMENT, "unknown tile_mode %d", o.tile_mode);
     if (o.launch_mode == MUON_LAUNCH_CHAIN && !kChainEnabled)
       return fail(MUON_ERR_UNSUPPORTED, "the persistent chain is switched off in this build");
     if (o.launch_mode == MUON_LAUNCH_CHAIN && c.ns_steps > MAX_CHAIN_STEPS)
@@ -717,25 +714,34 @@ muon_status run(const Call& c) {
                 "dependency; the results of that call are invalid");
   }
 
-  // which precision groups run as one persistent chain
+  // working format per matrix: a bf16 stack whose GRAM phase has fewer
+  // 256 x 256 tiles than the GPU has resident workgroups takes 128 x 128
+  // tiles (measured: 12 x 768^2 0.41 -> 0.34 ms per step; with three d24
+  // layers, 378 GRAM tiles, the pipelined 256 x 256 tiles stay faster)
+  std::vector<int> iprec(size_t(c.count), PREC_BF16);
+  if (c.mode != MODE_NORMS) {
+    const int32_t tmode = (c.mode == MODE_STEP && c.opt) ? c.opt->tile_mode : MUON_TILES_AUTO;
+    int64_t bf16_gram = 0;
+    for (int32_t i = 0; i < c.count; ++i)
+      if (c.shapes[i].precision == MUON_NS_BF16) bf16_gram += gram_tiles_of(c.shapes[i], PREC_BF16);
+    const bool small = tmode == MUON_TILES_SMALL ||
+                       (tmode == MUON_TILES_AUTO && bf16_gram < int64_t(NUM_XCD) * ds.cus_per_xcd);
+    for (int32_t i = 0; i < c.count; ++i)
+      iprec[size_t(i)] = (c.shapes[i].precision == MUON_NS_BF16 && small) ? int(PREC_BF16S) : c.shapes[i].precision;
+  }
+
+  // which working formats run as one persistent chain: only when asked for
+  // (AUTO keeps the per-phase grids: measured on MI355X, the chain is slower
+  // on every workload tried; it gives up the grids' cross-tile prefetch of
+  // stage 0, pays a release per tile, and spills more)
   std::map<int, bool> use_chain;
   size_t chain_need = 0;
   if (c.mode != MODE_NORMS && c.ns_steps >= 1) {
     const int32_t lm = (c.mode == MODE_STEP && c.opt) ? c.opt->launch_mode : MUON_LAUNCH_AUTO;
-    for (const auto& kv : gram_tiles(c.shapes, c.count)) {
-      const int64_t resident = int64_t(NUM_XCD) * ds.cus_per_xcd * per_cu_blocks(kv.first);
-      bool u = false;
-      // AUTO keeps the per-phase grids: measured on MI355X, the chain is
-      // slower on every workload tried (it gives up the grids' cross-tile
-      // prefetch of stage 0, pays a release per tile, and spills more)
-      (void)resident;
-      if (kChainEnabled && c.ns_steps <= MAX_CHAIN_STEPS) u = lm == MUON_LAUNCH_CHAIN;
-      use_chain[kv.first] = u;
-    }
-    for (int32_t i = 0; i < c.count; ++i) {
-      const MatGeom g = geom_of(c.shapes[i]);
-      if (use_chain[g.prec]) chain_need += chain_bytes(g, c.ns_steps);
-    }
+    for (int32_t i = 0; i < c.count; ++i)
+      use_chain[iprec[size_t(i)]] = kChainEnabled && c.ns_steps <= MAX_CHAIN_STEPS && lm == MUON_LAUNCH_CHAIN;
+    for (int32_t i = 0; i < c.count; ++i)
+      if (use_chain[iprec[size_t(i)]]) chain_need += chain_bytes(geom_of(c.shapes[i]), c.ns_steps);
   }
 
   // workspace
@@ -791,7 +797,7 @@ muon_status run(const Call& c) {
     key.push_back(uint64_t(d.ld_grad));
     key.push_back(uint64_t(d.ld_mom));
     key.push_back((uint64_t(uint32_t(d.param_dtype)) << 32) | uint32_t(d.grad_dtype));
-    key.push_back((uint64_t(uint32_t(d.mom_dtype)) << 32) | uint32_t(d.precision));
+    key.push_back((uint64_t(uint32_t(d.mom_dtype)) << 32) | uint32_t(iprec[size_t(i)]));
   }
   Plan* plan = nullptr;
   for (auto it = ds.plans.begin(); it != ds.plans.end(); ++it) {
@@ -840,7 +846,7 @@ muon_status run(const Call& c) {
         m.wvec_ok = (reinterpret_cast<uintptr_t>(c.params[i]) % 16 == 0 && (d.ld_param * psz) % 16 == 0) ? 1 : 0;
       }
       if (m.upd) m.uvec_ok = (reinterpret_cast<uintptr_t>(m.upd) % 16 == 0 && d.cols % 4 == 0) ? 1 : 0;
-      m.prec = c.mode == MODE_NORMS ? PREC_BF16 : d.precision;
+      m.prec = c.mode == MODE_NORMS ? int(PREC_BF16) : iprec[size_t(i)];
       const int64_t rp = g.transposed ? g.Np : g.Mp;  // natural padded rows
       const int64_t cp = g.transposed ? g.Mp : g.Np;  // natural padded cols
       m.etile_cols = int32_t(cp / ETILE);
@@ -929,7 +935,7 @@ muon_status run(const Call& c) {
           // chain buffers of the earlier precision groups come first
           size_t base = 0;
           for (int32_t i = 0; i < c.count; ++i)
-            if (geo[i].prec < prec && use_chain[geo[i].prec]) base += chain_bytes(geo[i], c.ns_steps);
+            if (iprec[size_t(i)] < prec && use_chain[iprec[size_t(i)]]) base += chain_bytes(geo[i], c.ns_steps);
           ch.key.clear();
           st = build_chain(plan, gi, c.ns_steps, cmask, reinterpret_cast<char*>(ds.chain_ws) + base, geo, c.stream);
           if (st != MUON_OK) return st;

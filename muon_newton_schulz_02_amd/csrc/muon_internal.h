@@ -19,7 +19,10 @@ constexpr int ETILE = 64;
 // Dispatch order puts consecutive workgroups on different XCDs.
 constexpr int NUM_XCD = 8;
 
-enum Prec : int { PREC_BF16 = 0, PREC_BF16X3 = 1, PREC_F32 = 2 };
+// Working formats of the Newton-Schulz products.  PREC_BF16S is the bf16
+// format on 128 x 128 tiles (a one-stage k-loop), chosen for stacks too small
+// to fill the GPU with 256 x 256 tiles; it stores exactly what PREC_BF16 does.
+enum Prec : int { PREC_BF16 = 0, PREC_BF16X3 = 1, PREC_F32 = 2, PREC_BF16S = 3 };
 
 // Per-matrix device descriptor.  "natural" means the caller's orientation
 // (rows x cols); the iteration runs on the wide orientation m x n (m <= n).
@@ -149,5 +152,6 @@ hipError_t launch_ns_phase(int prec, int phase, const MatDev* mats, const MatSca
 // bf16 (LDS holds two stages of 256x64 bf16 per operand); 128 where an
 // operand takes twice the bytes (split-bf16 planes, float32).
 constexpr int ns_tile(int prec) { return prec == PREC_BF16 ? 256 : 128; }
+constexpr bool bf16_single(int prec) { return prec == PREC_BF16 || prec == PREC_BF16S; }
 
 }  // namespace muon

@@ -38,6 +38,7 @@ template <int PREC> struct Fmt;
 template <> struct Fmt<PREC_BF16> { static constexpr int esz = 2, npl = 1; };
 template <> struct Fmt<PREC_BF16X3> { static constexpr int esz = 2, npl = 2; };
 template <> struct Fmt<PREC_F32> { static constexpr int esz = 4, npl = 1; };
+template <> struct Fmt<PREC_BF16S> { static constexpr int esz = 2, npl = 1; };
 
 // Tile shape per format: T x T tile, WP x WQ waves (rows x columns), NT threads.
 // bf16: 256 x 256 over eight waves (two per SIMD, each 128 x 64, 128
@@ -53,6 +54,7 @@ template <int PREC> struct Cfg;
 template <> struct Cfg<PREC_BF16> { static constexpr int BT = 256, WP = 2, WQ = 4, NT = 512; };
 template <> struct Cfg<PREC_BF16X3> { static constexpr int BT = 128, WP = 2, WQ = 2, NT = 256; };
 template <> struct Cfg<PREC_F32> { static constexpr int BT = 128, WP = 2, WQ = 2, NT = 256; };
+template <> struct Cfg<PREC_BF16S> { static constexpr int BT = 128, WP = 2, WQ = 2, NT = 256; };
 
 // LDS operand layout of the split-bf16 and binary32 tiles: row r at r * PITCH,
 // 16-byte chunk ch at 16 (ch ^ ((r >> 4) & 7)).  (The bf16 tiles use their
@@ -214,7 +216,7 @@ __device__ __forceinline__ void write_back_runs(const MatDev& md, const float* s
 // acc += A operand (Q side) x B operand (P side) over one k-slab.
 template <int PREC>
 __device__ __forceinline__ void mfma_step(f32x16& acc, const u32x4* q, const u32x4* p) {
-  if constexpr (PREC == PREC_BF16) {
+  if constexpr (bf16_single(PREC)) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q[0]),
                                                    __builtin_bit_cast(bf16x8, p[0]), acc, 0, 0, 0);
   } else if constexpr (PREC == PREC_BF16X3) {
@@ -263,7 +265,7 @@ __device__ __forceinline__ void identity_frag(u32x4* out, int pos, float alpha) 
 
 template <int PREC>
 __device__ __forceinline__ void mfma_identity(f32x16& acc, const u32x4* q, const u32x4* id) {
-  if constexpr (PREC == PREC_BF16) {
+  if constexpr (bf16_single(PREC)) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q[0]),
                                                    __builtin_bit_cast(bf16x8, id[1]), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q[0]),

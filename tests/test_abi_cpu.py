@@ -126,6 +126,12 @@ def _floats(*v):
     return ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)), arr
 
 
+def test_tile_mode_errors(L):
+    assert _call_v2(L, ctypes.byref(_opt(tile_mode=3))) == mb.MUON_ERR_INVALID_ARGUMENT
+    assert _call_v2(L, ctypes.byref(_opt(tile_mode=-1))) == mb.MUON_ERR_INVALID_ARGUMENT
+    assert _call_v2(L, ctypes.byref(_opt(tile_mode=mb.TILES_SMALL))) != mb.MUON_ERR_INVALID_ARGUMENT
+
+
 def test_launch_mode_errors(L):
     assert _call_v2(L, ctypes.byref(_opt(launch_mode=3))) == mb.MUON_ERR_INVALID_ARGUMENT
     assert _call_v2(L, ctypes.byref(_opt(launch_mode=-1))) == mb.MUON_ERR_INVALID_ARGUMENT

@@ -98,3 +98,23 @@ def test_default_options_match_plain_step():
     for i in range(len(SHAPES)):
         assert np.array_equal(bits(a[0][i]), bits(to_np(w_d[i])))
         assert np.array_equal(bits(a[1][i]), bits(to_np(m_d[i])))
+
+
+@pytest.mark.parametrize("tile_mode", [mb.TILES_LARGE, mb.TILES_SMALL])
+@pytest.mark.parametrize("launch_mode", [mb.LAUNCH_PHASE_GRIDS, mb.LAUNCH_CHAIN])
+def test_bf16_tile_sizes(tile_mode, launch_mode):
+    # 256 x 256 (pipelined) and 128 x 128 (one-stage) bf16 tiles, per-phase
+    # grids and the persistent chain: O within the bf16 gate, W bit-exact given O
+    _announce(f"bf16 tiles mode={tile_mode} launch={launch_mode}")
+    ws, gs, ms = _inputs(67 + tile_mode, torch.bfloat16)
+    lr = f32(0.02)
+    w1, m1, o1 = _run_v2(ws, gs, ms, precision=mb.NS_BF16, steps=5, lr=lr, beta=0.95, nesterov=1,
+                         tile_mode=tile_mode, launch_mode=launch_mode)
+    for i in range(len(SHAPES)):
+        w0, g0, m0 = to_np(ws[i]), to_np(gs[i]), to_np(ms[i])
+        ref = orc.muon_step(w0, g0, m0, lr=lr, beta=0.95, nesterov=True, coeffs=MUON, steps=5, param_bf16=True)
+        assert np.array_equal(bits(m1[i]), bits(ref.m))
+        err = orc.rel_frobenius(o1[i], ref.o)
+        print(f"  {SHAPES[i]}: rel-F {err:.2e}")
+        assert err <= PREC_TOL[mb.NS_BF16]
+        assert np.array_equal(bits(w1[i]), bits(orc.write_back(w0, o1[i], lr, 1.0, True)))
