@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <list>
 #include <map>
@@ -421,6 +422,19 @@ muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vec
 // ------------------------------------------------------------ chain plan
 // Whether AUTO may pick the persistent chain and CHAIN is accepted.
 constexpr bool kChainEnabled = true;
+
+// Polls (about 1 us each) before a chain dependency wait gives up: 2^20, or
+// MUON_CHAIN_SPIN_LIMIT from the environment (read per call), which tests
+// set very low to drive the give-up path from the host.
+int64_t chain_spin_limit() {
+  const char* e = std::getenv("MUON_CHAIN_SPIN_LIMIT");
+  if (e && *e) {
+    char* end = nullptr;
+    const long long v = std::strtoll(e, &end, 10);
+    if (end && *end == '\0' && v >= 0) return int64_t(v);
+  }
+  return int64_t(1) << 20;
+}
 
 int per_cu_blocks(int prec) { return (ns_tile(prec) == 256 || prec == PREC_BF16X3) ? 1 : 2; }
 
@@ -953,6 +967,7 @@ muon_status run(const Call& c) {
         ca.scale_rule = c.scale_rule;
         ca.cus_per_xcd = ds.cus_per_xcd;
         ca.wb = wb;
+        ca.spin_limit = chain_spin_limit();
         e = timed(MUON_KC_CHAIN, c.stream, [&] {
           return launch_ns_chain(prec, ch.d_imats, plan->d_scal, ch.d_items, ch.d_xcd_off, ch.per_xcd_max,
                                  ch.d_steps, ch.d_sync, ch.nsync, ds.fail_flag, ca, c.stream);

@@ -137,6 +137,7 @@ struct ChainArgs {
   int32_t scale_rule;
   int32_t cus_per_xcd;
   const float2* wb;
+  int64_t spin_limit;     // polls before a dependency wait gives up
 };
 
 // Zeroes sync[0, nsync) (heads, abort word, completion counters) and writes

@@ -21,7 +21,7 @@ namespace {
 // order.  The earliest unfinished item overall therefore either is being run
 // (its inputs are complete) or waits at the head of its queue, whose
 // workgroups hold only finished items; so it runs.  The wait is bounded all
-// the same: after CHAIN_SPIN polls it gives up, raises the abort word (every
+// the same: after spin_limit polls it gives up, raises the abort word (every
 // other wait then gives up at its next poll) and the host's failure flag,
 // and skips the tile (the call's results are then invalid and the host
 // reports it), so the launch always ends.
@@ -32,8 +32,6 @@ namespace {
 // producer makes its stores visible with a release fence (L2 write-back)
 // before its agent-scope count, and the consumer reads the count with an
 // agent-scope atomic load before any load of the data.
-
-constexpr int64_t CHAIN_SPIN = int64_t(1) << 20;   // polls of about 1 us each
 
 template <int PREC, int PHASE, int VAR>
 __device__ __forceinline__ void chain_tile(const MatDev& md, const MatScal* __restrict__ scal, int mat, int ti,
@@ -54,7 +52,8 @@ __global__ __launch_bounds__(Cfg<PREC>::NT) void ns_chain_kernel(const MatDev* _
                                                                  const ChainItem* __restrict__ items,
                                                                  const int32_t* __restrict__ xcd_off,
                                                                  const PhaseArgs* __restrict__ steps,
-                                                                 int32_t* __restrict__ sync, int32_t* fail) {
+                                                                 int32_t* __restrict__ sync, int32_t* fail,
+                                                                 int64_t spin_limit) {
   constexpr int NPL = Fmt<PREC>::npl;
   constexpr int STAGE = 2 * NPL * Cfg<PREC>::BT * PITCH;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
@@ -91,7 +90,7 @@ __global__ __launch_bounds__(Cfg<PREC>::NT) void ns_chain_kernel(const MatDev* _
               ok = 0;
               break;
             }
-            if (polls >= CHAIN_SPIN) {
+            if (polls >= spin_limit) {
               ok = 0;
               __hip_atomic_store(abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               __hip_atomic_store(fail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -167,7 +166,7 @@ hipError_t launch_chain_prec(const MatDev* imats, const MatScal* scal, const Cha
   constexpr int per_cu = (ns_tile(PREC) == 256 || PREC == PREC_BF16X3) ? 1 : 2;
   const int per_xcd = std::min(per_xcd_max, args.cus_per_xcd * per_cu);
   hipLaunchKernelGGL(ns_chain_kernel<PREC>, dim3(unsigned(NUM_XCD) * unsigned(per_xcd)), dim3(Cfg<PREC>::NT), 0,
-                     stream, imats, scal, items, xcd_off, steps, sync, fail);
+                     stream, imats, scal, items, xcd_off, steps, sync, fail, args.spin_limit);
   return hipGetLastError();
 }
 

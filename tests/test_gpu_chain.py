@@ -2,6 +2,7 @@
 step, per-XCD work queues, per-(matrix, phase) completion counts) against the
 per-phase grids: the same tiles in the same arithmetic, so W, M and the
 exported update must agree bit for bit; and against the oracle directly."""
+import os
 import sys
 
 import numpy as np
@@ -145,3 +146,24 @@ def test_chain_d24_share_equals_phase_grids():
         outs.append([w.view(torch.int16).cpu().numpy() for w in w_d])
     for i, (a, b) in enumerate(zip(*outs)):
         assert np.array_equal(a, b), f"{wl.specs[i].name}: W differs between the chain and the grids"
+
+
+def test_chain_wait_give_up_is_reported_and_cleared():
+    # the host sets the chain's wait limit to zero polls: items that find
+    # their inputs incomplete give up and skip, every wait ends, the launch
+    # finishes, and the next call on the device reports it once
+    _announce("chain give-up path")
+    shapes = [(1024, 1024)] * 4
+    ws, gs, ms = _inputs(shapes, 101)
+    os.environ["MUON_CHAIN_SPIN_LIMIT"] = "0"
+    try:
+        _run(ws, gs, ms, mb.LAUNCH_CHAIN, precision=mb.NS_BF16, steps=5)
+    finally:
+        del os.environ["MUON_CHAIN_SPIN_LIMIT"]
+    with pytest.raises(mb.MuonError) as ei:
+        _run(ws, gs, ms, mb.LAUNCH_CHAIN, precision=mb.NS_BF16, steps=5)
+    assert ei.value.status == mb.MUON_ERR_HIP and "gave up" in ei.value.detail
+    # cleared: the next calls run and agree with the per-phase grids
+    a = _run(ws, gs, ms, mb.LAUNCH_PHASE_GRIDS, precision=mb.NS_BF16, steps=5)
+    b = _run(ws, gs, ms, mb.LAUNCH_CHAIN, precision=mb.NS_BF16, steps=5)
+    _same(a[0], b[0], "W")
