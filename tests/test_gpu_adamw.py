@@ -170,3 +170,16 @@ def test_d24_adamw_full_size_sampled():
         assert np.array_equal(bits(to_np(v_d[i][it])), bits(rv)), f"{wl.specs[i].name}: exp_avg_sq"
         assert np.array_equal(bits(to_np(p_d[i][it])), bits(rp)), f"{wl.specs[i].name}: param"
     assert all(torch.isfinite(p.float()).all().item() for p in p_d)
+
+
+def test_mfma_probe_counts_and_leaves_sink():
+    # the measurement aid: its operation count follows from the grid it
+    # launches (8 waves per compute unit, 4 chains of 32x32x16 MFMAs per
+    # round) and the kernel never writes its sink
+    _announce("mfma probe")
+    sink = torch.full((1,), 7.0, device="cuda")
+    flops = mb.muon_mfma_probe(100, sink)
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert flops == cus * 8 * 100 * 4 * (2 * 32 * 32 * 16)
+    assert sink.item() == 7.0
