@@ -284,10 +284,19 @@ struct TileSrc {
   double cost;
 };
 
-std::vector<int2> xcd_lists(const std::vector<TileSrc>& src, int32_t* per_xcd) {
+//
+// `blocks` > 0 is the number of workgroups that will walk each XCD's list
+// (entry b, b + blocks, ... for workgroup b).  Where that strided walk leaves
+// one workgroup far more work than the others (tiles of very different cost,
+// few per workgroup: a stack's rectangular GRAM tiles beside its square
+// ones), the XCD's list is laid out instead as the workgroups' longest-first
+// assignments, interleaved (workgroup b's k-th tile at entry b + blocks k,
+// its walk ending at its first empty entry).
+std::vector<int2> xcd_lists(const std::vector<TileSrc>& src, int32_t* per_xcd, int blocks = 0) {
   double total = 0;
   for (const auto& t : src) total += t.cost;
   std::vector<std::vector<int2>> bins(NUM_XCD);
+  std::vector<std::vector<double>> costs(NUM_XCD);
   const double target = total / NUM_XCD;
   double acc = 0;
   int bin = 0;
@@ -295,14 +304,44 @@ std::vector<int2> xcd_lists(const std::vector<TileSrc>& src, int32_t* per_xcd) {
     // move on once this XCD holds its share (the last XCD takes the rest)
     if (bin < NUM_XCD - 1 && acc + 0.5 * t.cost > target * (bin + 1)) ++bin;
     bins[bin].push_back(make_int2(t.mat, (t.ti << 16) | t.tj));
+    costs[bin].push_back(t.cost);
     acc += t.cost;
   }
+  std::vector<std::vector<int2>> lay(NUM_XCD);
+  for (int x = 0; x < NUM_XCD; ++x) {
+    lay[x] = bins[x];
+    const size_t n = bins[x].size();
+    if (blocks <= 0 || n <= size_t(blocks)) continue;
+    double strided = 0;
+    for (int b = 0; b < blocks; ++b) {
+      double w = 0;
+      for (size_t i = size_t(b); i < n; i += size_t(blocks)) w += costs[x][i];
+      strided = std::max(strided, w);
+    }
+    std::vector<size_t> idx(n);
+    for (size_t i = 0; i < n; ++i) idx[i] = i;
+    std::stable_sort(idx.begin(), idx.end(), [&](size_t a, size_t b) { return costs[x][a] > costs[x][b]; });
+    std::vector<double> load(size_t(blocks), 0.0);
+    std::vector<std::vector<int2>> per(static_cast<size_t>(blocks));
+    for (size_t i : idx) {
+      const size_t b = size_t(std::min_element(load.begin(), load.end()) - load.begin());
+      load[b] += costs[x][i];
+      per[b].push_back(bins[x][i]);
+    }
+    const double lpt = *std::max_element(load.begin(), load.end());
+    if (lpt > 0.95 * strided) continue;
+    size_t kmax = 0;
+    for (auto& v : per) kmax = std::max(kmax, v.size());
+    lay[x].assign(kmax * size_t(blocks), make_int2(-1, 0));
+    for (int b = 0; b < blocks; ++b)
+      for (size_t k = 0; k < per[size_t(b)].size(); ++k) lay[x][size_t(b) + k * size_t(blocks)] = per[size_t(b)][k];
+  }
   size_t mx = 0;
-  for (auto& b : bins) mx = std::max(mx, b.size());
+  for (auto& l : lay) mx = std::max(mx, l.size());
   *per_xcd = int32_t(mx);
   std::vector<int2> out(mx * NUM_XCD, make_int2(-1, 0));
   for (int x = 0; x < NUM_XCD; ++x)
-    for (size_t i = 0; i < bins[x].size(); ++i) out[x * mx + i] = bins[x][i];
+    for (size_t i = 0; i < lay[x].size(); ++i) out[x * mx + i] = lay[x][i];
   return out;
 }
 
@@ -345,7 +384,7 @@ std::vector<TileSrc> phase_tiles(const std::vector<MatDev>& hm, const std::vecto
 }
 
 muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vector<int32_t>& etile_off,
-                       hipStream_t stream) {
+                       int cus_per_xcd, hipStream_t stream) {
   const int32_t count = int32_t(hm.size());
   const std::vector<int> order = cost_order(hm);
   std::vector<int> precs;
@@ -359,7 +398,8 @@ muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vec
     Plan::Group g;
     g.prec = prec;
     for (int ph = 0; ph < 3; ++ph) {
-      lists.push_back(xcd_lists(phase_tiles(hm, order, prec, ph), &g.per_xcd[ph]));
+      const int blocks = cus_per_xcd * ((ns_tile(prec) == 256 || prec == PREC_BF16X3) ? 1 : 2);
+      lists.push_back(xcd_lists(phase_tiles(hm, order, prec, ph), &g.per_xcd[ph], blocks));
       g.tiles[ph] = nullptr;
     }
     groups.push_back(g);
@@ -878,7 +918,7 @@ muon_status run(const Call& c) {
       return fail(MUON_ERR_UNSUPPORTED, "too many elements in one call");
     plan = new Plan();
     plan->key = key;
-    st = build_plan(plan, hm, etile_off, c.stream);
+    st = build_plan(plan, hm, etile_off, ds.cus_per_xcd, c.stream);
     if (st != MUON_OK) {
       if (plan->dmem) hipFree(plan->dmem);
       delete plan;
