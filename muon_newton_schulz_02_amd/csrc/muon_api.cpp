@@ -345,6 +345,9 @@ std::vector<int2> xcd_lists(const std::vector<TileSrc>& src, int32_t* per_xcd, i
   return out;
 }
 
+// Workgroups of a phase kernel per compute unit (as the launchers size their grids).
+int per_cu_blocks(int prec) { return (ns_tile(prec) == 256 || prec == PREC_BF16X3) ? 1 : 2; }
+
 // Matrices by decreasing Newton-Schulz cost, so large ones start first.
 std::vector<int> cost_order(const std::vector<MatDev>& hm) {
   std::vector<int> order(hm.size());
@@ -398,7 +401,7 @@ muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vec
     Plan::Group g;
     g.prec = prec;
     for (int ph = 0; ph < 3; ++ph) {
-      const int blocks = cus_per_xcd * ((ns_tile(prec) == 256 || prec == PREC_BF16X3) ? 1 : 2);
+      const int blocks = cus_per_xcd * per_cu_blocks(prec);
       lists.push_back(xcd_lists(phase_tiles(hm, order, prec, ph), &g.per_xcd[ph], blocks));
       g.tiles[ph] = nullptr;
     }
@@ -460,9 +463,6 @@ muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vec
 }
 
 // ------------------------------------------------------------ chain plan
-// Whether AUTO may pick the persistent chain and CHAIN is accepted.
-constexpr bool kChainEnabled = true;
-
 // Polls (about 1 us each) before a chain dependency wait gives up: 2^20, or
 // MUON_CHAIN_SPIN_LIMIT from the environment (read per call), which tests
 // set very low to drive the give-up path from the host.
@@ -476,7 +476,6 @@ int64_t chain_spin_limit() {
   return int64_t(1) << 20;
 }
 
-int per_cu_blocks(int prec) { return (ns_tile(prec) == 256 || prec == PREC_BF16X3) ? 1 : 2; }
 
 // GRAM tiles of a matrix in working format `prec` (the phase that fills
 // the grid least in the d24-like stacks).
@@ -667,8 +666,6 @@ muon_status validate_call(const Call& c) {
       return fail(MUON_ERR_INVALID_ARGUMENT, "unknown launch_mode %d", o.launch_mode);
     if (o.tile_mode < MUON_TILES_AUTO || o.tile_mode > MUON_TILES_SMALL)
       return fail(MUON_ERR_INVALID_ARGUMENT, "unknown tile_mode %d", o.tile_mode);
-    if (o.launch_mode == MUON_LAUNCH_CHAIN && !kChainEnabled)
-      return fail(MUON_ERR_UNSUPPORTED, "the persistent chain is switched off in this build");
     if (o.launch_mode == MUON_LAUNCH_CHAIN && c.ns_steps > MAX_CHAIN_STEPS)
       return fail(MUON_ERR_UNSUPPORTED, "the persistent chain takes at most %d Newton-Schulz steps", MAX_CHAIN_STEPS);
     if (o.ns_schedule)
@@ -793,7 +790,7 @@ muon_status run(const Call& c) {
   if (c.mode != MODE_NORMS && c.ns_steps >= 1) {
     const int32_t lm = (c.mode == MODE_STEP && c.opt) ? c.opt->launch_mode : MUON_LAUNCH_AUTO;
     for (int32_t i = 0; i < c.count; ++i)
-      use_chain[iprec[size_t(i)]] = kChainEnabled && c.ns_steps <= MAX_CHAIN_STEPS && lm == MUON_LAUNCH_CHAIN;
+      use_chain[iprec[size_t(i)]] = c.ns_steps <= MAX_CHAIN_STEPS && lm == MUON_LAUNCH_CHAIN;
     for (int32_t i = 0; i < c.count; ++i)
       if (use_chain[iprec[size_t(i)]]) chain_need += chain_bytes(geom_of(c.shapes[i]), c.ns_steps);
   }
