@@ -360,8 +360,23 @@ std::vector<int> cost_order(const std::vector<MatDev>& hm) {
   return order;
 }
 
+// Tile rows per raster band of a matrix with tm tile rows.  The tiles in
+// flight on one XCD (32 of 256 x 256, 64 of 128 x 128) then cover h row
+// panels and about 32 / h (64 / h) column panels; h + 32 / h is least near
+// h = 6, and a band height that divides tm leaves no short band.  256 x 256:
+// the whole height up to 8 rows, else the divisor of tm in 4..8 nearest 6,
+// else 6; 128 x 128: 8.  (d24 COMBINE, tm = 6: 1 % faster than 4-row bands.)
+int band_rows(int tm, int T) {
+  if (T != 256) return 8;
+  if (tm <= 8) return std::max(tm, 1);
+  int best = 0;
+  for (int h = 4; h <= 8; ++h)
+    if (tm % h == 0 && (best == 0 || std::abs(h - 6) <= std::abs(best - 6))) best = h;
+  return best ? best : 6;
+}
+
 // The tiles of one phase over the matrices of one precision, in `order`:
-// a grouped raster (bands of GROUP_M tile rows walked column by column) so
+// a grouped raster (bands of band_rows tile rows walked column by column) so
 // that tiles in flight together share row and column operand panels; GRAM
 // and POLY take the tiles on or above the diagonal.  Cost = K.
 std::vector<TileSrc> phase_tiles(const std::vector<MatDev>& hm, const std::vector<int>& order, int prec, int ph) {
@@ -370,8 +385,8 @@ std::vector<TileSrc> phase_tiles(const std::vector<MatDev>& hm, const std::vecto
     const MatDev& m = hm[i];
     if (m.prec != prec) continue;
     const int T = ns_tile(prec);
-    const int GROUP_M = T == 256 ? 4 : 8;
     const int tm = m.Mp / T, tn = m.Np / T;
+    const int GROUP_M = band_rows(tm, T);
     if (ph == PH_COMB) {
       for (int g0 = 0; g0 < tm; g0 += GROUP_M)
         for (int b = 0; b < tn; ++b)
