@@ -241,30 +241,30 @@ hipError_t timed(int kc, hipStream_t stream, F&& launch) {
   if (!g_timing) return launch();
   hipEvent_t b = pool_event(), e = pool_event();
   if (!b || !e) return launch();
-  hipEventRecord(b, stream);
+  (void)hipEventRecord(b, stream);
   hipError_t r = launch();
-  hipEventRecord(e, stream);
+  (void)hipEventRecord(e, stream);
   g_timed.push_back({b, e, kc});
   return r;
 }
 
 void free_plan(Plan* p) {
   if (p->last_use) {
-    hipEventSynchronize(p->last_use);
-    hipEventDestroy(p->last_use);
+    (void)hipEventSynchronize(p->last_use);
+    (void)hipEventDestroy(p->last_use);
   }
-  if (p->dmem) hipFree(p->dmem);
+  if (p->dmem) (void)hipFree(p->dmem);
   for (auto& ch : p->chains)
-    if (ch.dmem) hipFree(ch.dmem);
+    if (ch.dmem) (void)hipFree(ch.dmem);
   delete p;
 }
 
 void free_adamw_plan(AdamwPlan* p) {
   if (p->last_use) {
-    hipEventSynchronize(p->last_use);
-    hipEventDestroy(p->last_use);
+    (void)hipEventSynchronize(p->last_use);
+    (void)hipEventDestroy(p->last_use);
   }
-  if (p->dmem) hipFree(p->dmem);
+  if (p->dmem) (void)hipFree(p->dmem);
   delete p;
 }
 
@@ -275,16 +275,15 @@ void drop_plans(DeviceState& ds) {
   ds.adamw_plans.clear();
 }
 
-// Split each matrix's tiles over the XCDs: matrices in order, tiles of one
-// matrix contiguous, each XCD taking a contiguous run of about 1/8 of the
-// total cost.  Returns per-XCD lists padded to a common length with -1.
 struct TileSrc {
   int mat;
   int ti, tj;
   double cost;
 };
 
-//
+// Split each matrix's tiles over the XCDs: matrices in order, tiles of one
+// matrix contiguous, each XCD taking a contiguous run of about 1/8 of the
+// total cost.  Returns per-XCD lists padded to a common length with -1.
 // `blocks` > 0 is the number of workgroups that will walk each XCD's list
 // (entry b, b + blocks, ... for workgroup b).  Where that strided walk leaves
 // one workgroup far more work than the others (tiles of very different cost,
@@ -451,7 +450,7 @@ muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vec
     memcpy(host.data() + off_lists[i], lists[i].data(), sizeof(int2) * lists[i].size());
   if (hipMemcpyAsync(dmem, host.data(), off, hipMemcpyHostToDevice, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess) {
-    hipFree(dmem);
+    (void)hipFree(dmem);
     return fail(MUON_ERR_HIP, "plan upload failed: %s", hipGetErrorString(hipGetLastError()));
   }
   char* base = reinterpret_cast<char*>(dmem);
@@ -511,7 +510,7 @@ muon_status build_chain(Plan* plan, size_t gi, int k, uint32_t cmask, char* chai
                         const std::vector<MatGeom>& geo, hipStream_t stream) {
   Plan::Chain& ch = plan->chains[gi];
   if (ch.dmem) {
-    hipFree(ch.dmem);
+    (void)hipFree(ch.dmem);
     ch.dmem = nullptr;
   }
   const int prec = ch.prec;
@@ -611,7 +610,7 @@ muon_status build_chain(Plan* plan, size_t gi, int k, uint32_t cmask, char* chai
   memcpy(host.data() + o_xoff, xoff.data(), sizeof(int32_t) * (NUM_XCD + 1));
   if (hipMemcpyAsync(dmem, host.data(), off, hipMemcpyHostToDevice, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess) {
-    hipFree(dmem);
+    (void)hipFree(dmem);
     return fail(MUON_ERR_HIP, "chain plan upload failed: %s", hipGetErrorString(hipGetLastError()));
   }
   char* b = reinterpret_cast<char*>(dmem);
@@ -817,7 +816,7 @@ muon_status run(const Call& c) {
       return fail(MUON_ERR_HIP, "hipDeviceSynchronize failed: %s", hipGetErrorString(hipGetLastError()));
     }
     drop_plans(ds);
-    if (ds.ws) hipFree(ds.ws);
+    if (ds.ws) (void)hipFree(ds.ws);
     ds.ws = nullptr;
     ds.ws_bytes = 0;
     void* p = nullptr;
@@ -833,7 +832,7 @@ muon_status run(const Call& c) {
       return fail(MUON_ERR_HIP, "hipDeviceSynchronize failed: %s", hipGetErrorString(hipGetLastError()));
     }
     drop_plans(ds);
-    if (ds.chain_ws) hipFree(ds.chain_ws);
+    if (ds.chain_ws) (void)hipFree(ds.chain_ws);
     ds.chain_ws = nullptr;
     ds.chain_ws_bytes = 0;
     void* p = nullptr;
@@ -932,7 +931,7 @@ muon_status run(const Call& c) {
     plan->key = key;
     st = build_plan(plan, hm, etile_off, ds.cus_per_xcd, c.stream);
     if (st != MUON_OK) {
-      if (plan->dmem) hipFree(plan->dmem);
+      if (plan->dmem) (void)hipFree(plan->dmem);
       delete plan;
       return st;
     }
@@ -1052,7 +1051,7 @@ muon_status run(const Call& c) {
     }
   }
   if (e != hipSuccess) return fail(MUON_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  hipEventRecord(plan->last_use, c.stream);
+  (void)hipEventRecord(plan->last_use, c.stream);
   return MUON_OK;
 }
 
@@ -1171,7 +1170,7 @@ muon_status build_adamw_plan(AdamwPlan* plan, const AdamwCall& c) {
   memcpy(host.data() + o_off, off.data(), sizeof(int32_t) * (n + 1));
   if (hipMemcpyAsync(dmem, host.data(), bytes, hipMemcpyHostToDevice, c.stream) != hipSuccess ||
       hipStreamSynchronize(c.stream) != hipSuccess) {
-    hipFree(dmem);
+    (void)hipFree(dmem);
     return fail(MUON_ERR_HIP, "AdamW plan upload failed: %s", hipGetErrorString(hipGetLastError()));
   }
   char* base = reinterpret_cast<char*>(dmem);
@@ -1275,7 +1274,7 @@ muon_status run_adamw(const AdamwCall& c) {
     });
   }
   if (e != hipSuccess) return fail(MUON_ERR_HIP, "AdamW launch failed: %s", hipGetErrorString(e));
-  hipEventRecord(plan->last_use, c.stream);
+  (void)hipEventRecord(plan->last_use, c.stream);
   return MUON_OK;
 }
 
@@ -1397,7 +1396,7 @@ muon_status muon_timing_enable(int32_t enable) {
   t_last_error.clear();
   if (!enable) {
     for (auto& t : g_timed) {
-      hipEventSynchronize(t.end);
+      (void)hipEventSynchronize(t.end);
       g_event_pool.push_back(t.beg);
       g_event_pool.push_back(t.end);
     }
@@ -1444,18 +1443,18 @@ muon_status muon_release_workspace(void) {
   const bool have_dev = hipGetDevice(&cur) == hipSuccess;
   for (auto& kv : g_dev) {
     if (hipSetDevice(kv.first) != hipSuccess) continue;
-    hipDeviceSynchronize();
+    (void)hipDeviceSynchronize();
     drop_plans(kv.second);
-    if (kv.second.ws) hipFree(kv.second.ws);
+    if (kv.second.ws) (void)hipFree(kv.second.ws);
     kv.second.ws = nullptr;
     kv.second.ws_bytes = 0;
-    if (kv.second.chain_ws) hipFree(kv.second.chain_ws);
+    if (kv.second.chain_ws) (void)hipFree(kv.second.chain_ws);
     kv.second.chain_ws = nullptr;
     kv.second.chain_ws_bytes = 0;
-    if (kv.second.fail_flag) hipHostFree(kv.second.fail_flag);
+    if (kv.second.fail_flag) (void)hipHostFree(kv.second.fail_flag);
     kv.second.fail_flag = nullptr;
   }
-  if (have_dev) hipSetDevice(cur);
+  if (have_dev) (void)hipSetDevice(cur);
   g_dev.clear();
   (void)hipGetLastError();
   return MUON_OK;

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(Cfg<PREC>::NT) void ns_gemm_kernel(const MatDev* __
   using G = Geo<Fmt<PREC>::esz, Cfg<PREC>::BT, Cfg<PREC>::NT>;
   u32x4 rp[NPL][G::NREG], rq[NPL][G::NREG];  // the next stage 0, carried across tiles
   int slot = blockIdx.x / NUM_XCD;
-  // lists are padded at their end only
+  // a walk ends at its first padding entry (workgroup slot, slot + stride, ...)
   int2 te = slot < pa.per_xcd ? list[slot] : int2{-1, 0};
   if (te.x >= 0) {
     OpSrc sp, sq;

@@ -1,0 +1,325 @@
+// CPU check of the library's host-side planning: muon_api.cpp compiled for
+// the host with the HIP runtime calls replaced by host-memory stubs and the
+// kernel launchers replaced by checkers that walk the device lists exactly as
+// the kernels do.
+//   - per-phase grids: every tile of every matrix visited exactly once, no
+//     tile outside its matrix, GRAM/POLY only on or above the diagonal, and
+//     the busiest workgroup's work against the mean (load balance);
+//   - persistent chain: every wait names a counter that receives exactly the
+//     awaited number of signals, every buffer an item uses lies inside a
+//     workspace allocation, and a round-robin scheduler over the per-XCD
+//     queues (a workgroup holding an item whose inputs are incomplete makes
+//     no progress) finishes every item without deadlock.
+// Exit status 0 when every case passes; one "CASE" line per case.
+#include <hip/hip_runtime.h>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <set>
+#include <string>
+#include <tuple>
+#include <vector>
+
+static std::vector<std::pair<char*, size_t>> g_allocs;
+static hipError_t s_malloc(void** p, size_t n) {
+  const size_t m = (n + 255) / 256 * 256;
+  *p = aligned_alloc(256, m);
+  if (!*p) return hipErrorOutOfMemory;
+  if (m <= (size_t(64) << 20)) memset(*p, 0, m);  // larger workspaces stay untouched (lazily mapped)
+  g_allocs.push_back({static_cast<char*>(*p), m});
+  return hipSuccess;
+}
+static hipError_t s_free(void* p) {
+  for (auto it = g_allocs.begin(); it != g_allocs.end(); ++it)
+    if (it->first == p) { g_allocs.erase(it); break; }
+  free(p);
+  return hipSuccess;
+}
+static hipError_t s_hostmalloc(void** p, size_t n, unsigned) { return s_malloc(p, n); }
+static hipError_t s_memcpy(void* d, const void* s, size_t n, hipMemcpyKind, hipStream_t) { memcpy(d, s, n); return hipSuccess; }
+static hipError_t s_ok0() { return hipSuccess; }
+static hipError_t s_ok1(hipStream_t) { return hipSuccess; }
+static hipError_t s_getdev(int* d) { *d = 0; return hipSuccess; }
+static hipError_t s_attr(int* v, hipDeviceAttribute_t, int) { *v = 256; return hipSuccess; }  // 256 CUs
+static hipError_t s_evc(hipEvent_t* e, unsigned) { *e = reinterpret_cast<hipEvent_t>(0x1); return hipSuccess; }
+static hipError_t s_evc2(hipEvent_t* e) { *e = reinterpret_cast<hipEvent_t>(0x1); return hipSuccess; }
+static hipError_t s_evr(hipEvent_t, hipStream_t) { return hipSuccess; }
+static hipError_t s_ev1(hipEvent_t) { return hipSuccess; }
+static hipError_t s_setdev(int) { return hipSuccess; }
+static hipError_t s_elapsed(float* ms, hipEvent_t, hipEvent_t) { *ms = 0; return hipSuccess; }
+static const char* s_errstr(hipError_t) { return "stub"; }
+#define hipMalloc s_malloc
+#define hipFree s_free
+#define hipHostMalloc s_hostmalloc
+#define hipHostFree s_free
+#define hipMemcpyAsync s_memcpy
+#define hipStreamSynchronize s_ok1
+#define hipDeviceSynchronize s_ok0
+#define hipGetDevice s_getdev
+#define hipSetDevice s_setdev
+#define hipDeviceGetAttribute s_attr
+#define hipEventCreateWithFlags s_evc
+#define hipEventCreate s_evc2
+#define hipEventRecord s_evr
+#define hipEventSynchronize s_ev1
+#define hipEventDestroy s_ev1
+#define hipGetLastError s_ok0
+#define hipEventElapsedTime s_elapsed
+#define hipGetErrorString s_errstr
+#include "muon_api.cpp"
+
+static int g_fail = 0;
+static int g_count = 0;              // matrices in the current call
+static double g_max_imbalance = 0;   // worst makespan / mean over the current call's phases
+static int g_phase_launches = 0, g_chain_launches = 0;
+
+#define CHECK(cond, ...)                   \
+  do {                                     \
+    if (!(cond)) {                         \
+      printf("  FAIL: " __VA_ARGS__);      \
+      printf("\n");                        \
+      g_fail = 1;                          \
+    }                                      \
+  } while (0)
+
+static bool in_alloc(const void* p) {
+  for (auto& a : g_allocs)
+    if (static_cast<const char*>(p) >= a.first && static_cast<const char*>(p) < a.first + a.second) return true;
+  return false;
+}
+
+namespace muon {
+hipError_t launch_momentum(const MatDev*, const int32_t*, int32_t, int64_t, float, int32_t, int32_t, int32_t, float*,
+                           hipStream_t) { return hipSuccess; }
+hipError_t launch_norm_finalize(const int32_t*, int32_t, const float*, MatScal*, float*, hipStream_t) { return hipSuccess; }
+hipError_t launch_writeback_direct(const MatDev*, const int32_t*, int32_t, int64_t, const MatScal*, float, int32_t,
+                                   const float2*, hipStream_t) { return hipSuccess; }
+hipError_t launch_adamw(const AdamwTensor*, const int32_t*, int32_t, int64_t, const float2*, float, float,
+                        const AdamwConsts&, hipStream_t) { return hipSuccess; }
+hipError_t launch_mfma_probe(int64_t, int32_t, float*, double*, hipStream_t) { return hipSuccess; }
+
+// The walk of ns_gemm_kernel: workgroup g on XCD g % 8 starts at slot g / 8
+// of its XCD's list, steps by the XCD's workgroup count, stops at the first
+// padding entry; the grid is what launch_one sizes it to.
+hipError_t launch_ns_phase(int prec, int phase, const MatDev* mats, const MatScal*, const int2* tiles,
+                           const PhaseArgs& pa, hipStream_t) {
+  ++g_phase_launches;
+  if (pa.per_xcd <= 0) return hipSuccess;
+  const int T = ns_tile(prec);
+  const int per_cu = (T == 256 || prec == PREC_BF16X3) ? 1 : 2;
+  const int B = std::min(pa.per_xcd, pa.cus_per_xcd * per_cu);
+  std::set<std::tuple<int, int, int>> expect, seen;
+  for (int i = 0; i < g_count; ++i) {
+    if (mats[i].prec != prec) continue;
+    const int tm = mats[i].Mp / T, tn = mats[i].Np / T;
+    CHECK(mats[i].Mp % T == 0 && mats[i].Np % T == 0 && mats[i].Mp >= mats[i].m && mats[i].Np >= mats[i].n,
+          "matrix %d: padded shape %d x %d does not cover %d x %d in %d-tiles", i, mats[i].Mp, mats[i].Np, mats[i].m,
+          mats[i].n, T);
+    for (int a = 0; a < tm; ++a)
+      for (int b = phase == PH_COMB ? 0 : a; b < (phase == PH_COMB ? tn : tm); ++b) expect.insert({i, a, b});
+  }
+  double worst = 0, total = 0;
+  for (int x = 0; x < NUM_XCD; ++x) {
+    // a workgroup's walk ends at its first padding entry, so no tile may
+    // follow one on the same walk
+    for (int b = 0; b < B; ++b) {
+      bool pad = false;
+      for (int slot = b; slot < pa.per_xcd; slot += B) {
+        const bool is_pad = tiles[int64_t(x) * pa.per_xcd + slot].x < 0;
+        CHECK(!(pad && !is_pad), "XCD %d: tile after the end of workgroup %d's walk (slot %d)", x, b, slot);
+        pad = pad || is_pad;
+      }
+    }
+    double xtotal = 0, xworst = 0, xmax = 0;
+    for (int b = 0; b < B; ++b) {
+      double w = 0;
+      for (int slot = b; slot < pa.per_xcd; slot += B) {
+        const int2 t = tiles[int64_t(x) * pa.per_xcd + slot];
+        if (t.x < 0) break;
+        const int a = t.y >> 16, c = t.y & 0xFFFF;
+        CHECK(t.x < g_count && mats[t.x].prec == prec, "tile of matrix %d in the prec %d list", t.x, prec);
+        if (t.x >= g_count) continue;
+        CHECK(seen.insert({t.x, a, c}).second, "phase %d: tile (%d, %d, %d) visited twice", phase, t.x, a, c);
+        CHECK(expect.count({t.x, a, c}) == 1, "phase %d: tile (%d, %d, %d) is not a tile of its matrix", phase, t.x,
+              a, c);
+        const double cost = phase == PH_GRAM ? mats[t.x].Np : mats[t.x].Mp;
+        w += cost;
+        xmax = std::max(xmax, cost);
+      }
+      xworst = std::max(xworst, w);
+      xtotal += w;
+    }
+    // list-scheduling bound: no workgroup gets more than the XCD's mean plus
+    // its costliest tile (5 % slack: a strided walk within 5 % of the
+    // longest-first layout is kept)
+    CHECK(xworst <= 1.05 * (xtotal / B + xmax) + 1e-9, "phase %d XCD %d: makespan %.0f above mean %.0f + tile %.0f",
+          phase, x, xworst, xtotal / B, xmax);
+    worst = std::max(worst, xworst);
+    total += xtotal;
+  }
+  CHECK(seen.size() == expect.size(), "phase %d prec %d: %zu of %zu tiles visited", phase, prec, seen.size(),
+        expect.size());
+  const double mean = total / (NUM_XCD * B);
+  if (mean > 0) g_max_imbalance = std::max(g_max_imbalance, worst / mean);
+  printf("  phase %d prec %d: %zu tiles, makespan %.0f, mean %.0f (K-units per workgroup)\n", phase, prec,
+         seen.size(), worst, mean);
+  return hipSuccess;
+}
+
+hipError_t launch_ns_chain(int prec, const MatDev* imats, const MatScal*, const ChainItem* items, const int32_t* xoff,
+                           int32_t per_xcd_max, PhaseArgs*, int32_t*, int32_t nsync, int32_t*, const ChainArgs& a,
+                           hipStream_t) {
+  ++g_chain_launches;
+  const int per_cu = (ns_tile(prec) == 256 || prec == PREC_BF16X3) ? 1 : 2;
+  const int per_xcd = std::min(per_xcd_max, a.cus_per_xcd * per_cu);
+  const int nitems = xoff[NUM_XCD];
+  const int ncnt = nsync - CHAIN_SYNC_HEAD;
+  std::vector<int> done(ncnt, 0), signals(ncnt, 0);
+  for (int i = 0; i < nitems; ++i) {
+    const ChainItem& it = items[i];
+    CHECK(it.signal >= 0 && it.signal < ncnt, "item %d: signal counter %d out of range", i, it.signal);
+    if (it.signal >= 0 && it.signal < ncnt) signals[it.signal]++;
+    CHECK(it.wait < ncnt, "item %d: wait counter %d out of range", i, it.wait);
+    const MatDev& md = imats[it.desc];
+    CHECK(in_alloc(md.X[0]) && in_alloc(md.A) && in_alloc(md.B), "item %d: a buffer lies outside the workspace", i);
+  }
+  for (int i = 0; i < nitems; ++i) {
+    const ChainItem& it = items[i];
+    if (it.wait >= 0 && it.wait < ncnt)
+      CHECK(signals[it.wait] == it.need, "item %d waits for %d signals on counter %d, which gets %d", i, it.need,
+            it.wait, signals[it.wait]);
+  }
+  std::vector<int> head(NUM_XCD, 0);
+  struct Blk { int q, item; };
+  std::vector<Blk> blocks;
+  for (int b = 0; b < NUM_XCD * per_xcd; ++b) blocks.push_back({b % NUM_XCD, -2});
+  int finished = 0, rounds = 0;
+  while (finished < nitems) {
+    bool prog = false;
+    for (auto& bl : blocks) {
+      if (bl.item == -1) continue;
+      if (bl.item == -2) {  // take the next item of this XCD's queue
+        const int i = xoff[bl.q] + head[bl.q]++;
+        bl.item = i < xoff[bl.q + 1] ? i : -1;
+        prog = true;
+        continue;
+      }
+      const ChainItem& it = items[bl.item];
+      if (it.wait >= 0 && done[it.wait] < it.need) continue;
+      done[it.signal]++;
+      ++finished;
+      bl.item = -2;
+      prog = true;
+    }
+    ++rounds;
+    if (!prog) {
+      CHECK(false, "chain deadlock after %d of %d items", finished, nitems);
+      break;
+    }
+  }
+  printf("  chain prec %d: %d items, %d steps, %d queues x %d workgroups, %d scheduler rounds\n", prec, nitems,
+         a.steps, NUM_XCD, per_xcd, rounds);
+  return hipSuccess;
+}
+}  // namespace muon
+
+struct Shape { int rows, cols, prec; };
+
+static muon_matrix_desc desc_of(const Shape& s) {
+  const bool f32 = s.prec == MUON_NS_F32 || s.prec == MUON_NS_BF16X3;
+  return {s.rows, s.cols, s.cols, s.cols, s.cols, f32 ? MUON_DTYPE_F32 : MUON_DTYPE_BF16, MUON_DTYPE_BF16,
+          MUON_DTYPE_F32, s.prec};
+}
+
+// Per-phase grids over shapes whose data is never touched: far-apart fake
+// device addresses (validation only compares them).
+static void grid_case(const char* name, const std::vector<Shape>& shapes, double max_imbalance) {
+  const int n = int(shapes.size());
+  std::vector<muon_matrix_desc> d(n);
+  std::vector<void*> P(n), G(n), M(n);
+  for (int i = 0; i < n; ++i) {
+    d[i] = desc_of(shapes[i]);
+    P[i] = reinterpret_cast<void*>(uintptr_t(0x100000000000ull) + uintptr_t(i) * (uintptr_t(3) << 34));
+    G[i] = reinterpret_cast<void*>(uintptr_t(P[i]) + (uintptr_t(1) << 34));
+    M[i] = reinterpret_cast<void*>(uintptr_t(P[i]) + (uintptr_t(2) << 34));
+  }
+  printf("CASE grids %s (%d matrices)\n", name, n);
+  g_count = n;
+  g_max_imbalance = 0;
+  const int before = g_phase_launches;
+  const muon_ns_coeffs co{3.4445f, -4.775f, 2.0315f};
+  muon_step_options o{};
+  o.launch_mode = MUON_LAUNCH_PHASE_GRIDS;
+  const muon_status st = muon_step_batched_v2(P.data(), G.data(), M.data(), d.data(), n, 0.02f, 0.95f, 1, co, 1, 0,
+                                              &o, nullptr, nullptr);
+  CHECK(st == MUON_OK, "status %d: %s", int(st), muon_last_error());
+  CHECK(g_phase_launches > before, "no phase launched");
+  CHECK(g_max_imbalance <= max_imbalance, "makespan / mean %.3f above %.3f", g_max_imbalance, max_imbalance);
+  printf("  worst makespan / mean %.3f\n", g_max_imbalance);
+}
+
+// The persistent chain over small matrices with real (host) buffers.
+static void chain_case(const char* name, const std::vector<Shape>& shapes, int steps, bool schedule) {
+  const int n = int(shapes.size());
+  std::vector<muon_matrix_desc> d(n);
+  std::vector<void*> P(n), G(n), M(n);
+  for (int i = 0; i < n; ++i) {
+    d[i] = desc_of(shapes[i]);
+    const size_t el = size_t(shapes[i].rows) * shapes[i].cols;
+    (void)s_malloc(&P[i], el * (d[i].param_dtype == MUON_DTYPE_F32 ? 4 : 2));
+    (void)s_malloc(&G[i], el * 2);
+    (void)s_malloc(&M[i], el * 4);
+  }
+  printf("CASE chain %s (%d matrices, %d steps)\n", name, n, steps);
+  g_count = n;
+  const int before = g_chain_launches;
+  const muon_ns_coeffs co{3.4445f, -4.775f, 2.0315f}, cubic{1.5f, -0.5f, 0.f};
+  std::vector<muon_ns_coeffs> sched;
+  for (int k = 0; k < steps; ++k) sched.push_back(k % 2 ? cubic : co);
+  muon_step_options o{};
+  o.launch_mode = MUON_LAUNCH_CHAIN;
+  if (schedule) o.ns_schedule = sched.data();
+  const muon_status st = muon_step_batched_v2(P.data(), G.data(), M.data(), d.data(), n, 0.02f, 0.95f, 1, co, steps,
+                                              0, &o, nullptr, nullptr);
+  CHECK(st == MUON_OK, "status %d: %s", int(st), muon_last_error());
+  CHECK(g_chain_launches > before, "no chain launched");
+  for (int i = 0; i < n; ++i) {
+    (void)s_free(P[i]);
+    (void)s_free(G[i]);
+    (void)s_free(M[i]);
+  }
+}
+
+int main() {
+  const int BF = MUON_NS_BF16, F32 = MUON_NS_F32, X3 = MUON_NS_BF16X3;
+  std::vector<Shape> share, d24, lm;
+  for (int l = 0; l < 24; ++l) {
+    std::vector<Shape> layer = {{1536, 1536, BF}, {1536, 1536, BF}, {1536, 1536, BF}, {1536, 1536, BF},
+                                {1536, 6144, BF}, {6144, 1536, BF}};
+    d24.insert(d24.end(), layer.begin(), layer.end());
+    if (l < 3) share.insert(share.end(), layer.begin(), layer.end());
+  }
+  for (int l = 0; l < 2; ++l) {
+    std::vector<Shape> layer = {{3072, 3072, BF}, {3072, 1024, BF}, {3072, 1024, BF},
+                                {3072, 3072, BF}, {3072, 12288, BF}, {12288, 3072, BF}};
+    lm.insert(lm.end(), layer.begin(), layer.end());
+  }
+  grid_case("d24 stack", d24, 1.05);
+  grid_case("d24, one GPU's share (3 layers)", share, 1e9);
+  grid_case("3.8B-like, 2 layers", lm, 1e9);
+  grid_case("ragged, mixed formats",
+            {{700, 1100, BF}, {1100, 700, BF}, {769, 769, F32}, {300, 520, X3}, {64, 64, BF}, {1, 300, F32},
+             {2049, 257, BF}, {257, 2049, X3}, {5000, 3, BF}, {1, 1, BF}},
+            1e9);
+  grid_case("single 256 x 256, binary32", {{256, 256, F32}}, 1e9);
+  const std::vector<Shape> mixed = {{700, 1100, BF}, {1100, 700, BF}, {769, 769, BF},
+                                    {300, 520, BF},  {64, 64, BF},    {1, 300, BF}};
+  chain_case("bf16, 5 steps", mixed, 5, false);
+  chain_case("bf16, 1 step", mixed, 1, false);
+  chain_case("bf16, schedule with c = 0 steps", mixed, 4, true);
+  chain_case("binary32 and split-bf16, 3 steps",
+             {{769, 769, F32}, {300, 520, X3}, {64, 64, F32}, {129, 257, X3}}, 3, false);
+  printf(g_fail ? "PLAN-CHECK FAILED\n" : "PLAN-CHECK OK\n");
+  return g_fail;
+}

@@ -1,0 +1,43 @@
+"""The library's host-side planning (tile lists, band rasters, XCD segments,
+longest-first layouts, the persistent chain's queues and completion counts),
+checked on the CPU by host_plan/plan_check.cpp: muon_api.cpp compiled for the
+host with the HIP runtime replaced by host-memory stubs and the kernel
+launchers replaced by checkers that walk the device lists as the kernels do.
+Built with address and undefined-behaviour sanitizers."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+HIP_INC = "/opt/rocm/include"
+
+
+@pytest.fixture(scope="module")
+def plan_check(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None or not os.path.exists(os.path.join(HIP_INC, "hip", "hip_runtime.h")):
+        pytest.skip("needs g++ and the HIP headers")
+    exe = tmp_path_factory.mktemp("plan") / "plan_check"
+    cmd = [gxx, "-std=c++17", "-O1", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", HIP_INC,
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "muon_newton_schulz_02_amd", "csrc"),
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-o", str(exe), os.path.join(HERE, "host_plan", "plan_check.cpp")]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-4000:]
+    return exe
+
+
+def test_tile_walks_and_chain_queues(plan_check):
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0")
+    r = subprocess.run([str(plan_check)], capture_output=True, text=True, timeout=600, env=env)
+    out = r.stdout
+    assert r.returncode == 0 and "PLAN-CHECK OK" in out and "FAIL" not in out, out[-6000:] + r.stderr[-3000:]
+    # the d24 stack: 144 matrices, 6 x 6 tile rows and columns (square) or
+    # 6 x 24 (rectangular): 21 triangle tiles each for GRAM and POLY
+    d24 = out.split("CASE grids d24 stack")[1].split("CASE")[0]
+    assert d24.count(" 3024 tiles") == 2 and " 10368 tiles" in d24
+    assert out.count("CASE ") == 9
+    assert out.count("  chain prec ") == 5
