@@ -50,7 +50,7 @@ __device__ inline float load_elem(const void* p, int64_t idx, int bf16) {
 
 // Store four consecutive values of the Newton-Schulz working format.
 __device__ inline void store4_ws(void* base, int64_t plane, int prec, int64_t idx, const float v[4]) {
-  if (prec == PREC_F32) {
+  if (is_f32(prec)) {
     *gmem(reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + idx)) = f32x4{v[0], v[1], v[2], v[3]};
   } else {
     uint16_t* p = reinterpret_cast<uint16_t*>(base);
@@ -65,7 +65,7 @@ __device__ inline void store4_ws(void* base, int64_t plane, int prec, int64_t id
 }
 
 __device__ inline float load_ws(const void* base, int64_t plane, int prec, int64_t idx) {
-  if (prec == PREC_F32) return gmem(reinterpret_cast<const float*>(base))[idx];
+  if (is_f32(prec)) return gmem(reinterpret_cast<const float*>(base))[idx];
   auto p = gmem(reinterpret_cast<const uint16_t*>(base));
   float v = bf16_bits_to_float(p[idx]);
   if (prec == PREC_BF16X3) v = v + bf16_bits_to_float(p[plane + idx]);

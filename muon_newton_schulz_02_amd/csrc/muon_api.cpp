@@ -77,7 +77,7 @@ MatGeom geom_of(const muon_matrix_desc& d) {
   g.ldx = g.Np + LDPAD;
   g.lda = g.Mp + LDPAD;
   g.prec = d.precision;
-  g.esz = g.prec == PREC_F32 ? 4 : 2;
+  g.esz = is_f32(g.prec) ? 4 : 2;
   g.npl = g.prec == PREC_BF16X3 ? 2 : 1;
   g.x_bytes = align256(size_t(g.Mp) * size_t(g.ldx) * g.esz * g.npl);
   g.a_bytes = align256(size_t(g.Mp) * size_t(g.lda) * g.esz * g.npl);
@@ -780,19 +780,28 @@ muon_status run(const Call& c) {
   }
 
   // working format per matrix: a bf16 stack whose GRAM phase has fewer
-  // 256 x 256 tiles than the GPU has resident workgroups takes 128 x 128
-  // tiles (measured: 12 x 768^2 0.41 -> 0.34 ms per step; with three d24
-  // layers, 378 GRAM tiles, the pipelined 256 x 256 tiles stay faster)
+  // 256 x 256 tiles than the GPU has compute units takes 128 x 128 tiles
+  // (measured: 12 x 768^2 0.41 -> 0.34 ms per step; with three d24 layers,
+  // 378 GRAM tiles, the pipelined 256 x 256 tiles stay faster), and a
+  // binary32 stack with fewer 128 x 128 GRAM tiles than that takes 64 x 64
+  // tiles (one 256 x 256 matrix: 3 GRAM tiles of 128, 10 of 64)
   std::vector<int> iprec(size_t(c.count), PREC_BF16);
   if (c.mode != MODE_NORMS) {
     const int32_t tmode = (c.mode == MODE_STEP && c.opt) ? c.opt->tile_mode : MUON_TILES_AUTO;
-    int64_t bf16_gram = 0;
-    for (int32_t i = 0; i < c.count; ++i)
+    int64_t bf16_gram = 0, f32_gram = 0;
+    for (int32_t i = 0; i < c.count; ++i) {
       if (c.shapes[i].precision == MUON_NS_BF16) bf16_gram += gram_tiles_of(c.shapes[i], PREC_BF16);
-    const bool small = tmode == MUON_TILES_SMALL ||
-                       (tmode == MUON_TILES_AUTO && bf16_gram < int64_t(NUM_XCD) * ds.cus_per_xcd);
-    for (int32_t i = 0; i < c.count; ++i)
-      iprec[size_t(i)] = (c.shapes[i].precision == MUON_NS_BF16 && small) ? int(PREC_BF16S) : c.shapes[i].precision;
+      if (c.shapes[i].precision == MUON_NS_F32) f32_gram += gram_tiles_of(c.shapes[i], PREC_F32);
+    }
+    const int64_t cus = int64_t(NUM_XCD) * ds.cus_per_xcd;
+    const bool small_bf16 = tmode == MUON_TILES_SMALL || (tmode == MUON_TILES_AUTO && bf16_gram < cus);
+    const bool small_f32 = tmode == MUON_TILES_SMALL || (tmode == MUON_TILES_AUTO && f32_gram < cus);
+    for (int32_t i = 0; i < c.count; ++i) {
+      const int p = c.shapes[i].precision;
+      iprec[size_t(i)] = (p == MUON_NS_BF16 && small_bf16) ? int(PREC_BF16S)
+                         : (p == MUON_NS_F32 && small_f32) ? int(PREC_F32S)
+                                                           : p;
+    }
   }
 
   // which working formats run as one persistent chain: only when asked for

@@ -22,7 +22,9 @@ constexpr int NUM_XCD = 8;
 // Working formats of the Newton-Schulz products.  PREC_BF16S is the bf16
 // format on 128 x 128 tiles (a one-stage k-loop), chosen for stacks too small
 // to fill the GPU with 256 x 256 tiles; it stores exactly what PREC_BF16 does.
-enum Prec : int { PREC_BF16 = 0, PREC_BF16X3 = 1, PREC_F32 = 2, PREC_BF16S = 3 };
+// PREC_F32S is likewise the binary32 format on 64 x 64 tiles, for binary32
+// stacks too small to fill the GPU with 128 x 128 tiles.
+enum Prec : int { PREC_BF16 = 0, PREC_BF16X3 = 1, PREC_F32 = 2, PREC_BF16S = 3, PREC_F32S = 4 };
 
 // Per-matrix device descriptor.  "natural" means the caller's orientation
 // (rows x cols); the iteration runs on the wide orientation m x n (m <= n).
@@ -151,8 +153,10 @@ hipError_t launch_ns_phase(int prec, int phase, const MatDev* mats, const MatSca
 
 // Tile edge of the Newton-Schulz products (square tiles) per format: 256 for
 // bf16 (LDS holds two stages of 256x64 bf16 per operand); 128 where an
-// operand takes twice the bytes (split-bf16 planes, float32).
-constexpr int ns_tile(int prec) { return prec == PREC_BF16 ? 256 : 128; }
+// operand takes twice the bytes (split-bf16 planes, float32) and for the
+// small-stack bf16 tiles; 64 for the small-stack binary32 tiles.
+constexpr int ns_tile(int prec) { return prec == PREC_BF16 ? 256 : prec == PREC_F32S ? 64 : 128; }
 constexpr bool bf16_single(int prec) { return prec == PREC_BF16 || prec == PREC_BF16S; }
+constexpr bool is_f32(int prec) { return prec == PREC_F32 || prec == PREC_F32S; }
 
 }  // namespace muon

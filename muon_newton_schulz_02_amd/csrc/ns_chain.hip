@@ -188,6 +188,9 @@ hipError_t launch_ns_chain(int prec, const MatDev* imats, const MatScal* scal, c
     case PREC_BF16S:
       return launch_chain_prec<PREC_BF16S>(imats, scal, items, xcd_off, per_xcd_max, steps, sync, nsync, fail, args,
                                            stream);
+    case PREC_F32S:
+      return launch_chain_prec<PREC_F32S>(imats, scal, items, xcd_off, per_xcd_max, steps, sync, nsync, fail, args,
+                                          stream);
   }
   return hipErrorInvalidValue;
 }

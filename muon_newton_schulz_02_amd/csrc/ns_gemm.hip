@@ -131,6 +131,7 @@ hipError_t launch_ns_phase(int prec, int phase, const MatDev* mats, const MatSca
     case PREC_BF16X3: return launch_prec<PREC_BF16X3>(phase, mats, scal, tiles, args, stream);
     case PREC_F32: return launch_prec<PREC_F32>(phase, mats, scal, tiles, args, stream);
     case PREC_BF16S: return launch_prec<PREC_BF16S>(phase, mats, scal, tiles, args, stream);
+    case PREC_F32S: return launch_prec<PREC_F32S>(phase, mats, scal, tiles, args, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -39,6 +39,7 @@ template <> struct Fmt<PREC_BF16> { static constexpr int esz = 2, npl = 1; };
 template <> struct Fmt<PREC_BF16X3> { static constexpr int esz = 2, npl = 2; };
 template <> struct Fmt<PREC_F32> { static constexpr int esz = 4, npl = 1; };
 template <> struct Fmt<PREC_BF16S> { static constexpr int esz = 2, npl = 1; };
+template <> struct Fmt<PREC_F32S> { static constexpr int esz = 4, npl = 1; };
 
 // Tile shape per format: T x T tile, WP x WQ waves (rows x columns), NT threads.
 // bf16: 256 x 256 over eight waves (two per SIMD, each 128 x 64, 128
@@ -55,6 +56,8 @@ template <> struct Cfg<PREC_BF16> { static constexpr int BT = 256, WP = 2, WQ = 
 template <> struct Cfg<PREC_BF16X3> { static constexpr int BT = 128, WP = 2, WQ = 2, NT = 256; };
 template <> struct Cfg<PREC_F32> { static constexpr int BT = 128, WP = 2, WQ = 2, NT = 256; };
 template <> struct Cfg<PREC_BF16S> { static constexpr int BT = 128, WP = 2, WQ = 2, NT = 256; };
+// small-stack binary32: 64 x 64 over two waves of 32 x 64
+template <> struct Cfg<PREC_F32S> { static constexpr int BT = 64, WP = 2, WQ = 1, NT = 128; };
 
 // LDS operand layout of the split-bf16 and binary32 tiles: row r at r * PITCH,
 // 16-byte chunk ch at 16 (ch ^ ((r >> 4) & 7)).  (The bf16 tiles use their
@@ -73,7 +76,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // of 4); the split-bf16 format keeps its lo plane `plane` elements further.
 template <int PREC>
 __device__ __forceinline__ void st4(void* base, int64_t plane, int64_t idx, const float* v) {
-  if constexpr (PREC == PREC_F32) {
+  if constexpr (is_f32(PREC)) {
     *gmem(reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + idx)) = f32x4{v[0], v[1], v[2], v[3]};
   } else {
     uint16_t* p = reinterpret_cast<uint16_t*>(base);
@@ -243,7 +246,7 @@ __device__ __forceinline__ void mfma_step(f32x16& acc, const u32x4* q, const u32
 // hi + lo bf16 values: out[0] carries hi, out[1] lo.
 template <int PREC>
 __device__ __forceinline__ void identity_frag(u32x4* out, int pos, float alpha) {
-  if constexpr (PREC == PREC_F32) {
+  if constexpr (is_f32(PREC)) {
     const uint32_t bits = __float_as_uint(alpha);
     u32x4 v;
 #pragma unroll

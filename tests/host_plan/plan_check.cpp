@@ -312,7 +312,10 @@ int main() {
             {{700, 1100, BF}, {1100, 700, BF}, {769, 769, F32}, {300, 520, X3}, {64, 64, BF}, {1, 300, F32},
              {2049, 257, BF}, {257, 2049, X3}, {5000, 3, BF}, {1, 1, BF}},
             1e9);
-  grid_case("single 256 x 256, binary32", {{256, 256, F32}}, 1e9);
+  grid_case("single 256 x 256, binary32 (64 x 64 tiles)", {{256, 256, F32}}, 1e9);
+  grid_case("binary32 stack on 128 x 128 tiles", {{2048, 2048, F32}, {2048, 2048, F32}, {1024, 4096, F32},
+                                                  {4096, 1024, F32}},
+            1e9);
   const std::vector<Shape> mixed = {{700, 1100, BF}, {1100, 700, BF}, {769, 769, BF},
                                     {300, 520, BF},  {64, 64, BF},    {1, 300, BF}};
   chain_case("bf16, 5 steps", mixed, 5, false);

@@ -34,7 +34,8 @@ def _announce(msg):
 
 
 @pytest.mark.parametrize("prec,tiles", [(mb.NS_BF16, mb.TILES_AUTO), (mb.NS_BF16, mb.TILES_LARGE),
-                                        (mb.NS_BF16X3, mb.TILES_AUTO), (mb.NS_F32, mb.TILES_AUTO)])
+                                        (mb.NS_BF16X3, mb.TILES_AUTO), (mb.NS_F32, mb.TILES_AUTO),
+                                        (mb.NS_F32, mb.TILES_LARGE)])
 def test_mixed_shape_sweep(prec, tiles):
     _announce(f"sweep prec={prec} tiles={tiles}")
     shapes = _shapes(300 + prec * 10 + tiles, 16)

@@ -39,5 +39,11 @@ def test_tile_walks_and_chain_queues(plan_check):
     # 6 x 24 (rectangular): 21 triangle tiles each for GRAM and POLY
     d24 = out.split("CASE grids d24 stack")[1].split("CASE")[0]
     assert d24.count(" 3024 tiles") == 2 and " 10368 tiles" in d24
-    assert out.count("CASE ") == 9
+    assert out.count("CASE ") == 10
+    # formats: one 256 x 256 binary32 matrix on 64 x 64 tiles (4 x 4: 10
+    # triangle tiles, 16 product tiles); the larger binary32 stack on 128 x 128
+    one = out.split("CASE grids single 256 x 256")[1].split("CASE")[0]
+    assert "phase 0 prec 4: 10 tiles" in one and "phase 2 prec 4: 16 tiles" in one
+    big = out.split("CASE grids binary32 stack on 128 x 128 tiles")[1].split("CASE")[0]
+    assert "phase 0 prec 2:" in big and "prec 4" not in big
     assert out.count("  chain prec ") == 5
