@@ -65,7 +65,8 @@ def parse():
     ap.add_argument("--launch-mode", choices=("auto", "grids", "chain"), default="auto",
                     help="Newton-Schulz launches: the library's choice, one grid per phase, or one persistent chain")
     ap.add_argument("--tile-mode", choices=("auto", "large", "small"), default="auto",
-                    help="bf16 tile size of the Newton-Schulz products: the library's choice, 256 or 128")
+                    help="tile size of the Newton-Schulz products: the library's choice, "
+                         "large (bf16 256, fp32 128) or small (bf16 128, fp32 64)")
     ap.add_argument("--no-adamw", action="store_true",
                     help="skip timing the AdamW half of the hybrid optimizer (d24 non-matrix parameters)")
     ap.add_argument("--copy-calibration", action="store_true",
