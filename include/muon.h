@@ -175,7 +175,11 @@ typedef struct muon_step_options {
 
 /* One 2-D matrix.  rows, cols in [1, 65536]; ld_* >= cols.
  * param_dtype and grad_dtype: MUON_DTYPE_F32 or MUON_DTYPE_BF16;
- * mom_dtype: MUON_DTYPE_F32 only; precision: a muon_ns_precision.        */
+ * mom_dtype: MUON_DTYPE_F32 only; precision: a muon_ns_precision.
+ * Size cap (UNSUPPORTED): the library's working copy of the matrix, both
+ * dimensions rounded up to multiples of 256, stays below 2 GiB: 2 bytes per
+ * element for BF16, 4 for BF16X3 and F32 (a bf16 32512 x 32512 or an fp32
+ * 23040 x 23040 matrix is accepted; 32768 x 32768 bf16 is not).           */
 typedef struct muon_matrix_desc {
   int64_t rows, cols;
   int64_t ld_param, ld_grad, ld_mom;

@@ -109,6 +109,15 @@ muon_status validate_desc(const muon_matrix_desc* shapes, int32_t count, Mode mo
     if (mode != MODE_NORMS && d.precision != MUON_NS_BF16 && d.precision != MUON_NS_BF16X3 &&
         d.precision != MUON_NS_F32)
       return fail(MUON_ERR_INVALID_ARGUMENT, "matrix %d: unknown precision %d", i, d.precision);
+    if (mode != MODE_NORMS) {
+      // the products address a workspace matrix (all planes) with 32-bit
+      // buffer offsets from its first element
+      const MatGeom g = geom_of(d);
+      if (g.x_bytes > size_t(INT32_MAX) || g.a_bytes > size_t(INT32_MAX))
+        return fail(MUON_ERR_UNSUPPORTED,
+                    "matrix %d: %lld x %lld needs a %.2f GiB working copy in this precision; the limit is 2 GiB", i,
+                    (long long)d.rows, (long long)d.cols, double(std::max(g.x_bytes, g.a_bytes)) / double(1 << 30));
+    }
     if (mode == MODE_STEP) {
       if (d.param_dtype != MUON_DTYPE_F32 && d.param_dtype != MUON_DTYPE_BF16)
         return fail(MUON_ERR_UNSUPPORTED, "matrix %d: param_dtype %d is not F32 or BF16", i, d.param_dtype);

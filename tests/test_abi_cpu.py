@@ -208,6 +208,28 @@ def test_alias_detection(L):
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU error path")
+@pytest.mark.parametrize("rows,cols,prec,status", [
+    (32512, 32512, mb.NS_BF16, mb.MUON_ERR_HIP),          # 1.97 GiB working copy: accepted
+    (32768, 32768, mb.NS_BF16, mb.MUON_ERR_UNSUPPORTED),  # 2 GiB
+    (16128, 65536, mb.NS_BF16, mb.MUON_ERR_HIP),
+    (65536, 16384, mb.NS_BF16, mb.MUON_ERR_UNSUPPORTED),  # tall: the same copy as 16384 x 65536
+    (23040, 23040, mb.NS_F32, mb.MUON_ERR_HIP),
+    (23296, 23296, mb.NS_F32, mb.MUON_ERR_UNSUPPORTED),
+    (23296, 23296, mb.NS_BF16X3, mb.MUON_ERR_UNSUPPORTED),
+    (23296, 23296, mb.NS_BF16, mb.MUON_ERR_HIP),
+])
+def test_working_copy_size_cap(L, rows, cols, prec, status):
+    # the Newton-Schulz products address one working copy with 32-bit offsets;
+    # accepted sizes get as far as the device (no GPU here: MUON_ERR_HIP)
+    pdt = mb.DTYPE_F32 if prec != mb.NS_BF16 else mb.DTYPE_BF16
+    d = _desc(rows, cols, pdt=pdt, prec=prec)
+    p = BASE
+    g, m = p + (1 << 36), p + (2 << 36)
+    assert _call(L, [d], [p], [g], [m]) == status
+    if status == mb.MUON_ERR_UNSUPPORTED:
+        assert "2 GiB" in mb.muon_last_error()
+
+
 def test_valid_call_without_gpu_reports_hip_error(L):
     p, g, m = _ptrs(0, 16, 32)
     assert _call(L, [_desc(16, 32)], [p], [g], [m]) == mb.MUON_ERR_HIP
