@@ -6,8 +6,8 @@ import oracle as orc
 from muon_newton_schulz_02_amd import binding as mb
 
 # Gates, relative Frobenius error of the update O against the float64 oracle:
-# float32 path 1e-4 and bf16 path 2e-2 as the task's hot-path definition
-# fixes them; the split-bf16 path is held to the bf16 gate and, on
+# 1e-4 for the float32 path and 2e-2 for the bf16 path (the tolerances the
+# library is specified to); the split-bf16 path is held to the bf16 gate and, on
 # well-conditioned inputs, to TOL_BF16X3_TIGHT (about 16 significant bits per
 # operand, five products per step: errors of order 1e-4 expected).
 TOL_F32 = 1e-4
