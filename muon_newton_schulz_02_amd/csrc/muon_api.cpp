@@ -369,11 +369,12 @@ std::vector<int> cost_order(const std::vector<MatDev>& hm) {
 }
 
 // Tile rows per raster band of a matrix with tm tile rows.  The tiles in
-// flight on one XCD (32 of 256 x 256, 64 of 128 x 128) then cover h row
-// panels and about 32 / h (64 / h) column panels; h + 32 / h is least near
-// h = 6, and a band height that divides tm leaves no short band.  256 x 256:
-// the whole height up to 8 rows, else the divisor of tm in 4..8 nearest 6,
-// else 6; 128 x 128: 8.  (d24 COMBINE, tm = 6: 1 % faster than 4-row bands.)
+// flight on one XCD (32 of 256 x 256, 64 of the smaller sizes) then cover h
+// row panels and about 32 / h (64 / h) column panels; h + 32 / h is least
+// near h = 6, and a band height that divides tm leaves no short band.
+// 256 x 256: the whole height up to 8 rows, else the divisor of tm in 4..8
+// nearest 6, else 6; smaller tiles: 8.  (d24 COMBINE, tm = 6: 1 % faster
+// than 4-row bands.)
 int band_rows(int tm, int T) {
   if (T != 256) return 8;
   if (tm <= 8) return std::max(tm, 1);
