@@ -378,6 +378,170 @@ def test_bf16_emulation_reduces_to_definition(coeffs, shape):
     assert 1e-5 < e < 5e-2
 
 
+def _recording(rnd):
+    """A rounding function that records (as float64) every value it is given."""
+    calls = []
+
+    def rec(v):
+        calls.append(np.array(v, dtype=np.float64))
+        return rnd(v)
+    return rec, calls
+
+
+@pytest.mark.parametrize("coeffs", [MUON, CUBIC, TEXTBOOK])
+@pytest.mark.parametrize("shape", [(20, 33), (33, 20)])
+def test_bf16_emulation_rounds_at_the_storage_points(coeffs, shape):
+    """The emulation rounds exactly where the bf16 path stores: the unscaled U
+    (oriented); per step the Gram matrix A and then B = b A + c A A (or, when
+    c = 0, B = b s^2 X X^T with no stored A); the next iterate before every
+    step but the last.  Each rounded value must be, up to float64 evaluation
+    order, what the definition gives from the previously stored values."""
+    steps = 3
+    a, b, c = coeffs
+    rng = np.random.default_rng(17)
+    u = rng.standard_normal(shape).astype(np.float32)
+    rec, calls = _recording(orc.to_bf16)
+    out = orc.orthogonalise_bf16_storage(u, coeffs, steps, rnd=rec)
+    per_step = 2 if c != 0.0 else 1
+    assert len(calls) == 1 + steps * per_step + (steps - 1)
+
+    def close(x, y):
+        return np.allclose(x, y, rtol=1e-12, atol=1e-300)
+
+    xw = u.T if shape[0] > shape[1] else u
+    assert np.array_equal(calls[0], xw.astype(np.float64)), "first rounding is not the unscaled, oriented U"
+    x = orc.to_bf16(calls[0]).astype(np.float64)
+    s = 1.0 / (math.sqrt(float(np.sum(u.astype(np.float64) ** 2))) + orc.EPS)
+    i = 1
+    for k in range(steps):
+        gram = s * s * (x @ x.T)
+        if c != 0.0:
+            assert close(calls[i], gram), f"step {k}: A is not rounded as s^2 X X^T"
+            a_st = orc.to_bf16(calls[i]).astype(np.float64)
+            assert close(calls[i + 1], b * a_st + c * (a_st @ a_st)), f"step {k}: B not formed from the stored A"
+            b_st = orc.to_bf16(calls[i + 1]).astype(np.float64)
+            i += 2
+        else:
+            assert close(calls[i], b * gram), f"step {k}: B is not rounded as b s^2 X X^T"
+            b_st = orc.to_bf16(calls[i]).astype(np.float64)
+            i += 1
+        xn = s * (a * x + b_st @ x)
+        s = 1.0
+        if k < steps - 1:
+            assert close(calls[i], xn), f"step {k}: the iterate is not rounded as s (a X + B X)"
+            x = orc.to_bf16(calls[i]).astype(np.float64)
+            i += 1
+        else:
+            assert close(out, xn.T if shape[0] > shape[1] else xn), "the last iterate is rounded"
+
+
+ROUND_BITS = 6
+
+
+def _round_bits(q: Fraction) -> Fraction:
+    """Round a rational to ROUND_BITS significant bits, ties to even (a tiny float)."""
+    if q == 0:
+        return Fraction(0)
+    ulp = _ulp(q)
+    return round(q / ulp) * ulp          # round() of a Fraction ties to even
+
+
+def _ulp(q: Fraction) -> Fraction:
+    e = math.floor(math.log2(abs(q)))
+    while Fraction(2) ** e > abs(q):
+        e -= 1
+    while Fraction(2) ** (e + 1) <= abs(q):
+        e += 1
+    return Fraction(2) ** (e - ROUND_BITS + 1)
+
+
+def _round_margin(q: Fraction) -> Fraction:
+    """Distance of q from the nearest rounding boundary of _round_bits, in ulps
+    (1/2 for values that are representable)."""
+    if q == 0:
+        return Fraction(1, 2)
+    n = abs(q) / _ulp(q)
+    return abs(n - math.floor(n) - Fraction(1, 2))
+
+
+def _mat(rows):
+    return [[Fraction(v) for v in r] for r in rows]
+
+
+def _mm(x, y):
+    return [[sum((x[i][k] * y[k][j] for k in range(len(y))), Fraction(0)) for j in range(len(y[0]))]
+            for i in range(len(x))]
+
+
+def _tr(x):
+    return [list(r) for r in zip(*x)]
+
+
+def _lin(alpha, x, beta, y):
+    return [[alpha * x[i][j] + beta * y[i][j] for j in range(len(x[0]))] for i in range(len(x))]
+
+
+def _rnd_mat(x, margins):
+    for r in x:
+        for v in r:
+            margins.append(_round_margin(v))
+    return [[_round_bits(v) for v in r] for r in x]
+
+
+def _exact_storage_ns(u, coeffs, steps, inv, skip=None):
+    """Exact rational evaluation of the storage-point schedule with the
+    rounding of _round_bits; `skip` names one storage point to leave out ("U", "A", "B",
+    "X"), or "U_scaled" to round s U instead of U."""
+    a, b, c = (Fraction(v) for v in coeffs)
+    margins = []
+    rnd = lambda x, pt: x if skip == pt else _rnd_mat(x, margins)  # noqa: E731
+    s = Fraction(inv)
+    if skip == "U_scaled":
+        x = _rnd_mat([[s * v for v in r] for r in u], margins)
+        s = Fraction(1)
+    else:
+        x = rnd(u, "U")
+    for k in range(steps):
+        gram = [[s * s * v for v in r] for r in _mm(x, _tr(x))]
+        if c != 0:
+            a_st = rnd(gram, "A")
+            b_st = rnd(_lin(b, a_st, c, _mm(a_st, a_st)), "B")
+        else:
+            b_st = rnd([[b * v for v in r] for r in gram], "B")
+        xn = [[s * v for v in r] for r in _lin(a, x, Fraction(1), _mm(b_st, x))]
+        s = Fraction(1)
+        x = xn if k == steps - 1 else rnd(xn, "X")
+    return x, margins
+
+
+@pytest.mark.parametrize("coeffs", [TEXTBOOK, CUBIC])
+def test_bf16_emulation_exact_rational_storage_points(coeffs):
+    """Exact brute force of the storage schedule on a 2x2 input with a 6-bit
+    rounding in place of bf16 (8 bits): the emulation equals the rational evaluation,
+    and leaving out any one storage point, or rounding U after its scaling,
+    changes the result by far more than float64 evaluation can."""
+    u = np.array([[151.0, 37.0], [203.0, 177.0]], np.float32)   # 8-bit integers, none a tie
+    steps = 2
+
+    def round_array(v):
+        f = np.asarray(v, dtype=np.float64)
+        return np.vectorize(lambda t: float(_round_bits(Fraction(float(t)))))(f)
+
+    inv = 1.0 / (math.sqrt(float(np.sum(u.astype(np.float64) ** 2))) + orc.EPS)
+    full, margins = _exact_storage_ns(_mat(u.tolist()), coeffs, steps, inv)
+    # no value sits within 1e-6 ulp of a rounding boundary, so float64
+    # evaluation order cannot change a rounding decision
+    assert min(margins) > Fraction(1, 10 ** 6)
+    emu = orc.orthogonalise_bf16_storage(u, coeffs, steps, rnd=round_array)
+    full_f = np.array([[float(v) for v in r] for r in full])
+    assert np.allclose(emu, full_f, rtol=1e-12, atol=0)
+    points = ["U", "U_scaled", "B", "X"] + (["A"] if coeffs[2] != 0 else [])
+    for pt in points:
+        alt, _ = _exact_storage_ns(_mat(u.tolist()), coeffs, steps, inv, skip=pt)
+        alt_f = np.array([[float(v) for v in r] for r in alt])
+        assert orc.rel_frobenius(alt_f, full_f) > 1e-3, f"storage point {pt} does not change the result"
+
+
 # ---------------------------------------------------------------------------
 # the pages' shapes
 # ---------------------------------------------------------------------------
