@@ -41,16 +41,21 @@
  *     so a call that returns an error has changed nothing.
  *   - The library keeps a per-device workspace (grown on demand, freed by
  *     muon_release_workspace) and a cache of launch plans keyed by the
- *     pointers and shapes.  Calls that overlap in time on one device (two
- *     host threads, or two streams) share that workspace and race; issue
- *     them on one stream or serialise them.
+ *     pointers and shapes.  Every call first makes its stream wait for the
+ *     device's previous call (an event recorded after each call's last
+ *     launch), so calls made on different streams, or from different host
+ *     threads, run on the device one after another in the order they were
+ *     made, never overlapping.
  *   - Nothing crosses the ABI as an exception; errors are status codes with
  *     a thread-local message from muon_last_error().
  *   - The persistent chain (muon_launch_mode) bounds every dependency wait;
  *     a wait that gives up (only possible when the GPU cannot hold the whole
- *     grid at once) skips its tile and raises a flag, and the next call on
- *     that device returns MUON_ERR_HIP saying the earlier results are
- *     invalid.
+ *     grid at once) skips its tile and raises a flag.  The next call on that
+ *     device waits on the host for that launch to end, reads the flag and
+ *     returns MUON_ERR_HIP saying the earlier results are invalid.
+ *   - Small per-call tables (per-matrix rates, per-tensor AdamW rates) are
+ *     copied to the device from pinned staging memory: the call does not
+ *     wait for earlier work on its stream.
  */
 #ifndef MUON_MI355X_H
 #define MUON_MI355X_H
@@ -196,7 +201,11 @@ typedef struct muon_matrix_desc {
  * lr         learning rate, finite, as a binary32 value; t = fl32(lr*s).
  * beta       momentum coefficient in [0, 1), used as its binary32 value.
  * nesterov   0 or 1.
- * ns_coeffs  finite a, b, c (c = 0 skips the A*A product).
+ * ns_coeffs  finite a, b, c (c = 0 skips the A*A product).  The products
+ *            add a X and (b/c) A as bfloat16 hi + lo pairs, so a and, when
+ *            c != 0, fl32(b/c) must round to a finite bfloat16 (magnitude
+ *            below about 3.3961e38; a subnormal c beside an ordinary b is
+ *            not): UNSUPPORTED otherwise.  Checked only when ns_steps > 0.
  * ns_steps   >= 0; 0 writes back the normalised momentum direction.
  * scale_rule a muon_scale_rule.
  *
@@ -226,7 +235,8 @@ muon_status muon_step_batched_ex(void* const* params, const void* const* grads,
 
 /* muon_step_batched_ex with the update variants of `options` (may be NULL,
  * see muon_step_options).  Per-matrix learning rates, scales or a weight
- * decay add one small host-to-device copy (8 bytes per matrix) on `stream`.
+ * decay add one small host-to-device copy (8 bytes per matrix) on `stream`,
+ * from pinned staging memory.
  * Errors as muon_step_batched, and INVALID_ARGUMENT for an option out of
  * its range.                                                              */
 muon_status muon_step_batched_v2(void* const* params, const void* const* grads,

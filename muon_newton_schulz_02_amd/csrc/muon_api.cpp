@@ -207,12 +207,34 @@ struct AdamwPlan {
   hipEvent_t last_use = nullptr;
 };
 
+// Pinned host staging of the small per-call tables (per-matrix write-back
+// scalars, per-tensor AdamW rates): copies from pinned memory are DMA
+// transfers that do not wait on the host for earlier work on the stream,
+// which copies from pageable memory may.  A ring of regions, each held until
+// the event recorded after its copy has completed.
+struct PinnedRing {
+  char* host = nullptr;
+  size_t bytes = 0;
+  size_t head = 0;
+  struct Use {
+    size_t off, len;
+    hipEvent_t ev;
+  };
+  std::vector<Use> busy;
+  std::vector<hipEvent_t> idle_events;
+};
+
 struct DeviceState {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   void* chain_ws = nullptr;            // per-step buffers of the persistent chain
   size_t chain_ws_bytes = 0;
   int32_t* fail_flag = nullptr;        // pinned host word the chain raises when a wait times out
+  hipEvent_t chain_done = nullptr;     // recorded after the last persistent-chain launch
+  bool chain_pending = false;          // a chain was launched since the flag was last read
+  hipEvent_t last_call = nullptr;      // recorded after every call's last launch on this device
+  bool last_call_recorded = false;
+  PinnedRing ring;
   int cus_per_xcd = 0;
   std::list<Plan*> plans;              // most recently used first
   std::list<AdamwPlan*> adamw_plans;   // most recently used first
@@ -282,6 +304,90 @@ void drop_plans(DeviceState& ds) {
   ds.plans.clear();
   for (AdamwPlan* p : ds.adamw_plans) free_adamw_plan(p);
   ds.adamw_plans.clear();
+}
+
+void release_ring(PinnedRing& r) {
+  for (auto& u : r.busy) {
+    (void)hipEventSynchronize(u.ev);
+    r.idle_events.push_back(u.ev);
+  }
+  r.busy.clear();
+  for (hipEvent_t e : r.idle_events) (void)hipEventDestroy(e);
+  r.idle_events.clear();
+  if (r.host) (void)hipHostFree(r.host);
+  r.host = nullptr;
+  r.bytes = 0;
+  r.head = 0;
+}
+
+// Copies `len` bytes from `src` to device memory `dst` on `stream` through
+// the device's pinned ring.  Waits on the host only when the ring region it
+// needs still feeds a copy that has not completed.
+hipError_t staged_copy(DeviceState& ds, void* dst, const void* src, size_t len, hipStream_t stream) {
+  PinnedRing& r = ds.ring;
+  const size_t need = align256(std::max<size_t>(len, 1));
+  if (need > r.bytes) {
+    release_ring(r);
+    const size_t bytes = std::max<size_t>(size_t(1) << 18, 2 * need);
+    void* h = nullptr;
+    if (hipHostMalloc(&h, bytes, hipHostMallocDefault) != hipSuccess) return hipErrorOutOfMemory;
+    r.host = reinterpret_cast<char*>(h);
+    r.bytes = bytes;
+  }
+  size_t off = r.head;
+  if (off + need > r.bytes) off = 0;
+  // retire completed copies; wait for any still in flight over [off, off + need)
+  for (size_t i = 0; i < r.busy.size();) {
+    PinnedRing::Use& u = r.busy[i];
+    const bool overlap = u.off < off + need && off < u.off + u.len;
+    bool done = hipEventQuery(u.ev) == hipSuccess;
+    if (!done && overlap) done = hipEventSynchronize(u.ev) == hipSuccess;
+    if (done) {
+      r.idle_events.push_back(u.ev);
+      r.busy[i] = r.busy.back();
+      r.busy.pop_back();
+    } else {
+      ++i;
+    }
+  }
+  (void)hipGetLastError();  // hipEventQuery reports hipErrorNotReady for copies in flight
+  memcpy(r.host + off, src, len);
+  hipError_t e = hipMemcpyAsync(dst, r.host + off, len, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return e;
+  hipEvent_t ev = nullptr;
+  if (!r.idle_events.empty()) {
+    ev = r.idle_events.back();
+    r.idle_events.pop_back();
+  } else if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) {
+    // without an event the region cannot be tracked: wait for the copy
+    (void)hipGetLastError();
+    return hipStreamSynchronize(stream);
+  }
+  if ((e = hipEventRecord(ev, stream)) != hipSuccess) {
+    r.idle_events.push_back(ev);
+    return e;
+  }
+  r.busy.push_back({off, need, ev});
+  r.head = off + need;
+  return hipSuccess;
+}
+
+// Every call on a device first makes its stream wait for the device's
+// previous call (their launches share the workspace, plans and tables), so
+// calls issued on different streams run in the order they were made.
+hipError_t order_after_last_call(DeviceState& ds, hipStream_t stream) {
+  if (!ds.last_call) {
+    if (hipEventCreateWithFlags(&ds.last_call, hipEventDisableTiming) != hipSuccess) {
+      ds.last_call = nullptr;
+      return hipGetLastError();
+    }
+  }
+  if (!ds.last_call_recorded) return hipSuccess;
+  return hipStreamWaitEvent(stream, ds.last_call, 0);
+}
+
+void record_last_call(DeviceState& ds, hipStream_t stream) {
+  if (ds.last_call && hipEventRecord(ds.last_call, stream) == hipSuccess) ds.last_call_recorded = true;
 }
 
 struct TileSrc {
@@ -661,6 +767,34 @@ double rule_scale(int rule, int64_t rows, int64_t cols) {
   return 1.0;
 }
 
+// The products add a X and (b/c) A on the matrix cores, each scale split into
+// bfloat16 hi + lo parts of its binary32 value, and B = c (A A + (b/c) A).  A
+// triple is usable when a and, for c != 0, fl32(b/c) are finite and round to a
+// finite bfloat16 hi part (magnitude below 0x7F7F8000 as binary32, about
+// 3.3961e38): a subnormal c beside an ordinary b gives b/c = +-inf, whose
+// split would fill B with NaN.
+bool split_ok(float v) {
+  const uint32_t lim = 0x7F7F8000u;
+  float fl;
+  memcpy(&fl, &lim, sizeof(fl));
+  return std::isfinite(v) && std::fabs(v) < fl;
+}
+
+muon_status check_triple(const muon_ns_coeffs& co, const char* what, int k) {
+  if (!std::isfinite(co.a) || !std::isfinite(co.b) || !std::isfinite(co.c))
+    return fail(MUON_ERR_INVALID_ARGUMENT, "%s[%d] is not finite", what, k);
+  if (!split_ok(co.a))
+    return fail(MUON_ERR_UNSUPPORTED, "%s[%d]: a = %g is too large to split into bfloat16 hi + lo", what, k,
+                double(co.a));
+  if (co.c != 0.f) {
+    const float q = co.b / co.c;
+    if (!split_ok(q))
+      return fail(MUON_ERR_UNSUPPORTED, "%s[%d]: b/c = %g/%g is %g in binary32, too large to split into bfloat16 "
+                  "hi + lo", what, k, double(co.b), double(co.c), double(q));
+  }
+  return MUON_OK;
+}
+
 // Whether the write-back takes per-matrix scalars from the host.
 bool per_matrix_wb(const Call& c) {
   return c.opt && (c.opt->weight_decay != 0.f || c.opt->lr_per_matrix || c.opt->scale_per_matrix);
@@ -693,10 +827,10 @@ muon_status validate_call(const Call& c) {
     if (o.launch_mode == MUON_LAUNCH_CHAIN && c.ns_steps > MAX_CHAIN_STEPS)
       return fail(MUON_ERR_UNSUPPORTED, "the persistent chain takes at most %d Newton-Schulz steps", MAX_CHAIN_STEPS);
     if (o.ns_schedule)
-      for (int32_t k = 0; k < c.ns_steps; ++k)
-        if (!std::isfinite(o.ns_schedule[k].a) || !std::isfinite(o.ns_schedule[k].b) ||
-            !std::isfinite(o.ns_schedule[k].c))
-          return fail(MUON_ERR_INVALID_ARGUMENT, "ns_schedule[%d] is not finite", k);
+      for (int32_t k = 0; k < c.ns_steps; ++k) {
+        const muon_status st = check_triple(o.ns_schedule[k], "ns_schedule", k);
+        if (st != MUON_OK) return st;
+      }
     for (int32_t i = 0; i < c.count; ++i) {
       if (o.lr_per_matrix && !std::isfinite(o.lr_per_matrix[i]))
         return fail(MUON_ERR_INVALID_ARGUMENT, "lr_per_matrix[%d] is not finite", i);
@@ -711,6 +845,11 @@ muon_status validate_call(const Call& c) {
       return fail(MUON_ERR_INVALID_ARGUMENT, "ns_steps %d out of range [0, %d]", c.ns_steps, MAX_NS_STEPS);
     if (!std::isfinite(c.co.a) || !std::isfinite(c.co.b) || !std::isfinite(c.co.c))
       return fail(MUON_ERR_INVALID_ARGUMENT, "ns_coeffs must be finite");
+    const bool sched = c.mode == MODE_STEP && c.opt && c.opt->ns_schedule;
+    if (!sched && c.ns_steps > 0) {
+      const muon_status st = check_triple(c.co, "ns_coeffs", 0);
+      if (st != MUON_OK) return st;
+    }
   }
   muon_status st = validate_desc(c.shapes, c.count, c.mode);
   if (st != MUON_OK) return st;
@@ -782,6 +921,13 @@ muon_status run(const Call& c) {
     }
     ds.fail_flag = reinterpret_cast<int32_t*>(f);
     *ds.fail_flag = 0;
+  }
+  // the flag is final once the chain that may raise it has ended
+  if (ds.chain_pending) {
+    if (hipEventSynchronize(ds.chain_done) != hipSuccess)
+      return fail(MUON_ERR_HIP, "waiting for the earlier persistent Newton-Schulz launch failed: %s",
+                  hipGetErrorString(hipGetLastError()));
+    ds.chain_pending = false;
   }
   if (__atomic_load_n(ds.fail_flag, __ATOMIC_ACQUIRE) != 0) {
     __atomic_store_n(ds.fail_flag, 0, __ATOMIC_RELEASE);
@@ -962,12 +1108,12 @@ muon_status run(const Call& c) {
   }
 
   // ------------------------------------------------------------ launches
-  hipError_t e = hipSuccess;
+  hipError_t e = order_after_last_call(ds, c.stream);
   const int kmode = c.mode == MODE_STEP ? 0 : (c.mode == MODE_NS ? 1 : 2);
   const int32_t ema = (c.mode == MODE_STEP && c.opt && c.opt->momentum_kind == MUON_MOMENTUM_EMA) ? 1 : 0;
   // per-matrix write-back scalars t_i = fl32(lr_i * s_i), d_i = fl32(1 - fl32(lr_i * wd))
   const float2* wb = nullptr;
-  if (c.mode == MODE_STEP && per_matrix_wb(c)) {
+  if (e == hipSuccess && c.mode == MODE_STEP && per_matrix_wb(c)) {
     std::vector<float2> hwb(size_t(c.count));
     for (int32_t i = 0; i < c.count; ++i) {
       const float lr_i = c.opt->lr_per_matrix ? c.opt->lr_per_matrix[i] : c.lr;
@@ -977,8 +1123,7 @@ muon_status run(const Call& c) {
       const float lw = lr_i * decay;
       hwb[size_t(i)] = make_float2(float(double(lr_i) * s_i), decay != 0.f ? 1.f - lw : 1.f);
     }
-    // pageable source: the copy takes the data before the call returns
-    e = hipMemcpyAsync(plan->d_wb, hwb.data(), sizeof(float2) * size_t(c.count), hipMemcpyHostToDevice, c.stream);
+    e = staged_copy(ds, plan->d_wb, hwb.data(), sizeof(float2) * size_t(c.count), c.stream);
     wb = plan->d_wb;
   }
   if (e == hipSuccess)
@@ -1042,6 +1187,14 @@ muon_status run(const Call& c) {
           return launch_ns_chain(prec, ch.d_imats, plan->d_scal, ch.d_items, ch.d_xcd_off, ch.per_xcd_max,
                                  ch.d_steps, ch.d_sync, ch.nsync, ds.fail_flag, ca, c.stream);
         });
+        if (e == hipSuccess) {
+          if (!ds.chain_done && hipEventCreateWithFlags(&ds.chain_done, hipEventDisableTiming) != hipSuccess) {
+            ds.chain_done = nullptr;
+            e = hipGetLastError();
+          }
+          if (e == hipSuccess) e = hipEventRecord(ds.chain_done, c.stream);
+          if (e == hipSuccess) ds.chain_pending = true;
+        }
       }
       for (int it = 0; it < c.ns_steps && e == hipSuccess; ++it) {
         const muon_ns_coeffs co = cos[size_t(it)];
@@ -1071,6 +1224,7 @@ muon_status run(const Call& c) {
   }
   if (e != hipSuccess) return fail(MUON_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   (void)hipEventRecord(plan->last_use, c.stream);
+  record_last_call(ds, c.stream);
   return MUON_OK;
 }
 
@@ -1274,8 +1428,8 @@ muon_status run_adamw(const AdamwCall& c) {
   k.bc2 = float(1.0 - std::pow(double(h.beta2), double(h.step)));
   k.eps = h.eps;
   const float2* rates = nullptr;
-  hipError_t e = hipSuccess;
-  if (h.lr_per_tensor || h.wd_per_tensor) {
+  hipError_t e = order_after_last_call(ds, c.stream);
+  if (e == hipSuccess && (h.lr_per_tensor || h.wd_per_tensor)) {
     std::vector<float2> hr(plan->count);
     for (int32_t j = 0; j < plan->count; ++j) {
       const int32_t i = plan->kept[j];
@@ -1283,7 +1437,7 @@ muon_status run_adamw(const AdamwCall& c) {
       const float wd = h.wd_per_tensor ? h.wd_per_tensor[i] : h.weight_decay;
       hr[j] = make_float2(lr, decay_factor(lr, wd));
     }
-    e = hipMemcpyAsync(plan->d_rates, hr.data(), sizeof(float2) * hr.size(), hipMemcpyHostToDevice, c.stream);
+    e = staged_copy(ds, plan->d_rates, hr.data(), sizeof(float2) * hr.size(), c.stream);
     rates = plan->d_rates;
   }
   if (e == hipSuccess) {
@@ -1294,6 +1448,7 @@ muon_status run_adamw(const AdamwCall& c) {
   }
   if (e != hipSuccess) return fail(MUON_ERR_HIP, "AdamW launch failed: %s", hipGetErrorString(e));
   (void)hipEventRecord(plan->last_use, c.stream);
+  record_last_call(ds, c.stream);
   return MUON_OK;
 }
 
@@ -1472,6 +1627,9 @@ muon_status muon_release_workspace(void) {
     kv.second.chain_ws_bytes = 0;
     if (kv.second.fail_flag) (void)hipHostFree(kv.second.fail_flag);
     kv.second.fail_flag = nullptr;
+    release_ring(kv.second.ring);
+    if (kv.second.chain_done) (void)hipEventDestroy(kv.second.chain_done);
+    if (kv.second.last_call) (void)hipEventDestroy(kv.second.last_call);
   }
   if (have_dev) (void)hipSetDevice(cur);
   g_dev.clear();

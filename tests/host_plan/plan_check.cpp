@@ -47,6 +47,7 @@ static hipError_t s_evc2(hipEvent_t* e) { *e = reinterpret_cast<hipEvent_t>(0x1)
 static hipError_t s_evr(hipEvent_t, hipStream_t) { return hipSuccess; }
 static hipError_t s_ev1(hipEvent_t) { return hipSuccess; }
 static hipError_t s_setdev(int) { return hipSuccess; }
+static hipError_t s_wait(hipStream_t, hipEvent_t, unsigned) { return hipSuccess; }
 static hipError_t s_elapsed(float* ms, hipEvent_t, hipEvent_t) { *ms = 0; return hipSuccess; }
 static const char* s_errstr(hipError_t) { return "stub"; }
 #define hipMalloc s_malloc
@@ -63,6 +64,8 @@ static const char* s_errstr(hipError_t) { return "stub"; }
 #define hipEventCreate s_evc2
 #define hipEventRecord s_evr
 #define hipEventSynchronize s_ev1
+#define hipEventQuery s_ev1
+#define hipStreamWaitEvent s_wait
 #define hipEventDestroy s_ev1
 #define hipGetLastError s_ok0
 #define hipEventElapsedTime s_elapsed

@@ -105,6 +105,36 @@ def test_scalar_errors(L, kw, status):
     assert _call(L, [_desc(16, 32)], [p], [g], [m], **kw) == status
 
 
+@pytest.mark.parametrize("coeffs", [
+    (3.4445, -4.775, 1e-39),             # subnormal c: b/c is -inf in binary32
+    (3.4445, -4.775, 1e-38),             # b/c = -4.8e38: finite binary32, but its bf16 part is not
+    (3.4e38, -4.775, 2.0315),            # a too large for a finite bf16 hi part
+])
+def test_coefficients_that_cannot_be_split_are_rejected(L, coeffs):
+    # the products run a X and (b/c) A as bfloat16 hi + lo pairs; a triple
+    # whose a or fl32(b/c) has no finite bf16 hi part would turn B into NaN
+    p, g, m = _ptrs(0, 16, 32)
+    assert _call(L, [_desc(16, 32)], [p], [g], [m], coeffs=coeffs) == mb.MUON_ERR_UNSUPPORTED
+    assert "split" in mb.muon_last_error()
+    # the same triple in a schedule, at its step only
+    sched = (mb.NsCoeffs * 2)(mb.NsCoeffs(3.4445, -4.775, 2.0315), mb.NsCoeffs(*coeffs))
+    o = _opt(ns_schedule=ctypes.cast(sched, ctypes.POINTER(mb.NsCoeffs)))
+    assert _call_v2(L, ctypes.byref(o), steps=2) == mb.MUON_ERR_UNSUPPORTED
+    assert "ns_schedule[1]" in mb.muon_last_error()
+    assert _call_v2(L, ctypes.byref(o), steps=1) != mb.MUON_ERR_UNSUPPORTED
+
+
+def test_coefficients_at_the_split_limit_pass(L):
+    # c = 0 never forms b/c; a large but splittable b/c passes validation
+    p, g, m = _ptrs(0, 16, 32)
+    for coeffs in [(1.5, -0.5, 0.0), (3.4445, -4.775, 1e-30), (3.3e38, 1.0, 0.0)]:
+        st = _call(L, [_desc(16, 32)], [p], [g], [m], coeffs=coeffs)
+        assert st not in (mb.MUON_ERR_UNSUPPORTED, mb.MUON_ERR_INVALID_ARGUMENT), (coeffs, mb.muon_last_error())
+    # with no Newton-Schulz step the triple is not used
+    assert _call(L, [_desc(16, 32)], [p], [g], [m], coeffs=(1.0, 1.0, 1e-39), steps=0) \
+        not in (mb.MUON_ERR_UNSUPPORTED, mb.MUON_ERR_INVALID_ARGUMENT)
+
+
 def _call_v2(L, opt, steps=5, n=1):
     descs = [_desc(16, 32) for _ in range(n)]
     ptrs = [_ptrs(i, 16, 32) for i in range(n)]

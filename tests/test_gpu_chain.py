@@ -163,6 +163,20 @@ def test_chain_wait_give_up_is_reported_and_cleared():
     with pytest.raises(mb.MuonError) as ei:
         _run(ws, gs, ms, mb.LAUNCH_CHAIN, precision=mb.NS_BF16, steps=5)
     assert ei.value.status == mb.MUON_ERR_HIP and "gave up" in ei.value.detail
+    # the next call reports it with no synchronisation in between: it waits
+    # for the earlier chain to end before reading the flag
+    w_d, g_d, m_d = ([t.cuda() for t in x] for x in (ws, gs, ms))
+    torch.cuda.synchronize()
+    kw = dict(lr=f32(0.02), beta=0.95, nesterov=1, ns_coeffs=MUON, ns_steps=5, launch_mode=mb.LAUNCH_CHAIN)
+    os.environ["MUON_CHAIN_SPIN_LIMIT"] = "0"
+    try:
+        mb.muon_step_batched_v2(w_d, g_d, m_d, **kw)
+    finally:
+        del os.environ["MUON_CHAIN_SPIN_LIMIT"]
+    with pytest.raises(mb.MuonError) as ei:
+        mb.muon_step_batched_v2(w_d, g_d, m_d, **kw)
+    assert ei.value.status == mb.MUON_ERR_HIP and "gave up" in ei.value.detail
+    torch.cuda.synchronize()
     # cleared: the next calls run and agree with the per-phase grids
     a = _run(ws, gs, ms, mb.LAUNCH_PHASE_GRIDS, precision=mb.NS_BF16, steps=5)
     b = _run(ws, gs, ms, mb.LAUNCH_CHAIN, precision=mb.NS_BF16, steps=5)

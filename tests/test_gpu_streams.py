@@ -1,0 +1,139 @@
+"""Calls on more than one stream, and calls that must not wait on the host.
+
+* Two calls issued back to back on two streams share the device's workspace
+  and tables; the library orders each call after the device's previous one,
+  so the results equal those of the same calls made one after the other.
+* The per-call tables (per-matrix write-back scalars, per-tensor AdamW rates)
+  go to the device through pinned staging, so a call returns while earlier
+  work on its stream is still running.
+"""
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from muon_newton_schulz_02_amd import binding as mb
+
+from gpu_helpers import MUON, f32
+
+pytestmark = pytest.mark.gpu
+
+# a register-only matrix-core loop of about a quarter of a second, enqueued
+# ahead of a call to keep its stream busy
+PROBE_ITERATIONS = 2_000_000
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _stack(shapes, seed):
+    gen = torch.Generator().manual_seed(seed)
+    ws = [(torch.randn(s, generator=gen) * 0.02).to(torch.bfloat16).cuda() for s in shapes]
+    gs = [torch.randn(s, generator=gen).to(torch.bfloat16).cuda() for s in shapes]
+    ms = [torch.randn(s, generator=gen).cuda() for s in shapes]
+    return ws, gs, ms
+
+
+def _bits(ts):
+    return [t.view(torch.int16).cpu().numpy() if t.dtype == torch.bfloat16 else t.view(torch.int32).cpu().numpy()
+            for t in ts]
+
+
+def test_calls_on_two_streams_run_in_call_order():
+    _announce("two stacks on two streams")
+    kw = dict(lr=f32(0.02), beta=0.95, nesterov=1, ns_coeffs=MUON, ns_steps=5)
+    p = _stack([(1024, 1024)] * 8, 5)
+    q = _stack([(768, 2048), (2048, 768)] * 2, 6)
+    p0 = [[t.clone() for t in x] for x in (p[0], p[2])]
+    q0 = [[t.clone() for t in x] for x in (q[0], q[2])]
+    # one after the other on the current stream (also builds both plans)
+    mb.muon_step_batched(*p, **kw)
+    torch.cuda.synchronize()
+    mb.muon_step_batched(*q, **kw)
+    torch.cuda.synchronize()
+    ref = (_bits(p[0]) + _bits(p[2]), _bits(q[0]) + _bits(q[2]))
+    for dst, src in ((p[0], p0[0]), (p[2], p0[1]), (q[0], q0[0]), (q[2], q0[1])):
+        for d, s in zip(dst, src):
+            d.copy_(s)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        # the second call's inputs are ready; only the library's ordering
+        # keeps it from overwriting the workspace the first call still reads
+        mb.muon_step_batched(*p, stream=s1, **kw)
+        mb.muon_step_batched(*q, stream=s2, **kw)
+        torch.cuda.synchronize()
+        got = (_bits(p[0]) + _bits(p[2]), _bits(q[0]) + _bits(q[2]))
+        for a, b in zip(ref, got):
+            for x, y in zip(a, b):
+                assert np.array_equal(x, y), "a call on a second stream changed the result of the first"
+        for dst, src in ((p[0], p0[0]), (p[2], p0[1]), (q[0], q0[0]), (q[2], q0[1])):
+            for d, s in zip(dst, src):
+                d.copy_(s)
+        torch.cuda.synchronize()
+
+
+def _busy_stream(stream):
+    sink = torch.zeros(1, device="cuda")
+    mb.muon_mfma_probe(PROBE_ITERATIONS, sink, stream=stream)
+    return sink
+
+
+def test_per_matrix_tables_do_not_block_the_host():
+    _announce("v2 with weight decay and per-matrix rates behind a busy stream")
+    shapes = [(512, 768), (768, 512), (256, 256)]
+    w, g, m = _stack(shapes, 9)
+    w0, m0 = [t.clone() for t in w], [t.clone() for t in m]
+    kw = dict(lr=f32(0.02), beta=0.95, nesterov=1, ns_coeffs=MUON, ns_steps=3, weight_decay=0.05,
+              lr_per_matrix=[0.02, 0.01, 0.03], scale_per_matrix=[1.0, 2.0, 0.5])
+    mb.muon_step_batched_v2(w, g, m, **kw)             # builds and caches the plan
+    torch.cuda.synchronize()
+    ref = _bits(w) + _bits(m)
+    for d, s in zip(w + m, w0 + m0):
+        d.copy_(s)
+    stream = torch.cuda.current_stream()
+    sink = _busy_stream(stream)
+    t0 = time.perf_counter()
+    mb.muon_step_batched_v2(w, g, m, **kw)
+    dt = time.perf_counter() - t0
+    busy = not stream.query()
+    torch.cuda.synchronize()
+    print(f"call returned after {dt * 1e3:.2f} ms; stream busy: {busy}")
+    assert busy, "the call waited on the host for earlier work on its stream"
+    assert dt < 0.1
+    assert all(np.array_equal(a, b) for a, b in zip(ref, _bits(w) + _bits(m)))
+    del sink
+
+
+def test_adamw_per_tensor_rates_do_not_block_the_host():
+    _announce("AdamW with per-tensor rates behind a busy stream")
+    gen = torch.Generator().manual_seed(3)
+    n = [5000, 70000, 33]
+    p = [(torch.randn(k, generator=gen) * 0.02).to(torch.bfloat16).cuda() for k in n]
+    gr = [(torch.randn(k, generator=gen) * 1e-3).to(torch.bfloat16).cuda() for k in n]
+    ea = [(torch.randn(k, generator=gen) * 1e-3).cuda() for k in n]
+    eq = [(torch.randn(k, generator=gen) * 1e-3).square().cuda() for k in n]
+    keep = [t.clone() for t in p + ea + eq]
+    kw = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, step=7,
+              lr_per_tensor=[1e-3, 2e-3, 5e-4], wd_per_tensor=[0.1, 0.0, 0.01])
+    mb.muon_adamw_batched(p, gr, ea, eq, **kw)
+    torch.cuda.synchronize()
+    ref = _bits(p) + _bits(ea) + _bits(eq)
+    for d, s in zip(p + ea + eq, keep):
+        d.copy_(s)
+    stream = torch.cuda.current_stream()
+    sink = _busy_stream(stream)
+    t0 = time.perf_counter()
+    mb.muon_adamw_batched(p, gr, ea, eq, **kw)
+    dt = time.perf_counter() - t0
+    busy = not stream.query()
+    torch.cuda.synchronize()
+    print(f"call returned after {dt * 1e3:.2f} ms; stream busy: {busy}")
+    assert busy and dt < 0.1
+    assert all(np.array_equal(a, b) for a, b in zip(ref, _bits(p) + _bits(ea) + _bits(eq)))
+    del sink
