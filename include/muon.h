@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 3
+#define MUON_ABI_VERSION 4
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -326,6 +326,69 @@ muon_status muon_adamw_batched(void* const* params, const void* const* grads,
                                float* const* exp_avg, float* const* exp_avg_sq,
                                const muon_adamw_desc* tensors, int32_t count,
                                const muon_adamw_hparams* hparams, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Streaming the step into backward.  "把 GPT-2 的训练租金估算从 4.3 万美元压到
+ * 40 美元…" (magicnetworld.com), section "speedrun 全流程：一条命令背后发生了什么",
+ * places the Muon step inside pretraining (base_train), after every backward
+ * pass.  Backward produces the last layer's gradients first; a stream plan
+ * lets the step of each group of matrices (a layer, say) start on the device
+ * as soon as that group's gradients are complete, on the optimizer's stream,
+ * while backward goes on with the earlier layers on its own.
+ * --------------------------------------------------------------------- */
+
+typedef struct muon_stream_plan_s* muon_stream_plan;
+
+/* The arguments of one step, as muon_step_batched_v2 takes them.           */
+typedef struct muon_step_hparams {
+  float lr;
+  float beta;
+  int32_t nesterov;
+  muon_ns_coeffs ns_coeffs;
+  int32_t ns_steps;
+  int32_t scale_rule;
+  const muon_step_options* options;   /* may be NULL */
+} muon_step_hparams;
+
+/* Builds a stream plan over `count` >= 1 matrices split into `ngroups` >= 1
+ * groups.  params, grads, momenta, shapes and updates_out (may be NULL) are
+ * as for muon_step_batched_ex and must stay valid until the plan is
+ * destroyed; group_of is a host array of `count` group indices in
+ * [0, ngroups) (groups may be empty), read during the call.  tile_mode (a
+ * muon_tile_mode) fixes the working format of every matrix from the whole
+ * set, as one call over all of them would choose it.  The plan owns a
+ * workspace for its largest group and uploads every launch table here, so a
+ * submit neither allocates nor synchronises.  *plan_out receives the plan.
+ * Errors: those of muon_step_batched_ex's matrices and pointers,
+ * INVALID_ARGUMENT for a bad group index, count, ngroups or tile_mode,
+ * OUT_OF_MEMORY, HIP.                                                       */
+muon_status muon_stream_plan_create(void* const* params, const void* const* grads, void* const* momenta,
+                                    const muon_matrix_desc* shapes, int32_t count, const int32_t* group_of,
+                                    int32_t ngroups, int32_t tile_mode, float* const* updates_out,
+                                    muon_stream_plan* plan_out);
+
+/* Enqueues one whole Muon step (momentum, normalisation, Newton-Schulz,
+ * write-back) of the matrices of `group` on `stream`, behind `ready_event`
+ * and behind the device's previous call.  ready_event is a hipEvent_t that
+ * the caller recorded after the last write of those gradients (typically on
+ * its backward stream) BEFORE this call, since a wait on an event never
+ * recorded does not wait; NULL: no wait.  Submit every group once per step,
+ * in any order.  W, M and the exported O of every matrix are then
+ * bit-identical to one muon_step_batched_v2 call over the whole set with the
+ * same hparams: the per-matrix arithmetic does not depend on the grouping.
+ * The groups' steps share the plan's workspace and run one after another on
+ * the device.  hparams->options: lr_per_matrix and scale_per_matrix are
+ * indexed over the whole set; launch_mode must be AUTO or PHASE_GRIDS
+ * (CHAIN: UNSUPPORTED); tile_mode is ignored (fixed by the plan).  The
+ * current device must be the plan's.  An empty group is a no-op.
+ * Errors: INVALID_ARGUMENT (null plan or hparams, group out of range, a bad
+ * hyperparameter, another device), UNSUPPORTED, HIP.                        */
+muon_status muon_stream_submit(muon_stream_plan plan, int32_t group, void* ready_event,
+                               const muon_step_hparams* hparams, void* stream);
+
+/* Waits for the plan's submitted work, then frees its workspace and tables.
+ * NULL is a no-op.                                                          */
+muon_status muon_stream_plan_destroy(muon_stream_plan plan);
 
 /* Kernel classes of the launch sequence, for muon_timing_read.            */
 typedef enum muon_kernel_class {

@@ -98,6 +98,15 @@ class AdamwHparams(ctypes.Structure):
     ]
 
 
+class StepHparams(ctypes.Structure):
+    """muon_step_hparams (include/muon.h)."""
+    _fields_ = [
+        ("lr", ctypes.c_float), ("beta", ctypes.c_float), ("nesterov", ctypes.c_int32),
+        ("ns_coeffs", NsCoeffs), ("ns_steps", ctypes.c_int32), ("scale_rule", ctypes.c_int32),
+        ("options", ctypes.POINTER(StepOptions)),
+    ]
+
+
 _VP = ctypes.c_void_p
 _PP = ctypes.POINTER(ctypes.c_void_p)
 _lib = None
@@ -150,6 +159,12 @@ def lib() -> ctypes.CDLL:
     L.muon_timing_read.restype = i32
     L.muon_abi_version.argtypes = []
     L.muon_abi_version.restype = i32
+    L.muon_stream_plan_create.argtypes = [_PP, _PP, _PP, D, i32, ctypes.POINTER(i32), i32, i32, _PP, _PP]
+    L.muon_stream_plan_create.restype = i32
+    L.muon_stream_submit.argtypes = [_VP, i32, _VP, ctypes.POINTER(StepHparams), _VP]
+    L.muon_stream_submit.restype = i32
+    L.muon_stream_plan_destroy.argtypes = [_VP]
+    L.muon_stream_plan_destroy.restype = i32
     _lib = L
     return L
 
@@ -304,6 +319,18 @@ def muon_step_batched_v2(params, grads=None, momenta=None, *, lr, beta, nesterov
     args = params if isinstance(params, StepArgs) else StepArgs(params, grads, momenta, precision, updates_out)
     a, b, c = ns_coeffs
     co = NsCoeffs(float(a), float(b), float(c))
+    opt, keep = _step_options(args.count, ns_steps, ns_schedule, weight_decay, momentum_kind, lr_per_matrix,
+                              scale_per_matrix, launch_mode, tile_mode)
+    status = lib().muon_step_batched_v2(args.params, args.grads, args.momenta, args.descs, args.count,
+                                        float(lr), float(beta), int(nesterov), co, int(ns_steps),
+                                        int(scale_rule), ctypes.byref(opt), args.updates, _stream_handle(stream))
+    del keep
+    _check(status)
+
+
+def _step_options(count, ns_steps, ns_schedule, weight_decay, momentum_kind, lr_per_matrix, scale_per_matrix,
+                  launch_mode, tile_mode):
+    """A muon_step_options and the ctypes arrays it points into (keep them alive)."""
     opt = StepOptions()
     keep = []
     if ns_schedule is not None:
@@ -318,16 +345,64 @@ def muon_step_batched_v2(params, grads=None, momenta=None, *, lr, beta, nesterov
     opt.tile_mode = int(tile_mode)
     for name, vals in (("lr_per_matrix", lr_per_matrix), ("scale_per_matrix", scale_per_matrix)):
         if vals is not None:
-            if len(vals) != args.count:
+            if len(vals) != count:
                 raise ValueError(f"{name} needs one value per matrix")
             arr = (ctypes.c_float * max(len(vals), 1))(*[float(v) for v in vals])
             keep.append(arr)
             setattr(opt, name, ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)))
-    status = lib().muon_step_batched_v2(args.params, args.grads, args.momenta, args.descs, args.count,
-                                        float(lr), float(beta), int(nesterov), co, int(ns_steps),
-                                        int(scale_rule), ctypes.byref(opt), args.updates, _stream_handle(stream))
-    del keep
-    _check(status)
+    return opt, keep
+
+
+class StreamPlan:
+    """A stream plan (muon_stream_plan_create): the step of each group of
+    matrices is submitted on its own, behind the event that marks that
+    group's gradients complete, so it can start while backward still runs.
+    The results equal one muon_step_batched_v2 call over every matrix."""
+
+    def __init__(self, params, grads, momenta, group_of, ngroups=None, *, precision=NS_BF16,
+                 tile_mode=TILES_AUTO, updates_out=None):
+        self.args = StepArgs(params, grads, momenta, precision, updates_out)
+        if len(group_of) != self.args.count:
+            raise ValueError("one group index per matrix")
+        self.ngroups = int(ngroups) if ngroups is not None else (max(group_of) + 1 if len(group_of) else 0)
+        grp = (ctypes.c_int32 * max(len(group_of), 1))(*[int(v) for v in group_of])
+        self._h = ctypes.c_void_p()
+        _check(lib().muon_stream_plan_create(self.args.params, self.args.grads, self.args.momenta, self.args.descs,
+                                             self.args.count, grp, self.ngroups, int(tile_mode), self.args.updates,
+                                             ctypes.byref(self._h)))
+
+    def submit(self, group, ready_event=None, *, lr, beta, nesterov, ns_coeffs, ns_steps, scale_rule=SCALE_NONE,
+               stream=None, ns_schedule=None, weight_decay=0.0, momentum_kind=MOMENTUM_HEAVY_BALL,
+               lr_per_matrix=None, scale_per_matrix=None, launch_mode=LAUNCH_AUTO):
+        """Enqueue group `group`'s step behind `ready_event` (a recorded
+        torch.cuda.Event, a raw hipEvent_t as an int, or None)."""
+        if self._h is None or not self._h.value:
+            raise ValueError("the stream plan is closed")
+        opt, keep = _step_options(self.args.count, ns_steps, ns_schedule, weight_decay, momentum_kind,
+                                  lr_per_matrix, scale_per_matrix, launch_mode, TILES_AUTO)
+        a, b, c = ns_coeffs
+        hp = StepHparams(float(lr), float(beta), int(nesterov), NsCoeffs(float(a), float(b), float(c)),
+                         int(ns_steps), int(scale_rule), ctypes.pointer(opt))
+        if ready_event is None:
+            ev = None
+        elif isinstance(ready_event, int):
+            ev = ready_event
+        else:
+            ev = ready_event.cuda_event
+        status = lib().muon_stream_submit(self._h, int(group), ev, ctypes.byref(hp), _stream_handle(stream))
+        del keep
+        _check(status)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().muon_stream_plan_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001
+            pass
 
 
 def muon_step_batched_ex(params, grads, momenta, updates_out, **kw):

@@ -891,18 +891,17 @@ bool vec_aligned(const void* p, int64_t ld, int esz) {
   return (reinterpret_cast<uintptr_t>(p) % uintptr_t(4 * esz) == 0) && (ld % 4 == 0);
 }
 
-muon_status run(const Call& c) {
-  t_last_error.clear();
-  muon_status st = validate_call(c);
-  if (st != MUON_OK || c.count == 0) return st;
-
+// The calling thread's current device and its state (g_mu held): compute
+// units per XCD, and the give-up flag of an earlier persistent chain.
+muon_status acquire_device(DeviceState** out, int* dev_out = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
     return fail(MUON_ERR_HIP, "hipGetDevice failed (no HIP device?)");
   }
-  std::lock_guard<std::mutex> lock(g_mu);
   DeviceState& ds = g_dev[dev];
+  *out = &ds;
+  if (dev_out) *dev_out = dev;
   if (ds.cus_per_xcd == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
@@ -934,181 +933,105 @@ muon_status run(const Call& c) {
     return fail(MUON_ERR_HIP, "an earlier persistent Newton-Schulz launch on this device gave up waiting for a "
                 "dependency; the results of that call are invalid");
   }
+  return MUON_OK;
+}
 
-  // working format per matrix: a bf16 stack whose GRAM phase has fewer
-  // 256 x 256 tiles than the GPU has compute units takes 128 x 128 tiles
-  // (measured: 12 x 768^2 0.41 -> 0.34 ms per step; with three d24 layers,
-  // 378 GRAM tiles, the pipelined 256 x 256 tiles stay faster), and a
-  // binary32 stack with fewer 128 x 128 GRAM tiles than that takes 64 x 64
-  // tiles (one 256 x 256 matrix: 3 GRAM tiles of 128, 10 of 64)
-  std::vector<int> iprec(size_t(c.count), PREC_BF16);
-  if (c.mode != MODE_NORMS) {
-    const int32_t tmode = (c.mode == MODE_STEP && c.opt) ? c.opt->tile_mode : MUON_TILES_AUTO;
+// Working format of each matrix (a Prec) for a call of `mode` with tile mode
+// `tmode` on a GPU with `cus` compute units.
+std::vector<int> working_formats(const muon_matrix_desc* shapes, int32_t count, Mode mode, int32_t tmode,
+                                 int64_t cus) {
+  std::vector<int> iprec(size_t(count), PREC_BF16);
+  if (mode != MODE_NORMS) {
     int64_t bf16_gram = 0, f32_gram = 0;
-    for (int32_t i = 0; i < c.count; ++i) {
-      if (c.shapes[i].precision == MUON_NS_BF16) bf16_gram += gram_tiles_of(c.shapes[i], PREC_BF16);
-      if (c.shapes[i].precision == MUON_NS_F32) f32_gram += gram_tiles_of(c.shapes[i], PREC_F32);
+    for (int32_t i = 0; i < count; ++i) {
+      if (shapes[i].precision == MUON_NS_BF16) bf16_gram += gram_tiles_of(shapes[i], PREC_BF16);
+      if (shapes[i].precision == MUON_NS_F32) f32_gram += gram_tiles_of(shapes[i], PREC_F32);
     }
-    const int64_t cus = int64_t(NUM_XCD) * ds.cus_per_xcd;
     const bool small_bf16 = tmode == MUON_TILES_SMALL || (tmode == MUON_TILES_AUTO && bf16_gram < cus);
     const bool small_f32 = tmode == MUON_TILES_SMALL || (tmode == MUON_TILES_AUTO && f32_gram < cus);
-    for (int32_t i = 0; i < c.count; ++i) {
-      const int p = c.shapes[i].precision;
+    for (int32_t i = 0; i < count; ++i) {
+      const int p = shapes[i].precision;
       iprec[size_t(i)] = (p == MUON_NS_BF16 && small_bf16) ? int(PREC_BF16S)
                          : (p == MUON_NS_F32 && small_f32) ? int(PREC_F32S)
                                                            : p;
     }
   }
+  return iprec;
+}
 
-  // which working formats run as one persistent chain: only when asked for
-  // (AUTO keeps the per-phase grids: measured on MI355X, the chain is slower
-  // on every workload tried; it gives up the grids' cross-tile prefetch of
-  // stage 0, pays a release per tile, and spills more)
-  std::map<int, bool> use_chain;
-  size_t chain_need = 0;
-  if (c.mode != MODE_NORMS && c.ns_steps >= 1) {
-    const int32_t lm = (c.mode == MODE_STEP && c.opt) ? c.opt->launch_mode : MUON_LAUNCH_AUTO;
-    for (int32_t i = 0; i < c.count; ++i)
-      use_chain[iprec[size_t(i)]] = c.ns_steps <= MAX_CHAIN_STEPS && lm == MUON_LAUNCH_CHAIN;
-    for (int32_t i = 0; i < c.count; ++i)
-      if (use_chain[iprec[size_t(i)]]) chain_need += chain_bytes(geom_of(c.shapes[i]), c.ns_steps);
-  }
-
-  // workspace
-  const size_t need = c.mode == MODE_NORMS ? 0 : workspace_bytes(c.shapes, c.count);
-  if (need > ds.ws_bytes) {
-    if (hipDeviceSynchronize() != hipSuccess) {
-      return fail(MUON_ERR_HIP, "hipDeviceSynchronize failed: %s", hipGetErrorString(hipGetLastError()));
-    }
-    drop_plans(ds);
-    if (ds.ws) (void)hipFree(ds.ws);
-    ds.ws = nullptr;
-    ds.ws_bytes = 0;
-    void* p = nullptr;
-    if (hipMalloc(&p, need) != hipSuccess) {
-      (void)hipGetLastError();
-      return fail(MUON_ERR_OUT_OF_MEMORY, "workspace allocation of %zu bytes failed", need);
-    }
-    ds.ws = p;
-    ds.ws_bytes = need;
-  }
-  if (chain_need > ds.chain_ws_bytes) {
-    if (hipDeviceSynchronize() != hipSuccess) {
-      return fail(MUON_ERR_HIP, "hipDeviceSynchronize failed: %s", hipGetErrorString(hipGetLastError()));
-    }
-    drop_plans(ds);
-    if (ds.chain_ws) (void)hipFree(ds.chain_ws);
-    ds.chain_ws = nullptr;
-    ds.chain_ws_bytes = 0;
-    void* p = nullptr;
-    if (hipMalloc(&p, chain_need) != hipSuccess) {
-      (void)hipGetLastError();
-      return fail(MUON_ERR_OUT_OF_MEMORY, "chain workspace allocation of %zu bytes failed", chain_need);
-    }
-    ds.chain_ws = p;
-    ds.chain_ws_bytes = chain_need;
-  }
-
-  // plan key
-  std::vector<uint64_t> key;
-  key.reserve(size_t(c.count) * 14 + 3);
-  key.push_back(uint64_t(c.mode));
-  key.push_back(uint64_t(c.count));
-  key.push_back(reinterpret_cast<uint64_t>(ds.ws));
+// Launch plan of the call's matrices with workspace buffers laid out from
+// `ws` (device tables uploaded on c.stream, which is synchronised).
+muon_status new_plan(const Call& c, const std::vector<int>& iprec, char* ws, int cus_per_xcd, Plan** out) {
+  std::vector<MatDev> hm(c.count);
+  std::vector<int32_t> etile_off(c.count + 1, 0);
+  size_t wo = 0;
   for (int32_t i = 0; i < c.count; ++i) {
     const muon_matrix_desc& d = c.shapes[i];
-    key.push_back(reinterpret_cast<uint64_t>(c.grads[i]));
-    key.push_back(c.mode == MODE_STEP ? reinterpret_cast<uint64_t>(c.params[i]) : 0);
-    key.push_back(c.mode == MODE_STEP ? reinterpret_cast<uint64_t>(c.momenta[i]) : 0);
-    key.push_back(c.updates ? reinterpret_cast<uint64_t>(c.updates[i]) : 0);
-    key.push_back(uint64_t(d.rows));
-    key.push_back(uint64_t(d.cols));
-    key.push_back(uint64_t(d.ld_param));
-    key.push_back(uint64_t(d.ld_grad));
-    key.push_back(uint64_t(d.ld_mom));
-    key.push_back((uint64_t(uint32_t(d.param_dtype)) << 32) | uint32_t(d.grad_dtype));
-    key.push_back((uint64_t(uint32_t(d.mom_dtype)) << 32) | uint32_t(iprec[size_t(i)]));
-  }
-  Plan* plan = nullptr;
-  for (auto it = ds.plans.begin(); it != ds.plans.end(); ++it) {
-    if ((*it)->key == key) {
-      plan = *it;
-      ds.plans.erase(it);
-      ds.plans.push_front(plan);
-      break;
+    MatGeom g = geom_of(d);
+    MatDev& m = hm[i];
+    memset(&m, 0, sizeof(m));
+    m.param = c.mode == MODE_STEP ? c.params[i] : nullptr;
+    m.grad = c.grads[i];
+    m.mom = c.mode == MODE_STEP ? reinterpret_cast<float*>(c.momenta[i]) : nullptr;
+    m.upd = c.updates ? c.updates[i] : nullptr;
+    m.ld_param = d.ld_param;
+    m.ld_grad = d.ld_grad;
+    m.ld_mom = d.ld_mom;
+    m.ld_upd = d.cols;
+    m.rows = int32_t(d.rows);
+    m.cols = int32_t(d.cols);
+    m.m = int32_t(g.m);
+    m.n = int32_t(g.n);
+    m.Mp = int32_t(g.Mp);
+    m.Np = int32_t(g.Np);
+    m.ldx = int32_t(g.ldx);
+    m.lda = int32_t(g.lda);
+    m.transposed = g.transposed ? 1 : 0;
+    m.param_bf16 = (c.mode == MODE_STEP && d.param_dtype == MUON_DTYPE_BF16) ? 1 : 0;
+    m.grad_bf16 = d.grad_dtype == MUON_DTYPE_BF16 ? 1 : 0;
+    bool vec = vec_aligned(c.grads[i], d.ld_grad, dtype_size(d.grad_dtype));
+    if (c.mode == MODE_STEP) vec = vec && vec_aligned(c.momenta[i], d.ld_mom, 4);
+    m.vec_ok = vec ? 1 : 0;
+    if (c.mode == MODE_STEP) {
+      const int psz = dtype_size(d.param_dtype);
+      // rows start 16-byte aligned; columns go in groups of 8 from a multiple of 8
+      m.wvec_ok = (reinterpret_cast<uintptr_t>(c.params[i]) % 16 == 0 && (d.ld_param * psz) % 16 == 0) ? 1 : 0;
+    }
+    if (m.upd) m.uvec_ok = (reinterpret_cast<uintptr_t>(m.upd) % 16 == 0 && d.cols % 4 == 0) ? 1 : 0;
+    m.prec = c.mode == MODE_NORMS ? int(PREC_BF16) : iprec[size_t(i)];
+    const int64_t rp = g.transposed ? g.Np : g.Mp;  // natural padded rows
+    const int64_t cp = g.transposed ? g.Mp : g.Np;  // natural padded cols
+    m.etile_cols = int32_t(cp / ETILE);
+    etile_off[i + 1] = etile_off[i] + int32_t((rp / ETILE) * (cp / ETILE));
+    if (c.mode != MODE_NORMS) {
+      m.plane_X = g.Mp * g.ldx;
+      m.plane_A = g.Mp * g.lda;
+      m.X[0] = ws + wo; wo += g.x_bytes;
+      m.X[1] = ws + wo; wo += g.x_bytes;
+      m.A = ws + wo; wo += g.a_bytes;
+      m.B = ws + wo; wo += g.a_bytes;
     }
   }
-  if (!plan) {
-    std::vector<MatDev> hm(c.count);
-    std::vector<int32_t> etile_off(c.count + 1, 0);
-    char* ws = reinterpret_cast<char*>(ds.ws);
-    size_t wo = 0;
-    for (int32_t i = 0; i < c.count; ++i) {
-      const muon_matrix_desc& d = c.shapes[i];
-      MatGeom g = geom_of(d);
-      MatDev& m = hm[i];
-      memset(&m, 0, sizeof(m));
-      m.param = c.mode == MODE_STEP ? c.params[i] : nullptr;
-      m.grad = c.grads[i];
-      m.mom = c.mode == MODE_STEP ? reinterpret_cast<float*>(c.momenta[i]) : nullptr;
-      m.upd = c.updates ? c.updates[i] : nullptr;
-      m.ld_param = d.ld_param;
-      m.ld_grad = d.ld_grad;
-      m.ld_mom = d.ld_mom;
-      m.ld_upd = d.cols;
-      m.rows = int32_t(d.rows);
-      m.cols = int32_t(d.cols);
-      m.m = int32_t(g.m);
-      m.n = int32_t(g.n);
-      m.Mp = int32_t(g.Mp);
-      m.Np = int32_t(g.Np);
-      m.ldx = int32_t(g.ldx);
-      m.lda = int32_t(g.lda);
-      m.transposed = g.transposed ? 1 : 0;
-      m.param_bf16 = (c.mode == MODE_STEP && d.param_dtype == MUON_DTYPE_BF16) ? 1 : 0;
-      m.grad_bf16 = d.grad_dtype == MUON_DTYPE_BF16 ? 1 : 0;
-      bool vec = vec_aligned(c.grads[i], d.ld_grad, dtype_size(d.grad_dtype));
-      if (c.mode == MODE_STEP) vec = vec && vec_aligned(c.momenta[i], d.ld_mom, 4);
-      m.vec_ok = vec ? 1 : 0;
-      if (c.mode == MODE_STEP) {
-        const int psz = dtype_size(d.param_dtype);
-        // rows start 16-byte aligned; columns go in groups of 8 from a multiple of 8
-        m.wvec_ok = (reinterpret_cast<uintptr_t>(c.params[i]) % 16 == 0 && (d.ld_param * psz) % 16 == 0) ? 1 : 0;
-      }
-      if (m.upd) m.uvec_ok = (reinterpret_cast<uintptr_t>(m.upd) % 16 == 0 && d.cols % 4 == 0) ? 1 : 0;
-      m.prec = c.mode == MODE_NORMS ? int(PREC_BF16) : iprec[size_t(i)];
-      const int64_t rp = g.transposed ? g.Np : g.Mp;  // natural padded rows
-      const int64_t cp = g.transposed ? g.Mp : g.Np;  // natural padded cols
-      m.etile_cols = int32_t(cp / ETILE);
-      etile_off[i + 1] = etile_off[i] + int32_t((rp / ETILE) * (cp / ETILE));
-      if (c.mode != MODE_NORMS) {
-        m.plane_X = g.Mp * g.ldx;
-        m.plane_A = g.Mp * g.lda;
-        m.X[0] = ws + wo; wo += g.x_bytes;
-        m.X[1] = ws + wo; wo += g.x_bytes;
-        m.A = ws + wo; wo += g.a_bytes;
-        m.B = ws + wo; wo += g.a_bytes;
-      }
-    }
-    if (int64_t(etile_off[c.count]) >= (int64_t(1) << 31) - 1)
-      return fail(MUON_ERR_UNSUPPORTED, "too many elements in one call");
-    plan = new Plan();
-    plan->key = key;
-    st = build_plan(plan, hm, etile_off, ds.cus_per_xcd, c.stream);
-    if (st != MUON_OK) {
-      if (plan->dmem) (void)hipFree(plan->dmem);
-      delete plan;
-      return st;
-    }
-    ds.plans.push_front(plan);
-    while (ds.plans.size() > MAX_PLANS) {
-      free_plan(ds.plans.back());
-      ds.plans.pop_back();
-    }
+  if (int64_t(etile_off[c.count]) >= (int64_t(1) << 31) - 1)
+    return fail(MUON_ERR_UNSUPPORTED, "too many elements in one call");
+  Plan* plan = new Plan();
+  const muon_status st = build_plan(plan, hm, etile_off, cus_per_xcd, c.stream);
+  if (st != MUON_OK) {
+    if (plan->dmem) (void)hipFree(plan->dmem);
+    delete plan;
+    return st;
   }
+  *out = plan;
+  return MUON_OK;
+}
 
-  // ------------------------------------------------------------ launches
+// Enqueues the launch sequence of one step of `c` with `plan` on c.stream:
+// after the device's previous call and, when given, after `ready`.
+muon_status enqueue_step(DeviceState& ds, Plan* plan, const Call& c, const std::vector<int>& iprec,
+                         std::map<int, bool>& use_chain, hipEvent_t ready) {
   hipError_t e = order_after_last_call(ds, c.stream);
+  if (e == hipSuccess && ready) e = hipStreamWaitEvent(c.stream, ready, 0);
+  muon_status st = MUON_OK;
   const int kmode = c.mode == MODE_STEP ? 0 : (c.mode == MODE_NS ? 1 : 2);
   const int32_t ema = (c.mode == MODE_STEP && c.opt && c.opt->momentum_kind == MUON_MOMENTUM_EMA) ? 1 : 0;
   // per-matrix write-back scalars t_i = fl32(lr_i * s_i), d_i = fl32(1 - fl32(lr_i * wd))
@@ -1226,6 +1149,274 @@ muon_status run(const Call& c) {
   (void)hipEventRecord(plan->last_use, c.stream);
   record_last_call(ds, c.stream);
   return MUON_OK;
+}
+
+muon_status run(const Call& c) {
+  t_last_error.clear();
+  muon_status st = validate_call(c);
+  if (st != MUON_OK || c.count == 0) return st;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState* dsp = nullptr;
+  if ((st = acquire_device(&dsp)) != MUON_OK) return st;
+  DeviceState& ds = *dsp;
+
+  // working format per matrix: a bf16 stack whose GRAM phase has fewer
+  // 256 x 256 tiles than the GPU has compute units takes 128 x 128 tiles
+  // (measured: 12 x 768^2 0.41 -> 0.34 ms per step; with three d24 layers,
+  // 378 GRAM tiles, the pipelined 256 x 256 tiles stay faster), and a
+  // binary32 stack with fewer 128 x 128 GRAM tiles than that takes 64 x 64
+  // tiles (one 256 x 256 matrix: 3 GRAM tiles of 128, 10 of 64)
+  const int32_t tmode = (c.mode == MODE_STEP && c.opt) ? c.opt->tile_mode : MUON_TILES_AUTO;
+  const std::vector<int> iprec =
+      working_formats(c.shapes, c.count, c.mode, tmode, int64_t(NUM_XCD) * ds.cus_per_xcd);
+
+  // which working formats run as one persistent chain: only when asked for
+  // (AUTO keeps the per-phase grids: measured on MI355X, the chain is slower
+  // on every workload tried; it gives up the grids' cross-tile prefetch of
+  // stage 0, pays a release per tile, and spills more)
+  std::map<int, bool> use_chain;
+  size_t chain_need = 0;
+  if (c.mode != MODE_NORMS && c.ns_steps >= 1) {
+    const int32_t lm = (c.mode == MODE_STEP && c.opt) ? c.opt->launch_mode : MUON_LAUNCH_AUTO;
+    for (int32_t i = 0; i < c.count; ++i)
+      use_chain[iprec[size_t(i)]] = c.ns_steps <= MAX_CHAIN_STEPS && lm == MUON_LAUNCH_CHAIN;
+    for (int32_t i = 0; i < c.count; ++i)
+      if (use_chain[iprec[size_t(i)]]) chain_need += chain_bytes(geom_of(c.shapes[i]), c.ns_steps);
+  }
+
+  // workspace
+  const size_t need = c.mode == MODE_NORMS ? 0 : workspace_bytes(c.shapes, c.count);
+  if (need > ds.ws_bytes) {
+    if (hipDeviceSynchronize() != hipSuccess) {
+      return fail(MUON_ERR_HIP, "hipDeviceSynchronize failed: %s", hipGetErrorString(hipGetLastError()));
+    }
+    drop_plans(ds);
+    if (ds.ws) (void)hipFree(ds.ws);
+    ds.ws = nullptr;
+    ds.ws_bytes = 0;
+    void* p = nullptr;
+    if (hipMalloc(&p, need) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MUON_ERR_OUT_OF_MEMORY, "workspace allocation of %zu bytes failed", need);
+    }
+    ds.ws = p;
+    ds.ws_bytes = need;
+  }
+  if (chain_need > ds.chain_ws_bytes) {
+    if (hipDeviceSynchronize() != hipSuccess) {
+      return fail(MUON_ERR_HIP, "hipDeviceSynchronize failed: %s", hipGetErrorString(hipGetLastError()));
+    }
+    drop_plans(ds);
+    if (ds.chain_ws) (void)hipFree(ds.chain_ws);
+    ds.chain_ws = nullptr;
+    ds.chain_ws_bytes = 0;
+    void* p = nullptr;
+    if (hipMalloc(&p, chain_need) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MUON_ERR_OUT_OF_MEMORY, "chain workspace allocation of %zu bytes failed", chain_need);
+    }
+    ds.chain_ws = p;
+    ds.chain_ws_bytes = chain_need;
+  }
+
+  // plan key
+  std::vector<uint64_t> key;
+  key.reserve(size_t(c.count) * 14 + 3);
+  key.push_back(uint64_t(c.mode));
+  key.push_back(uint64_t(c.count));
+  key.push_back(reinterpret_cast<uint64_t>(ds.ws));
+  for (int32_t i = 0; i < c.count; ++i) {
+    const muon_matrix_desc& d = c.shapes[i];
+    key.push_back(reinterpret_cast<uint64_t>(c.grads[i]));
+    key.push_back(c.mode == MODE_STEP ? reinterpret_cast<uint64_t>(c.params[i]) : 0);
+    key.push_back(c.mode == MODE_STEP ? reinterpret_cast<uint64_t>(c.momenta[i]) : 0);
+    key.push_back(c.updates ? reinterpret_cast<uint64_t>(c.updates[i]) : 0);
+    key.push_back(uint64_t(d.rows));
+    key.push_back(uint64_t(d.cols));
+    key.push_back(uint64_t(d.ld_param));
+    key.push_back(uint64_t(d.ld_grad));
+    key.push_back(uint64_t(d.ld_mom));
+    key.push_back((uint64_t(uint32_t(d.param_dtype)) << 32) | uint32_t(d.grad_dtype));
+    key.push_back((uint64_t(uint32_t(d.mom_dtype)) << 32) | uint32_t(iprec[size_t(i)]));
+  }
+  Plan* plan = nullptr;
+  for (auto it = ds.plans.begin(); it != ds.plans.end(); ++it) {
+    if ((*it)->key == key) {
+      plan = *it;
+      ds.plans.erase(it);
+      ds.plans.push_front(plan);
+      break;
+    }
+  }
+  if (!plan) {
+    if ((st = new_plan(c, iprec, reinterpret_cast<char*>(ds.ws), ds.cus_per_xcd, &plan)) != MUON_OK) return st;
+    plan->key = key;
+    ds.plans.push_front(plan);
+    while (ds.plans.size() > MAX_PLANS) {
+      free_plan(ds.plans.back());
+      ds.plans.pop_back();
+    }
+  }
+  return enqueue_step(ds, plan, c, iprec, use_chain, nullptr);
+}
+
+// ------------------------------------------------------------ stream plans
+// One launch plan per group over a workspace of the plan's own; the working
+// format of every matrix is fixed from the whole set at creation, so each
+// matrix runs exactly the tile code one call over the whole set would run.
+struct StreamGroup {
+  std::vector<int32_t> members;          // indices in the whole set
+  std::vector<muon_matrix_desc> shapes;  // argument arrays in group order
+  std::vector<void*> params, moms;
+  std::vector<const void*> grads;
+  std::vector<float*> upd;
+  std::vector<int> prec;                 // working format of each member
+  Plan* plan = nullptr;
+};
+
+struct StreamPlanImpl {
+  int dev = 0;
+  int32_t count = 0;
+  bool has_upd = false;
+  std::vector<StreamGroup> groups;
+  void* ws = nullptr;
+};
+
+void free_stream_plan(StreamPlanImpl* sp) {
+  for (auto& g : sp->groups)
+    if (g.plan) free_plan(g.plan);       // waits for the group's last use
+  if (sp->ws) (void)hipFree(sp->ws);
+  delete sp;
+}
+
+Call group_call(const StreamGroup& g, bool has_upd) {
+  Call c{};
+  c.mode = MODE_STEP;
+  c.params = g.params.data();
+  c.grads = g.grads.data();
+  c.momenta = g.moms.data();
+  c.updates = has_upd ? g.upd.data() : nullptr;
+  c.shapes = g.shapes.data();
+  c.count = int32_t(g.members.size());
+  return c;
+}
+
+muon_status stream_plan_create(void* const* params, const void* const* grads, void* const* momenta,
+                               const muon_matrix_desc* shapes, int32_t count, const int32_t* group_of,
+                               int32_t ngroups, int32_t tile_mode, float* const* updates_out,
+                               muon_stream_plan* plan_out) {
+  t_last_error.clear();
+  if (!plan_out) return fail(MUON_ERR_INVALID_ARGUMENT, "plan_out is NULL");
+  *plan_out = nullptr;
+  if (count < 1 || count > MAX_COUNT) return fail(MUON_ERR_INVALID_ARGUMENT, "count %d out of [1, %d]", count, MAX_COUNT);
+  if (ngroups < 1 || ngroups > MAX_COUNT)
+    return fail(MUON_ERR_INVALID_ARGUMENT, "ngroups %d out of [1, %d]", ngroups, MAX_COUNT);
+  if (!group_of) return fail(MUON_ERR_INVALID_ARGUMENT, "group_of is NULL");
+  if (tile_mode < MUON_TILES_AUTO || tile_mode > MUON_TILES_SMALL)
+    return fail(MUON_ERR_INVALID_ARGUMENT, "unknown tile_mode %d", tile_mode);
+  for (int32_t i = 0; i < count; ++i)
+    if (group_of[i] < 0 || group_of[i] >= ngroups)
+      return fail(MUON_ERR_INVALID_ARGUMENT, "group_of[%d] = %d out of [0, %d)", i, group_of[i], ngroups);
+  // the matrices and pointers, checked as one step call over the whole set
+  Call all{};
+  all.mode = MODE_STEP;
+  all.params = params;
+  all.grads = grads;
+  all.momenta = momenta;
+  all.updates = updates_out;
+  all.shapes = shapes;
+  all.count = count;
+  all.co = {1.f, 0.f, 0.f};
+  muon_status st = validate_call(all);
+  if (st != MUON_OK) return st;
+
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState* ds = nullptr;
+  int dev = 0;
+  if ((st = acquire_device(&ds, &dev)) != MUON_OK) return st;
+  const std::vector<int> iprec =
+      working_formats(shapes, count, MODE_STEP, tile_mode, int64_t(NUM_XCD) * ds->cus_per_xcd);
+  StreamPlanImpl* sp = new StreamPlanImpl();
+  sp->dev = dev;
+  sp->count = count;
+  sp->has_upd = updates_out != nullptr;
+  sp->groups.resize(size_t(ngroups));
+  for (int32_t i = 0; i < count; ++i) {
+    StreamGroup& g = sp->groups[size_t(group_of[i])];
+    g.members.push_back(i);
+    g.shapes.push_back(shapes[i]);
+    g.params.push_back(params[i]);
+    g.grads.push_back(grads[i]);
+    g.moms.push_back(momenta[i]);
+    g.upd.push_back(updates_out ? updates_out[i] : nullptr);
+    g.prec.push_back(iprec[size_t(i)]);
+  }
+  size_t need = 0;
+  for (const auto& g : sp->groups) need = std::max(need, workspace_bytes(g.shapes.data(), int32_t(g.shapes.size())));
+  if (hipMalloc(&sp->ws, std::max<size_t>(need, 256)) != hipSuccess) {
+    (void)hipGetLastError();
+    sp->ws = nullptr;
+    free_stream_plan(sp);
+    return fail(MUON_ERR_OUT_OF_MEMORY, "stream plan workspace allocation of %zu bytes failed", need);
+  }
+  for (auto& g : sp->groups) {
+    if (g.members.empty()) continue;
+    Call c = group_call(g, sp->has_upd);
+    if ((st = new_plan(c, g.prec, reinterpret_cast<char*>(sp->ws), ds->cus_per_xcd, &g.plan)) != MUON_OK) {
+      g.plan = nullptr;
+      free_stream_plan(sp);
+      return st;
+    }
+  }
+  *plan_out = reinterpret_cast<muon_stream_plan>(sp);
+  return MUON_OK;
+}
+
+muon_status stream_submit(StreamPlanImpl* sp, int32_t group, void* ready, const muon_step_hparams* hp,
+                          void* stream) {
+  t_last_error.clear();
+  if (!sp) return fail(MUON_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!hp) return fail(MUON_ERR_INVALID_ARGUMENT, "hparams is NULL");
+  if (group < 0 || group >= int32_t(sp->groups.size()))
+    return fail(MUON_ERR_INVALID_ARGUMENT, "group %d out of [0, %d)", group, int32_t(sp->groups.size()));
+  const StreamGroup& g = sp->groups[size_t(group)];
+  // options for the group: per-matrix arrays taken in group order
+  muon_step_options opt{};
+  std::vector<float> lrs, scs;
+  if (hp->options) {
+    opt = *hp->options;
+    if (opt.launch_mode == MUON_LAUNCH_CHAIN)
+      return fail(MUON_ERR_UNSUPPORTED, "a stream plan runs the per-phase grids; launch_mode CHAIN is not supported");
+    if (opt.launch_mode == MUON_LAUNCH_AUTO) opt.launch_mode = MUON_LAUNCH_PHASE_GRIDS;
+    opt.tile_mode = MUON_TILES_AUTO;      // the plan's formats are fixed
+    if (opt.lr_per_matrix) {
+      for (int32_t i : g.members) lrs.push_back(opt.lr_per_matrix[i]);
+      opt.lr_per_matrix = lrs.data();
+    }
+    if (opt.scale_per_matrix) {
+      for (int32_t i : g.members) scs.push_back(opt.scale_per_matrix[i]);
+      opt.scale_per_matrix = scs.data();
+    }
+  }
+  Call c = group_call(g, sp->has_upd);
+  c.lr = hp->lr;
+  c.beta = hp->beta;
+  c.nesterov = hp->nesterov;
+  c.co = hp->ns_coeffs;
+  c.ns_steps = hp->ns_steps;
+  c.scale_rule = hp->scale_rule;
+  c.opt = hp->options ? &opt : nullptr;
+  c.stream = reinterpret_cast<hipStream_t>(stream);
+  muon_status st = validate_call(c);
+  if (st != MUON_OK || g.members.empty()) return st;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState* ds = nullptr;
+  int dev = 0;
+  if ((st = acquire_device(&ds, &dev)) != MUON_OK) return st;
+  if (dev != sp->dev)
+    return fail(MUON_ERR_INVALID_ARGUMENT, "the plan belongs to device %d, the current device is %d", sp->dev, dev);
+  std::map<int, bool> use_chain;          // every group runs the per-phase grids
+  return enqueue_step(*ds, g.plan, c, g.prec, use_chain, reinterpret_cast<hipEvent_t>(ready));
 }
 
 // ------------------------------------------------------------------ AdamW
@@ -1545,6 +1736,27 @@ muon_status muon_adamw_batched(void* const* params, const void* const* grads, fl
                                const muon_adamw_hparams* hparams, void* stream) {
   AdamwCall c{params, grads, exp_avg, exp_avg_sq, tensors, count, hparams, reinterpret_cast<hipStream_t>(stream)};
   return run_adamw(c);
+}
+
+muon_status muon_stream_plan_create(void* const* params, const void* const* grads, void* const* momenta,
+                                    const muon_matrix_desc* shapes, int32_t count, const int32_t* group_of,
+                                    int32_t ngroups, int32_t tile_mode, float* const* updates_out,
+                                    muon_stream_plan* plan_out) {
+  return stream_plan_create(params, grads, momenta, shapes, count, group_of, ngroups, tile_mode, updates_out,
+                            plan_out);
+}
+
+muon_status muon_stream_submit(muon_stream_plan plan, int32_t group, void* ready_event,
+                               const muon_step_hparams* hparams, void* stream) {
+  return stream_submit(reinterpret_cast<StreamPlanImpl*>(plan), group, ready_event, hparams, stream);
+}
+
+muon_status muon_stream_plan_destroy(muon_stream_plan plan) {
+  t_last_error.clear();
+  if (!plan) return MUON_OK;
+  std::lock_guard<std::mutex> lock(g_mu);
+  free_stream_plan(reinterpret_cast<StreamPlanImpl*>(plan));
+  return MUON_OK;
 }
 
 muon_status muon_mfma_probe(int64_t iterations, float* sink, double* flops_out, void* stream) {

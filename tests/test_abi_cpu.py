@@ -20,7 +20,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = mb.exported_names()
-    assert len(names) == 14
+    assert len(names) == 17
     out = subprocess.run(["nm", "-D", "--defined-only", mb.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert mb.muon_abi_version() == 3
+    assert mb.muon_abi_version() == 4
     assert mb.muon_status_string(mb.MUON_OK) == "MUON_OK"
     assert mb.muon_status_string(mb.MUON_ERR_ALIAS) == "MUON_ERR_ALIAS"
     assert mb.muon_status_string(99) == "MUON_ERR_UNKNOWN"
@@ -395,3 +395,45 @@ def test_mfma_probe_argument_errors(L):
     assert L.muon_mfma_probe(10, None, ctypes.byref(flops), None) == mb.MUON_ERR_INVALID_ARGUMENT
     assert L.muon_mfma_probe(10, sink, None, None) == mb.MUON_ERR_INVALID_ARGUMENT
     assert L.muon_mfma_probe(10, sink + 2, ctypes.byref(flops), None) == mb.MUON_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- stream plans
+
+def _create(L, descs, group_of, ngroups, tile_mode=0, out=True):
+    n = len(descs)
+    D = (mb.MatrixDesc * max(n, 1))(*descs)
+    ptrs = [_ptrs(i, d.rows, d.cols) for i, d in enumerate(descs)]
+    grp = (ctypes.c_int32 * max(n, 1))(*group_of)
+    h = ctypes.c_void_p()
+    return L.muon_stream_plan_create(mb._ptr_array([p for p, _, _ in ptrs]), mb._ptr_array([g for _, g, _ in ptrs]),
+                                     mb._ptr_array([m for _, _, m in ptrs]), D, n, grp, ngroups, tile_mode, None,
+                                     ctypes.byref(h) if out else None)
+
+
+@pytest.mark.parametrize("group_of,ngroups,tile_mode,out", [
+    ([0, 2], 2, 0, True),        # group index out of range
+    ([0, -1], 2, 0, True),
+    ([0, 0], 0, 0, True),        # no groups
+    ([0, 1], 2, 5, True),        # unknown tile mode
+    ([0, 1], 2, 0, False),       # no place for the plan
+])
+def test_stream_plan_create_errors(L, group_of, ngroups, tile_mode, out):
+    descs = [_desc(16, 32), _desc(32, 16)]
+    assert _create(L, descs, group_of, ngroups, tile_mode, out) == mb.MUON_ERR_INVALID_ARGUMENT
+    assert mb.muon_last_error() != ""
+
+
+def test_stream_plan_create_checks_matrices(L):
+    # the matrices are checked as for a step call over the whole set
+    d = _desc(16, 32)
+    d.ld_grad = 8
+    assert _create(L, [_desc(16, 32), d], [0, 1], 2) == mb.MUON_ERR_INVALID_ARGUMENT
+    assert _create(L, [], [], 1) == mb.MUON_ERR_INVALID_ARGUMENT
+    # valid arguments: without a GPU the call fails only at the device
+    assert _create(L, [_desc(16, 32), _desc(32, 16)], [1, 1], 3) == mb.MUON_ERR_HIP
+
+
+def test_stream_submit_and_destroy_arguments(L):
+    hp = mb.StepHparams(0.02, 0.95, 1, mb.NsCoeffs(3.4445, -4.775, 2.0315), 5, 0, None)
+    assert L.muon_stream_submit(None, 0, None, ctypes.byref(hp), None) == mb.MUON_ERR_INVALID_ARGUMENT
+    assert L.muon_stream_plan_destroy(None) == mb.MUON_OK
