@@ -246,6 +246,26 @@ muon_status muon_step_batched_v2(void* const* params, const void* const* grads,
                                  int32_t scale_rule, const muon_step_options* options,
                                  float* const* updates_out, void* stream);
 
+/* muon_step_batched_ex for callers that cannot allocate memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, kernels and results bit for bit, with no device,
+ * pinned or event allocation.  Its Newton-Schulz workspace and launch tables
+ * live in a fixed 64 MiB device array that the library holds on every GPU
+ * it runs on until the process ends, rewritten by every call; nothing in it
+ * needs to start at zero.  Inputs whose workspace (2 bytes per element of
+ * two iterates and two Gram matrices for BF16, 4 for BF16X3 and F32, each
+ * dimension padded to 256) and tables exceed it are rejected with
+ * UNSUPPORTED (a stack of twelve bf16 768 x 768 matrices fits; one d24
+ * layer does not).  Calls on one GPU share the array: calls that overlap in
+ * time on one GPU (two streams, two host threads) race, and are not ordered
+ * against each other or against the other entry points.  The launch tables
+ * are copied from host memory on `stream` and the call may wait on the host
+ * for that copy.  Errors as muon_step_batched_ex.                          */
+muon_status muon_step_batched_noalloc(void* const* params, const void* const* grads, void* const* momenta,
+                                      const muon_matrix_desc* shapes, int32_t count, float lr, float beta,
+                                      int32_t nesterov, muon_ns_coeffs ns_coeffs, int32_t ns_steps,
+                                      int32_t scale_rule, float* const* updates_out, void* stream);
+
 /* Newton-Schulz orthogonalisation only: x_out[i] = NS^ns_steps(x / (||x||_F
  * + 1e-7)) for x = x_in[i] (rows x cols, grad_dtype, row stride ld_grad),
  * oriented as above.  x_out[i] is binary32 rows x cols with row stride

@@ -133,6 +133,8 @@ def lib() -> ctypes.CDLL:
     L.muon_step_batched.restype = i32
     L.muon_step_batched_ex.argtypes = [_PP, _PP, _PP, D, i32, f32, f32, i32, NsCoeffs, i32, i32, _PP, _VP]
     L.muon_step_batched_ex.restype = i32
+    L.muon_step_batched_noalloc.argtypes = [_PP, _PP, _PP, D, i32, f32, f32, i32, NsCoeffs, i32, i32, _PP, _VP]
+    L.muon_step_batched_noalloc.restype = i32
     L.muon_step_batched_v2.argtypes = [_PP, _PP, _PP, D, i32, f32, f32, i32, NsCoeffs, i32, i32,
                                        ctypes.POINTER(StepOptions), _PP, _VP]
     L.muon_step_batched_v2.restype = i32

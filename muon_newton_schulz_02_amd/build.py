@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmuon_mi355x.so")
 
-SOURCES = ["muon_api.cpp", "elementwise.hip", "ns_gemm.hip", "ns_chain.hip", "adamw.hip", "probe.hip"]
+SOURCES = ["muon_api.cpp", "elementwise.hip", "ns_gemm.hip", "ns_chain.hip", "adamw.hip", "probe.hip",
+           "noalloc.hip"]
 ARCH = os.environ.get("MUON_OFFLOAD_ARCH", "gfx950")
 
 

@@ -279,6 +279,12 @@ hipError_t timed(int kc, hipStream_t stream, F&& launch) {
   return r;
 }
 
+// timed(), or the bare launch when `plain`.
+template <class F>
+hipError_t timed_unless(bool plain, int kc, hipStream_t stream, F&& launch) {
+  return plain ? launch() : timed(kc, stream, launch);
+}
+
 void free_plan(Plan* p) {
   if (p->last_use) {
     (void)hipEventSynchronize(p->last_use);
@@ -516,8 +522,18 @@ std::vector<TileSrc> phase_tiles(const std::vector<MatDev>& hm, const std::vecto
   return src;
 }
 
-muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vector<int32_t>& etile_off,
-                       int cus_per_xcd, hipStream_t stream) {
+// Host image of a launch plan's device tables: matrix descriptors, the
+// elementwise tiles' offsets, norm scalars, norm partials, write-back
+// scalars and the per-phase tile lists of each working format.
+struct PlanImage {
+  std::vector<char> host;
+  size_t off_mats = 0, off_etile = 0, off_scal = 0, off_part = 0, off_wb = 0;
+  std::vector<size_t> off_lists;
+  std::vector<Plan::Group> groups;
+};
+
+void plan_image(const std::vector<MatDev>& hm, const std::vector<int32_t>& etile_off, int cus_per_xcd,
+                PlanImage& im) {
   const int32_t count = int32_t(hm.size());
   const std::vector<int> order = cost_order(hm);
   std::vector<int> precs;
@@ -526,7 +542,7 @@ muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vec
   std::sort(precs.begin(), precs.end());
 
   std::vector<std::vector<int2>> lists;
-  std::vector<Plan::Group> groups;
+  im.groups.clear();
   for (int prec : precs) {
     Plan::Group g;
     g.prec = prec;
@@ -535,56 +551,69 @@ muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vec
       lists.push_back(xcd_lists(phase_tiles(hm, order, prec, ph), &g.per_xcd[ph], blocks));
       g.tiles[ph] = nullptr;
     }
-    groups.push_back(g);
+    im.groups.push_back(g);
   }
 
   size_t off = 0;
-  const size_t off_mats = off;
+  im.off_mats = off;
   off = align256(off + sizeof(MatDev) * count);
-  const size_t off_etile = off;
+  im.off_etile = off;
   off = align256(off + sizeof(int32_t) * (count + 1));
-  const size_t off_scal = off;
+  im.off_scal = off;
   off = align256(off + sizeof(MatScal) * count);
-  const size_t off_part = off;
+  im.off_part = off;
   off = align256(off + sizeof(float) * size_t(std::max<int64_t>(etile_off[count], 1)));
-  const size_t off_wb = off;
+  im.off_wb = off;
   off = align256(off + sizeof(float2) * count);
-  std::vector<size_t> off_lists;
+  im.off_lists.clear();
   for (auto& l : lists) {
-    off_lists.push_back(off);
+    im.off_lists.push_back(off);
     off = align256(off + sizeof(int2) * std::max<size_t>(l.size(), 1));
   }
-  void* dmem = nullptr;
-  if (hipMalloc(&dmem, off) != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(MUON_ERR_OUT_OF_MEMORY, "plan allocation of %zu bytes failed", off);
-  }
-  std::vector<char> host(off, 0);
-  memcpy(host.data() + off_mats, hm.data(), sizeof(MatDev) * count);
-  memcpy(host.data() + off_etile, etile_off.data(), sizeof(int32_t) * (count + 1));
+  im.host.assign(off, 0);
+  memcpy(im.host.data() + im.off_mats, hm.data(), sizeof(MatDev) * count);
+  memcpy(im.host.data() + im.off_etile, etile_off.data(), sizeof(int32_t) * (count + 1));
   for (size_t i = 0; i < lists.size(); ++i)
-    memcpy(host.data() + off_lists[i], lists[i].data(), sizeof(int2) * lists[i].size());
-  if (hipMemcpyAsync(dmem, host.data(), off, hipMemcpyHostToDevice, stream) != hipSuccess ||
+    memcpy(im.host.data() + im.off_lists[i], lists[i].data(), sizeof(int2) * lists[i].size());
+}
+
+// Points `plan` at the tables of `im` uploaded to device memory `base`.
+void bind_plan(Plan* plan, const PlanImage& im, char* base, const std::vector<MatDev>& hm,
+               const std::vector<int32_t>& etile_off) {
+  const int32_t count = int32_t(hm.size());
+  plan->count = count;
+  plan->total_etiles = etile_off[count];
+  plan->d_mats = reinterpret_cast<MatDev*>(base + im.off_mats);
+  plan->d_etile_off = reinterpret_cast<int32_t*>(base + im.off_etile);
+  plan->d_scal = reinterpret_cast<MatScal*>(base + im.off_scal);
+  plan->d_partials = reinterpret_cast<float*>(base + im.off_part);
+  plan->d_wb = reinterpret_cast<float2*>(base + im.off_wb);
+  plan->groups = im.groups;
+  size_t li = 0;
+  for (auto& g : plan->groups)
+    for (int ph = 0; ph < 3; ++ph) g.tiles[ph] = reinterpret_cast<int2*>(base + im.off_lists[li++]);
+  plan->host_mats = hm;
+  plan->chains.resize(plan->groups.size());
+  for (size_t gi = 0; gi < plan->groups.size(); ++gi) plan->chains[gi].prec = plan->groups[gi].prec;
+}
+
+muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vector<int32_t>& etile_off,
+                       int cus_per_xcd, hipStream_t stream) {
+  PlanImage im;
+  plan_image(hm, etile_off, cus_per_xcd, im);
+  const size_t bytes = im.host.size();
+  void* dmem = nullptr;
+  if (hipMalloc(&dmem, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MUON_ERR_OUT_OF_MEMORY, "plan allocation of %zu bytes failed", bytes);
+  }
+  if (hipMemcpyAsync(dmem, im.host.data(), bytes, hipMemcpyHostToDevice, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess) {
     (void)hipFree(dmem);
     return fail(MUON_ERR_HIP, "plan upload failed: %s", hipGetErrorString(hipGetLastError()));
   }
-  char* base = reinterpret_cast<char*>(dmem);
   plan->dmem = dmem;
-  plan->count = count;
-  plan->total_etiles = etile_off[count];
-  plan->d_mats = reinterpret_cast<MatDev*>(base + off_mats);
-  plan->d_etile_off = reinterpret_cast<int32_t*>(base + off_etile);
-  plan->d_scal = reinterpret_cast<MatScal*>(base + off_scal);
-  plan->d_partials = reinterpret_cast<float*>(base + off_part);
-  plan->d_wb = reinterpret_cast<float2*>(base + off_wb);
-  size_t li = 0;
-  for (auto& g : groups)
-    for (int ph = 0; ph < 3; ++ph) g.tiles[ph] = reinterpret_cast<int2*>(base + off_lists[li++]);
-  plan->groups = groups;
-  plan->host_mats = hm;
-  plan->chains.resize(groups.size());
-  for (size_t gi = 0; gi < groups.size(); ++gi) plan->chains[gi].prec = groups[gi].prec;
+  bind_plan(plan, im, reinterpret_cast<char*>(dmem), hm, etile_off);
   if (hipEventCreateWithFlags(&plan->last_use, hipEventDisableTiming) != hipSuccess) {
     plan->last_use = nullptr;
     return fail(MUON_ERR_HIP, "hipEventCreate failed");
@@ -959,11 +988,12 @@ std::vector<int> working_formats(const muon_matrix_desc* shapes, int32_t count, 
   return iprec;
 }
 
-// Launch plan of the call's matrices with workspace buffers laid out from
-// `ws` (device tables uploaded on c.stream, which is synchronised).
-muon_status new_plan(const Call& c, const std::vector<int>& iprec, char* ws, int cus_per_xcd, Plan** out) {
-  std::vector<MatDev> hm(c.count);
-  std::vector<int32_t> etile_off(c.count + 1, 0);
+// Device descriptors of the call's matrices with workspace buffers laid out
+// from `ws`, and the elementwise tiles' offsets.
+muon_status host_mats(const Call& c, const std::vector<int>& iprec, char* ws, std::vector<MatDev>& hm,
+                      std::vector<int32_t>& etile_off) {
+  hm.assign(size_t(c.count), MatDev{});
+  etile_off.assign(size_t(c.count) + 1, 0);
   size_t wo = 0;
   for (int32_t i = 0; i < c.count; ++i) {
     const muon_matrix_desc& d = c.shapes[i];
@@ -1014,6 +1044,16 @@ muon_status new_plan(const Call& c, const std::vector<int>& iprec, char* ws, int
   }
   if (int64_t(etile_off[c.count]) >= (int64_t(1) << 31) - 1)
     return fail(MUON_ERR_UNSUPPORTED, "too many elements in one call");
+  return MUON_OK;
+}
+
+// Launch plan of the call's matrices with workspace buffers laid out from
+// `ws` (device tables uploaded on c.stream, which is synchronised).
+muon_status new_plan(const Call& c, const std::vector<int>& iprec, char* ws, int cus_per_xcd, Plan** out) {
+  std::vector<MatDev> hm;
+  std::vector<int32_t> etile_off;
+  muon_status hs = host_mats(c, iprec, ws, hm, etile_off);
+  if (hs != MUON_OK) return hs;
   Plan* plan = new Plan();
   const muon_status st = build_plan(plan, hm, etile_off, cus_per_xcd, c.stream);
   if (st != MUON_OK) {
@@ -1026,10 +1066,13 @@ muon_status new_plan(const Call& c, const std::vector<int>& iprec, char* ws, int
 }
 
 // Enqueues the launch sequence of one step of `c` with `plan` on c.stream:
-// after the device's previous call and, when given, after `ready`.
+// after the device's previous call and, when given, after `ready`.  `plain`
+// (the allocation-free entry point): no ordering, timing or plan events, no
+// per-matrix table (c has no options) and no persistent chain, so nothing
+// here creates an event or allocates.
 muon_status enqueue_step(DeviceState& ds, Plan* plan, const Call& c, const std::vector<int>& iprec,
-                         std::map<int, bool>& use_chain, hipEvent_t ready) {
-  hipError_t e = order_after_last_call(ds, c.stream);
+                         std::map<int, bool>& use_chain, hipEvent_t ready, bool plain = false) {
+  hipError_t e = plain ? hipSuccess : order_after_last_call(ds, c.stream);
   if (e == hipSuccess && ready) e = hipStreamWaitEvent(c.stream, ready, 0);
   muon_status st = MUON_OK;
   const int kmode = c.mode == MODE_STEP ? 0 : (c.mode == MODE_NS ? 1 : 2);
@@ -1050,18 +1093,18 @@ muon_status enqueue_step(DeviceState& ds, Plan* plan, const Call& c, const std::
     wb = plan->d_wb;
   }
   if (e == hipSuccess)
-    e = timed(MUON_KC_MOMENTUM, c.stream, [&] {
+    e = timed_unless(plain, MUON_KC_MOMENTUM, c.stream, [&] {
       return launch_momentum(plan->d_mats, plan->d_etile_off, plan->count, plan->total_etiles, c.beta,
                              c.nesterov, ema, kmode, plan->d_partials, c.stream);
     });
   if (e == hipSuccess)
-    e = timed(MUON_KC_NORM, c.stream, [&] {
+    e = timed_unless(plain, MUON_KC_NORM, c.stream, [&] {
       return launch_norm_finalize(plan->d_etile_off, plan->count, plan->d_partials, plan->d_scal,
                                   c.mode == MODE_NORMS ? c.norms_out : nullptr, c.stream);
     });
   if (e == hipSuccess && c.mode != MODE_NORMS) {
     if (c.ns_steps == 0) {
-      e = timed(MUON_KC_WRITEBACK, c.stream, [&] {
+      e = timed_unless(plain, MUON_KC_WRITEBACK, c.stream, [&] {
         return launch_writeback_direct(plan->d_mats, plan->d_etile_off, plan->count, plan->total_etiles,
                                        plan->d_scal, c.lr, c.scale_rule, wb, c.stream);
       });
@@ -1106,7 +1149,7 @@ muon_status enqueue_step(DeviceState& ds, Plan* plan, const Call& c, const std::
         ca.cus_per_xcd = ds.cus_per_xcd;
         ca.wb = wb;
         ca.spin_limit = chain_spin_limit();
-        e = timed(MUON_KC_CHAIN, c.stream, [&] {
+        e = timed_unless(plain, MUON_KC_CHAIN, c.stream, [&] {
           return launch_ns_chain(prec, ch.d_imats, plan->d_scal, ch.d_items, ch.d_xcd_off, ch.per_xcd_max,
                                  ch.d_steps, ch.d_sync, ch.nsync, ds.fail_flag, ca, c.stream);
         });
@@ -1137,7 +1180,7 @@ muon_status enqueue_step(DeviceState& ds, Plan* plan, const Call& c, const std::
           for (int ph = 0; ph < 3 && e == hipSuccess; ++ph) {
             if (ph == PH_POLY && co.c == 0.f) continue;  // GRAM already formed B = b A
             pa.per_xcd = g.per_xcd[ph];
-            e = timed(MUON_KC_GRAM + ph, c.stream, [&] {
+            e = timed_unless(plain, MUON_KC_GRAM + ph, c.stream, [&] {
               return launch_ns_phase(g.prec, ph, plan->d_mats, plan->d_scal, g.tiles[ph], pa, c.stream);
             });
           }
@@ -1146,8 +1189,10 @@ muon_status enqueue_step(DeviceState& ds, Plan* plan, const Call& c, const std::
     }
   }
   if (e != hipSuccess) return fail(MUON_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  (void)hipEventRecord(plan->last_use, c.stream);
-  record_last_call(ds, c.stream);
+  if (!plain) {
+    (void)hipEventRecord(plan->last_use, c.stream);
+    record_last_call(ds, c.stream);
+  }
   return MUON_OK;
 }
 
@@ -1258,6 +1303,60 @@ muon_status run(const Call& c) {
     }
   }
   return enqueue_step(ds, plan, c, iprec, use_chain, nullptr);
+}
+
+// ------------------------------------------------------------ no allocation
+// muon_step_batched_ex over the device's fixed scratch array: the workspace
+// from its start, the launch tables after it, uploaded every call from a
+// host image kept per device until the next call.  No plan cache, no events,
+// no device or pinned allocation.
+std::map<int, PlanImage> g_noalloc_image;
+
+muon_status run_noalloc(const Call& c) {
+  t_last_error.clear();
+  muon_status st = validate_call(c);
+  if (st != MUON_OK || c.count == 0) return st;
+  const size_t ws_need = workspace_bytes(c.shapes, c.count);
+  if (ws_need > NOALLOC_SCRATCH_BYTES)
+    return fail(MUON_ERR_UNSUPPORTED,
+                "the matrices need %zu bytes of Newton-Schulz workspace; the allocation-free entry point has a "
+                "fixed %zu-byte scratch array per GPU (use muon_step_batched_ex)", ws_need,
+                size_t(NOALLOC_SCRATCH_BYTES));
+  std::lock_guard<std::mutex> lock(g_mu);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return fail(MUON_ERR_HIP, "cannot query the current device");
+  }
+  void* scratch = nullptr;
+  hipError_t e = noalloc_scratch(dev, &scratch);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MUON_ERR_HIP, "cannot take the scratch array's address on device %d: %s", dev, hipGetErrorString(e));
+  }
+  const int cus_per_xcd = std::max(1, cus / NUM_XCD);
+  const std::vector<int> iprec = working_formats(c.shapes, c.count, MODE_STEP, MUON_TILES_AUTO, int64_t(cus));
+  char* base = reinterpret_cast<char*>(scratch);
+  std::vector<MatDev> hm;
+  std::vector<int32_t> etile_off;
+  if ((st = host_mats(c, iprec, base, hm, etile_off)) != MUON_OK) return st;
+  PlanImage& im = g_noalloc_image[dev];
+  plan_image(hm, etile_off, cus_per_xcd, im);
+  const size_t tables = align256(ws_need);
+  if (tables + im.host.size() > NOALLOC_SCRATCH_BYTES)
+    return fail(MUON_ERR_UNSUPPORTED,
+                "the matrices need %zu bytes of workspace and %zu of launch tables; the allocation-free entry point "
+                "has a fixed %zu-byte scratch array per GPU (use muon_step_batched_ex)", ws_need, im.host.size(),
+                size_t(NOALLOC_SCRATCH_BYTES));
+  e = hipMemcpyAsync(base + tables, im.host.data(), im.host.size(), hipMemcpyHostToDevice, c.stream);
+  if (e != hipSuccess) return fail(MUON_ERR_HIP, "launch table upload failed: %s", hipGetErrorString(e));
+  Plan plan;
+  bind_plan(&plan, im, base + tables, hm, etile_off);
+  std::map<int, bool> use_chain;
+  DeviceState& ds = g_dev[dev];
+  if (ds.cus_per_xcd == 0) ds.cus_per_xcd = cus_per_xcd;   // sizes the persistent grids
+  return enqueue_step(ds, &plan, c, iprec, use_chain, nullptr, true);
 }
 
 // ------------------------------------------------------------ stream plans
@@ -1678,6 +1777,28 @@ muon_status muon_step_batched_ex(void* const* params, const void* const* grads, 
   c.scale_rule = scale_rule;
   c.stream = reinterpret_cast<hipStream_t>(stream);
   return run(c);
+}
+
+muon_status muon_step_batched_noalloc(void* const* params, const void* const* grads, void* const* momenta,
+                                      const muon_matrix_desc* shapes, int32_t count, float lr, float beta,
+                                      int32_t nesterov, muon_ns_coeffs ns_coeffs, int32_t ns_steps,
+                                      int32_t scale_rule, float* const* updates_out, void* stream) {
+  Call c{};
+  c.mode = MODE_STEP;
+  c.params = params;
+  c.grads = grads;
+  c.momenta = momenta;
+  c.updates = updates_out;
+  c.shapes = shapes;
+  c.count = count;
+  c.lr = lr;
+  c.beta = beta;
+  c.nesterov = nesterov;
+  c.co = ns_coeffs;
+  c.ns_steps = ns_steps;
+  c.scale_rule = scale_rule;
+  c.stream = reinterpret_cast<hipStream_t>(stream);
+  return run_noalloc(c);
 }
 
 muon_status muon_step_batched_v2(void* const* params, const void* const* grads, void* const* momenta,

@@ -151,6 +151,12 @@ hipError_t launch_ns_chain(int prec, const MatDev* imats, const MatScal* scal, c
 hipError_t launch_ns_phase(int prec, int phase, const MatDev* mats, const MatScal* scal,
                            const int2* tiles, const PhaseArgs& args, hipStream_t stream);
 
+// Bytes of the per-GPU device array of muon_step_batched_noalloc (its
+// Newton-Schulz workspace and launch tables), and its device address on
+// device `dev` (taken once per device, with `dev` current).
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
+hipError_t noalloc_scratch(int dev, void** out);
+
 // Tile edge of the Newton-Schulz products (square tiles) per format: 256 for
 // bf16 (LDS holds two stages of 256x64 bf16 per operand); 128 where an
 // operand takes twice the bytes (split-bf16 planes, float32) and for the

@@ -92,6 +92,18 @@ static bool in_alloc(const void* p) {
   return false;
 }
 
+// [p, p + n) inside one allocation
+static bool in_one_alloc(const void* p, size_t n) {
+  const char* c = static_cast<const char*>(p);
+  for (auto& a : g_allocs)
+    if (c >= a.first && c + n <= a.first + a.second) return true;
+  return false;
+}
+
+// The allocation-free entry point's scratch array: one host block of its size.
+static void* g_scratch = nullptr;
+static bool g_check_buffers = false;   // grids: every workspace buffer and table inside one allocation
+
 namespace muon {
 hipError_t launch_momentum(const MatDev*, const int32_t*, int32_t, int64_t, float, int32_t, int32_t, int32_t, float*,
                            hipStream_t) { return hipSuccess; }
@@ -101,6 +113,11 @@ hipError_t launch_writeback_direct(const MatDev*, const int32_t*, int32_t, int64
 hipError_t launch_adamw(const AdamwTensor*, const int32_t*, int32_t, int64_t, const float2*, float, float,
                         const AdamwConsts&, hipStream_t) { return hipSuccess; }
 hipError_t launch_mfma_probe(int64_t, int32_t, float*, double*, hipStream_t) { return hipSuccess; }
+hipError_t noalloc_scratch(int, void** out) {
+  if (!g_scratch && s_malloc(&g_scratch, NOALLOC_SCRATCH_BYTES) != hipSuccess) return hipErrorOutOfMemory;
+  *out = g_scratch;
+  return hipSuccess;
+}
 
 // The walk of ns_gemm_kernel: workgroup g on XCD g % 8 starts at slot g / 8
 // of its XCD's list, steps by the XCD's workgroup count, stops at the first
@@ -110,6 +127,18 @@ hipError_t launch_ns_phase(int prec, int phase, const MatDev* mats, const MatSca
   ++g_phase_launches;
   if (pa.per_xcd <= 0) return hipSuccess;
   const int T = ns_tile(prec);
+  if (g_check_buffers) {
+    CHECK(in_one_alloc(mats, sizeof(MatDev) * g_count), "matrix table outside an allocation");
+    CHECK(in_one_alloc(tiles, sizeof(int2) * NUM_XCD * pa.per_xcd), "tile list outside an allocation");
+    for (int i = 0; i < g_count; ++i) {
+      const MatDev& md = mats[i];
+      const int esz = is_f32(md.prec) ? 4 : 2, npl = md.prec == PREC_BF16X3 ? 2 : 1;
+      const size_t xb = size_t(md.Mp) * md.ldx * esz * npl, ab = size_t(md.Mp) * md.lda * esz * npl;
+      CHECK(in_one_alloc(md.X[0], xb) && in_one_alloc(md.X[1], xb) && in_one_alloc(md.A, ab) &&
+                in_one_alloc(md.B, ab),
+            "matrix %d: a workspace buffer lies outside the allocation", i);
+    }
+  }
   const int per_cu = (T == 256 || prec == PREC_BF16X3) ? 1 : 2;
   const int B = std::min(pa.per_xcd, pa.cus_per_xcd * per_cu);
   std::set<std::tuple<int, int, int>> expect, seen;
@@ -294,6 +323,42 @@ static void chain_case(const char* name, const std::vector<Shape>& shapes, int s
   }
 }
 
+// The allocation-free entry point over small matrices with real (host)
+// buffers: every workspace buffer and table inside the scratch block, and
+// inputs too large for it refused.
+static void noalloc_case(const char* name, const std::vector<Shape>& shapes, muon_status expect) {
+  const int n = int(shapes.size());
+  std::vector<muon_matrix_desc> d(n);
+  std::vector<void*> P(n), G(n), M(n);
+  for (int i = 0; i < n; ++i) {
+    d[i] = desc_of(shapes[i]);
+    const size_t el = size_t(shapes[i].rows) * shapes[i].cols;
+    (void)s_malloc(&P[i], el * (d[i].param_dtype == MUON_DTYPE_F32 ? 4 : 2));
+    (void)s_malloc(&G[i], el * 2);
+    (void)s_malloc(&M[i], el * 4);
+  }
+  printf("CASE no-allocation %s (%d matrices)\n", name, n);
+  g_count = n;
+  g_check_buffers = true;
+  const int before = g_phase_launches;
+  const size_t allocs = g_allocs.size();
+  const muon_ns_coeffs co{3.4445f, -4.775f, 2.0315f};
+  const muon_status st = muon_step_batched_noalloc(P.data(), G.data(), M.data(), d.data(), n, 0.02f, 0.95f, 1, co, 5,
+                                                   0, nullptr, nullptr);
+  g_check_buffers = false;
+  CHECK(st == expect, "status %d (expected %d): %s", int(st), int(expect), muon_last_error());
+  if (expect == MUON_OK) CHECK(g_phase_launches > before, "no phase launched");
+  else CHECK(g_phase_launches == before, "a refused call launched");
+  // the scratch block may appear on the first call; nothing else is allocated
+  CHECK(g_allocs.size() <= allocs + (g_scratch && allocs == g_allocs.size() ? 0 : 1), "the call allocated");
+  printf("  status %d%s%s\n", int(st), st == MUON_OK ? "" : ": ", st == MUON_OK ? "" : muon_last_error());
+  for (int i = 0; i < n; ++i) {
+    (void)s_free(P[i]);
+    (void)s_free(G[i]);
+    (void)s_free(M[i]);
+  }
+}
+
 int main() {
   const int BF = MUON_NS_BF16, F32 = MUON_NS_F32, X3 = MUON_NS_BF16X3;
   std::vector<Shape> share, d24, lm;
@@ -326,6 +391,12 @@ int main() {
   chain_case("bf16, schedule with c = 0 steps", mixed, 4, true);
   chain_case("binary32 and split-bf16, 3 steps",
              {{769, 769, F32}, {300, 520, X3}, {64, 64, F32}, {129, 257, X3}}, 3, false);
+  noalloc_case("twelve 768 x 768 bf16", std::vector<Shape>(12, Shape{768, 768, BF}), MUON_OK);
+  noalloc_case("ragged, mixed formats", {{700, 1100, BF}, {1100, 700, BF}, {300, 520, X3}, {64, 64, F32}, {1, 300, BF}},
+               MUON_OK);
+  noalloc_case("one d24 layer (too large)", {{1536, 1536, BF}, {1536, 1536, BF}, {1536, 1536, BF},
+                                             {1536, 1536, BF}, {1536, 6144, BF}, {6144, 1536, BF}},
+               MUON_ERR_UNSUPPORTED);
   printf(g_fail ? "PLAN-CHECK FAILED\n" : "PLAN-CHECK OK\n");
   return g_fail;
 }

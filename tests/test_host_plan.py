@@ -39,7 +39,12 @@ def test_tile_walks_and_chain_queues(plan_check):
     # 6 x 24 (rectangular): 21 triangle tiles each for GRAM and POLY
     d24 = out.split("CASE grids d24 stack")[1].split("CASE")[0]
     assert d24.count(" 3024 tiles") == 2 and " 10368 tiles" in d24
-    assert out.count("CASE ") == 10
+    assert out.count("CASE ") == 13
+    # the allocation-free entry point: buffers and tables inside its scratch
+    # block, and a stack too large for it refused before any launch
+    assert out.count("CASE no-allocation") == 3
+    big_na = out.split("CASE no-allocation one d24 layer (too large)")[1].split("CASE")[0]
+    assert "status 2" in big_na and "fixed" in big_na
     # formats: one 256 x 256 binary32 matrix on 64 x 64 tiles (4 x 4: 10
     # triangle tiles, 16 product tiles); the larger binary32 stack on 128 x 128
     one = out.split("CASE grids single 256 x 256")[1].split("CASE")[0]
