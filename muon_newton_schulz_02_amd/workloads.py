@@ -207,6 +207,26 @@ def _studentt_spectral(rows, cols, device, seed, idx):
     return (qu * s) @ qv.t().contiguous()
 
 
+def spectral_factors(rows, cols, seed, idx, device="cpu"):
+    """The stress gradients' construction in float64 on `device`: (Q_u, s,
+    Q_v) with Q_u (rows x r) and Q_v (cols x r) the orthonormal factors (QR)
+    of Student-t(3) matrices, s_i = i^-2, r = min(rows, cols); G = Q_u
+    diag(s) Q_v^T.  Float64 throughout, so G has the exact i^-2 spectrum to
+    float64 accuracy.  (Not the stream the stack's float32 draw takes.)"""
+    r = min(rows, cols)
+    gen = _gen(device, seed, idx, 0, 2)
+
+    def student_t(shape):
+        z = torch.randn(shape, generator=gen, device=device, dtype=torch.float64)
+        chi = torch.randn((3,) + tuple(shape), generator=gen, device=device, dtype=torch.float64).square_().sum(0)
+        return z / torch.sqrt(chi / 3.0)
+
+    qu, _ = torch.linalg.qr(student_t((rows, r)))
+    qv, _ = torch.linalg.qr(student_t((cols, r)))
+    s = torch.arange(1, r + 1, device=device, dtype=torch.float64).pow_(-2.0)
+    return qu, s, qv
+
+
 def initial_state(wl: Workload, idx: int, device="cpu"):
     """(W, M0) for matrix `idx`: W in the parameter dtype, M0 float32."""
     spec = wl.specs[idx]
