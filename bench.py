@@ -393,16 +393,59 @@ def measured_traffic(workload, kernel):
     return float(kv[kernel])
 
 
+def _host_description():
+    """CPU model, logical CPUs and the BLAS library (with its thread count)
+    that NumPy calls, as this host reports them."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = None, os.cpu_count() or 1
+    try:
+        import numpy  # noqa: F401  (loads the BLAS the oracle calls)
+        from threadpoolctl import threadpool_info
+        for p in threadpool_info():
+            if p.get("user_api") == "blas":
+                blas = f"{p.get('internal_api')} {p.get('version')} ({p.get('architecture')})"
+                threads = int(p.get("num_threads", threads))
+                break
+    except Exception:  # noqa: BLE001
+        pass
+    return model, os.cpu_count(), blas, threads
+
+
+def _config1_one_thread(orc, wlm):
+    """The oracle on the single 256 x 256 binary32 configuration (5 cubic
+    steps), BLAS held to one thread: steps per second."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    wl = wlm.workload("single256_f32")
+    w, m = (t.numpy() for t in wlm.initial_state(wl, 0))
+    g = wlm.gradient(wl, 0).numpy()
+    kw = dict(lr=float(np.float32(wl.lr)), beta=wl.beta, nesterov=wl.nesterov, coeffs=wl.coeffs,
+              steps=wl.ns_steps)
+    with threadpool_limits(limits=1):
+        orc.muon_step(w, g, m, **kw)
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 0.5:
+            orc.muon_step(w, g, m, **kw)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+    return {"workload": "single256_f32 (1 x 256x256 f32, 5 cubic NS steps)", "threads": 1,
+            "value": round(1.0 / dt, 2), "unit": "steps/s", "ms_per_step": round(dt * 1e3, 3)}
+
+
 def cpu_baseline(wl, sample, sample_idx, kw, n_total):
     """Time the float64 oracle on the sample; scale by nominal FLOPs to a full step."""
-    import numpy as np
-
     import oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
+    from muon_newton_schulz_02_amd import workloads as wlm
+
+    model, ncpu, blas, threads = _host_description()
     t0 = time.perf_counter()
     for w, g, m in sample:
         orc.muon_step(w, g, m, lr=kw["lr"], beta=kw["beta"], nesterov=bool(kw["nesterov"]),
@@ -416,10 +459,15 @@ def cpu_baseline(wl, sample, sample_idx, kw, n_total):
 
     frac = sum(cost(wl.specs[i]) for i in sample_idx) / sum(cost(s) for s in wl.specs)
     step_s = dt / frac
-    return {"value": round(1.0 / step_s, 6), "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(sample)} of {n_total} matrices (first layers), float64 NumPy oracle, "
-                      f"{dt:.2f} s, scaled by nominal NS FLOPs to the full step",
-            "seconds_per_step": round(step_s, 3)}
+    out = {"value": round(1.0 / step_s, 6), "unit": "steps/s", "cores": threads, "kind": "oracle",
+           "sample": f"{len(sample)} of {n_total} matrices (first layers), float64 NumPy oracle, "
+                     f"{dt:.2f} s, scaled by nominal NS FLOPs ({frac:.4f} of the step) to the full step",
+           "seconds_per_step": round(step_s, 3), "cpu_model": model, "logical_cpus": ncpu, "blas": blas}
+    try:
+        out["config1_one_thread"] = _config1_one_thread(orc, wlm)
+    except Exception as e:  # noqa: BLE001
+        out["config1_one_thread"] = {"error": str(e)}
+    return out
 
 
 if __name__ == "__main__":
