@@ -193,6 +193,10 @@ typedef struct muon_matrix_desc {
 } muon_matrix_desc;
 
 /* One Muon step on `count` matrices in one grouped launch sequence.
+ * Source: the Muon optimizer of "把 GPT-2 的训练租金估算从 4.3 万美元压到 40
+ * 美元…" (magicnetworld.com), table 符号与约定, row "Muon" (momentum of a
+ * matrix parameter, orthogonalised), with the Newton-Schulz orthogonalisation
+ * of "开发者千美元训3.8B模型 击败GPT-2" (aiproducthub.cn), paragraph 影响.
  *
  * params[i]  rows x cols weight (param_dtype), updated in place.
  * grads[i]   rows x cols gradient (grad_dtype), read only.
@@ -269,7 +273,11 @@ muon_status muon_step_batched_noalloc(void* const* params, const void* const* gr
 /* Newton-Schulz orthogonalisation only: x_out[i] = NS^ns_steps(x / (||x||_F
  * + 1e-7)) for x = x_in[i] (rows x cols, grad_dtype, row stride ld_grad),
  * oriented as above.  x_out[i] is binary32 rows x cols with row stride
- * cols.  param, momentum fields of the descriptors are ignored.            */
+ * cols.  param, momentum fields of the descriptors are ignored.
+ * Source: the Newton-Schulz orthogonalisation named in "开发者千美元训3.8B模型
+ * 击败GPT-2" (aiproducthub.cn), paragraph 影响, in its polynomial form
+ * (Higham, Functions of Matrices, ch. 8).  Errors as muon_step_batched,
+ * INVALID_ARGUMENT for a NULL x_out entry.                                 */
 muon_status muon_ns_batched(const void* const* x_in, float* const* x_out,
                             const muon_matrix_desc* shapes, int32_t count,
                             muon_ns_coeffs ns_coeffs, int32_t ns_steps, void* stream);
@@ -277,7 +285,12 @@ muon_status muon_ns_batched(const void* const* x_in, float* const* x_out,
 /* Frobenius norms: norms_out[i] = ||x_in[i]||_F (binary32, device array of
  * `count` floats), summed as binary32 partials per 64x64 tile and reduced in
  * a fixed order (deterministic).  x_in[i] is grad_dtype with row stride
- * ld_grad.                                                                */
+ * ld_grad.  The same reduction gives the step's normalisation X = U /
+ * (||U||_F + 1e-7); the pages leave the normalisation open, and dividing by
+ * the Frobenius norm bounds every singular value by 1, which the iteration
+ * needs to converge (Higham, Functions of Matrices, ch. 8).  Errors:
+ * INVALID_ARGUMENT (NULL arrays or entries, bad sizes), UNSUPPORTED
+ * (dtype, alignment), ALIAS (norms_out overlaps an input), HIP.           */
 muon_status muon_frobenius_norms(const void* const* x_in, const muon_matrix_desc* shapes,
                                  int32_t count, float* norms_out, void* stream);
 
