@@ -5,7 +5,9 @@
 //    stores U into the workspace in the wide orientation X (m x n, m <= n;
 //    through an LDS transpose for tall matrices) in the Newton-Schulz storage
 //    format, zero-filling the padding; writes one binary32 sum of u^2 per
-//    64x64 tile (wavefront shuffles, then LDS across the four waves).
+//    4096-element tile (wavefront shuffles, then LDS across the four waves).
+//    Tall matrices go in 64 x 64 tiles through the LDS transpose; the others
+//    in 16 x 256 tiles, one 256-element row run per wave and instruction.
 //    G and M are touched once per step, so their vector loads and the M
 //    store carry the nontemporal hint (measured 4 % faster); U is read
 //    again by the Newton-Schulz products and is stored normally.
@@ -78,6 +80,99 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
+// Momentum of four consecutive elements: M' = beta M + g_in, U = Nesterov ?
+// g_in + beta M' : M', g_in = g (heavy ball) or fl32((1 - beta) g) (EMA), each
+// operation rounded once in binary32 (contraction is off in this file).
+__device__ inline void momentum4(const float* g, const float* m, float* mn, float* u, float beta, int nesterov,
+                                 int ema) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float gi = ema ? (1.f - beta) * g[e] : g[e];
+    const float bm = beta * m[e];
+    mn[e] = bm + gi;
+    const float bn = beta * mn[e];
+    u[e] = nesterov ? (gi + bn) : mn[e];
+  }
+}
+
+// The RTILE_R x RTILE_C tile (tr0, tc0) of a matrix iterated untransposed:
+// wave w takes rows w, w + 4, w + 8, w + 12 and lane l the four columns from
+// tc0 + 4 l, so every load and store instruction of a wave covers one
+// contiguous run of a row (1 KB of M).  All four rows' loads are issued
+// before any store.  Returns this thread's sum of u^2.
+__device__ inline float momentum_rows(const MatDev& md, int tr0, int tc0, float beta, int32_t nesterov, int32_t ema,
+                                      int32_t mode) {
+  static_assert(RTILE_C == 4 * 64 && RTILE_R == 4 * 4, "four rows of one wave-wide run per wave");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = tc0 + 4 * lane;
+  const int rows = md.rows, cols = md.cols;
+  float g[4][4], m[4][4];
+  bool live[4], full[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = tr0 + w + 4 * q;
+    live[q] = row < rows && col < cols;
+    full[q] = live[q] && md.vec_ok && col + 3 < cols;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[q][e] = m[q][e] = 0.f;
+    const int64_t gi = int64_t(row) * md.ld_grad + col;
+    const int64_t mi = int64_t(row) * md.ld_mom + col;
+    if (full[q]) {
+      if (md.grad_bf16) {
+        const u32x2 raw = __builtin_nontemporal_load(
+            gmem(reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(md.grad) + gi)));
+        g[q][0] = bf16_bits_to_float(raw[0] & 0xFFFFu);
+        g[q][1] = bf16_bits_to_float(raw[0] >> 16);
+        g[q][2] = bf16_bits_to_float(raw[1] & 0xFFFFu);
+        g[q][3] = bf16_bits_to_float(raw[1] >> 16);
+      } else {
+        const f32x4 raw = __builtin_nontemporal_load(
+            gmem(reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(md.grad) + gi)));
+        g[q][0] = raw[0]; g[q][1] = raw[1]; g[q][2] = raw[2]; g[q][3] = raw[3];
+      }
+      if (mode == 0) {
+        const f32x4 raw = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4*>(md.mom + mi)));
+        m[q][0] = raw[0]; m[q][1] = raw[1]; m[q][2] = raw[2]; m[q][3] = raw[3];
+      }
+    } else if (live[q]) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col + e < cols) {
+          g[q][e] = load_elem(md.grad, gi + e, md.grad_bf16);
+          if (mode == 0) m[q][e] = gmem(md.mom)[mi + e];
+        }
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = tr0 + w + 4 * q;
+    float mn[4], u[4];
+    if (mode == 0) {
+      momentum4(g[q], m[q], mn, u, beta, nesterov, ema);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = g[q][e];
+    }
+    // elements outside the matrix loaded as zero and stay zero: they fill
+    // the workspace padding
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += u[e] * u[e];
+    if (mode == 0 && live[q]) {
+      const int64_t mi = int64_t(row) * md.ld_mom + col;
+      if (full[q]) {
+        __builtin_nontemporal_store(f32x4{mn[0], mn[1], mn[2], mn[3]}, gmem(reinterpret_cast<f32x4*>(md.mom + mi)));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e < cols) gmem(md.mom)[mi + e] = mn[e];
+      }
+    }
+    if (mode != 2) store4_ws(md.X[0], md.plane_X, md.prec, int64_t(row) * md.ldx + col, u);
+  }
+  return ss;
+}
+
 }  // namespace
 
 // mode 0: momentum step; mode 1: U = G (Newton-Schulz only); mode 2: norms
@@ -92,9 +187,17 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
   const int mi = find_matrix(etile_off, count, b);
   const MatDev& md = mats[mi];
   const int local = b - etile_off[mi];
+  const int tid = threadIdx.x;
+  if (!md.transposed) {
+    const float ssr = wave_sum(momentum_rows(md, (local / md.etile_cols) * RTILE_R,
+                                             (local % md.etile_cols) * RTILE_C, beta, nesterov, ema, mode));
+    if ((tid & 63) == 0) red[tid >> 6] = ssr;
+    __syncthreads();
+    if (tid == 0) partials[b] = (red[0] + red[1]) + (red[2] + red[3]);
+    return;
+  }
   const int tr0 = (local / md.etile_cols) * ETILE;   // natural row of the tile
   const int tc0 = (local % md.etile_cols) * ETILE;   // natural col of the tile
-  const int tid = threadIdx.x;
   const int cg = tid & 15;
   const int rg = tid >> 4;
   const int rows = md.rows, cols = md.cols;
@@ -144,16 +247,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
             if (col + e < cols) m[e] = gmem(md.mom)[mi64 + e];
         }
         float mn[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // binary32, one rounding per operation (contraction is off here);
-          // EMA form: the gradient enters as fl32((1 - beta) * g)
-          const float gi = ema ? (1.f - beta) * g[e] : g[e];
-          const float bm = beta * m[e];
-          mn[e] = bm + gi;
-          const float bn = beta * mn[e];
-          u[e] = nesterov ? (gi + bn) : mn[e];
-        }
+        momentum4(g, m, mn, u, beta, nesterov, ema);
         if (full) {
           __builtin_nontemporal_store(f32x4{mn[0], mn[1], mn[2], mn[3]},
                                       gmem(reinterpret_cast<f32x4*>(md.mom + mi64)));
@@ -235,15 +329,16 @@ __global__ __launch_bounds__(256) void writeback_direct_kernel(const MatDev* __r
   const int mi = find_matrix(etile_off, count, b);
   const MatDev& md = mats[mi];
   const int local = b - etile_off[mi];
-  const int tr0 = (local / md.etile_cols) * ETILE;
-  const int tc0 = (local % md.etile_cols) * ETILE;
   const bool tr = md.transposed != 0;
+  const int th = tr ? ETILE : RTILE_R, tw = tr ? ETILE : RTILE_C;
+  const int tr0 = (local / md.etile_cols) * th;
+  const int tc0 = (local % md.etile_cols) * tw;
   const void* xw = md.X[0];
   const float inv = scal[mi].inv;
   const float t = wb ? wb[mi].x : update_scale(lr, scale_rule, md.rows, md.cols);
   const float d = wb ? wb[mi].y : 1.f;
-  for (int e = threadIdx.x; e < ETILE * ETILE; e += 256) {
-    const int row = tr0 + e / ETILE, col = tc0 + e % ETILE;
+  for (int e = threadIdx.x; e < th * tw; e += 256) {
+    const int row = tr0 + e / tw, col = tc0 + e % tw;
     if (row >= md.rows || col >= md.cols) continue;
     const int64_t xi = tr ? int64_t(col) * md.ldx + row : int64_t(row) * md.ldx + col;
     const float o = inv * load_ws(xw, md.plane_X, md.prec, xi);

@@ -1031,8 +1031,11 @@ muon_status host_mats(const Call& c, const std::vector<int>& iprec, char* ws, st
     m.prec = c.mode == MODE_NORMS ? int(PREC_BF16) : iprec[size_t(i)];
     const int64_t rp = g.transposed ? g.Np : g.Mp;  // natural padded rows
     const int64_t cp = g.transposed ? g.Mp : g.Np;  // natural padded cols
-    m.etile_cols = int32_t(cp / ETILE);
-    etile_off[i + 1] = etile_off[i] + int32_t((rp / ETILE) * (cp / ETILE));
+    // elementwise tiles: ETILE x ETILE for tall matrices, RTILE_R x RTILE_C
+    // for the others (both divide the 256-padded shape)
+    const int64_t th = g.transposed ? ETILE : RTILE_R, tw = g.transposed ? ETILE : RTILE_C;
+    m.etile_cols = int32_t(cp / tw);
+    etile_off[i + 1] = etile_off[i] + int32_t((rp / th) * (cp / tw));
     if (c.mode != MODE_NORMS) {
       m.plane_X = g.Mp * g.ldx;
       m.plane_A = g.Mp * g.lda;

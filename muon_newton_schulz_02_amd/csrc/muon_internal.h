@@ -14,8 +14,12 @@ constexpr int PAD = 256;
 // Workspace rows may hold LDPAD elements beyond the padded width (never
 // read); a pad of 64 was measured to change nothing on the d24 stack.
 constexpr int LDPAD = 0;
-// Elementwise tiles (momentum, transposed copy, norm partials).
+// Elementwise tiles (momentum, transposed copy, norm partials), 4096
+// elements each: ETILE x ETILE for tall matrices (transposed through LDS),
+// RTILE_R x RTILE_C for the others (one 256-element row run per wave and
+// instruction: 1 KB of binary32 momentum).
 constexpr int ETILE = 64;
+constexpr int RTILE_R = 16, RTILE_C = 256;
 // Dispatch order puts consecutive workgroups on different XCDs.
 constexpr int NUM_XCD = 8;
 
