@@ -56,6 +56,13 @@
  *   - Small per-call tables (per-matrix rates, per-tensor AdamW rates) are
  *     copied to the device from pinned staging memory: the call does not
  *     wait for earlier work on its stream.
+ *   - Fault hook for tests: with the environment variable MUON_FAULT_ALLOC
+ *     set to anything but "" or "0", every device allocation the library
+ *     attempts fails, so a call that needs one returns OUT_OF_MEMORY having
+ *     changed nothing.
+ *   - The optimizer's state is the caller's weights and momenta: saved and
+ *     restored, they give the same next step bit for bit, whatever the
+ *     library's caches hold.
  */
 #ifndef MUON_MI355X_H
 #define MUON_MI355X_H

@@ -396,6 +396,18 @@ void record_last_call(DeviceState& ds, hipStream_t stream) {
   if (ds.last_call && hipEventRecord(ds.last_call, stream) == hipSuccess) ds.last_call_recorded = true;
 }
 
+// Device allocations of the library.  MUON_FAULT_ALLOC set to anything but
+// "" or "0" makes every one fail as if the device were out of memory (a fault
+// hook for testing the allocation-failure paths; read per allocation).
+hipError_t device_alloc(void** p, size_t bytes) {
+  const char* f = std::getenv("MUON_FAULT_ALLOC");
+  if (f && *f && std::strcmp(f, "0") != 0) {
+    *p = nullptr;
+    return hipErrorOutOfMemory;
+  }
+  return hipMalloc(p, bytes);
+}
+
 struct TileSrc {
   int mat;
   int ti, tj;
@@ -603,7 +615,7 @@ muon_status build_plan(Plan* plan, const std::vector<MatDev>& hm, const std::vec
   plan_image(hm, etile_off, cus_per_xcd, im);
   const size_t bytes = im.host.size();
   void* dmem = nullptr;
-  if (hipMalloc(&dmem, bytes) != hipSuccess) {
+  if (device_alloc(&dmem, bytes) != hipSuccess) {
     (void)hipGetLastError();
     return fail(MUON_ERR_OUT_OF_MEMORY, "plan allocation of %zu bytes failed", bytes);
   }
@@ -744,7 +756,7 @@ muon_status build_chain(Plan* plan, size_t gi, int k, uint32_t cmask, char* chai
   const size_t o_sync = off;
   off = align256(off + sizeof(int32_t) * nsync);
   void* dmem = nullptr;
-  if (hipMalloc(&dmem, off) != hipSuccess) {
+  if (device_alloc(&dmem, off) != hipSuccess) {
     (void)hipGetLastError();
     return fail(MUON_ERR_OUT_OF_MEMORY, "chain plan allocation of %zu bytes failed", off);
   }
@@ -1243,7 +1255,7 @@ muon_status run(const Call& c) {
     ds.ws = nullptr;
     ds.ws_bytes = 0;
     void* p = nullptr;
-    if (hipMalloc(&p, need) != hipSuccess) {
+    if (device_alloc(&p, need) != hipSuccess) {
       (void)hipGetLastError();
       return fail(MUON_ERR_OUT_OF_MEMORY, "workspace allocation of %zu bytes failed", need);
     }
@@ -1259,7 +1271,7 @@ muon_status run(const Call& c) {
     ds.chain_ws = nullptr;
     ds.chain_ws_bytes = 0;
     void* p = nullptr;
-    if (hipMalloc(&p, chain_need) != hipSuccess) {
+    if (device_alloc(&p, chain_need) != hipSuccess) {
       (void)hipGetLastError();
       return fail(MUON_ERR_OUT_OF_MEMORY, "chain workspace allocation of %zu bytes failed", chain_need);
     }
@@ -1455,7 +1467,7 @@ muon_status stream_plan_create(void* const* params, const void* const* grads, vo
   }
   size_t need = 0;
   for (const auto& g : sp->groups) need = std::max(need, workspace_bytes(g.shapes.data(), int32_t(g.shapes.size())));
-  if (hipMalloc(&sp->ws, std::max<size_t>(need, 256)) != hipSuccess) {
+  if (device_alloc(&sp->ws, std::max<size_t>(need, 256)) != hipSuccess) {
     (void)hipGetLastError();
     sp->ws = nullptr;
     free_stream_plan(sp);
@@ -1627,7 +1639,7 @@ muon_status build_adamw_plan(AdamwPlan* plan, const AdamwCall& c) {
   const size_t o_rates = bytes;
   bytes = align256(bytes + sizeof(float2) * n);
   void* dmem = nullptr;
-  if (hipMalloc(&dmem, bytes) != hipSuccess) {
+  if (device_alloc(&dmem, bytes) != hipSuccess) {
     (void)hipGetLastError();
     return fail(MUON_ERR_OUT_OF_MEMORY, "AdamW plan allocation of %zu bytes failed", bytes);
   }

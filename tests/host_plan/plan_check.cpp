@@ -359,6 +359,39 @@ static void noalloc_case(const char* name, const std::vector<Shape>& shapes, muo
   }
 }
 
+// The allocation fault hook: with MUON_FAULT_ALLOC set, a call that needs a
+// new plan (or workspace) fails with OUT_OF_MEMORY before any launch, and
+// the next call without it succeeds.
+static void fault_case() {
+  const std::vector<Shape> shapes = {{333, 444, MUON_NS_BF16}, {444, 333, MUON_NS_BF16}};
+  const int n = int(shapes.size());
+  std::vector<muon_matrix_desc> d(n);
+  std::vector<void*> P(n), G(n), M(n);
+  for (int i = 0; i < n; ++i) {
+    d[i] = desc_of(shapes[i]);
+    P[i] = reinterpret_cast<void*>(uintptr_t(0x300000000000ull) + uintptr_t(i) * (uintptr_t(3) << 34));
+    G[i] = reinterpret_cast<void*>(uintptr_t(P[i]) + (uintptr_t(1) << 34));
+    M[i] = reinterpret_cast<void*>(uintptr_t(P[i]) + (uintptr_t(2) << 34));
+  }
+  printf("CASE allocation fault hook\n");
+  g_count = n;
+  const muon_ns_coeffs co{3.4445f, -4.775f, 2.0315f};
+  setenv("MUON_FAULT_ALLOC", "1", 1);
+  int before = g_phase_launches;
+  muon_status st = muon_step_batched(P.data(), G.data(), M.data(), d.data(), n, 0.02f, 0.95f, 1, co, 5, 0, nullptr);
+  CHECK(st == MUON_ERR_OUT_OF_MEMORY, "with the hook: status %d (%s)", int(st), muon_last_error());
+  CHECK(g_phase_launches == before, "a call that failed to allocate launched");
+  const int32_t grp[2] = {0, 1};
+  muon_stream_plan sp = nullptr;
+  st = muon_stream_plan_create(P.data(), G.data(), M.data(), d.data(), n, grp, 2, 0, nullptr, &sp);
+  CHECK(st == MUON_ERR_OUT_OF_MEMORY && sp == nullptr, "stream plan with the hook: status %d", int(st));
+  unsetenv("MUON_FAULT_ALLOC");
+  st = muon_step_batched(P.data(), G.data(), M.data(), d.data(), n, 0.02f, 0.95f, 1, co, 5, 0, nullptr);
+  CHECK(st == MUON_OK, "without the hook: status %d (%s)", int(st), muon_last_error());
+  CHECK(g_phase_launches > before, "no launch without the hook");
+  printf("  out of memory with the hook, launched without it\n");
+}
+
 int main() {
   const int BF = MUON_NS_BF16, F32 = MUON_NS_F32, X3 = MUON_NS_BF16X3;
   std::vector<Shape> share, d24, lm;
@@ -391,6 +424,7 @@ int main() {
   chain_case("bf16, schedule with c = 0 steps", mixed, 4, true);
   chain_case("binary32 and split-bf16, 3 steps",
              {{769, 769, F32}, {300, 520, X3}, {64, 64, F32}, {129, 257, X3}}, 3, false);
+  fault_case();
   noalloc_case("twelve 768 x 768 bf16", std::vector<Shape>(12, Shape{768, 768, BF}), MUON_OK);
   noalloc_case("ragged, mixed formats", {{700, 1100, BF}, {1100, 700, BF}, {300, 520, X3}, {64, 64, F32}, {1, 300, BF}},
                MUON_OK);

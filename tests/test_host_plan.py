@@ -39,7 +39,8 @@ def test_tile_walks_and_chain_queues(plan_check):
     # 6 x 24 (rectangular): 21 triangle tiles each for GRAM and POLY
     d24 = out.split("CASE grids d24 stack")[1].split("CASE")[0]
     assert d24.count(" 3024 tiles") == 2 and " 10368 tiles" in d24
-    assert out.count("CASE ") == 13
+    assert out.count("CASE ") == 14
+    assert "out of memory with the hook, launched without it" in out
     # the allocation-free entry point: buffers and tables inside its scratch
     # block, and a stack too large for it refused before any launch
     assert out.count("CASE no-allocation") == 3
