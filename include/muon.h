@@ -41,11 +41,14 @@
  *     so a call that returns an error has changed nothing.
  *   - The library keeps a per-device workspace (grown on demand, freed by
  *     muon_release_workspace) and a cache of launch plans keyed by the
- *     pointers and shapes.  Every call first makes its stream wait for the
- *     device's previous call (an event recorded after each call's last
- *     launch), so calls made on different streams, or from different host
- *     threads, run on the device one after another in the order they were
- *     made, never overlapping.
+ *     pointers and shapes.  Every Muon call (muon_step_batched*,
+ *     muon_ns_batched, muon_frobenius_norms, muon_stream_submit) first makes
+ *     its stream wait for the device's previous Muon call, and every AdamW
+ *     call for the previous AdamW call (an event recorded after each call's
+ *     last launch): calls of one family made on different streams, or from
+ *     different host threads, run on the device one after another in the
+ *     order they were made, never overlapping.  A Muon call and an AdamW call
+ *     share no device memory and may run concurrently on two streams.
  *   - Nothing crosses the ABI as an exception; errors are status codes with
  *     a thread-local message from muon_last_error().
  *   - The persistent chain (muon_launch_mode) bounds every dependency wait;

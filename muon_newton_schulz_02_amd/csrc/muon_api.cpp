@@ -232,8 +232,11 @@ struct DeviceState {
   int32_t* fail_flag = nullptr;        // pinned host word the chain raises when a wait times out
   hipEvent_t chain_done = nullptr;     // recorded after the last persistent-chain launch
   bool chain_pending = false;          // a chain was launched since the flag was last read
-  hipEvent_t last_call = nullptr;      // recorded after every call's last launch on this device
-  bool last_call_recorded = false;
+  // recorded after every call's last launch on this device, one per family
+  // of calls that share device memory: the Muon step (workspace, plans,
+  // tables) and AdamW (its plans' rate tables)
+  hipEvent_t last_call[2] = {nullptr, nullptr};
+  bool last_call_recorded[2] = {false, false};
   PinnedRing ring;
   int cus_per_xcd = 0;
   std::list<Plan*> plans;              // most recently used first
@@ -379,21 +382,26 @@ hipError_t staged_copy(DeviceState& ds, void* dst, const void* src, size_t len, 
 }
 
 // Every call on a device first makes its stream wait for the device's
-// previous call (their launches share the workspace, plans and tables), so
-// calls issued on different streams run in the order they were made.
-hipError_t order_after_last_call(DeviceState& ds, hipStream_t stream) {
-  if (!ds.last_call) {
-    if (hipEventCreateWithFlags(&ds.last_call, hipEventDisableTiming) != hipSuccess) {
-      ds.last_call = nullptr;
+// previous call of the same family (Muon steps share the workspace, plans and
+// tables; AdamW calls their plans' rate tables), so calls issued on different
+// streams run in the order they were made.  The two families share no device
+// memory and may overlap.
+enum CallFamily : int { FAMILY_MUON = 0, FAMILY_ADAMW = 1 };
+
+hipError_t order_after_last_call(DeviceState& ds, hipStream_t stream, int family = FAMILY_MUON) {
+  if (!ds.last_call[family]) {
+    if (hipEventCreateWithFlags(&ds.last_call[family], hipEventDisableTiming) != hipSuccess) {
+      ds.last_call[family] = nullptr;
       return hipGetLastError();
     }
   }
-  if (!ds.last_call_recorded) return hipSuccess;
-  return hipStreamWaitEvent(stream, ds.last_call, 0);
+  if (!ds.last_call_recorded[family]) return hipSuccess;
+  return hipStreamWaitEvent(stream, ds.last_call[family], 0);
 }
 
-void record_last_call(DeviceState& ds, hipStream_t stream) {
-  if (ds.last_call && hipEventRecord(ds.last_call, stream) == hipSuccess) ds.last_call_recorded = true;
+void record_last_call(DeviceState& ds, hipStream_t stream, int family = FAMILY_MUON) {
+  if (ds.last_call[family] && hipEventRecord(ds.last_call[family], stream) == hipSuccess)
+    ds.last_call_recorded[family] = true;
 }
 
 // Device allocations of the library.  MUON_FAULT_ALLOC set to anything but
@@ -1733,7 +1741,7 @@ muon_status run_adamw(const AdamwCall& c) {
   k.bc2 = float(1.0 - std::pow(double(h.beta2), double(h.step)));
   k.eps = h.eps;
   const float2* rates = nullptr;
-  hipError_t e = order_after_last_call(ds, c.stream);
+  hipError_t e = order_after_last_call(ds, c.stream, FAMILY_ADAMW);
   if (e == hipSuccess && (h.lr_per_tensor || h.wd_per_tensor)) {
     std::vector<float2> hr(plan->count);
     for (int32_t j = 0; j < plan->count; ++j) {
@@ -1753,7 +1761,7 @@ muon_status run_adamw(const AdamwCall& c) {
   }
   if (e != hipSuccess) return fail(MUON_ERR_HIP, "AdamW launch failed: %s", hipGetErrorString(e));
   (void)hipEventRecord(plan->last_use, c.stream);
-  record_last_call(ds, c.stream);
+  record_last_call(ds, c.stream, FAMILY_ADAMW);
   return MUON_OK;
 }
 
@@ -1977,7 +1985,8 @@ muon_status muon_release_workspace(void) {
     kv.second.fail_flag = nullptr;
     release_ring(kv.second.ring);
     if (kv.second.chain_done) (void)hipEventDestroy(kv.second.chain_done);
-    if (kv.second.last_call) (void)hipEventDestroy(kv.second.last_call);
+    for (hipEvent_t ev : kv.second.last_call)
+      if (ev) (void)hipEventDestroy(ev);
   }
   if (have_dev) (void)hipSetDevice(cur);
   g_dev.clear();

@@ -6,6 +6,8 @@
 * The per-call tables (per-matrix write-back scalars, per-tensor AdamW rates)
   go to the device through pinned staging, so a call returns while earlier
   work on its stream is still running.
+* A Muon step and an AdamW call share no device memory: on two streams they
+  overlap, and give what they give one after the other.
 """
 import sys
 import time
@@ -137,3 +139,66 @@ def test_adamw_per_tensor_rates_do_not_block_the_host():
     assert busy and dt < 0.1
     assert all(np.array_equal(a, b) for a, b in zip(ref, _bits(p) + _bits(ea) + _bits(eq)))
     del sink
+
+
+def _concurrent_streams():
+    """Two streams on different hardware queues (HIP maps a process's streams
+    onto a few of them; two streams that share one run in submission order)."""
+    torch.cuda._sleep(1000)
+    torch.cuda.synchronize()
+    a = torch.cuda.Stream()
+    x = torch.ones(1024, device="cuda")
+    for _ in range(8):
+        b = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(a)
+        with torch.cuda.stream(a):
+            torch.cuda._sleep(50_000_000)
+        with torch.cuda.stream(b):
+            x.add_(1.0)
+        t1.record(b)
+        torch.cuda.synchronize()
+        if t0.elapsed_time(t1) < 5.0:
+            return a, b
+    return None, None
+
+
+def test_muon_and_adamw_on_two_streams_overlap():
+    _announce("a Muon step and an AdamW call on two streams")
+    s1, s2 = _concurrent_streams()
+    if s1 is None:
+        pytest.skip("no two streams of this process run concurrently (they share a hardware queue)")
+    shapes = [(1536, 1536)] * 16 + [(1536, 6144)] * 4
+    w, g, m = _stack(shapes, 11)
+    gen = torch.Generator().manual_seed(12)
+    p = [(torch.randn(1 << 20, generator=gen) * 0.02).to(torch.bfloat16).cuda()]
+    gr = [(torch.randn(1 << 20, generator=gen) * 1e-3).to(torch.bfloat16).cuda()]
+    ea = [(torch.randn(1 << 20, generator=gen) * 1e-3).cuda()]
+    eq = [(torch.randn(1 << 20, generator=gen) * 1e-3).square().cuda()]
+    keep = [t.clone() for t in w + m + p + ea + eq]
+    kw = dict(lr=f32(0.02), beta=0.95, nesterov=1, ns_coeffs=MUON, ns_steps=5)
+    akw = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.01, step=5, lr_per_tensor=[2e-3])
+    mb.muon_step_batched(w, g, m, **kw)
+    mb.muon_adamw_batched(p, gr, ea, eq, **akw)
+    torch.cuda.synchronize()
+    ref = _bits(w + m + p + ea + eq)
+    for d, src in zip(w + m + p + ea + eq, keep):
+        d.copy_(src)
+    torch.cuda.synchronize()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    start = torch.cuda.Event(enable_timing=True)
+    muon_done, adamw_done = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(s1)
+    mb.muon_step_batched(w, g, m, stream=s1, **kw)
+    muon_done.record(s1)
+    s2.wait_event(start)
+    mb.muon_adamw_batched(p, gr, ea, eq, stream=s2, **akw)
+    adamw_done.record(s2)
+    torch.cuda.synchronize()
+    t_m, t_a = start.elapsed_time(muon_done), start.elapsed_time(adamw_done)
+    print(f"Muon step done at {t_m:.3f} ms, AdamW (issued after it, other stream) at {t_a:.3f} ms")
+    assert t_a < t_m, "the AdamW call waited for the Muon step"
+    got = _bits(w + m + p + ea + eq)
+    assert all(np.array_equal(a, b) for a, b in zip(ref, got))
