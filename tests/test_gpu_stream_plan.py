@@ -190,3 +190,40 @@ def test_stream_plan_overlaps_the_producer():
           f"(optimizer hidden: {(t_seq - t_stream):.2f} ms)")
     assert t_stream < t_seq - 0.25 * t_prod, "the streamed step did not overlap the producer"
     plan.close()
+
+
+def test_stream_plan_mixed_formats_and_ragged_shapes():
+    """Groups that mix binary32, split-bf16 and bf16 matrices of ragged shapes,
+    one group empty: every matrix keeps the working format the whole set
+    gives it (a group alone would get smaller tiles), so the result is
+    bit-identical to one call, whatever the order of the submits."""
+    _announce("stream plan over mixed formats and ragged shapes")
+    spec = [((700, 1100), mb.NS_BF16), ((1100, 700), mb.NS_BF16), ((769, 769), mb.NS_F32),
+            ((300, 520), mb.NS_BF16X3), ((64, 64), mb.NS_BF16), ((1, 300), mb.NS_F32),
+            ((2049, 257), mb.NS_BF16), ((257, 2049), mb.NS_BF16X3)]
+    group_of = [0, 1, 0, 3, 1, 3, 0, 1]            # group 2 is empty
+    gen = torch.Generator().manual_seed(31)
+    w = [(torch.randn(s, generator=gen) * 0.02).to(torch.float32 if p == mb.NS_F32 else torch.bfloat16).cuda()
+         for s, p in spec]
+    g = [torch.randn(s, generator=gen).to(torch.bfloat16).cuda() for s, _ in spec]
+    m = [torch.randn(s, generator=gen).cuda() for s, _ in spec]
+    precs = [p for _, p in spec]
+    w0 = [t.clone() for t in w]
+    m0 = [t.clone() for t in m]
+    hp = dict(lr=f32(0.02), beta=0.95, nesterov=1, ns_coeffs=(3.4445, -4.775, 2.0315), ns_steps=4,
+              weight_decay=0.02, scale_per_matrix=[1.0, 1.5, 0.5, 2.0, 1.0, 0.25, 1.0, 3.0])
+    o_ref = [torch.empty(s, device="cuda") for s, _ in spec]
+    mb.muon_step_batched_v2(w, g, m, precision=precs, updates_out=o_ref, **hp)
+    torch.cuda.synchronize()
+    ref = [_bits(t) for t in w + m + o_ref]
+    for d, s in zip(w + m, w0 + m0):
+        d.copy_(s)
+    o = [torch.full(s, float("nan"), device="cuda") for s, _ in spec]
+    plan = mb.StreamPlan(w, g, m, group_of, 4, precision=precs, updates_out=o)
+    for grp in (3, 2, 0, 1):
+        plan.submit(grp, None, **hp)
+    torch.cuda.synchronize()
+    got = [_bits(t) for t in w + m + o]
+    for i, (a, b) in enumerate(zip(ref, got)):
+        assert np.array_equal(a, b), f"tensor {i} differs from the one-call result"
+    plan.close()
