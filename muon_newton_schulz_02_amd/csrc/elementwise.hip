@@ -168,7 +168,7 @@ __device__ inline float momentum_rows(const MatDev& md, int tr0, int tc0, float 
           if (col + e < cols) gmem(md.mom)[mi + e] = mn[e];
       }
     }
-    if (mode != 2) store4_ws(md.X[0], md.plane_X, md.prec, int64_t(row) * md.ldx + col, u);
+    if (mode != 2) store4_ws(md.X[0], md.plane_X, md.prec, ws_index(md.prec, row, col, md.ldx), u);
   }
   return ss;
 }
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
     for (int e = 0; e < 4; ++e) ss += u[e] * u[e];
     if (mode != 2) {
       if (!tr) {
-        store4_ws(xw, md.plane_X, prec, int64_t(row) * ldx + col, u);
+        store4_ws(xw, md.plane_X, prec, ws_index(prec, row, col, ldx), u);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) tile[rl][4 * cg + e] = u[e];
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = tile[4 * cg + e][j];
-      store4_ws(xw, md.plane_X, prec, int64_t(tc0 + j) * ldx + tr0 + 4 * cg, v);
+      store4_ws(xw, md.plane_X, prec, ws_index(prec, tc0 + j, tr0 + 4 * cg, ldx), v);
     }
   }
 
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(256) void writeback_direct_kernel(const MatDev* __r
   for (int e = threadIdx.x; e < th * tw; e += 256) {
     const int row = tr0 + e / tw, col = tc0 + e % tw;
     if (row >= md.rows || col >= md.cols) continue;
-    const int64_t xi = tr ? int64_t(col) * md.ldx + row : int64_t(row) * md.ldx + col;
+    const int64_t xi = tr ? ws_index(md.prec, col, row, md.ldx) : ws_index(md.prec, row, col, md.ldx);
     const float o = inv * load_ws(xw, md.plane_X, md.prec, xi);
     if (md.param) {
       const int64_t pi = int64_t(row) * md.ld_param + col;

@@ -81,6 +81,10 @@ MatGeom geom_of(const muon_matrix_desc& d) {
   g.npl = g.prec == PREC_BF16X3 ? 2 : 1;
   g.x_bytes = align256(size_t(g.Mp) * size_t(g.ldx) * g.esz * g.npl);
   g.a_bytes = align256(size_t(g.Mp) * size_t(g.lda) * g.esz * g.npl);
+  if (g.esz == 2 && g.npl == 1) {  // the 256 x 256 bf16 format may store tile by tile (ws_index)
+    g.x_bytes += align256(size_t(g.Mp / 256) * size_t(g.ldx / 256) * WS_TILE_PAD);
+    g.a_bytes += align256(size_t(g.Mp / 256) * size_t(g.lda / 256) * WS_TILE_PAD);
+  }
   return g;
 }
 

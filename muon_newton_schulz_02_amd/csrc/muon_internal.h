@@ -169,4 +169,24 @@ constexpr int ns_tile(int prec) { return prec == PREC_BF16 ? 256 : prec == PREC_
 constexpr bool bf16_single(int prec) { return prec == PREC_BF16 || prec == PREC_BF16S; }
 constexpr bool is_f32(int prec) { return prec == PREC_F32 || prec == PREC_F32S; }
 
+// Element (row, col) of a workspace matrix (X, A or B; wide orientation, row
+// stride ld elements).  The 256 x 256 bf16 format stores its buffers tile by
+// tile: tile (row / 256, col / 256) is 128 KB holding its 256 rows of 512
+// bytes one after the other, and the tiles of a tile row follow each other
+// (ld / 256 of them).  A product tile's output then leaves as one contiguous
+// block, and a 64-k stage of an operand is 256 runs of 128 bytes 512 bytes
+// apart (or, for a k-row operand, 32 KB in one piece).  The other formats
+// keep rows of ld elements.
+static_assert(LDPAD % PAD == 0, "tiled rows are whole tiles");
+constexpr int WS_TILE_BYTES = 256 * 256 * 2;
+// Tiles start WS_TILE_STRIDE bytes apart: the gap puts the same offset of
+// neighbouring tiles on different memory channels.
+constexpr int WS_TILE_PAD = 0;
+constexpr int WS_TILE_STRIDE = WS_TILE_BYTES + WS_TILE_PAD;
+__host__ __device__ inline int64_t ws_index(int prec, int64_t row, int64_t col, int64_t ld) {
+  if (prec == PREC_BF16)
+    return ((row >> 8) * (ld >> 8) + (col >> 8)) * (WS_TILE_STRIDE / 2) + ((row & 255) << 8) + (col & 255);
+  return row * ld + col;
+}
+
 }  // namespace muon

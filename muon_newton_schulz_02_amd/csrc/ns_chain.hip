@@ -43,7 +43,8 @@ __device__ __forceinline__ void chain_tile(const MatDev& md, const MatScal* __re
   const OpRsrc rsp = op_rsrc(sp), rsq = op_rsrc(sq);
   load_operand<PREC, PHASE, 0>(rp, sp, rsp, 0, threadIdx.x);
   load_operand<PREC, PHASE, 1>(rq, sq, rsq, 0, threadIdx.x);
-  ns_tile_body<PREC, PHASE, VAR, G::NREG>(md, scal, mat, ti, tj, pa, smem, rp, rq, false, sp, sq);
+  ns_tile_body<PREC, PHASE, VAR, G::NREG>(md, scal, mat, ti, tj, pa, smem, rp, rq,
+                                          [](OpSrc&, OpSrc&) { return false; });
 }
 
 template <int PREC>

@@ -89,10 +89,13 @@ __global__ __launch_bounds__(Cfg<PREC>::NT) void ns_gemm_kernel(const MatDev* __
   while (te.x >= 0) {
     const int nslot = slot + stride;
     const int2 tn = nslot < pa.per_xcd ? list[nslot] : int2{-1, 0};
-    OpSrc np = {}, nq = {};
-    if (tn.x >= 0) tile_ops<PREC, PHASE>(mats[tn.x], tn.y >> 16, tn.y & 0xFFFF, pa, np, nq);
-    ns_tile_body<PREC, PHASE, VAR, G::NREG>(mats[te.x], scal, te.x, te.y >> 16, te.y & 0xFFFF, pa, smem, rp, rq,
-                                            tn.x >= 0, np, nq);
+    // the next tile's operand sources, formed when its first stage is loaded
+    auto next = [&](OpSrc& np, OpSrc& nq) {
+      if (tn.x < 0) return false;
+      tile_ops<PREC, PHASE>(mats[tn.x], tn.y >> 16, tn.y & 0xFFFF, pa, np, nq);
+      return true;
+    };
+    ns_tile_body<PREC, PHASE, VAR, G::NREG>(mats[te.x], scal, te.x, te.y >> 16, te.y & 0xFFFF, pa, smem, rp, rq, next);
     lds_barrier();
     slot = nslot;
     te = tn;

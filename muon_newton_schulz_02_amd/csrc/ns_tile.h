@@ -307,6 +307,10 @@ struct OpSrc {
   int64_t plane_b;         // bytes between the hi and lo planes
   int sym_tile;            // symmetric operand: its tile-row index; -1: fixed layout
   int always_trans;        // COMB's X operand
+  // tiled bf16 (one buffer resource at `direct`, the matrix): byte offsets
+  // of the direct and transposed origins, and from one 256-k block of the
+  // transposed layout to the next
+  int org_d, org_t, kblk_t;
 };
 
 // Buffer resources over the two layouts of an operand: loads then take a
@@ -327,6 +331,16 @@ __device__ __forceinline__ bool stage_is_trans(const OpSrc& s, int kt) {
   if (s.always_trans) return true;
   if (s.sym_tile < 0) return false;
   return (kt * (KB / ESZ)) / BT < s.sym_tile;  // below the diagonal: read the mirror block
+}
+
+// The same choice for operand OPD (0: P, 1: Q) of a product, with what the
+// phase fixes decided at compile time: GRAM reads rows of X only, COMBINE's
+// iterate is read along its columns only.
+template <int PHASE, int OPD, int ESZ, int BT>
+__device__ __forceinline__ bool op_trans(const OpSrc& s, int kt) {
+  if constexpr (PHASE == PH_GRAM) return false;
+  else if constexpr (PHASE == PH_COMB && OPD == 1) return true;
+  else return (kt * (KB / ESZ)) / BT < s.sym_tile;
 }
 
 // Loads number I0 .. I1 - 1 of this thread's loads of one operand of stage kt
@@ -371,12 +385,16 @@ __device__ __forceinline__ void load_operand(u32x4 (&r)[Fmt<PREC>::npl][4], cons
     // row form (chunk tid + NT i: row tid / 8 + (NT / 8) i, 16 bytes at 16 (tid % 8))
     // or k-row form (k-row tid / 32 + (NT / 32) i, 16 bytes at 16 (tid % 32))
     static_assert(ESZ == 2 && BT * 2 == 32 * 16, "bf16 256-wide stages");
-    const bool tr = stage_is_trans<ESZ, BT>(s, kt);
-    const __amdgpu_buffer_rsrc_t rsrc = tr ? rs.trans : rs.direct;
-    const int ld = int(s.ld_b);
+    // tiled buffers (ws_index): 512-byte rows; stage kt is quarter kt % 4 of
+    // k-block kt / 4, the next tile of a direct operand's tile row or the
+    // next tile row (kblk_t bytes on) of a transposed one
+    const bool tr = op_trans<PHASE, OPD, ESZ, BT>(s, kt);
+    constexpr int ld = 512;
     const int off = tr ? (tid >> 5) * ld + (tid & 31) * 16 : (tid >> 3) * ld + (tid & 7) * 16;
     const int step = tr ? (NT / 32) * ld : (NT / 8) * ld;
-    const int sbase = tr ? kt * (KB / 2) * ld : kt * KB;
+    const int sbase = tr ? s.org_t + (kt >> 2) * s.kblk_t + (kt & 3) * ((KB / 2) * ld)
+                         : s.org_d + (kt >> 2) * WS_TILE_STRIDE + (kt & 3) * KB;
+    const __amdgpu_buffer_rsrc_t rsrc = rs.direct;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       r[0][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, sbase + i * step, 0));
@@ -471,25 +489,48 @@ template <int PREC, int PHASE>
 __device__ __forceinline__ int tile_ops(const MatDev& md, int ti, int tj, const PhaseArgs& pa, OpSrc& sp, OpSrc& sq) {
   constexpr int ESZ = Fmt<PREC>::esz;
   constexpr int BT = Cfg<PREC>::BT;
-  if constexpr (PHASE == PH_GRAM) {
+  if constexpr (PREC == PREC_BF16) {
+    // tiled buffers (ws_index): rows of 512 bytes inside a tile; the k-blocks
+    // of a direct operand are consecutive tiles of its tile row, those of a
+    // transposed one consecutive tile rows of its tile column
+    constexpr int TB = WS_TILE_STRIDE;
+    const int tpx = md.ldx >> 8, tpa = md.lda >> 8;
+    if constexpr (PHASE == PH_GRAM) {
+      const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
+      sp = {x, nullptr, 512, 0, -1, 0, ti * tpx * TB, 0, 0};
+      sq = {x, nullptr, 512, 0, -1, 0, tj * tpx * TB, 0, 0};
+      return md.Np;
+    } else if constexpr (PHASE == PH_POLY) {
+      const char* a = reinterpret_cast<const char*>(md.A);
+      sp = {a, nullptr, 512, 0, ti, 0, ti * tpa * TB, ti * TB, tpa * TB};
+      sq = {a, nullptr, 512, 0, tj, 0, tj * tpa * TB, tj * TB, tpa * TB};
+      return md.Mp;
+    } else {
+      const char* b = reinterpret_cast<const char*>(md.B);
+      const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
+      sp = {b, nullptr, 512, 0, ti, 0, ti * tpa * TB, ti * TB, tpa * TB};
+      sq = {x, nullptr, 512, 0, -1, 1, 0, tj * TB, tpx * TB};
+      return md.Mp;
+    }
+  } else if constexpr (PHASE == PH_GRAM) {
     const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
     const int64_t ld = int64_t(md.ldx) * ESZ;
-    sp = {x + int64_t(ti) * BT * ld, nullptr, ld, md.plane_X * ESZ, -1, 0};
-    sq = {x + int64_t(tj) * BT * ld, nullptr, ld, md.plane_X * ESZ, -1, 0};
+    sp = {x + int64_t(ti) * BT * ld, nullptr, ld, md.plane_X * ESZ, -1, 0, 0, 0, 0};
+    sq = {x + int64_t(tj) * BT * ld, nullptr, ld, md.plane_X * ESZ, -1, 0, 0, 0, 0};
     return md.Np;
   } else if constexpr (PHASE == PH_POLY) {
     const char* a = reinterpret_cast<const char*>(md.A);
     const int64_t ld = int64_t(md.lda) * ESZ;
     // blocks below the diagonal are read through their mirror block
-    sp = {a + int64_t(ti) * BT * ld, a + int64_t(ti) * BT * ESZ, ld, md.plane_A * ESZ, ti, 0};
-    sq = {a + int64_t(tj) * BT * ld, a + int64_t(tj) * BT * ESZ, ld, md.plane_A * ESZ, tj, 0};
+    sp = {a + int64_t(ti) * BT * ld, a + int64_t(ti) * BT * ESZ, ld, md.plane_A * ESZ, ti, 0, 0, 0, 0};
+    sq = {a + int64_t(tj) * BT * ld, a + int64_t(tj) * BT * ESZ, ld, md.plane_A * ESZ, tj, 0, 0, 0, 0};
     return md.Mp;
   } else {
     const char* b = reinterpret_cast<const char*>(md.B);
     const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
     const int64_t lda = int64_t(md.lda) * ESZ, ldx = int64_t(md.ldx) * ESZ;
-    sp = {b + int64_t(ti) * BT * lda, b + int64_t(ti) * BT * ESZ, lda, md.plane_A * ESZ, ti, 0};
-    sq = {nullptr, x + int64_t(tj) * BT * ESZ, ldx, md.plane_X * ESZ, -1, 1};
+    sp = {b + int64_t(ti) * BT * lda, b + int64_t(ti) * BT * ESZ, lda, md.plane_A * ESZ, ti, 0, 0, 0, 0};
+    sq = {nullptr, x + int64_t(tj) * BT * ESZ, ldx, md.plane_X * ESZ, -1, 1, 0, 0, 0};
     return md.Mp;
   }
 }
@@ -500,11 +541,11 @@ __device__ __forceinline__ int tile_ops(const MatDev& md, int ti, int tj, const 
 // rp / rq hold this thread's part of the tile's stage 0 on entry (loaded
 // while the previous tile finished); during the last stage they receive the
 // next tile's stage 0 (when has_next), whose operand sources are np / nq.
-template <int PREC, int PHASE, int VAR, int NREG>
+template <int PREC, int PHASE, int VAR, int NREG, typename NEXT>
 __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __restrict__ scal, int mat,
                                              int ti, int tj, const PhaseArgs& pa, char* smem,
                                              u32x4 (&rp)[Fmt<PREC>::npl][NREG], u32x4 (&rq)[Fmt<PREC>::npl][NREG],
-                                             bool has_next, const OpSrc& np, const OpSrc& nq) {
+                                             const NEXT& next) {
   constexpr int ESZ = Fmt<PREC>::esz;
   constexpr int NPL = Fmt<PREC>::npl;
   constexpr int BT = Cfg<PREC>::BT, NT = Cfg<PREC>::NT, WQN = Cfg<PREC>::WQ;
@@ -525,7 +566,6 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
   const int K = tile_ops<PREC, PHASE>(md, ti, tj, pa, sp, sq);
   const int nk = K / KE;
   const OpRsrc rsp = op_rsrc(sp), rsq = op_rsrc(sq);
-  const OpRsrc rnp = op_rsrc(np), rnq = op_rsrc(nq);
 
   // additive term alpha * D on the tile's own rows (POLY: (b/c) A, COMB: a X)
   constexpr bool ADD = PHASE != PH_GRAM;
@@ -655,16 +695,17 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     auto store_half = [&](const u32x4 (&r)[NPL][G::NREG], const OpSrc& src, int kt, auto base_c, auto h_c) {
       constexpr int BASE = decltype(base_c)::value;
       constexpr int H = decltype(h_c)::value;
-      const bool tr = stage_is_trans<ESZ, BT>(src, kt);
+      const bool tr = op_trans<PHASE, (BASE >= QOFF ? 1 : 0), ESZ, BT>(src, kt);
 #pragma unroll
       for (int i = 2 * H; i < 2 * H + 2; ++i) {
         const int off = tr ? stK + i * (NT / 32) * KP : stD + i * (NT / 8) * PITCH;
         *reinterpret_cast<u32x4*>(lds + BASE + off) = r[0][i];
       }
     };
-    const OpSrc& xp = has_next ? np : sp;   // the next tile's sources (or this tile's)
-    const OpSrc& xq = has_next ? nq : sq;
-    const OpRsrc rxp = op_rsrc(xp), rxq = op_rsrc(xq);
+    // the next tile's sources (or, without a next tile, this tile's), formed
+    // just before the last two stages load from them
+    OpSrc xp, xq;
+    OpRsrc rxp, rxq;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
 
@@ -675,8 +716,9 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     lds_barrier();
     load_operand<PREC, PHASE, 0>(rp, sp, rsp, 1, tid);
     load_operand<PREC, PHASE, 1>(rq, sq, rsq, 1, tid);
-    auto ktr = [&](const OpSrc& src, int kt) { return stage_is_trans<ESZ, BT>(src, kt); };
-    read_frags(F[0], I0{}, 0, ktr(sp, 0), ktr(sq, 0));
+    auto ktrP = [&](int kt) { return op_trans<PHASE, 0, ESZ, BT>(sp, kt); };
+    auto ktrQ = [&](int kt) { return op_trans<PHASE, 1, ESZ, BT>(sq, kt); };
+    read_frags(F[0], I0{}, 0, ktrP(0), ktrQ(0));
 
     // MODE 0: store stage kt + 1, load stage kt + 2 of this tile; 1: store
     // stage kt + 1, load the next tile's stage 0; 2: the last stage.
@@ -688,7 +730,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       using NP = std::integral_constant<int, (BUF ^ 1) * OPB>;
       using NQ = std::integral_constant<int, QOFF + (BUF ^ 1) * OPB>;
       // slab 0
-      const bool ptr = ktr(sp, kt), qtr = ktr(sq, kt);
+      const bool ptr = ktrP(kt), qtr = ktrQ(kt);
       read_frags(F[1], CUR{}, 1, ptr, qtr);
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(F[0], 0);
@@ -730,7 +772,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       identity_add(F[0], kt, 2);
       lds_barrier();
       // slab 3
-      if constexpr (MODE != 2) read_frags(F[0], NXT{}, 0, ktr(sp, kt + 1), ktr(sq, kt + 1));
+      if constexpr (MODE != 2) read_frags(F[0], NXT{}, 0, ktrP(kt + 1), ktrQ(kt + 1));
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(F[1], 0);
       mfma_half(F[1], 1);
@@ -742,6 +784,12 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       stage(kt, I0{}, I0{});
       stage(kt + 1, I1{}, I0{});
     }
+    if (!next(xp, xq)) {
+      xp = sp;
+      xq = sq;
+    }
+    rxp = op_rsrc(xp);
+    rxq = op_rsrc(xq);
     stage(nk - 2, I0{}, I1{});
     stage(nk - 1, I1{}, std::integral_constant<int, 2>{});
     lds_barrier();
@@ -758,6 +806,9 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     // One stage of the k-loop.  MORE: stage kt + 1 follows and is loaded; else
     // (the last stage) the loads fetch the next tile's stage 0, if any, which
     // then lands while this tile's epilogue runs.
+    OpSrc np, nq;                            // the next tile's sources (last stage)
+    OpRsrc rnp, rnq;
+    bool has_next = false;
     auto stage = [&](const int kt, auto more_c) {
       constexpr bool MORE = decltype(more_c)::value;
       const int s = kt & 1;
@@ -830,6 +881,11 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     };
   #pragma unroll 1
     for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, std::true_type{});
+    has_next = next(np, nq);
+    if (has_next) {
+      rnp = op_rsrc(np);
+      rnq = op_rsrc(nq);
+    }
     stage(nk - 1, std::false_type{});
   }
 
@@ -842,9 +898,8 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     char* out = reinterpret_cast<char*>((PHASE == PH_GRAM && VAR == 1) ? md.A : md.B);
     const float sc = PHASE == PH_POLY ? pa.c
                                       : (pa.first ? scal[mat].inv2 : 1.f) * (VAR == 1 ? 1.f : pa.b);
-    const int64_t ld = int64_t(md.lda) * 2;
-    store_tile_bf16<FQ, FP, WTP, WTQ, BT, NT, 2 * STAGE>(acc, sc, out + int64_t(ti) * BT * ld + int64_t(tj) * BT * 2,
-                                                       ld, smem, wp, wq, lane, tid);
+    store_tile_bf16<FQ, FP, WTP, WTQ, BT, NT, 2 * STAGE>(acc, sc, out + (int64_t(ti) * (md.lda >> 8) + tj) * WS_TILE_STRIDE,
+                                                       512, smem, wp, wq, lane, tid);
   } else if constexpr (PHASE == PH_GRAM || PHASE == PH_POLY) {
     void* out = (PHASE == PH_GRAM && VAR == 1) ? md.A : md.B;
     const float sc = PHASE == PH_POLY ? pa.c
@@ -863,9 +918,8 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
   } else {
     const float s = pa.first ? scal[mat].inv : 1.f;
     if constexpr (VAR == 0 && PREC == PREC_BF16) {
-      const int64_t ld = int64_t(md.ldx) * 2;
-      char* xn = reinterpret_cast<char*>(md.X[pa.cur ^ 1]) + int64_t(ti) * BT * ld + int64_t(tj) * BT * 2;
-      store_tile_bf16<FQ, FP, WTP, WTQ, BT, NT, 2 * STAGE>(acc, s, xn, ld, smem, wp, wq, lane, tid);
+      char* xn = reinterpret_cast<char*>(md.X[pa.cur ^ 1]) + (int64_t(ti) * (md.ldx >> 8) + tj) * WS_TILE_STRIDE;
+      store_tile_bf16<FQ, FP, WTP, WTQ, BT, NT, 2 * STAGE>(acc, s, xn, 512, smem, wp, wq, lane, tid);
     } else if constexpr (VAR == 0) {
       void* xn = md.X[pa.cur ^ 1];
 #pragma clang loop unroll(full)
