@@ -1,7 +1,7 @@
 """Benchmark of the Muon step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload d24_bf16]
-                    [--no-cpu-baseline] [--quiet-kernels]
+                    [--no-cpu-baseline] [--power SECONDS] [--copy-calibration]
 
 A step is one muon_step_batched call over every matrix of the workload
 (momentum, norm, Newton-Schulz, write-back), with weights, gradients and
@@ -69,6 +69,9 @@ def parse():
                          "large (bf16 256, fp32 128) or small (bf16 128, fp32 64)")
     ap.add_argument("--no-adamw", action="store_true",
                     help="skip timing the AdamW half of the hybrid optimizer (d24 non-matrix parameters)")
+    ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
+                    help="after the timed steps, run steps for SECONDS more while amd-smi samples the "
+                         "socket power and the shader clocks (reported as `power`; off by default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device once (a plain copy kernel "
                          "of known size, to scale HBM byte counters)")
@@ -156,6 +159,8 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step_plain = e0.elapsed_time(e1) / args.steps
+
+    power = sample_power(args.power, step, torch) if args.power > 0 else None
 
     if args.copy_calibration:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)
@@ -268,7 +273,57 @@ def main():
         "mfma_probe_tflops": round(mfma_tflops, 1),
         "cpu_baseline": cpu,
     }
+    if power is not None:
+        out["power"] = power
     print(json.dumps(out))
+
+
+def sample_power(seconds, step, torch, period=0.4):
+    """Socket power and shader clock while the step runs back to back: amd-smi
+    (`metric -p -c --json`) is sampled from a thread; the first second is
+    skipped.  Returns means over the samples, or an error string."""
+    import subprocess
+    import threading
+
+    samples, stop = [], threading.Event()
+
+    def parse(txt):
+        d = json.loads(txt)
+        d = d[0] if isinstance(d, list) else d
+        d = d.get("gpu_data", [d])[0] if isinstance(d, dict) and "gpu_data" in d else d
+        pw = d["power"]["socket_power"]
+        pw = pw["value"] if isinstance(pw, dict) else pw
+        clk = [v["clk"]["value"] for k, v in d["clock"].items()
+               if k.startswith("gfx_") and isinstance(v.get("clk"), dict) and isinstance(v["clk"]["value"], (int, float))]
+        return float(pw), sum(clk) / len(clk)
+
+    def sampler():
+        stop.wait(1.0)
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"],
+                                   capture_output=True, text=True, timeout=10)
+                if r.returncode == 0:
+                    samples.append(parse(r.stdout))
+            except Exception:  # noqa: BLE001 - a failed sample is skipped
+                pass
+            stop.wait(period)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    if not samples:
+        return {"error": "no amd-smi sample"}
+    return {"socket_power_w": round(sum(p for p, _ in samples) / len(samples), 1),
+            "socket_power_w_min": min(p for p, _ in samples), "socket_power_w_max": max(p for p, _ in samples),
+            "gfx_clock_mhz": round(sum(c for _, c in samples) / len(samples), 1), "samples": len(samples),
+            "seconds": seconds, "tool": "amd-smi metric -g 0 -p -c --json"}
 
 
 def mfma_probe_tflops(mb, torch, dev, stream, iterations=200000):
