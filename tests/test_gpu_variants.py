@@ -86,6 +86,27 @@ def test_weight_decay_and_per_matrix_rates(pdt, steps):
         assert np.array_equal(bits(w1[i]), bits(w_exp)), f"matrix {i}: write-back"
 
 
+@pytest.mark.parametrize("tile_mode", [mb.TILES_LARGE, mb.TILES_SMALL])
+@pytest.mark.parametrize("steps", [0, 1])
+def test_few_steps_on_both_bf16_tile_sizes(tile_mode, steps):
+    # no Newton-Schulz step (the write-back reads U back from the workspace)
+    # and one step, on the tile-major workspace of the 256 x 256 tiles and on
+    # the row-major one of the 128 x 128 tiles
+    _announce(f"bf16 steps={steps} tile_mode={tile_mode}")
+    ws, gs, ms = _inputs(83 + steps + 2 * tile_mode, torch.bfloat16)
+    lr = f32(0.02)
+    w1, m1, o1 = _run_v2(ws, gs, ms, precision=mb.NS_BF16, steps=steps, lr=lr, beta=0.95, nesterov=1,
+                         tile_mode=tile_mode)
+    for i in range(len(SHAPES)):
+        w0, g0, m0 = to_np(ws[i]), to_np(gs[i]), to_np(ms[i])
+        ref = orc.muon_step(w0, g0, m0, lr=lr, beta=0.95, nesterov=True, coeffs=MUON, steps=steps, param_bf16=True)
+        assert np.array_equal(bits(m1[i]), bits(ref.m)), f"matrix {i}: momentum"
+        err = orc.rel_frobenius(o1[i], ref.o)
+        print(f"  {SHAPES[i]}: rel-F {err:.2e}")
+        assert err <= PREC_TOL[mb.NS_BF16]
+        assert np.array_equal(bits(w1[i]), bits(orc.write_back(w0, o1[i], lr, 1.0, True))), f"matrix {i}: write-back"
+
+
 def test_default_options_match_plain_step():
     _announce("v2 with default options equals the plain step")
     ws, gs, ms = _inputs(61, torch.bfloat16)
