@@ -58,7 +58,7 @@ __device__ inline void store4_ws(void* base, int64_t plane, int prec, int64_t id
     uint16_t* p = reinterpret_cast<uint16_t*>(base);
     const uint32_t h01 = float2_to_bf16x2_bits(v[0], v[1]), h23 = float2_to_bf16x2_bits(v[2], v[3]);
     *gmem(reinterpret_cast<u32x2*>(p + idx)) = u32x2{h01, h23};
-    if (prec == PREC_BF16X3) {
+    if (is_split(prec)) {
       const uint32_t l01 = float2_to_bf16x2_bits(v[0] - bf16_bits_to_float(h01), v[1] - bf16_bits_to_float(h01 >> 16));
       const uint32_t l23 = float2_to_bf16x2_bits(v[2] - bf16_bits_to_float(h23), v[3] - bf16_bits_to_float(h23 >> 16));
       *gmem(reinterpret_cast<u32x2*>(p + plane + idx)) = u32x2{l01, l23};
@@ -70,7 +70,7 @@ __device__ inline float load_ws(const void* base, int64_t plane, int prec, int64
   if (is_f32(prec)) return gmem(reinterpret_cast<const float*>(base))[idx];
   auto p = gmem(reinterpret_cast<const uint16_t*>(base));
   float v = bf16_bits_to_float(p[idx]);
-  if (prec == PREC_BF16X3) v = v + bf16_bits_to_float(p[plane + idx]);
+  if (is_split(prec)) v = v + bf16_bits_to_float(p[plane + idx]);
   return v;
 }
 

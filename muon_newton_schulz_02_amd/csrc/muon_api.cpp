@@ -78,13 +78,9 @@ MatGeom geom_of(const muon_matrix_desc& d) {
   g.lda = g.Mp + LDPAD;
   g.prec = d.precision;
   g.esz = is_f32(g.prec) ? 4 : 2;
-  g.npl = g.prec == PREC_BF16X3 ? 2 : 1;
+  g.npl = is_split(g.prec) ? 2 : 1;
   g.x_bytes = align256(size_t(g.Mp) * size_t(g.ldx) * g.esz * g.npl);
   g.a_bytes = align256(size_t(g.Mp) * size_t(g.lda) * g.esz * g.npl);
-  if (g.esz == 2 && g.npl == 1) {  // the 256 x 256 bf16 format may store tile by tile (ws_index)
-    g.x_bytes += align256(size_t(g.Mp / 256) * size_t(g.ldx / 256) * WS_TILE_PAD);
-    g.a_bytes += align256(size_t(g.Mp / 256) * size_t(g.lda / 256) * WS_TILE_PAD);
-  }
   return g;
 }
 
@@ -490,7 +486,7 @@ std::vector<int2> xcd_lists(const std::vector<TileSrc>& src, int32_t* per_xcd, i
 }
 
 // Workgroups of a phase kernel per compute unit (as the launchers size their grids).
-int per_cu_blocks(int prec) { return (ns_tile(prec) == 256 || prec == PREC_BF16X3) ? 1 : 2; }
+int per_cu_blocks(int prec) { return (ns_tile(prec) == 256 || is_split(prec)) ? 1 : 2; }
 
 // Matrices by decreasing Newton-Schulz cost, so large ones start first.
 std::vector<int> cost_order(const std::vector<MatDev>& hm) {
@@ -995,18 +991,21 @@ std::vector<int> working_formats(const muon_matrix_desc* shapes, int32_t count, 
                                  int64_t cus) {
   std::vector<int> iprec(size_t(count), PREC_BF16);
   if (mode != MODE_NORMS) {
-    int64_t bf16_gram = 0, f32_gram = 0;
+    int64_t bf16_gram = 0, f32_gram = 0, x3_gram = 0;
     for (int32_t i = 0; i < count; ++i) {
       if (shapes[i].precision == MUON_NS_BF16) bf16_gram += gram_tiles_of(shapes[i], PREC_BF16);
       if (shapes[i].precision == MUON_NS_F32) f32_gram += gram_tiles_of(shapes[i], PREC_F32);
+      if (shapes[i].precision == MUON_NS_BF16X3) x3_gram += gram_tiles_of(shapes[i], PREC_BF16X3);
     }
     const bool small_bf16 = tmode == MUON_TILES_SMALL || (tmode == MUON_TILES_AUTO && bf16_gram < cus);
     const bool small_f32 = tmode == MUON_TILES_SMALL || (tmode == MUON_TILES_AUTO && f32_gram < cus);
+    const bool small_x3 = tmode == MUON_TILES_SMALL || (tmode == MUON_TILES_AUTO && x3_gram < cus);
     for (int32_t i = 0; i < count; ++i) {
       const int p = shapes[i].precision;
       iprec[size_t(i)] = (p == MUON_NS_BF16 && small_bf16) ? int(PREC_BF16S)
                          : (p == MUON_NS_F32 && small_f32) ? int(PREC_F32S)
-                                                           : p;
+                         : (p == MUON_NS_BF16X3 && small_x3) ? int(PREC_BF16X3S)
+                                                             : p;
     }
   }
   return iprec;

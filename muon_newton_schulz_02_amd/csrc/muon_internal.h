@@ -26,9 +26,10 @@ constexpr int NUM_XCD = 8;
 // Working formats of the Newton-Schulz products.  PREC_BF16S is the bf16
 // format on 128 x 128 tiles (a one-stage k-loop), chosen for stacks too small
 // to fill the GPU with 256 x 256 tiles; it stores exactly what PREC_BF16 does.
-// PREC_F32S is likewise the binary32 format on 64 x 64 tiles, for binary32
-// stacks too small to fill the GPU with 128 x 128 tiles.
-enum Prec : int { PREC_BF16 = 0, PREC_BF16X3 = 1, PREC_F32 = 2, PREC_BF16S = 3, PREC_F32S = 4 };
+// PREC_BF16X3S is likewise the split-bf16 format on 128 x 128 tiles, and
+// PREC_F32S the binary32 format on 64 x 64 tiles, for binary32 stacks too
+// small to fill the GPU with 128 x 128 tiles.
+enum Prec : int { PREC_BF16 = 0, PREC_BF16X3 = 1, PREC_F32 = 2, PREC_BF16S = 3, PREC_F32S = 4, PREC_BF16X3S = 5 };
 
 // Per-matrix device descriptor.  "natural" means the caller's orientation
 // (rows x cols); the iteration runs on the wide orientation m x n (m <= n).
@@ -162,29 +163,31 @@ constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
 hipError_t noalloc_scratch(int dev, void** out);
 
 // Tile edge of the Newton-Schulz products (square tiles) per format: 256 for
-// bf16 (LDS holds two stages of 256x64 bf16 per operand); 128 where an
-// operand takes twice the bytes (split-bf16 planes, float32) and for the
-// small-stack bf16 tiles; 64 for the small-stack binary32 tiles.
-constexpr int ns_tile(int prec) { return prec == PREC_BF16 ? 256 : prec == PREC_F32S ? 64 : 128; }
+// bf16 and split-bf16 (LDS holds two stages of 256x64 bf16 per operand; the
+// split-bf16 products stage one plane at a time); 128 for float32 (an operand
+// takes twice the bytes) and for the small-stack bf16 and split-bf16 tiles;
+// 64 for the small-stack binary32 tiles.
+constexpr int ns_tile(int prec) {
+  return (prec == PREC_BF16 || prec == PREC_BF16X3) ? 256 : prec == PREC_F32S ? 64 : 128;
+}
 constexpr bool bf16_single(int prec) { return prec == PREC_BF16 || prec == PREC_BF16S; }
 constexpr bool is_f32(int prec) { return prec == PREC_F32 || prec == PREC_F32S; }
+constexpr bool is_split(int prec) { return prec == PREC_BF16X3 || prec == PREC_BF16X3S; }
 
 // Element (row, col) of a workspace matrix (X, A or B; wide orientation, row
-// stride ld elements).  The 256 x 256 bf16 format stores its buffers tile by
-// tile: tile (row / 256, col / 256) is 128 KB holding its 256 rows of 512
+// stride ld elements; for split-bf16, of either plane).  The 256 x 256 bf16
+// and split-bf16 formats store their buffers tile by tile: tile (row / 256, col / 256) is 128 KB holding its 256 rows of 512
 // bytes one after the other, and the tiles of a tile row follow each other
 // (ld / 256 of them).  A product tile's output then leaves as one contiguous
 // block, and a 64-k stage of an operand is 256 runs of 128 bytes 512 bytes
 // apart (or, for a k-row operand, 32 KB in one piece).  The other formats
 // keep rows of ld elements.
 static_assert(LDPAD % PAD == 0, "tiled rows are whole tiles");
-constexpr int WS_TILE_BYTES = 256 * 256 * 2;
-// Tiles start WS_TILE_STRIDE bytes apart: the gap puts the same offset of
-// neighbouring tiles on different memory channels.
-constexpr int WS_TILE_PAD = 0;
-constexpr int WS_TILE_STRIDE = WS_TILE_BYTES + WS_TILE_PAD;
+// Bytes from one tile to the next (no gap: gaps of 256 B to 8.25 KB between
+// tiles were measured to change nothing).
+constexpr int WS_TILE_STRIDE = 256 * 256 * 2;
 __host__ __device__ inline int64_t ws_index(int prec, int64_t row, int64_t col, int64_t ld) {
-  if (prec == PREC_BF16)
+  if (prec == PREC_BF16 || prec == PREC_BF16X3)
     return ((row >> 8) * (ld >> 8) + (col >> 8)) * (WS_TILE_STRIDE / 2) + ((row & 255) << 8) + (col & 255);
   return row * ld + col;
 }

@@ -37,12 +37,12 @@ template <int PREC, int PHASE, int VAR>
 __device__ __forceinline__ void chain_tile(const MatDev& md, const MatScal* __restrict__ scal, int mat, int ti,
                                            int tj, const PhaseArgs& pa, char* smem) {
   using G = Geo<Fmt<PREC>::esz, Cfg<PREC>::BT, Cfg<PREC>::NT>;
-  u32x4 rp[Fmt<PREC>::npl][G::NREG], rq[Fmt<PREC>::npl][G::NREG];
+  u32x4 rp[Fmt<PREC>::spl][G::NREG], rq[Fmt<PREC>::spl][G::NREG];
   OpSrc sp, sq;
   tile_ops<PREC, PHASE>(md, ti, tj, pa, sp, sq);
   const OpRsrc rsp = op_rsrc(sp), rsq = op_rsrc(sq);
-  load_operand<PREC, PHASE, 0>(rp, sp, rsp, 0, threadIdx.x);
-  load_operand<PREC, PHASE, 1>(rq, sq, rsq, 0, threadIdx.x);
+  load_operand<PREC, PHASE, 0>(rp, sp, rsp, 0, threadIdx.x, split_plane(0, 0));
+  load_operand<PREC, PHASE, 1>(rq, sq, rsq, 0, threadIdx.x, split_plane(1, 0));
   ns_tile_body<PREC, PHASE, VAR, G::NREG>(md, scal, mat, ti, tj, pa, smem, rp, rq,
                                           [](OpSrc&, OpSrc&) { return false; });
 }
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(Cfg<PREC>::NT) void ns_chain_kernel(const MatDev* _
                                                                  const PhaseArgs* __restrict__ steps,
                                                                  int32_t* __restrict__ sync, int32_t* fail,
                                                                  int64_t spin_limit) {
-  constexpr int NPL = Fmt<PREC>::npl;
+  constexpr int NPL = Fmt<PREC>::spl;
   constexpr int STAGE = 2 * NPL * Cfg<PREC>::BT * PITCH;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   __shared__ int s_item, s_ok;
@@ -164,7 +164,7 @@ hipError_t launch_chain_prec(const MatDev* imats, const MatScal* scal, const Cha
                      sync, nsync, steps, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || per_xcd_max <= 0) return e;
-  constexpr int per_cu = (ns_tile(PREC) == 256 || PREC == PREC_BF16X3) ? 1 : 2;
+  constexpr int per_cu = (ns_tile(PREC) == 256 || is_split(PREC)) ? 1 : 2;
   const int per_xcd = std::min(per_xcd_max, args.cus_per_xcd * per_cu);
   hipLaunchKernelGGL(ns_chain_kernel<PREC>, dim3(unsigned(NUM_XCD) * unsigned(per_xcd)), dim3(Cfg<PREC>::NT), 0,
                      stream, imats, scal, items, xcd_off, steps, sync, fail, args.spin_limit);
@@ -192,6 +192,9 @@ hipError_t launch_ns_chain(int prec, const MatDev* imats, const MatScal* scal, c
     case PREC_F32S:
       return launch_chain_prec<PREC_F32S>(imats, scal, items, xcd_off, per_xcd_max, steps, sync, nsync, fail, args,
                                           stream);
+    case PREC_BF16X3S:
+      return launch_chain_prec<PREC_BF16X3S>(imats, scal, items, xcd_off, per_xcd_max, steps, sync, nsync, fail,
+                                             args, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -67,7 +67,7 @@ template <int PREC, int PHASE, int VAR>
 __global__ __launch_bounds__(Cfg<PREC>::NT) void ns_gemm_kernel(const MatDev* __restrict__ mats,
                                                                 const MatScal* __restrict__ scal,
                                                                 const int2* __restrict__ tiles, PhaseArgs pa) {
-  constexpr int NPL = Fmt<PREC>::npl;
+  constexpr int NPL = Fmt<PREC>::spl;
   constexpr int STAGE = 2 * NPL * Cfg<PREC>::BT * PITCH;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
   const int xcd = blockIdx.x % NUM_XCD;
@@ -82,8 +82,8 @@ __global__ __launch_bounds__(Cfg<PREC>::NT) void ns_gemm_kernel(const MatDev* __
     OpSrc sp, sq;
     tile_ops<PREC, PHASE>(mats[te.x], te.y >> 16, te.y & 0xFFFF, pa, sp, sq);
     const OpRsrc rsp = op_rsrc(sp), rsq = op_rsrc(sq);
-    load_operand<PREC, PHASE, 0>(rp, sp, rsp, 0, threadIdx.x);
-    load_operand<PREC, PHASE, 1>(rq, sq, rsq, 0, threadIdx.x);
+    load_operand<PREC, PHASE, 0>(rp, sp, rsp, 0, threadIdx.x, split_plane(0, 0));
+    load_operand<PREC, PHASE, 1>(rq, sq, rsq, 0, threadIdx.x, split_plane(1, 0));
   }
 #pragma unroll 1
   while (te.x >= 0) {
@@ -107,7 +107,7 @@ hipError_t launch_one(const MatDev* mats, const MatScal* scal, const int2* tiles
                       const PhaseArgs& pa, hipStream_t stream) {
   if (pa.per_xcd <= 0) return hipSuccess;
   // resident workgroups per XCD: CUs per XCD times workgroups per CU (LDS-bound)
-  constexpr int per_cu = (ns_tile(PREC) == 256 || PREC == PREC_BF16X3) ? 1 : 2;
+  constexpr int per_cu = (ns_tile(PREC) == 256 || is_split(PREC)) ? 1 : 2;
   const int per_xcd = std::min(pa.per_xcd, pa.cus_per_xcd * per_cu);
   const unsigned grid = unsigned(NUM_XCD) * unsigned(per_xcd);
   static_assert(Cfg<PREC>::BT == ns_tile(PREC), "tile size disagrees with the host's tile lists");
@@ -141,6 +141,7 @@ hipError_t launch_ns_phase(int prec, int phase, const MatDev* mats, const MatSca
     case PREC_F32: return launch_prec<PREC_F32>(phase, mats, scal, tiles, args, stream);
     case PREC_BF16S: return launch_prec<PREC_BF16S>(phase, mats, scal, tiles, args, stream);
     case PREC_F32S: return launch_prec<PREC_F32S>(phase, mats, scal, tiles, args, stream);
+    case PREC_BF16X3S: return launch_prec<PREC_BF16X3S>(phase, mats, scal, tiles, args, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -34,12 +34,17 @@ typedef __attribute__((address_space(1))) const u32x2 gu32x2;
 constexpr int KB = 128;     // bytes of K per operand row per stage
 constexpr int PITCH = 144;  // LDS row pitch in bytes
 
+// Element size and the number of planes a k-step stages together: the
+// pipelined split-bf16 tiles stage one plane at a time (each product is three
+// bf16 products over K, one per pair of planes), the one-stage split-bf16
+// tiles both planes of a k-step.
 template <int PREC> struct Fmt;
-template <> struct Fmt<PREC_BF16> { static constexpr int esz = 2, npl = 1; };
-template <> struct Fmt<PREC_BF16X3> { static constexpr int esz = 2, npl = 2; };
-template <> struct Fmt<PREC_F32> { static constexpr int esz = 4, npl = 1; };
-template <> struct Fmt<PREC_BF16S> { static constexpr int esz = 2, npl = 1; };
-template <> struct Fmt<PREC_F32S> { static constexpr int esz = 4, npl = 1; };
+template <> struct Fmt<PREC_BF16> { static constexpr int esz = 2, spl = 1; };
+template <> struct Fmt<PREC_BF16X3> { static constexpr int esz = 2, spl = 1; };
+template <> struct Fmt<PREC_F32> { static constexpr int esz = 4, spl = 1; };
+template <> struct Fmt<PREC_BF16S> { static constexpr int esz = 2, spl = 1; };
+template <> struct Fmt<PREC_F32S> { static constexpr int esz = 4, spl = 1; };
+template <> struct Fmt<PREC_BF16X3S> { static constexpr int esz = 2, spl = 2; };
 
 // Tile shape per format: T x T tile, WP x WQ waves (rows x columns), NT threads.
 // bf16: 256 x 256 over eight waves (two per SIMD, each 128 x 64, 128
@@ -49,11 +54,12 @@ template <> struct Fmt<PREC_F32S> { static constexpr int esz = 4, npl = 1; };
 // The bf16 tiles run the software-pipelined k-loop with their own LDS layout
 // (and transposed-operand block order); the other formats stage one k-step at
 // a time in the swizzled layout.
-constexpr bool pipelined(int prec) { return prec == PREC_BF16; }
+constexpr bool pipelined(int prec) { return prec == PREC_BF16 || prec == PREC_BF16X3; }
 
 template <int PREC> struct Cfg;
 template <> struct Cfg<PREC_BF16> { static constexpr int BT = 256, WP = 2, WQ = 4, NT = 512; };
-template <> struct Cfg<PREC_BF16X3> { static constexpr int BT = 128, WP = 2, WQ = 2, NT = 256; };
+template <> struct Cfg<PREC_BF16X3> { static constexpr int BT = 256, WP = 2, WQ = 4, NT = 512; };
+template <> struct Cfg<PREC_BF16X3S> { static constexpr int BT = 128, WP = 2, WQ = 2, NT = 256; };
 template <> struct Cfg<PREC_F32> { static constexpr int BT = 128, WP = 2, WQ = 2, NT = 256; };
 template <> struct Cfg<PREC_BF16S> { static constexpr int BT = 128, WP = 2, WQ = 2, NT = 256; };
 // small-stack binary32: 64 x 64 over two waves of 32 x 64
@@ -82,7 +88,7 @@ __device__ __forceinline__ void st4(void* base, int64_t plane, int64_t idx, cons
     uint16_t* p = reinterpret_cast<uint16_t*>(base);
     const uint32_t h01 = float2_to_bf16x2_bits(v[0], v[1]), h23 = float2_to_bf16x2_bits(v[2], v[3]);
     *gmem(reinterpret_cast<u32x2*>(p + idx)) = u32x2{h01, h23};
-    if constexpr (PREC == PREC_BF16X3) {
+    if constexpr (is_split(PREC)) {
       const uint32_t l01 = float2_to_bf16x2_bits(v[0] - bf16_bits_to_float(h01), v[1] - bf16_bits_to_float(h01 >> 16));
       const uint32_t l23 = float2_to_bf16x2_bits(v[2] - bf16_bits_to_float(h23), v[3] - bf16_bits_to_float(h23 >> 16));
       *gmem(reinterpret_cast<u32x2*>(p + plane + idx)) = u32x2{l01, l23};
@@ -222,7 +228,7 @@ __device__ __forceinline__ void mfma_step(f32x16& acc, const u32x4* q, const u32
   if constexpr (bf16_single(PREC)) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q[0]),
                                                    __builtin_bit_cast(bf16x8, p[0]), acc, 0, 0, 0);
-  } else if constexpr (PREC == PREC_BF16X3) {
+  } else if constexpr (is_split(PREC)) {
     // small cross terms first, then hi*hi
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q[1]),
                                                    __builtin_bit_cast(bf16x8, p[0]), acc, 0, 0, 0);
@@ -343,6 +349,12 @@ __device__ __forceinline__ bool op_trans(const OpSrc& s, int kt) {
   else return (kt * (KB / ESZ)) / BT < s.sym_tile;
 }
 
+// The pipelined split-bf16 tiles run a product as three bf16 products over
+// K, one per segment of the k-loop: segment 0 pairs the lo plane of Q with
+// the hi plane of P, segment 1 hi with lo, segment 2 hi with hi (the small
+// cross terms first).  The plane (0: hi, 1: lo) operand OPD takes in segment seg.
+constexpr int split_plane(int opd, int seg) { return opd == 0 ? (seg == 1 ? 1 : 0) : (seg == 0 ? 1 : 0); }
+
 // Loads number I0 .. I1 - 1 of this thread's loads of one operand of stage kt
 // (numbered q * 4 + e for the transposed layout, q for the direct one).  Both
 // layouts take NREG loads per thread; the layout is selected per load (buffer
@@ -376,10 +388,11 @@ __device__ __forceinline__ void load_stage(u32x4 (&r)[NPL][NREG], const OpSrc& s
 }
 
 // Operand OPD (0: P, 1: Q) of stage kt into registers, in the form the
-// tile's k-loop stages it.
+// tile's k-loop stages it; the pipelined split-bf16 tiles take plane pl of it
+// (0: hi, 1: lo; the other formats stage every plane and ignore pl).
 template <int PREC, int PHASE, int OPD>
-__device__ __forceinline__ void load_operand(u32x4 (&r)[Fmt<PREC>::npl][4], const OpSrc& s, const OpRsrc& rs, int kt,
-                                             int tid) {
+__device__ __forceinline__ void load_operand(u32x4 (&r)[Fmt<PREC>::spl][4], const OpSrc& s, const OpRsrc& rs, int kt,
+                                             int tid, int pl) {
   constexpr int ESZ = Fmt<PREC>::esz, BT = Cfg<PREC>::BT, NT = Cfg<PREC>::NT;
   if constexpr (pipelined(PREC)) {
     // row form (chunk tid + NT i: row tid / 8 + (NT / 8) i, 16 bytes at 16 (tid % 8))
@@ -392,14 +405,15 @@ __device__ __forceinline__ void load_operand(u32x4 (&r)[Fmt<PREC>::npl][4], cons
     constexpr int ld = 512;
     const int off = tr ? (tid >> 5) * ld + (tid & 31) * 16 : (tid >> 3) * ld + (tid & 7) * 16;
     const int step = tr ? (NT / 32) * ld : (NT / 8) * ld;
-    const int sbase = tr ? s.org_t + (kt >> 2) * s.kblk_t + (kt & 3) * ((KB / 2) * ld)
-                         : s.org_d + (kt >> 2) * WS_TILE_STRIDE + (kt & 3) * KB;
+    int sbase = tr ? s.org_t + (kt >> 2) * s.kblk_t + (kt & 3) * ((KB / 2) * ld)
+                   : s.org_d + (kt >> 2) * WS_TILE_STRIDE + (kt & 3) * KB;
+    if constexpr (PREC == PREC_BF16X3) sbase += pl ? int(s.plane_b) : 0;
     const __amdgpu_buffer_rsrc_t rsrc = rs.direct;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       r[0][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, sbase + i * step, 0));
   } else {
-    load_stage<ESZ, BT, NT, Fmt<PREC>::npl, 4>(r, s, rs, kt, tid);
+    load_stage<ESZ, BT, NT, Fmt<PREC>::spl, 4>(r, s, rs, kt, tid);
   }
 }
 
@@ -455,7 +469,16 @@ __device__ __forceinline__ void store_stage(const u32x4 (&r)[NPL][NREG], const O
 // 32 lanes write 512 contiguous bytes of one row (stores straight from the
 // accumulators would put 16 bytes into each of 32 rows per instruction).
 // The k-loop has ended with a barrier, so the operand stages are free.
-template <int FQ, int FP, int WTP, int WTQ, int BT, int NT, int LDSB>
+// Plane PL of two values in the bf16 working formats: 0 the bf16 rounding
+// (hi), 1 the bf16 rounding of what hi leaves (lo).
+template <int PL>
+__device__ __forceinline__ uint32_t bf16x2_plane(float a, float b) {
+  const uint32_t h = float2_to_bf16x2_bits(a, b);
+  if constexpr (PL == 0) return h;
+  else return float2_to_bf16x2_bits(a - bf16_bits_to_float(h), b - bf16_bits_to_float(h >> 16));
+}
+
+template <int FQ, int FP, int WTP, int WTQ, int BT, int NT, int LDSB, int PL = 0>
 __device__ __forceinline__ void store_tile_bf16(const f32x16 (&acc)[FQ][FP], float sc, char* out, int64_t ld,
                                                 char* smem, int wp, int wq, int lane, int tid) {
   constexpr int EP = BT * 2 + 16;  // staging pitch in bytes
@@ -470,8 +493,8 @@ __device__ __forceinline__ void store_tile_bf16(const f32x16 (&acc)[FQ][FP], flo
         const int r = wp * WTP + 32 * i + (lane & 31), c = wq * WTQ + 32 * j + 8 * g + 4 * hsel;
         const f32x16& a = acc[j][i];
         *reinterpret_cast<u32x2*>(smem + r * EP + c * 2) =
-            u32x2{float2_to_bf16x2_bits(sc * a[4 * g], sc * a[4 * g + 1]),
-                  float2_to_bf16x2_bits(sc * a[4 * g + 2], sc * a[4 * g + 3])};
+            u32x2{bf16x2_plane<PL>(sc * a[4 * g], sc * a[4 * g + 1]),
+                  bf16x2_plane<PL>(sc * a[4 * g + 2], sc * a[4 * g + 3])};
       }
   lds_barrier();
   constexpr int CPR = BT * 2 / 16;  // 16-byte chunks per row
@@ -489,7 +512,7 @@ template <int PREC, int PHASE>
 __device__ __forceinline__ int tile_ops(const MatDev& md, int ti, int tj, const PhaseArgs& pa, OpSrc& sp, OpSrc& sq) {
   constexpr int ESZ = Fmt<PREC>::esz;
   constexpr int BT = Cfg<PREC>::BT;
-  if constexpr (PREC == PREC_BF16) {
+  if constexpr (pipelined(PREC)) {
     // tiled buffers (ws_index): rows of 512 bytes inside a tile; the k-blocks
     // of a direct operand are consecutive tiles of its tile row, those of a
     // transposed one consecutive tile rows of its tile column
@@ -497,19 +520,19 @@ __device__ __forceinline__ int tile_ops(const MatDev& md, int ti, int tj, const 
     const int tpx = md.ldx >> 8, tpa = md.lda >> 8;
     if constexpr (PHASE == PH_GRAM) {
       const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
-      sp = {x, nullptr, 512, 0, -1, 0, ti * tpx * TB, 0, 0};
-      sq = {x, nullptr, 512, 0, -1, 0, tj * tpx * TB, 0, 0};
+      sp = {x, nullptr, 512, md.plane_X * 2, -1, 0, ti * tpx * TB, 0, 0};
+      sq = {x, nullptr, 512, md.plane_X * 2, -1, 0, tj * tpx * TB, 0, 0};
       return md.Np;
     } else if constexpr (PHASE == PH_POLY) {
       const char* a = reinterpret_cast<const char*>(md.A);
-      sp = {a, nullptr, 512, 0, ti, 0, ti * tpa * TB, ti * TB, tpa * TB};
-      sq = {a, nullptr, 512, 0, tj, 0, tj * tpa * TB, tj * TB, tpa * TB};
+      sp = {a, nullptr, 512, md.plane_A * 2, ti, 0, ti * tpa * TB, ti * TB, tpa * TB};
+      sq = {a, nullptr, 512, md.plane_A * 2, tj, 0, tj * tpa * TB, tj * TB, tpa * TB};
       return md.Mp;
     } else {
       const char* b = reinterpret_cast<const char*>(md.B);
       const char* x = reinterpret_cast<const char*>(md.X[pa.cur]);
-      sp = {b, nullptr, 512, 0, ti, 0, ti * tpa * TB, ti * TB, tpa * TB};
-      sq = {x, nullptr, 512, 0, -1, 1, 0, tj * TB, tpx * TB};
+      sp = {b, nullptr, 512, md.plane_A * 2, ti, 0, ti * tpa * TB, ti * TB, tpa * TB};
+      sq = {x, nullptr, 512, md.plane_X * 2, -1, 1, 0, tj * TB, tpx * TB};
       return md.Mp;
     }
   } else if constexpr (PHASE == PH_GRAM) {
@@ -544,10 +567,10 @@ __device__ __forceinline__ int tile_ops(const MatDev& md, int ti, int tj, const 
 template <int PREC, int PHASE, int VAR, int NREG, typename NEXT>
 __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __restrict__ scal, int mat,
                                              int ti, int tj, const PhaseArgs& pa, char* smem,
-                                             u32x4 (&rp)[Fmt<PREC>::npl][NREG], u32x4 (&rq)[Fmt<PREC>::npl][NREG],
+                                             u32x4 (&rp)[Fmt<PREC>::spl][NREG], u32x4 (&rq)[Fmt<PREC>::spl][NREG],
                                              const NEXT& next) {
   constexpr int ESZ = Fmt<PREC>::esz;
-  constexpr int NPL = Fmt<PREC>::npl;
+  constexpr int NPL = Fmt<PREC>::spl;
   constexpr int BT = Cfg<PREC>::BT, NT = Cfg<PREC>::NT, WQN = Cfg<PREC>::WQ;
   using G = Geo<ESZ, BT, NT>;
   constexpr int WTP = BT / Cfg<PREC>::WP;  // wave tile rows (P side)
@@ -672,9 +695,18 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
           acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[j]),
                                                               __builtin_bit_cast(bf16x8, f[FQ + i]), acc[j][i], 0, 0, 0);
     };
-    auto identity_add = [&](const u32x4 (&f)[NF], int kt, int ks) {
+    // split-bf16: NSEG = 3 segments of nk stages each (split_plane); loop
+    // stage g is stage kin(g) of segment segof(g)
+    constexpr int NSEG = PREC == PREC_BF16X3 ? 3 : 1;
+    const int NK = NSEG * nk;
+    auto segof = [&](int g) { return NSEG == 1 ? 0 : (g >= 2 * nk ? 2 : (g >= nk ? 1 : 0)); };
+    auto kin = [&](int g) { return g - segof(g) * nk; };
+    // the additive term pairs alpha I with Q's hi plane and with its lo plane
+    // once each: in segments 0 and 2, not in segment 1 (Q hi again)
+    auto identity_add = [&](const u32x4 (&f)[NF], int g, int ks) {
       if constexpr (ADD) {
-        const int kk = kt * KE + ks * KS;
+        if (NSEG > 1 && segof(g) == 1) return;
+        const int kk = kin(g) * KE + ks * KS;
         const int d = kk - prow0;
         if (d >= 0 && d < WTP) {
           const int fi = d >> 5;
@@ -685,7 +717,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
           for (int i = 0; i < FP; ++i)
             if (i == fi) {
 #pragma clang loop unroll(full)
-              for (int j = 0; j < FQ; ++j) mfma_identity<PREC>(acc[j][i], &f[j], id);
+              for (int j = 0; j < FQ; ++j) mfma_identity<PREC_BF16>(acc[j][i], &f[j], id);
             }
         }
       }
@@ -695,7 +727,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     auto store_half = [&](const u32x4 (&r)[NPL][G::NREG], const OpSrc& src, int kt, auto base_c, auto h_c) {
       constexpr int BASE = decltype(base_c)::value;
       constexpr int H = decltype(h_c)::value;
-      const bool tr = op_trans<PHASE, (BASE >= QOFF ? 1 : 0), ESZ, BT>(src, kt);
+      const bool tr = op_trans<PHASE, (BASE >= QOFF ? 1 : 0), ESZ, BT>(src, kin(kt));
 #pragma unroll
       for (int i = 2 * H; i < 2 * H + 2; ++i) {
         const int off = tr ? stK + i * (NT / 32) * KP : stD + i * (NT / 8) * PITCH;
@@ -714,10 +746,10 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     store_half(rq, sq, 0, std::integral_constant<int, QOFF>{}, I0{});
     store_half(rq, sq, 0, std::integral_constant<int, QOFF>{}, I1{});
     lds_barrier();
-    load_operand<PREC, PHASE, 0>(rp, sp, rsp, 1, tid);
-    load_operand<PREC, PHASE, 1>(rq, sq, rsq, 1, tid);
-    auto ktrP = [&](int kt) { return op_trans<PHASE, 0, ESZ, BT>(sp, kt); };
-    auto ktrQ = [&](int kt) { return op_trans<PHASE, 1, ESZ, BT>(sq, kt); };
+    load_operand<PREC, PHASE, 0>(rp, sp, rsp, kin(1), tid, split_plane(0, segof(1)));
+    load_operand<PREC, PHASE, 1>(rq, sq, rsq, kin(1), tid, split_plane(1, segof(1)));
+    auto ktrP = [&](int g) { return op_trans<PHASE, 0, ESZ, BT>(sp, kin(g)); };
+    auto ktrQ = [&](int g) { return op_trans<PHASE, 1, ESZ, BT>(sq, kin(g)); };
     read_frags(F[0], I0{}, 0, ktrP(0), ktrQ(0));
 
     // MODE 0: store stage kt + 1, load stage kt + 2 of this tile; 1: store
@@ -752,8 +784,8 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(F[1], 1);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (MODE == 0) load_operand<PREC, PHASE, 0>(rp, sp, rsp, kt + 2, tid);
-      if constexpr (MODE == 1) load_operand<PREC, PHASE, 0>(rp, xp, rxp, 0, tid);
+      if constexpr (MODE == 0) load_operand<PREC, PHASE, 0>(rp, sp, rsp, kin(kt + 2), tid, split_plane(0, segof(kt + 2)));
+      if constexpr (MODE == 1) load_operand<PREC, PHASE, 0>(rp, xp, rxp, 0, tid, split_plane(0, 0));
       __builtin_amdgcn_sched_barrier(0);
       identity_add(F[1], kt, 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -766,8 +798,8 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(F[0], 1);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (MODE == 0) load_operand<PREC, PHASE, 1>(rq, sq, rsq, kt + 2, tid);
-      if constexpr (MODE == 1) load_operand<PREC, PHASE, 1>(rq, xq, rxq, 0, tid);
+      if constexpr (MODE == 0) load_operand<PREC, PHASE, 1>(rq, sq, rsq, kin(kt + 2), tid, split_plane(1, segof(kt + 2)));
+      if constexpr (MODE == 1) load_operand<PREC, PHASE, 1>(rq, xq, rxq, 0, tid, split_plane(1, 0));
       __builtin_amdgcn_sched_barrier(0);
       identity_add(F[0], kt, 2);
       lds_barrier();
@@ -780,7 +812,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       __builtin_amdgcn_sched_barrier(0);
     };
 #pragma unroll 1
-    for (int kt = 0; kt + 2 < nk; kt += 2) {
+    for (int kt = 0; kt + 2 < NK; kt += 2) {
       stage(kt, I0{}, I0{});
       stage(kt + 1, I1{}, I0{});
     }
@@ -790,8 +822,8 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     }
     rxp = op_rsrc(xp);
     rxq = op_rsrc(xq);
-    stage(nk - 2, I0{}, I1{});
-    stage(nk - 1, I1{}, std::integral_constant<int, 2>{});
+    stage(NK - 2, I0{}, I1{});
+    stage(NK - 1, I1{}, std::integral_constant<int, 2>{});
     lds_barrier();
   } else {
     store_stage<ESZ, BT, NT, NPL, G::NREG, OPB>(rp, sp, 0, smem, tid);
@@ -894,12 +926,17 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
   // output column tj*BT + wq*WTQ + 32 fj + 8g + 4h + e.
   const int orow = ti * BT + wp * WTP + (lane & 31);
   const int ocol = tj * BT + wq * WTQ + 4 * hsel;
-  if constexpr ((PHASE == PH_GRAM || PHASE == PH_POLY) && PREC == PREC_BF16) {
-    char* out = reinterpret_cast<char*>((PHASE == PH_GRAM && VAR == 1) ? md.A : md.B);
+  if constexpr ((PHASE == PH_GRAM || PHASE == PH_POLY) && pipelined(PREC)) {
+    char* out = reinterpret_cast<char*>((PHASE == PH_GRAM && VAR == 1) ? md.A : md.B) +
+                (int64_t(ti) * (md.lda >> 8) + tj) * WS_TILE_STRIDE;
     const float sc = PHASE == PH_POLY ? pa.c
                                       : (pa.first ? scal[mat].inv2 : 1.f) * (VAR == 1 ? 1.f : pa.b);
-    store_tile_bf16<FQ, FP, WTP, WTQ, BT, NT, 2 * STAGE>(acc, sc, out + (int64_t(ti) * (md.lda >> 8) + tj) * WS_TILE_STRIDE,
-                                                       512, smem, wp, wq, lane, tid);
+    store_tile_bf16<FQ, FP, WTP, WTQ, BT, NT, 2 * STAGE>(acc, sc, out, 512, smem, wp, wq, lane, tid);
+    if constexpr (PREC == PREC_BF16X3) {    // the lo plane, staged through the same LDS
+      lds_barrier();
+      store_tile_bf16<FQ, FP, WTP, WTQ, BT, NT, 2 * STAGE, 1>(acc, sc, out + md.plane_A * 2, 512, smem, wp, wq, lane,
+                                                              tid);
+    }
   } else if constexpr (PHASE == PH_GRAM || PHASE == PH_POLY) {
     void* out = (PHASE == PH_GRAM && VAR == 1) ? md.A : md.B;
     const float sc = PHASE == PH_POLY ? pa.c
@@ -917,9 +954,14 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
         }
   } else {
     const float s = pa.first ? scal[mat].inv : 1.f;
-    if constexpr (VAR == 0 && PREC == PREC_BF16) {
+    if constexpr (VAR == 0 && pipelined(PREC)) {
       char* xn = reinterpret_cast<char*>(md.X[pa.cur ^ 1]) + (int64_t(ti) * (md.ldx >> 8) + tj) * WS_TILE_STRIDE;
       store_tile_bf16<FQ, FP, WTP, WTQ, BT, NT, 2 * STAGE>(acc, s, xn, 512, smem, wp, wq, lane, tid);
+      if constexpr (PREC == PREC_BF16X3) {
+        lds_barrier();
+        store_tile_bf16<FQ, FP, WTP, WTQ, BT, NT, 2 * STAGE, 1>(acc, s, xn + md.plane_X * 2, 512, smem, wp, wq, lane,
+                                                                tid);
+      }
     } else if constexpr (VAR == 0) {
       void* xn = md.X[pa.cur ^ 1];
 #pragma clang loop unroll(full)

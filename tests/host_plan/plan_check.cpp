@@ -132,14 +132,14 @@ hipError_t launch_ns_phase(int prec, int phase, const MatDev* mats, const MatSca
     CHECK(in_one_alloc(tiles, sizeof(int2) * NUM_XCD * pa.per_xcd), "tile list outside an allocation");
     for (int i = 0; i < g_count; ++i) {
       const MatDev& md = mats[i];
-      const int esz = is_f32(md.prec) ? 4 : 2, npl = md.prec == PREC_BF16X3 ? 2 : 1;
+      const int esz = is_f32(md.prec) ? 4 : 2, npl = is_split(md.prec) ? 2 : 1;
       const size_t xb = size_t(md.Mp) * md.ldx * esz * npl, ab = size_t(md.Mp) * md.lda * esz * npl;
       CHECK(in_one_alloc(md.X[0], xb) && in_one_alloc(md.X[1], xb) && in_one_alloc(md.A, ab) &&
                 in_one_alloc(md.B, ab),
             "matrix %d: a workspace buffer lies outside the allocation", i);
     }
   }
-  const int per_cu = (T == 256 || prec == PREC_BF16X3) ? 1 : 2;
+  const int per_cu = (T == 256 || is_split(prec)) ? 1 : 2;
   const int B = std::min(pa.per_xcd, pa.cus_per_xcd * per_cu);
   std::set<std::tuple<int, int, int>> expect, seen;
   for (int i = 0; i < g_count; ++i) {
@@ -203,7 +203,7 @@ hipError_t launch_ns_chain(int prec, const MatDev* imats, const MatScal*, const 
                            int32_t per_xcd_max, PhaseArgs*, int32_t*, int32_t nsync, int32_t*, const ChainArgs& a,
                            hipStream_t) {
   ++g_chain_launches;
-  const int per_cu = (ns_tile(prec) == 256 || prec == PREC_BF16X3) ? 1 : 2;
+  const int per_cu = (ns_tile(prec) == 256 || is_split(prec)) ? 1 : 2;
   const int per_xcd = std::min(per_xcd_max, a.cus_per_xcd * per_cu);
   const int nitems = xoff[NUM_XCD];
   const int ncnt = nsync - CHAIN_SYNC_HEAD;
