@@ -50,14 +50,16 @@ def _same(a, b, what):
 MIXED = [(700, 1100), (1100, 700), (769, 769), (300, 520), (64, 64), (1, 300)]
 
 
-@pytest.mark.parametrize("prec,steps", [(mb.NS_BF16, 5), (mb.NS_BF16, 1), (mb.NS_BF16X3, 3), (mb.NS_F32, 5)])
-def test_chain_equals_phase_grids(prec, steps):
-    _announce(f"chain vs grids prec={prec} steps={steps}")
+@pytest.mark.parametrize("prec,steps,tiles", [(mb.NS_BF16, 5, mb.TILES_AUTO), (mb.NS_BF16, 1, mb.TILES_AUTO),
+                                               (mb.NS_BF16X3, 3, mb.TILES_AUTO), (mb.NS_BF16X3, 3, mb.TILES_LARGE),
+                                               (mb.NS_F32, 5, mb.TILES_AUTO)])
+def test_chain_equals_phase_grids(prec, steps, tiles):
+    _announce(f"chain vs grids prec={prec} steps={steps} tiles={tiles}")
     shapes = MIXED if prec == mb.NS_BF16 else MIXED[2:]
     pdt = torch.float32 if prec == mb.NS_F32 else torch.bfloat16
     ws, gs, ms = _inputs(shapes, 71 + steps, pdt)
-    a = _run(ws, gs, ms, mb.LAUNCH_PHASE_GRIDS, precision=prec, steps=steps)
-    b = _run(ws, gs, ms, mb.LAUNCH_CHAIN, precision=prec, steps=steps)
+    a = _run(ws, gs, ms, mb.LAUNCH_PHASE_GRIDS, precision=prec, steps=steps, tile_mode=tiles)
+    b = _run(ws, gs, ms, mb.LAUNCH_CHAIN, precision=prec, steps=steps, tile_mode=tiles)
     _same(a[0], b[0], "W")
     _same(a[1], b[1], "M")
     _same(a[2], b[2], "O")

@@ -143,6 +143,30 @@ def test_f32_tile_sizes(tile_mode, launch_mode):
 
 @pytest.mark.parametrize("tile_mode", [mb.TILES_LARGE, mb.TILES_SMALL])
 @pytest.mark.parametrize("launch_mode", [mb.LAUNCH_PHASE_GRIDS, mb.LAUNCH_CHAIN])
+def test_split_bf16_tile_sizes(tile_mode, launch_mode):
+    # split-bf16 on the pipelined 256 x 256 tiles (three bf16 products per
+    # product) and on the one-stage 128 x 128 tiles, per-phase grids and the
+    # persistent chain, with a schedule whose last step has c = 0 (GRAM then
+    # stores B = b A and POLY is skipped): O within the split-bf16 gate, W
+    # bit-exact given O
+    _announce(f"split-bf16 tiles mode={tile_mode} launch={launch_mode}")
+    ws, gs, ms = _inputs(91 + tile_mode, torch.float32)
+    lr = f32(0.02)
+    w1, m1, o1 = _run_v2(ws, gs, ms, precision=mb.NS_BF16X3, steps=len(SCHEDULE5), lr=lr, beta=0.95, nesterov=1,
+                         ns_schedule=SCHEDULE5, tile_mode=tile_mode, launch_mode=launch_mode)
+    for i in range(len(SHAPES)):
+        w0, g0, m0 = to_np(ws[i]), to_np(gs[i]), to_np(ms[i])
+        ref = orc.muon_step(w0, g0, m0, lr=lr, beta=0.95, nesterov=True, coeffs=SCHEDULE5, steps=len(SCHEDULE5),
+                            param_bf16=False)
+        assert np.array_equal(bits(m1[i]), bits(ref.m))
+        err = orc.rel_frobenius(o1[i], ref.o)
+        print(f"  {SHAPES[i]}: rel-F {err:.2e}")
+        assert err <= PREC_TOL[mb.NS_BF16X3]
+        assert np.array_equal(bits(w1[i]), bits(orc.write_back(w0, o1[i], lr, 1.0, False)))
+
+
+@pytest.mark.parametrize("tile_mode", [mb.TILES_LARGE, mb.TILES_SMALL])
+@pytest.mark.parametrize("launch_mode", [mb.LAUNCH_PHASE_GRIDS, mb.LAUNCH_CHAIN])
 def test_bf16_tile_sizes(tile_mode, launch_mode):
     # 256 x 256 (pipelined) and 128 x 128 (one-stage) bf16 tiles, per-phase
     # grids and the persistent chain: O within the bf16 gate, W bit-exact given O
