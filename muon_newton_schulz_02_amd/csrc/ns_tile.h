@@ -655,12 +655,26 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
     const int kfr = (8 * hsel + ((lane & 15) >> 2)) * KP + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
     const int fragP = (wp * WTP + (lane & 31)) * PITCH + hsel * 16;
     const int fragPk = kfr + 2 * wp * WTP;
-    const int fragQ = QOFF + (wq * WTQ + (lane & 31)) * PITCH + hsel * 16;
-    const int fragQk = QOFF + kfr + 2 * wq * WTQ;
+    // POLY, whose two operands both change form along k, derives Q's fragment
+    // addresses from P's plus a wave-uniform offset at each use (an opaque
+    // scalar copy keeps the sums out of registers): two vector registers fewer
+    // kept its k-loop free of spills.  GRAM and COMBINE keep them precomputed.
+    constexpr bool QDERIVED = PHASE == PH_POLY;
+    const int qdr = __builtin_amdgcn_readfirstlane(QOFF + (wq * WTQ - wp * WTP) * PITCH);
+    const int qdk = __builtin_amdgcn_readfirstlane(QOFF + 2 * (wq * WTQ - wp * WTP));
+    const int fragQ0 = QOFF + (wq * WTQ + (lane & 31)) * PITCH + hsel * 16;
+    const int fragQk0 = QOFF + kfr + 2 * wq * WTQ;
     const int stD = (tid >> 3) * PITCH + (tid & 7) * 16;               // row-form chunk tid, + q (NT / 8) rows
     const int stK = (tid >> 5) * KP + (tid & 31) * 16;                 // k-row piece tid, + i (NT / 32) k-rows
     auto read_frags = [&](u32x4 (&f)[NF], auto buf_c, int ks, bool ptr, bool qtr) {
       constexpr int BUF = decltype(buf_c)::value;
+      int fragQ = fragQ0, fragQk = fragQk0;
+      if constexpr (QDERIVED) {
+        int qd, qk;
+        asm volatile("s_mov_b32 %0, %2\n\ts_mov_b32 %1, %3" : "=s"(qd), "=s"(qk) : "s"(qdr), "s"(qdk));
+        fragQ = fragP + qd;
+        fragQk = fragPk + qk;
+      }
       typedef short s16x4 __attribute__((ext_vector_type(4)));
       typedef __attribute__((address_space(3))) s16x4 ls16x4;
       typedef __attribute__((address_space(3))) char lchar;
