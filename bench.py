@@ -416,10 +416,15 @@ CSRC = os.path.join(ROOT, "muon_newton_schulz_02_amd", "csrc")
 
 
 def _src_hash(*names):
+    """sha256 prefix of the kernel sources' code: `//` comments, trailing blanks
+    and empty lines removed, so that a comment edit keeps the hash."""
     h = hashlib.sha256()
     for nm in names:
-        with open(os.path.join(CSRC, nm), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, nm), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

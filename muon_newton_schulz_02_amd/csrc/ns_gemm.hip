@@ -29,28 +29,30 @@
 //    diagonal stages the mirror block transposed.
 //  * Q in COMB reads X along its rows (the contraction index k is X's row
 //    index), and so do the blocks of A and B below the diagonal, read through
-//    their mirror block.  The bf16 tiles stage such operands in k-row form
-//    (each LDS row a k-row as in memory) and read their fragments with
-//    ds_read_b64_tr_b16; the split-bf16 and float32 tiles load 4 k-values of
-//    8 rows (4 rows for float32), transpose them in registers and write 8
-//    bytes (16 for float32) per row into LDS.
+//    their mirror block.  The 256 x 256 tiles (bf16 and split-bf16) stage
+//    such operands in k-row form (each LDS row a k-row as in memory) and read
+//    their fragments with ds_read_b64_tr_b16; the 128 x 128 and 64 x 64 tiles
+//    load 4 k-values of 8 rows (4 rows for float32), transpose them in
+//    registers and write 8 bytes (16 for float32) per row into LDS.
 //  * The additive terms a X and (b/c) A run on the matrix cores: where the
 //    k-slab meets the tile's own rows, extra MFMAs pair the Q fragment with
 //    a scaled identity fragment (for bf16 the scale is split into hi + lo, so
 //    the term carries about 17 significant bits, far inside the bf16 storage
 //    error), and no epilogue reads memory.
-//  * LDS rows hold 128 bytes of K at a pitch of 144 bytes.  The bf16 tiles
-//    keep rows unswizzled (a fragment read of 32 consecutive rows then puts
-//    each 16-lane group of the LDS on distinct banks) and k-row stages at a
-//    576-byte pitch; the split-bf16 and float32 tiles put the 16-byte chunk
-//    ch of row r at chunk position ch ^ ((r >> 4) & 7), so their fragment
-//    reads and transposed writes are both free of bank conflicts.
-//  * Tiles: 256 x 256 over eight waves (2 x 4, each 128 x 64) for bf16,
-//    with a software-pipelined k-loop; 128 x 128 over four waves (2 x 2,
-//    each 64 x 64) for the split-bf16 and float32 formats and for small bf16
-//    stacks; 64 x 64 over two waves for small float32 stacks.  K is staged
-//    128 bytes per row, double-buffered through LDS with register staging.
-//    Operands are zero-padded to a multiple of 256.
+//  * LDS rows hold 128 bytes of K at a pitch of 144 bytes.  The 256 x 256
+//    tiles keep rows unswizzled (a fragment read of 32 consecutive rows then
+//    puts each 16-lane group of the LDS on distinct banks) and k-row stages
+//    at a 576-byte pitch; the smaller tiles put the 16-byte chunk ch of row r
+//    at chunk position ch ^ ((r >> 4) & 7), so their fragment reads and
+//    transposed writes are both free of bank conflicts.
+//  * Tiles: 256 x 256 over eight waves (2 x 4, each 128 x 64) for bf16 and
+//    split-bf16, with a software-pipelined k-loop (a split-bf16 product runs
+//    as three bf16 products over K, one plane pair each); 128 x 128 over four
+//    waves (2 x 2, each 64 x 64) for float32 and for small bf16 and
+//    split-bf16 stacks; 64 x 64 over two waves for small float32 stacks.  K
+//    is staged 128 bytes per row, double-buffered through LDS with register
+//    staging.  Operands are zero-padded to a multiple of 256; the 256 x 256
+//    formats keep their workspace tile by tile.
 //  * Tile lists are split into one contiguous, cost-balanced segment per XCD;
 //    a persistent grid walks them, workgroup b on XCD b % 8 taking entries
 //    b/8, b/8 + grid/8, ... of that XCD's segment, so tiles that share

@@ -47,13 +47,13 @@ template <> struct Fmt<PREC_F32S> { static constexpr int esz = 4, spl = 1; };
 template <> struct Fmt<PREC_BF16X3S> { static constexpr int esz = 2, spl = 2; };
 
 // Tile shape per format: T x T tile, WP x WQ waves (rows x columns), NT threads.
-// bf16: 256 x 256 over eight waves (two per SIMD, each 128 x 64, 128
-// accumulator registers), so one wave's barrier or LDS wait overlaps the
-// other's matrix-core work.  The formats whose operands take twice the bytes
-// use 128 x 128 over four waves.
-// The bf16 tiles run the software-pipelined k-loop with their own LDS layout
-// (and transposed-operand block order); the other formats stage one k-step at
-// a time in the swizzled layout.
+// bf16 and split-bf16: 256 x 256 over eight waves (two per SIMD, each
+// 128 x 64, 128 accumulator registers), so one wave's barrier or LDS wait
+// overlaps the other's matrix-core work.  float32 and the small-stack tiles
+// use 128 x 128 over four waves (small-stack float32: 64 x 64 over two).
+// The 256 x 256 tiles run the software-pipelined k-loop with their own LDS
+// layout (and transposed-operand block order); the others stage one k-step
+// at a time in the swizzled layout.
 constexpr bool pipelined(int prec) { return prec == PREC_BF16 || prec == PREC_BF16X3; }
 
 template <int PREC> struct Cfg;
@@ -65,9 +65,9 @@ template <> struct Cfg<PREC_BF16S> { static constexpr int BT = 128, WP = 2, WQ =
 // small-stack binary32: 64 x 64 over two waves of 32 x 64
 template <> struct Cfg<PREC_F32S> { static constexpr int BT = 64, WP = 2, WQ = 1, NT = 128; };
 
-// LDS operand layout of the split-bf16 and binary32 tiles: row r at r * PITCH,
-// 16-byte chunk ch at 16 (ch ^ ((r >> 4) & 7)).  (The bf16 tiles use their
-// own, unswizzled layout.)
+// LDS operand layout of the one-stage tiles: row r at r * PITCH, 16-byte
+// chunk ch at 16 (ch ^ ((r >> 4) & 7)).  (The pipelined tiles use their own,
+// unswizzled layout.)
 __device__ __forceinline__ int lds_off(int r, int ch) { return r * PITCH + ((ch ^ ((r >> 4) & 7)) << 4); }
 
 // Workgroup barrier for LDS reuse only: this wave's LDS accesses complete,
@@ -605,7 +605,7 @@ __device__ __forceinline__ void ns_tile_body(const MatDev& md, const MatScal* __
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
 
   const int hsel = lane >> 5;
-  // bf16: software-pipelined k-loop (below); the other formats: one stage at a time.
+  // 256 x 256 tiles: software-pipelined k-loop (below); the others: one stage at a time.
   constexpr bool PIPE = pipelined(PREC);
   static_assert(!PIPE || (KE / KS == 4 && G::NREG == 4 && G::PER == 1 && G::CH == 4 && NPL == 1), "pipelined geometry");
   if constexpr (PIPE) {
