@@ -141,18 +141,20 @@ typedef enum muon_launch_mode {
   MUON_LAUNCH_CHAIN = 2
 } muon_launch_mode;
 
-/* Tile size of the bf16 and fp32 Newton-Schulz products
- * (muon_step_options.tile_mode).
- *   AUTO   bf16: 128 x 128 when the call's bf16 matrices have fewer 256 x 256
- *          GRAM tiles than the GPU has compute units (GPT-2-small-sized
- *          stacks), else 256 x 256.  fp32: 64 x 64 when its fp32 matrices
- *          have fewer 128 x 128 GRAM tiles than that, else 128 x 128.
- *   LARGE  bf16: 256 x 256 tiles, eight waves, software-pipelined k-loop.
- *          fp32: 128 x 128 tiles, four waves.
- *   SMALL  bf16: 128 x 128 tiles, four waves, one-stage k-loop.
- *          fp32: 64 x 64 tiles, two waves.
- * The working format is the same either way; split-bf16 always uses
- * 128 x 128 tiles.                                                          */
+/* Tile size of the Newton-Schulz products (muon_step_options.tile_mode).
+ *   AUTO   bf16 and split-bf16 (each counted on its own): 128 x 128 when the
+ *          call's matrices of that precision have fewer 256 x 256 GRAM tiles
+ *          than the GPU has compute units (GPT-2-small-sized stacks), else
+ *          256 x 256.  fp32: 64 x 64 when its fp32 matrices have fewer
+ *          128 x 128 GRAM tiles than that, else 128 x 128.
+ *   LARGE  bf16 and split-bf16: 256 x 256 tiles, eight waves,
+ *          software-pipelined k-loop (a split-bf16 product as three bf16
+ *          products over K).  fp32: 128 x 128 tiles, four waves.
+ *   SMALL  bf16 and split-bf16: 128 x 128 tiles, four waves, one-stage
+ *          k-loop.  fp32: 64 x 64 tiles, two waves.
+ * The working format is the same either way.  The split-bf16 results of the
+ * two tile sizes differ within the format's rounding (the sums over K are
+ * taken in another order).                                                  */
 typedef enum muon_tile_mode {
   MUON_TILES_AUTO = 0,
   MUON_TILES_LARGE = 1,
