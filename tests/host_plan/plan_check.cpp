@@ -417,6 +417,7 @@ int main() {
   grid_case("binary32 stack on 128 x 128 tiles", {{2048, 2048, F32}, {2048, 2048, F32}, {1024, 4096, F32},
                                                   {4096, 1024, F32}},
             1e9);
+  grid_case("split-bf16 stack on 256 x 256 tiles", std::vector<Shape>(8, Shape{2048, 2048, X3}), 1e9);
   const std::vector<Shape> mixed = {{700, 1100, BF}, {1100, 700, BF}, {769, 769, BF},
                                     {300, 520, BF},  {64, 64, BF},    {1, 300, BF}};
   chain_case("bf16, 5 steps", mixed, 5, false);

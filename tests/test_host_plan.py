@@ -39,7 +39,7 @@ def test_tile_walks_and_chain_queues(plan_check):
     # 6 x 24 (rectangular): 21 triangle tiles each for GRAM and POLY
     d24 = out.split("CASE grids d24 stack")[1].split("CASE")[0]
     assert d24.count(" 3024 tiles") == 2 and " 10368 tiles" in d24
-    assert out.count("CASE ") == 14
+    assert out.count("CASE ") == 15
     assert "out of memory with the hook, launched without it" in out
     # the allocation-free entry point: buffers and tables inside its scratch
     # block, and a stack too large for it refused before any launch
@@ -52,4 +52,11 @@ def test_tile_walks_and_chain_queues(plan_check):
     assert "phase 0 prec 4: 10 tiles" in one and "phase 2 prec 4: 16 tiles" in one
     big = out.split("CASE grids binary32 stack on 128 x 128 tiles")[1].split("CASE")[0]
     assert "phase 0 prec 2:" in big and "prec 4" not in big
+    # split-bf16: eight 2048^2 matrices fill the GPU with 256 x 256 tiles (8 x 9 / 2
+    # = 36 triangle tiles each; format 1), the two small ones of the ragged
+    # case run on 128 x 128 tiles (format 5)
+    x3 = out.split("CASE grids split-bf16 stack on 256 x 256 tiles")[1].split("CASE")[0]
+    assert "phase 0 prec 1: 288 tiles" in x3 and "prec 5" not in x3
+    ragged = out.split("CASE grids ragged, mixed formats")[1].split("CASE")[0]
+    assert "prec 5" in ragged and "prec 1:" not in ragged
     assert out.count("  chain prec ") == 5
