@@ -483,14 +483,20 @@ __device__ __forceinline__ void store_tile_bf16(const f32x16 (&acc)[FQ][FP], flo
                                                 char* smem, int wp, int wq, int lane, int tid) {
   constexpr int EP = BT * 2 + 16;  // staging pitch in bytes
   static_assert(BT * EP <= LDSB, "staging does not fit");
-  const int hsel = lane >> 5;
+  // This thread's staging and store addresses are formed here, from a fresh
+  // copy of its index: formed before the k-loop, they were kept in scratch
+  // memory, and reloading them made the stores wait for every load in flight
+  // (the next tile's first stage included).
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(tid));
+  const int ln = t & 63, hsel = ln >> 5;
 #pragma clang loop unroll(full)
   for (int j = 0; j < FQ; ++j)
 #pragma clang loop unroll(full)
     for (int i = 0; i < FP; ++i)
 #pragma clang loop unroll(full)
       for (int g = 0; g < 4; ++g) {
-        const int r = wp * WTP + 32 * i + (lane & 31), c = wq * WTQ + 32 * j + 8 * g + 4 * hsel;
+        const int r = wp * WTP + 32 * i + (ln & 31), c = wq * WTQ + 32 * j + 8 * g + 4 * hsel;
         const f32x16& a = acc[j][i];
         *reinterpret_cast<u32x2*>(smem + r * EP + c * 2) =
             u32x2{bf16x2_plane<PL>(sc * a[4 * g], sc * a[4 * g + 1]),
@@ -498,8 +504,10 @@ __device__ __forceinline__ void store_tile_bf16(const f32x16 (&acc)[FQ][FP], flo
       }
   lds_barrier();
   constexpr int CPR = BT * 2 / 16;  // 16-byte chunks per row
-#pragma unroll 4
-  for (int q = tid; q < BT * CPR; q += NT) {
+  static_assert((BT * CPR) % NT == 0, "whole chunks per thread");
+#pragma clang loop unroll(full)
+  for (int k = 0; k < BT * CPR / NT; ++k) {
+    const int q = t + k * NT;
     const int r = q / CPR, c16 = q % CPR;
     *gmem(reinterpret_cast<u32x4*>(out + int64_t(r) * ld + c16 * 16)) = *reinterpret_cast<const u32x4*>(smem + r * EP + c16 * 16);
   }
