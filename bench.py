@@ -14,8 +14,8 @@ traffic is the HBM bytes per launch from the rocprofv3 FETCH_SIZE /
 WRITE_SIZE summary under profiles/, reported only while the kernel sources
 hash to the values recorded there (null otherwise).
 `roofline.measured_peak` is the achievable rate on the same box: the
-library's register-only MFMA loop (`muon_mfma_probe`) for the products, a
-torch device copy for HBM-bound kernels.
+library's register-only MFMA loop on random operands (`muon_mfma_probe`)
+for the products, a torch device copy for HBM-bound kernels.
 The cpu_baseline is the CPU oracle timed on a bounded sample of the same
 workload on this host.  The `adamw` object times the other half of the
 hybrid optimizer, AdamW on the d24 parameters that are not transformer
@@ -72,6 +72,10 @@ def parse():
     ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
                     help="after the timed steps, run steps for SECONDS more while amd-smi samples the "
                          "socket power and the shader clocks (reported as `power`; off by default)")
+    ap.add_argument("--power-zero-data", type=float, default=0.0, metavar="SECONDS",
+                    help="at the end, zero the gradients and momenta (every product then multiplies "
+                         "zeros, with the same memory traffic) and time and sample the step for SECONDS "
+                         "(reported as `power_zero_data`; a diagnostic of how the data sets the clock)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device once (a plain copy kernel "
                          "of known size, to scale HBM byte counters)")
@@ -275,6 +279,21 @@ def main():
     }
     if power is not None:
         out["power"] = power
+    if args.power_zero_data > 0:
+        for t in gs + ms:
+            t.zero_()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            step()
+        z0, z1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        z0.record(stream)
+        for _ in range(args.steps):
+            step()
+        z1.record(stream)
+        torch.cuda.synchronize()
+        zero = sample_power(args.power_zero_data, step, torch)
+        zero["ms_per_step"] = round(z0.elapsed_time(z1) / args.steps, 4)
+        out["power_zero_data"] = zero
     print(json.dumps(out))
 
 
@@ -326,15 +345,19 @@ def sample_power(seconds, step, torch, period=0.4):
             "seconds": seconds, "tool": "amd-smi metric -g 0 -p -c --json"}
 
 
-def mfma_probe_tflops(mb, torch, dev, stream, iterations=200000):
-    """Achievable dense bf16 MFMA rate: the library's register-only MFMA loop
-    on every SIMD, timed with events (about 30 ms)."""
+def mfma_probe_tflops(mb, torch, dev, stream, iterations=200000, launches=4):
+    """Achievable dense bf16 MFMA rate on random data: the library's
+    register-only MFMA loop on every SIMD, one untimed launch (the clock
+    settles under the load) and `launches` timed with events (about 35 ms
+    each)."""
     sink = torch.zeros(1, dtype=torch.float32, device=dev)
-    mb.muon_mfma_probe(1000, sink, stream=stream)
+    mb.muon_mfma_probe(iterations, sink, stream=stream)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    flops = mb.muon_mfma_probe(iterations, sink, stream=stream)
+    flops = 0.0
+    for _ in range(launches):
+        flops += mb.muon_mfma_probe(iterations, sink, stream=stream)
     stop.record(stream)
     torch.cuda.synchronize()
     tf = flops / (start.elapsed_time(stop) * 1e-3) / 1e12

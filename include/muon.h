@@ -459,13 +459,13 @@ muon_status muon_timing_enable(int32_t enable);
 muon_status muon_timing_read(double* ms_out, int64_t* launches_out);
 
 /* Measurement aid: enqueue on `stream` a kernel that keeps every matrix
- * core busy with independent v_mfma_f32_32x32x16_bf16 chains for
- * `iterations` rounds (1 to 2^30), operands in registers and changing every
- * round, two waves per SIMD; *flops_out receives its operation count.
- * Timing the launch gives the dense bf16 rate the chip sustains under MFMA
- * load (its clock may stay below the nominal 2.4 GHz).  `sink` is a device
- * float that the kernel never writes in practice (it keeps the chains
- * live).                                                                  */
+ * core busy with four independent v_mfma_f32_32x32x16_bf16 chains per wave
+ * for `iterations` rounds (1 to 2^30), two waves per SIMD, operands in
+ * registers: eight fragments of random bf16 values per lane, taken in turn;
+ * *flops_out receives its operation count.  Timing the launch gives the
+ * dense bf16 rate the chip sustains under MFMA load on random data (the
+ * clock it holds then stays well below the nominal 2.4 GHz).  `sink` is a
+ * device float that the kernel never writes (it keeps the chains live).  */
 muon_status muon_mfma_probe(int64_t iterations, float* sink, double* flops_out, void* stream);
 
 /* Bytes of device workspace a step on these shapes needs (0 on error).    */
