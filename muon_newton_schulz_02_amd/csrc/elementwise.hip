@@ -208,47 +208,58 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
   const int64_t ldx = md.ldx;
   float ss = 0.f;
 
+  // all four rows' loads before any store (the stores would otherwise hold
+  // back the next row's loads)
+  float g[4][4], m[4][4];
+  bool live[4], full[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int row = tr0 + rg + 16 * p;
+    const int col = tc0 + 4 * cg;
+    live[p] = row < rows && col < cols;
+    full[p] = live[p] && md.vec_ok && (col + 3 < cols);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[p][e] = m[p][e] = 0.f;
+    const int64_t gi = int64_t(row) * md.ld_grad + col;
+    const int64_t mi64 = int64_t(row) * md.ld_mom + col;
+    if (full[p]) {
+      if (md.grad_bf16) {
+        const u32x2 raw = __builtin_nontemporal_load(
+            gmem(reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(md.grad) + gi)));
+        g[p][0] = bf16_bits_to_float(raw[0] & 0xFFFFu);
+        g[p][1] = bf16_bits_to_float(raw[0] >> 16);
+        g[p][2] = bf16_bits_to_float(raw[1] & 0xFFFFu);
+        g[p][3] = bf16_bits_to_float(raw[1] >> 16);
+      } else {
+        const f32x4 raw = __builtin_nontemporal_load(
+            gmem(reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(md.grad) + gi)));
+        g[p][0] = raw[0]; g[p][1] = raw[1]; g[p][2] = raw[2]; g[p][3] = raw[3];
+      }
+      if (mode == 0) {
+        const f32x4 raw = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4*>(md.mom + mi64)));
+        m[p][0] = raw[0]; m[p][1] = raw[1]; m[p][2] = raw[2]; m[p][3] = raw[3];
+      }
+    } else if (live[p]) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col + e < cols) {
+          g[p][e] = load_elem(md.grad, gi + e, md.grad_bf16);
+          if (mode == 0) m[p][e] = gmem(md.mom)[mi64 + e];
+        }
+    }
+  }
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int rl = rg + 16 * p;
     const int row = tr0 + rl;
     const int col = tc0 + 4 * cg;
     float u[4] = {0.f, 0.f, 0.f, 0.f};
-    if (row < rows && col < cols) {
-      float g[4] = {0.f, 0.f, 0.f, 0.f}, m[4] = {0.f, 0.f, 0.f, 0.f};
-      const bool full = md.vec_ok && (col + 3 < cols);
-      const int64_t gi = int64_t(row) * md.ld_grad + col;
-      if (full) {
-        if (md.grad_bf16) {
-          const u32x2 raw = __builtin_nontemporal_load(
-              gmem(reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(md.grad) + gi)));
-          g[0] = bf16_bits_to_float(raw[0] & 0xFFFFu);
-          g[1] = bf16_bits_to_float(raw[0] >> 16);
-          g[2] = bf16_bits_to_float(raw[1] & 0xFFFFu);
-          g[3] = bf16_bits_to_float(raw[1] >> 16);
-        } else {
-          const f32x4 raw = __builtin_nontemporal_load(
-              gmem(reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(md.grad) + gi)));
-          g[0] = raw[0]; g[1] = raw[1]; g[2] = raw[2]; g[3] = raw[3];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (col + e < cols) g[e] = load_elem(md.grad, gi + e, md.grad_bf16);
-      }
+    if (live[p]) {
       if (mode == 0) {
-        const int64_t mi64 = int64_t(row) * md.ld_mom + col;
-        if (full) {
-          const f32x4 raw = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4*>(md.mom + mi64)));
-          m[0] = raw[0]; m[1] = raw[1]; m[2] = raw[2]; m[3] = raw[3];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (col + e < cols) m[e] = gmem(md.mom)[mi64 + e];
-        }
         float mn[4];
-        momentum4(g, m, mn, u, beta, nesterov, ema);
-        if (full) {
+        momentum4(g[p], m[p], mn, u, beta, nesterov, ema);
+        const int64_t mi64 = int64_t(row) * md.ld_mom + col;
+        if (full[p]) {
           __builtin_nontemporal_store(f32x4{mn[0], mn[1], mn[2], mn[3]},
                                       gmem(reinterpret_cast<f32x4*>(md.mom + mi64)));
         } else {
@@ -258,7 +269,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) u[e] = g[e];
+        for (int e = 0; e < 4; ++e) u[e] = g[p][e];
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) if (col + e >= cols) u[e] = 0.f;
