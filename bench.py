@@ -176,15 +176,7 @@ def main():
 
     # ------------------------------------------------------------ accounting
     k = wl.ns_steps
-    c_nz = wl.coeffs[2] != 0.0
-    nominal = 0.0
-    alg = {"gram": 0.0, "poly": 0.0, "combine": 0.0}
-    for s in wl.specs:
-        m_, n_ = min(s.rows, s.cols), max(s.rows, s.cols)
-        nominal += (4.0 * m_ * m_ * n_ + (2.0 * m_ ** 3 if c_nz else 0.0)) * k
-        alg["gram"] += float(m_) * (m_ + 1) * n_ * k          # unique entries of X X^T
-        alg["poly"] += (float(m_) * (m_ + 1) * m_ * k) if c_nz else 0.0
-        alg["combine"] += 2.0 * m_ * m_ * n_ * k
+    nominal, alg = ns_flops([(s.rows, s.cols) for s in wl.specs], k, wl.coeffs[2] != 0.0)
     elems = wl.elements
     gbytes = 2 if wl.grad_dtype == torch.bfloat16 else 4
     pbytes = 2 if wl.param_dtype == torch.bfloat16 else 4
@@ -297,6 +289,36 @@ def main():
     print(json.dumps(out))
 
 
+def ns_flops(shapes, ns_steps, c_nonzero):
+    """Flops of `ns_steps` Newton-Schulz steps over matrices of the given
+    (rows, cols): nominal, 4 m^2 n + 2 m^3 per step and matrix (m <= n; the
+    A^2 term dropped when c = 0), and algorithmic per product, the symmetric
+    products counting their unique entries once: GRAM m (m + 1) n, POLY
+    m^2 (m + 1), COMBINE 2 m^2 n."""
+    nominal = 0.0
+    alg = {"gram": 0.0, "poly": 0.0, "combine": 0.0}
+    for rows, cols in shapes:
+        m_, n_ = min(rows, cols), max(rows, cols)
+        nominal += (4.0 * m_ * m_ * n_ + (2.0 * m_ ** 3 if c_nonzero else 0.0)) * ns_steps
+        alg["gram"] += float(m_) * (m_ + 1) * n_ * ns_steps
+        alg["poly"] += (float(m_) * (m_ + 1) * m_ * ns_steps) if c_nonzero else 0.0
+        alg["combine"] += 2.0 * m_ * m_ * n_ * ns_steps
+    return nominal, alg
+
+
+def parse_amd_smi_metric(txt):
+    """Socket power (W) and the mean of the shader clocks gfx_0 .. (MHz) from
+    `amd-smi metric -g 0 -p -c --json` output."""
+    d = json.loads(txt)
+    d = d[0] if isinstance(d, list) else d
+    d = d.get("gpu_data", [d])[0] if isinstance(d, dict) and "gpu_data" in d else d
+    pw = d["power"]["socket_power"]
+    pw = pw["value"] if isinstance(pw, dict) else pw
+    clk = [v["clk"]["value"] for k, v in d["clock"].items()
+           if k.startswith("gfx_") and isinstance(v.get("clk"), dict) and isinstance(v["clk"]["value"], (int, float))]
+    return float(pw), sum(clk) / len(clk)
+
+
 def sample_power(seconds, step, torch, period=0.4):
     """Socket power and shader clock while the step runs back to back: amd-smi
     (`metric -p -c --json`) is sampled from a thread; the first second is
@@ -306,16 +328,6 @@ def sample_power(seconds, step, torch, period=0.4):
 
     samples, stop = [], threading.Event()
 
-    def parse(txt):
-        d = json.loads(txt)
-        d = d[0] if isinstance(d, list) else d
-        d = d.get("gpu_data", [d])[0] if isinstance(d, dict) and "gpu_data" in d else d
-        pw = d["power"]["socket_power"]
-        pw = pw["value"] if isinstance(pw, dict) else pw
-        clk = [v["clk"]["value"] for k, v in d["clock"].items()
-               if k.startswith("gfx_") and isinstance(v.get("clk"), dict) and isinstance(v["clk"]["value"], (int, float))]
-        return float(pw), sum(clk) / len(clk)
-
     def sampler():
         stop.wait(1.0)
         while not stop.is_set():
@@ -323,7 +335,7 @@ def sample_power(seconds, step, torch, period=0.4):
                 r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"],
                                    capture_output=True, text=True, timeout=10)
                 if r.returncode == 0:
-                    samples.append(parse(r.stdout))
+                    samples.append(parse_amd_smi_metric(r.stdout))
             except Exception:  # noqa: BLE001 - a failed sample is skipped
                 pass
             stop.wait(period)
