@@ -295,9 +295,10 @@ muon_status muon_ns_batched(const void* const* x_in, float* const* x_out,
                             muon_ns_coeffs ns_coeffs, int32_t ns_steps, void* stream);
 
 /* Frobenius norms: norms_out[i] = ||x_in[i]||_F (binary32, device array of
- * `count` floats), summed as binary32 partials per 4096-element tile (16 x
- * 256, or 64 x 64 for matrices with more rows than columns) and reduced in
- * a fixed order (deterministic).  x_in[i] is grad_dtype with row stride
+ * `count` floats), summed as binary32 partials per tile (16 x 256, or
+ * 64 x 128 for matrices with more rows than columns; the step's own
+ * reduction takes 64 x 64 tiles for tall matrices in the binary32 and split
+ * formats) and reduced in a fixed order (deterministic).  x_in[i] is grad_dtype with row stride
  * ld_grad.  The same reduction gives the step's normalisation X = U /
  * (||U||_F + 1e-7); the pages leave the normalisation open, and dividing by
  * the Frobenius norm bounds every singular value by 1, which the iteration

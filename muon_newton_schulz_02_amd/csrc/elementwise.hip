@@ -6,8 +6,10 @@
 //    through an LDS transpose for tall matrices) in the Newton-Schulz storage
 //    format, zero-filling the padding; writes one binary32 sum of u^2 per
 //    4096-element tile (wavefront shuffles, then LDS across the four waves).
-//    Tall matrices go in 64 x 64 tiles through the LDS transpose; the others
-//    in 16 x 256 tiles, one 256-element row run per wave and instruction.
+//    Tall matrices go through an LDS transpose, in 64 x 128 tiles staged as
+//    bf16 for the bf16 working format (two 128-element row runs per wave and
+//    load) and in 64 x 64 binary32 tiles for the others; the rest in 16 x 256
+//    tiles, one 256-element row run per wave and instruction.
 //    G and M are touched once per step, so their vector loads and the M
 //    store carry the nontemporal hint (measured 4 % faster); U is read
 //    again by the Newton-Schulz products and is stored normally.
@@ -173,6 +175,108 @@ __device__ inline float momentum_rows(const MatDev& md, int tr0, int tc0, float 
   return ss;
 }
 
+// The TBF_R x TBF_C tile (tr0, tc0) of a tall matrix in the bf16 working
+// format: thread (rg, cg) takes rows rg + RSTEP p (p = 0 .. 7, four at a
+// time, loads before stores) and the four columns from tc0 + 4 cg (for
+// 64 x 128, each wave load covers two 128-element row runs); u goes to LDS
+// as bf16 (the rounding the workspace stores), then each X row (a natural
+// column) leaves as one run of the tile's TBF_R natural rows, TBF_R / 4
+// threads per row.  Returns this thread's sum of u^2.
+__device__ inline float momentum_tall_bf16(const MatDev& md, int tr0, int tc0, float beta, int32_t nesterov,
+                                           int32_t ema, int32_t mode, uint16_t (*t16)[TBF_C + 4]) {
+  constexpr int CG = TBF_C / 4, RSTEP = 256 / CG;   // column groups of 4; row step between a thread's rows
+  constexpr int CGO = TBF_R / 4, JSTEP = 256 / CGO;  // store side: groups of 4 natural rows; X-row step
+  static_assert(TBF_R * TBF_C == 8 * 1024 && 8 * RSTEP == TBF_R && 8 * JSTEP == TBF_C, "8 rows, 8 stores a thread");
+  const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+  const int col = tc0 + 4 * cg;
+  const int rows = md.rows, cols = md.cols;
+  float ss = 0.f;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    float g[4][4], m[4][4];
+    bool live[4], full[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = tr0 + rg + RSTEP * (4 * half + q);
+      live[q] = row < rows && col < cols;
+      full[q] = live[q] && md.vec_ok && col + 3 < cols;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g[q][e] = m[q][e] = 0.f;
+      const int64_t gi = int64_t(row) * md.ld_grad + col;
+      const int64_t mi = int64_t(row) * md.ld_mom + col;
+      if (full[q]) {
+        if (md.grad_bf16) {
+          const u32x2 raw = __builtin_nontemporal_load(
+              gmem(reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(md.grad) + gi)));
+          g[q][0] = bf16_bits_to_float(raw[0] & 0xFFFFu);
+          g[q][1] = bf16_bits_to_float(raw[0] >> 16);
+          g[q][2] = bf16_bits_to_float(raw[1] & 0xFFFFu);
+          g[q][3] = bf16_bits_to_float(raw[1] >> 16);
+        } else {
+          const f32x4 raw = __builtin_nontemporal_load(
+              gmem(reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(md.grad) + gi)));
+          g[q][0] = raw[0]; g[q][1] = raw[1]; g[q][2] = raw[2]; g[q][3] = raw[3];
+        }
+        if (mode == 0) {
+          const f32x4 raw = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4*>(md.mom + mi)));
+          m[q][0] = raw[0]; m[q][1] = raw[1]; m[q][2] = raw[2]; m[q][3] = raw[3];
+        }
+      } else if (live[q]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e < cols) {
+            g[q][e] = load_elem(md.grad, gi + e, md.grad_bf16);
+            if (mode == 0) m[q][e] = gmem(md.mom)[mi + e];
+          }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rl = rg + RSTEP * (4 * half + q);
+      const int row = tr0 + rl;
+      float u[4] = {0.f, 0.f, 0.f, 0.f};
+      if (live[q]) {
+        if (mode == 0) {
+          float mn[4];
+          momentum4(g[q], m[q], mn, u, beta, nesterov, ema);
+          const int64_t mi = int64_t(row) * md.ld_mom + col;
+          if (full[q]) {
+            __builtin_nontemporal_store(f32x4{mn[0], mn[1], mn[2], mn[3]}, gmem(reinterpret_cast<f32x4*>(md.mom + mi)));
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (col + e < cols) gmem(md.mom)[mi + e] = mn[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) u[e] = g[q][e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) if (col + e >= cols) u[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss += u[e] * u[e];
+      if (mode != 2)
+        *reinterpret_cast<u32x2*>(&t16[rl][4 * cg]) =
+            u32x2{float2_to_bf16x2_bits(u[0], u[1]), float2_to_bf16x2_bits(u[2], u[3])};
+    }
+  }
+  if (mode != 2) {
+    __syncthreads();
+    const int cgo = tid % CGO, jo = tid / CGO;
+    uint16_t* xw = reinterpret_cast<uint16_t*>(md.X[0]);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int j = jo + JSTEP * p;       // natural column within the tile: X row tc0 + j
+      const uint32_t v0 = t16[4 * cgo][j], v1 = t16[4 * cgo + 1][j], v2 = t16[4 * cgo + 2][j],
+                     v3 = t16[4 * cgo + 3][j];
+      *gmem(reinterpret_cast<u32x2*>(xw + ws_index(md.prec, tc0 + j, tr0 + 4 * cgo, md.ldx))) =
+          u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
+    }
+  }
+  return ss;
+}
+
 }  // namespace
 
 // mode 0: momentum step; mode 1: U = G (Newton-Schulz only); mode 2: norms
@@ -181,7 +285,11 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
                                                        const int32_t* __restrict__ etile_off,
                                                        int32_t count, float beta, int32_t nesterov,
                                                        int32_t ema, int32_t mode, float* __restrict__ partials) {
-  __shared__ float tile[ETILE][ETILE + 1];
+  // the LDS of one tall tile: a 64 x 64 binary32 tile or a 64 x 128 bf16 one
+  constexpr int TILE_LDS = TBF_R * (TBF_C + 4) * 2 > ETILE * (ETILE + 1) * 4 ? TBF_R * (TBF_C + 4) * 2
+                                                                            : ETILE * (ETILE + 1) * 4;
+  __shared__ __attribute__((aligned(16))) char tile_lds[TILE_LDS];
+  float (*tile)[ETILE + 1] = reinterpret_cast<float (*)[ETILE + 1]>(tile_lds);
   __shared__ float red[4];
   const int b = blockIdx.x;
   const int mi = find_matrix(etile_off, count, b);
@@ -191,6 +299,15 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDev* __restrict_
   if (!md.transposed) {
     const float ssr = wave_sum(momentum_rows(md, (local / md.etile_cols) * RTILE_R,
                                              (local % md.etile_cols) * RTILE_C, beta, nesterov, ema, mode));
+    if ((tid & 63) == 0) red[tid >> 6] = ssr;
+    __syncthreads();
+    if (tid == 0) partials[b] = (red[0] + red[1]) + (red[2] + red[3]);
+    return;
+  }
+  if (md.prec == PREC_BF16) {
+    const float ssr = wave_sum(momentum_tall_bf16(md, (local / md.etile_cols) * TBF_R,
+                                                  (local % md.etile_cols) * TBF_C, beta, nesterov, ema, mode,
+                                                  reinterpret_cast<uint16_t (*)[TBF_C + 4]>(tile_lds)));
     if ((tid & 63) == 0) red[tid >> 6] = ssr;
     __syncthreads();
     if (tid == 0) partials[b] = (red[0] + red[1]) + (red[2] + red[3]);
@@ -341,7 +458,8 @@ __global__ __launch_bounds__(256) void writeback_direct_kernel(const MatDev* __r
   const MatDev& md = mats[mi];
   const int local = b - etile_off[mi];
   const bool tr = md.transposed != 0;
-  const int th = tr ? ETILE : RTILE_R, tw = tr ? ETILE : RTILE_C;
+  const bool tbf = tr && md.prec == PREC_BF16;
+  const int th = tr ? (tbf ? TBF_R : ETILE) : RTILE_R, tw = tr ? (tbf ? TBF_C : ETILE) : RTILE_C;
   const int tr0 = (local / md.etile_cols) * th;
   const int tc0 = (local % md.etile_cols) * tw;
   const void* xw = md.X[0];

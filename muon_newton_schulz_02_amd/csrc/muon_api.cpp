@@ -1054,9 +1054,12 @@ muon_status host_mats(const Call& c, const std::vector<int>& iprec, char* ws, st
     m.prec = c.mode == MODE_NORMS ? int(PREC_BF16) : iprec[size_t(i)];
     const int64_t rp = g.transposed ? g.Np : g.Mp;  // natural padded rows
     const int64_t cp = g.transposed ? g.Mp : g.Np;  // natural padded cols
-    // elementwise tiles: ETILE x ETILE for tall matrices, RTILE_R x RTILE_C
-    // for the others (both divide the 256-padded shape)
-    const int64_t th = g.transposed ? ETILE : RTILE_R, tw = g.transposed ? ETILE : RTILE_C;
+    // elementwise tiles: TBF_R x TBF_C for tall matrices in bf16, ETILE x
+    // ETILE for the other tall ones, RTILE_R x RTILE_C for the rest (all
+    // divide the 256-padded shape)
+    const bool tbf = g.transposed && m.prec == int(PREC_BF16);
+    const int64_t th = g.transposed ? (tbf ? TBF_R : ETILE) : RTILE_R;
+    const int64_t tw = g.transposed ? (tbf ? TBF_C : ETILE) : RTILE_C;
     m.etile_cols = int32_t(cp / tw);
     etile_off[i + 1] = etile_off[i] + int32_t((rp / th) * (cp / tw));
     if (c.mode != MODE_NORMS) {

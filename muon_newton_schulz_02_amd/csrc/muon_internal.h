@@ -20,6 +20,11 @@ constexpr int LDPAD = 0;
 // instruction: 1 KB of binary32 momentum).
 constexpr int ETILE = 64;
 constexpr int RTILE_R = 16, RTILE_C = 256;
+// Tall matrices in the bf16 working format: TBF_R x TBF_C tiles (8192
+// elements), staged through LDS as bf16 (two 128-element row runs per wave
+// and load, 128-byte U^T runs per store; 16.5 KB of LDS, about what a
+// 64 x 64 binary32 tile takes, so occupancy stays full).
+constexpr int TBF_R = 64, TBF_C = 128;
 // Dispatch order puts consecutive workgroups on different XCDs.
 constexpr int NUM_XCD = 8;
 
