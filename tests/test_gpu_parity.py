@@ -83,26 +83,32 @@ def test_dtypes_nesterov_scale(nesterov, pdt, gdt, rule):
                    param_bf16=pdt == torch.bfloat16, scale_rule=rule)
 
 
-def test_strided_rows():
-    _announce("strided rows")
+@pytest.mark.parametrize("prec,gdt,nesterov", [(mb.NS_BF16X3, torch.bfloat16, 1), (mb.NS_BF16, torch.bfloat16, 1),
+                                               (mb.NS_BF16, torch.float32, 0)])
+def test_strided_rows(prec, gdt, nesterov):
+    """Row strides beyond cols: the momentum pass takes its element path (no
+    vector loads); (100, 90) and (300, 130) are tall, so U leaves through the
+    LDS transpose (64 x 64 binary32 tiles for split-bf16, 64 x 128 bf16-staged
+    tiles for bf16)."""
+    _announce(f"strided rows prec={prec} gdt={gdt} nesterov={nesterov}")
     dev = "cuda"
-    shapes = [(100, 90), (90, 333)]
+    shapes = [(100, 90), (90, 333), (300, 130)]
     lr = f32(0.02)
     ws_full = [torch.randn(r, c + 24) * 0.02 for r, c in shapes]
-    gs_full = [torch.randn(r, c + 8).to(torch.bfloat16) for r, c in shapes]
+    gs_full = [torch.randn(r, c + 8).to(gdt) for r, c in shapes]
     ms_full = [torch.randn(r, c + 4) for r, c in shapes]
     w_d = [w.to(dev) for w in ws_full]
     g_d = [g.to(dev) for g in gs_full]
     m_d = [m.to(dev) for m in ms_full]
     views = lambda ts: [t[:, :c] for t, (r, c) in zip(ts, shapes)]  # noqa: E731
     u_d = [torch.empty(s, device=dev) for s in shapes]
-    mb.muon_step_batched(views(w_d), views(g_d), views(m_d), lr=lr, beta=0.95, nesterov=1,
-                         ns_coeffs=MUON, ns_steps=5, precision=mb.NS_BF16X3, updates_out=u_d)
+    mb.muon_step_batched(views(w_d), views(g_d), views(m_d), lr=lr, beta=0.95, nesterov=nesterov,
+                         ns_coeffs=MUON, ns_steps=5, precision=prec, updates_out=u_d)
     torch.cuda.synchronize()
     for i, (r, c) in enumerate(shapes):
         check_step(ws_full[i][:, :c].numpy(), to_np(gs_full[i][:, :c]), ms_full[i][:, :c].numpy(),
                    to_np(w_d[i][:, :c]), to_np(m_d[i][:, :c]), to_np(u_d[i]), lr=lr, beta=0.95,
-                   nesterov=1, coeffs=MUON, steps=5, tol=PREC_TOL[mb.NS_BF16X3], param_bf16=False)
+                   nesterov=nesterov, coeffs=MUON, steps=5, tol=PREC_TOL[prec], param_bf16=False)
         # the padding columns beyond cols are untouched
         assert torch.equal(w_d[i][:, c:].cpu(), ws_full[i][:, c:])
         assert torch.equal(m_d[i][:, c:].cpu(), ms_full[i][:, c:])
