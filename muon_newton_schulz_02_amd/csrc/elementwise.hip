@@ -5,7 +5,7 @@
 //    stores U into the workspace in the wide orientation X (m x n, m <= n;
 //    through an LDS transpose for tall matrices) in the Newton-Schulz storage
 //    format, zero-filling the padding; writes one binary32 sum of u^2 per
-//    4096-element tile (wavefront shuffles, then LDS across the four waves).
+//    tile (wavefront shuffles, then LDS across the four waves).
 //    Tall matrices go through an LDS transpose, in 64 x 128 tiles staged as
 //    bf16 for the bf16 working format (two 128-element row runs per wave and
 //    load) and in 64 x 64 binary32 tiles for the others; the rest in 16 x 256
