@@ -104,9 +104,39 @@ static bool in_one_alloc(const void* p, size_t n) {
 static void* g_scratch = nullptr;
 static bool g_check_buffers = false;   // grids: every workspace buffer and table inside one allocation
 
+static int g_mom_launches = 0;
+
 namespace muon {
-hipError_t launch_momentum(const MatDev*, const int32_t*, int32_t, int64_t, float, int32_t, int32_t, int32_t, float*,
-                           hipStream_t) { return hipSuccess; }
+// The walk of momentum_kernel: workgroup b takes tile b - etile_off[i] of
+// the matrix i whose range holds b, row-major over the tiles of the matrix's
+// padded natural shape, in the tile shape of its path (16 x 256 for
+// matrices iterated untransposed; for tall ones 64 x 128 in the bf16 working
+// format, 64 x 64 otherwise).  The tables must give every matrix exactly
+// that many tiles with that row length, so that the walk covers each padded
+// shape once; the U^T / U stores stay inside the X buffer.
+hipError_t launch_momentum(const MatDev* mats, const int32_t* etile_off, int32_t count, int64_t total_tiles, float,
+                           int32_t, int32_t, int32_t mode, float*, hipStream_t) {
+  ++g_mom_launches;
+  CHECK(etile_off[0] == 0 && etile_off[count] == total_tiles, "momentum: %lld tiles, offsets end at %d",
+        (long long)total_tiles, etile_off[count]);
+  for (int i = 0; i < count; ++i) {
+    const MatDev& md = mats[i];
+    const bool tr = md.transposed != 0;
+    const int th = !tr ? RTILE_R : (md.prec == PREC_BF16 ? TBF_R : ETILE);
+    const int tw = !tr ? RTILE_C : (md.prec == PREC_BF16 ? TBF_C : ETILE);
+    const int rp = tr ? md.Np : md.Mp, cp = tr ? md.Mp : md.Np;
+    CHECK(tr == (md.rows > md.cols) && md.rows <= rp && md.cols <= cp, "momentum: matrix %d shape", i);
+    CHECK(rp % th == 0 && cp % tw == 0, "momentum: matrix %d padded %d x %d not in %d x %d tiles", i, rp, cp, th, tw);
+    CHECK(md.etile_cols == cp / tw, "momentum: matrix %d has %d tiles per row, the walk needs %d", i, md.etile_cols,
+          cp / tw);
+    CHECK(etile_off[i + 1] - etile_off[i] == (rp / th) * (cp / tw), "momentum: matrix %d has %d tiles, the walk %d",
+          i, etile_off[i + 1] - etile_off[i], (rp / th) * (cp / tw));
+    if (mode != 2)   // the last X element any tile writes
+      CHECK(ws_index(md.prec, md.Mp - 1, md.Np - 1, md.ldx) < int64_t(md.Mp) * md.ldx,
+            "momentum: matrix %d stores beyond X", i);
+  }
+  return hipSuccess;
+}
 hipError_t launch_norm_finalize(const int32_t*, int32_t, const float*, MatScal*, float*, hipStream_t) { return hipSuccess; }
 hipError_t launch_writeback_direct(const MatDev*, const int32_t*, int32_t, int64_t, const MatScal*, float, int32_t,
                                    const float2*, hipStream_t) { return hipSuccess; }
@@ -279,7 +309,7 @@ static void grid_case(const char* name, const std::vector<Shape>& shapes, double
   printf("CASE grids %s (%d matrices)\n", name, n);
   g_count = n;
   g_max_imbalance = 0;
-  const int before = g_phase_launches;
+  const int before = g_phase_launches, mom_before = g_mom_launches;
   const muon_ns_coeffs co{3.4445f, -4.775f, 2.0315f};
   muon_step_options o{};
   o.launch_mode = MUON_LAUNCH_PHASE_GRIDS;
@@ -287,6 +317,7 @@ static void grid_case(const char* name, const std::vector<Shape>& shapes, double
                                               &o, nullptr, nullptr);
   CHECK(st == MUON_OK, "status %d: %s", int(st), muon_last_error());
   CHECK(g_phase_launches > before, "no phase launched");
+  CHECK(g_mom_launches > mom_before, "no momentum pass launched");
   CHECK(g_max_imbalance <= max_imbalance, "makespan / mean %.3f above %.3f", g_max_imbalance, max_imbalance);
   printf("  worst makespan / mean %.3f\n", g_max_imbalance);
 }
