@@ -5,6 +5,9 @@
 //   - per-phase grids: every tile of every matrix visited exactly once, no
 //     tile outside its matrix, GRAM/POLY only on or above the diagonal, and
 //     the busiest workgroup's work against the mean (load balance);
+//   - momentum pass: every matrix's elementwise tile count and row length
+//     are those of the kernel's tile shape for its path, and its U stores
+//     stay inside the X buffer;
 //   - persistent chain: every wait names a counter that receives exactly the
 //     awaited number of signals, every buffer an item uses lies inside a
 //     workspace allocation, and a round-robin scheduler over the per-XCD
