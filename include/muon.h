@@ -298,11 +298,12 @@ muon_status muon_ns_batched(const void* const* x_in, float* const* x_out,
  * `count` floats), summed as binary32 partials per tile (16 x 256, or
  * 64 x 128 for matrices with more rows than columns; the step's own
  * reduction takes 64 x 64 tiles for tall matrices in the binary32 and split
- * formats) and reduced in a fixed order (deterministic).  x_in[i] is grad_dtype with row stride
- * ld_grad.  The same reduction gives the step's normalisation X = U /
- * (||U||_F + 1e-7); the pages leave the normalisation open, and dividing by
- * the Frobenius norm bounds every singular value by 1, which the iteration
- * needs to converge (Higham, Functions of Matrices, ch. 8).  Errors:
+ * formats) and reduced in a fixed order (deterministic).  x_in[i] is
+ * grad_dtype with row stride ld_grad.  The same reduction gives the step's
+ * normalisation X = U / (||U||_F + 1e-7); the pages leave the normalisation
+ * open, and dividing by the Frobenius norm bounds every singular value by
+ * 1, which the iteration needs to converge (Higham, Functions of Matrices,
+ * ch. 8).  Errors:
  * INVALID_ARGUMENT (NULL arrays or entries, bad sizes), UNSUPPORTED
  * (dtype, alignment), ALIAS (norms_out overlaps an input), HIP.           */
 muon_status muon_frobenius_norms(const void* const* x_in, const muon_matrix_desc* shapes,
