@@ -31,7 +31,7 @@ def _inputs(shapes, seed, pdt, gdt, m_random=True):
     return ws, gs, ms
 
 
-SHAPES = [(1, 1), (1, 300), (300, 1), (130, 257), (257, 130), (64, 64), (520, 300), (256, 768)]
+SHAPES = [(1, 1), (1, 300), (300, 1), (130, 257), (257, 130), (64, 64), (520, 300), (256, 768), (4097, 5)]
 
 
 @pytest.mark.parametrize("prec", [mb.NS_F32, mb.NS_BF16X3, mb.NS_BF16])
